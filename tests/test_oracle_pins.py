@@ -1,0 +1,465 @@
+"""Pins for the fp64 oracle: each check ties it to something other than itself -
+closed forms, pure-Python brute force on tiny inputs, independent library
+routines (torch's CPU attention and softmax in float64, sorted()), invariants the
+pages state, and hand-derived fixtures under tests/golden/.
+
+The pages print no worked example with intermediate values, so no pin compares
+against numbers printed on the pages; the hand fixtures are derivations from
+the definitions they state."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dlm_oracle as O
+from sparse_query_attention_dlm_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# pure-Python brute force (no NumPy arithmetic)
+# --------------------------------------------------------------------------
+def bf_cos(a, b):
+    dot = sum(x * y for x, y in zip(a, b))
+    na = math.sqrt(sum(x * x for x in a))
+    nb = math.sqrt(sum(y * y for y in b))
+    return 0.0 if na * nb == 0 else dot / (na * nb)
+
+
+def bf_attention_row(q, keys, vals, scale):
+    s = [scale * sum(qi * ki for qi, ki in zip(q, k)) for k in keys]
+    m = max(s)
+    e = [math.exp(x - m) for x in s]
+    z = sum(e)
+    o = [sum(e[j] / z * vals[j][d] for j in range(len(keys))) for d in range(len(vals[0]))]
+    return o, m + math.log(z)
+
+
+def to_list(a):
+    return np.asarray(a, dtype=np.float64).tolist()
+
+
+# --------------------------------------------------------------------------
+# cosine
+# --------------------------------------------------------------------------
+def test_cosine_closed_forms():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((3, 5, 7))
+    assert np.allclose(O.cosine_scores(x, x), 1.0, atol=1e-15)
+    assert np.allclose(O.cosine_scores(x, -x), -1.0, atol=1e-15)
+    assert np.allclose(O.cosine_scores(x, 3.5 * x), 1.0, atol=1e-15)   # positive scaling
+    e = np.eye(4)
+    assert np.allclose(O.cosine_scores(e[0], e[1]), 0.0)
+    assert O.cosine_scores(np.array([1.0, 0.0]), np.array([1.0, 1.0])) == pytest.approx(1 / math.sqrt(2), abs=1e-15)
+    assert O.cosine_scores(np.array([1.0, 2, 3]), np.array([4.0, 5, 6])) == pytest.approx(
+        32 / (math.sqrt(14) * math.sqrt(77)), abs=1e-15)
+    # a zero vector on either side scores 0
+    z = np.zeros(6)
+    assert O.cosine_scores(z, np.ones(6)) == 0.0 and O.cosine_scores(np.ones(6), z) == 0.0
+
+
+def test_cosine_brute_force():
+    rng = np.random.default_rng(1)
+    a, b = rng.standard_normal((2, 4, 9))
+    got = O.cosine_scores(a[None], b[None])[0]
+    for i in range(4):
+        assert got[i] == pytest.approx(bf_cos(to_list(a[i]), to_list(b[i])), abs=1e-14)
+
+
+def test_planted_tiny_selects_exactly_the_redrawn_rows():
+    inp = W.cosine_step_inputs(W.TINY_FP32)
+    s = O.cosine_scores(inp.cur, inp.prev)
+    idx, counts, offsets = O.compact(s, 0, W.TINY_FP32.S, W.TINY_FP32.tau)
+    assert counts.tolist() == [16]
+    assert idx.tolist() == inp.redrawn[0].tolist()
+    stable = np.setdiff1d(np.arange(128), inp.redrawn[0])
+    assert s[0, stable].min() > 0.999 and s[0, inp.redrawn[0]].max() < 0.5
+
+
+def test_planted_bf16_selects_exactly_the_redrawn_rows():
+    sh = W.BF16_S1024
+    inp = W.cosine_step_inputs(sh, D=512)      # reduced hidden size, same structure
+    s = O.cosine_scores(inp.cur, inp.prev)
+    idx, counts, _ = O.compact(s, 0, sh.S, sh.tau)
+    assert counts.tolist() == [102]
+    assert idx.tolist() == inp.redrawn[0].tolist()
+
+
+# --------------------------------------------------------------------------
+# compaction
+# --------------------------------------------------------------------------
+def test_compact_brute_force_and_strictness():
+    rng = np.random.default_rng(2)
+    sc = rng.random((3, 50))
+    sc[1, 7] = 0.5                                  # exactly at the threshold: not selected
+    lo, hi, tau = 5, 44, 0.5
+    idx, counts, offsets = O.compact(sc, lo, hi, tau)
+    exp = [[i for i in range(lo, hi) if sc[b, i] < tau] for b in range(3)]
+    assert counts.tolist() == [len(e) for e in exp]
+    assert offsets.tolist() == [0, len(exp[0]), len(exp[0]) + len(exp[1]), sum(map(len, exp))]
+    assert idx.tolist() == exp[0] + exp[1] + exp[2]
+    assert 7 not in exp[1]
+
+
+def test_compact_empty_and_full():
+    sc = np.full((2, 10), 0.7)
+    idx, counts, offsets = O.compact(sc, 0, 10, 0.7)
+    assert idx.size == 0 and counts.tolist() == [0, 0] and offsets.tolist() == [0, 0, 0]
+    idx, counts, offsets = O.compact(sc, 2, 6, 0.8)
+    assert idx.tolist() == [2, 3, 4, 5, 2, 3, 4, 5] and offsets.tolist() == [0, 4, 8]
+
+
+# --------------------------------------------------------------------------
+# confidence
+# --------------------------------------------------------------------------
+def test_confidence_uniform_logits_tie_to_lowest_index():
+    V, D = 37, 8
+    mp, a, gap = O.confidence(np.ones((3, D)), np.zeros((V, D)))
+    assert np.allclose(mp, 1.0 / V) and a.tolist() == [0, 0, 0] and np.all(gap == 0)
+
+
+def test_confidence_closed_form_and_brute_force():
+    V, D = 11, 4
+    w = np.zeros((V, D))
+    w[6, 0] = 1.0                      # logit of token 6 = x0, others 0
+    x = np.array([[10.0, 0, 0, 0], [-3.0, 1, 2, 3]])
+    mp, a, gap = O.confidence(x, w)
+    assert a.tolist() == [6, 0]
+    assert mp[0] == pytest.approx(math.exp(10) / (math.exp(10) + V - 1), rel=1e-14)
+    assert mp[1] == pytest.approx(1.0 / (math.exp(-3) + V - 1), rel=1e-14)
+    assert gap[0] == pytest.approx(10.0) and gap[1] == pytest.approx(0.0)
+    rng = np.random.default_rng(3)
+    x, w = rng.standard_normal((5, 6)), rng.standard_normal((9, 6))
+    mp, a, _ = O.confidence(x, w)
+    for r in range(5):
+        z = [sum(x[r, d] * w[v, d] for d in range(6)) for v in range(9)]
+        zm = max(z)
+        assert a[r] == z.index(zm)
+        assert mp[r] == pytest.approx(1.0 / sum(math.exp(t - zm) for t in z), rel=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Q/K/V projection and scatter
+# --------------------------------------------------------------------------
+def test_qkv_identity_blocks_pin_head_and_block_order():
+    B, S, Hq, Hkv, hd = 2, 6, 2, 1, 3
+    D = Hq * hd
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((B, S, D))
+    I = np.eye(D)
+    w = np.concatenate([I, 2 * I[:hd], 3 * I[hd:2 * hd]])     # W_q = I, W_k = 2*(first hd dims), W_v = 3*(next hd)
+    idx = np.array([1, 4, 0, 5], dtype=np.int32)
+    offsets = np.array([0, 2, 4], dtype=np.int32)
+    kc0 = rng.standard_normal((B, S, Hkv, hd))
+    vc0 = rng.standard_normal((B, S, Hkv, hd))
+    q, kc, vc = O.qkv_project_scatter(x, idx, offsets, w, Hq, Hkv, hd, kc0, vc0)
+    assert np.allclose(q[0].reshape(-1), x[0, 1]) and np.allclose(q[3].reshape(-1), x[1, 5])
+    assert np.allclose(q[1, 1], x[0, 4, hd:])             # head 1 = dims [hd, 2hd)
+    assert np.allclose(kc[0, 4, 0], 2 * x[0, 4, :hd]) and np.allclose(vc[1, 0, 0], 3 * x[1, 0, hd:])
+    untouched = np.ones((B, S), bool)
+    untouched[0, [1, 4]] = untouched[1, [0, 5]] = False
+    assert np.array_equal(kc[untouched], kc0[untouched]) and np.array_equal(vc[untouched], vc0[untouched])
+
+
+def test_qkv_brute_force():
+    B, S, D, Hq, Hkv, hd = 1, 4, 5, 2, 1, 2
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((B, S, D))
+    w = rng.standard_normal(((Hq + 2 * Hkv) * hd, D))
+    idx, offsets = np.array([0, 3], np.int32), np.array([0, 2], np.int32)
+    q, kc, vc = O.qkv_project_scatter(x, idx, offsets, w, Hq, Hkv, hd,
+                                      np.zeros((B, S, Hkv, hd)), np.zeros((B, S, Hkv, hd)))
+    for r, i in enumerate([0, 3]):
+        y = [sum(x[0, i, d] * w[n, d] for d in range(D)) for n in range(w.shape[0])]
+        assert np.allclose(q[r].reshape(-1), y[:4], atol=1e-13)
+        assert np.allclose(kc[0, i].reshape(-1), y[4:6], atol=1e-13)
+        assert np.allclose(vc[0, i].reshape(-1), y[6:8], atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# partial attention
+# --------------------------------------------------------------------------
+def test_attention_brute_force_tiny():
+    B, S, Hq, Hkv, hd = 2, 7, 4, 2, 3
+    rng = np.random.default_rng(6)
+    kc, vc = rng.standard_normal((2, B, S, Hkv, hd))
+    idx = np.array([2, 6, 0, 1, 3], np.int32)
+    offsets = np.array([0, 2, 5], np.int32)
+    q = rng.standard_normal((5, Hq, hd))
+    scale = 0.61
+    o, lse = O.partial_attention(q, idx, offsets, kc, vc, Hq, Hkv, scale)
+    for b in range(B):
+        for r in range(offsets[b], offsets[b + 1]):
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                ob, lb = bf_attention_row(to_list(q[r, h]), to_list(kc[b, :, g]), to_list(vc[b, :, g]), scale)
+                assert np.allclose(o[r, h], ob, atol=1e-13) and lse[r, h] == pytest.approx(lb, abs=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(7)
+    hd = 4
+    # one key: o = v, lse = scale * q.k
+    k, v, q = rng.standard_normal((3, hd))
+    o, lse = O.partial_attention(q[None, None], [0], [0, 1], k[None, None, None], v[None, None, None], 1, 1, 0.5)
+    assert np.allclose(o[0, 0], v) and lse[0, 0] == pytest.approx(0.5 * q @ k)
+    # identical keys: o = mean(V), lse = s + log S
+    S = 6
+    kc = np.tile(k, (1, S, 1, 1))
+    vc = rng.standard_normal((1, S, 1, hd))
+    o, lse = O.partial_attention(q[None, None], [0], [0, 1], kc, vc, 1, 1, 0.5)
+    assert np.allclose(o[0, 0], vc[0, :, 0].mean(0)) and lse[0, 0] == pytest.approx(0.5 * q @ k + math.log(S))
+    # q = 0: uniform weights, lse = log S
+    o, lse = O.partial_attention(np.zeros((1, 1, hd)), [0], [0, 1], rng.standard_normal((1, S, 1, hd)), vc, 1, 1, 0.5)
+    assert np.allclose(o[0, 0], vc[0, :, 0].mean(0)) and lse[0, 0] == pytest.approx(math.log(S))
+
+
+def test_attention_gqa_head_map():
+    # KV head 0 values all 1, KV head 1 values all 2: query heads 0,1 -> 1 and 2,3 -> 2
+    B, S, Hq, Hkv, hd = 1, 5, 4, 2, 2
+    rng = np.random.default_rng(8)
+    kc = rng.standard_normal((B, S, Hkv, hd))
+    vc = np.zeros((B, S, Hkv, hd))
+    vc[:, :, 0] = 1.0
+    vc[:, :, 1] = 2.0
+    o, _ = O.partial_attention(rng.standard_normal((1, Hq, hd)), [3], [0, 1], kc, vc, Hq, Hkv, 1.0)
+    assert np.allclose(o[0, :2], 1.0) and np.allclose(o[0, 2:], 2.0)
+
+
+def test_full_selection_equals_library_dense_attention():
+    """All positions selected: the step equals plain dense bidirectional attention
+    computed by torch's CPU scaled_dot_product_attention in float64."""
+    B, S, D, Hq, Hkv, hd = 2, 9, 12, 4, 2, 3
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((B, S, D))
+    w = rng.standard_normal(((Hq + 2 * Hkv) * hd, D)) / 3
+    idx = np.tile(np.arange(S, dtype=np.int32), B)
+    offsets = np.arange(B + 1, dtype=np.int32) * S
+    z = np.zeros((B, S, Hkv, hd))
+    q, kc, vc = O.qkv_project_scatter(x, idx, offsets, w, Hq, Hkv, hd, z, z)
+    o, _ = O.partial_attention(q, idx, offsets, kc, vc, Hq, Hkv, 1 / math.sqrt(hd))
+    xt = torch.tensor(x)
+    y = xt @ torch.tensor(w).T
+    Q = y[..., :Hq * hd].reshape(B, S, Hq, hd).transpose(1, 2)
+    K = y[..., Hq * hd:(Hq + Hkv) * hd].reshape(B, S, Hkv, hd).transpose(1, 2)
+    V = y[..., (Hq + Hkv) * hd:].reshape(B, S, Hkv, hd).transpose(1, 2)
+    K = K.repeat_interleave(Hq // Hkv, dim=1)
+    V = V.repeat_interleave(Hq // Hkv, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V).transpose(1, 2).reshape(B * S, Hq, hd)
+    assert np.allclose(o, ref.numpy(), atol=1e-12)
+
+
+def test_zero_selection_returns_cache():
+    rng = np.random.default_rng(10)
+    B, S, D, Hq, Hkv, hd = 1, 8, 6, 2, 2, 3
+    cur = rng.standard_normal((B, S, D))
+    w = rng.standard_normal(((Hq + 2 * Hkv) * hd, D))
+    kc, vc, out = (rng.standard_normal((B, S, Hkv, hd)), rng.standard_normal((B, S, Hkv, hd)),
+                   rng.standard_normal((B, S, Hq * hd)))
+    r = O.cosine_step(cur, cur, w, Hq, Hkv, hd, tau=0.5, k_cache=kc, v_cache=vc, out_cache=out)
+    assert r["idx"].size == 0
+    assert np.array_equal(r["k_cache"], kc) and np.array_equal(r["v_cache"], vc) and np.array_equal(r["out_cache"], out)
+
+
+def test_full_selection_step_equals_full_recompute():
+    rng = np.random.default_rng(11)
+    B, S, D, Hq, Hkv, hd = 2, 6, 8, 2, 1, 4
+    cur = rng.standard_normal((B, S, D))
+    w = rng.standard_normal(((Hq + 2 * Hkv) * hd, D)) / 2
+    wo = rng.standard_normal((5, Hq * hd))
+    junk = lambda *s: rng.standard_normal(s)
+    r = O.cosine_step(cur, -cur, w, Hq, Hkv, hd, tau=0.5, k_cache=junk(B, S, Hkv, hd),
+                      v_cache=junk(B, S, Hkv, hd), out_cache=junk(B, S, 5), w_o=wo)
+    kc, vc, out = O.full_recompute_caches(cur, w, Hq, Hkv, hd, 1 / math.sqrt(hd), wo)
+    assert r["counts"].tolist() == [S, S]
+    assert np.allclose(r["k_cache"], kc) and np.allclose(r["out_cache"], out, atol=1e-12)
+
+
+def test_output_scatter_with_wo_brute_force():
+    rng = np.random.default_rng(12)
+    o = rng.standard_normal((2, 2, 3))
+    wo = rng.standard_normal((4, 6))
+    out0 = rng.standard_normal((1, 5, 4))
+    out = O.output_scatter(o, np.array([1, 3], np.int32), np.array([0, 2], np.int32), out0, wo)
+    for r, i in enumerate([1, 3]):
+        ctx = o[r].reshape(-1).tolist()
+        y = [sum(ctx[c] * wo[n, c] for c in range(6)) for n in range(4)]
+        assert np.allclose(out[0, i], y, atol=1e-13)
+    assert np.array_equal(out[0, [0, 2, 4]], out0[0, [0, 2, 4]])
+
+
+# --------------------------------------------------------------------------
+# column sums and top-k
+# --------------------------------------------------------------------------
+def _attn_inputs(B, S, nq, Hq, Hkv, hd, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B * nq, Hq, hd))
+    kc = rng.standard_normal((B, S, Hkv, hd))
+    vc = rng.standard_normal((B, S, Hkv, hd))
+    idx = np.tile(np.arange(S - nq, S, dtype=np.int32), B)
+    offsets = np.arange(B + 1, dtype=np.int32) * nq
+    return q, kc, vc, idx, offsets
+
+
+def test_colsum_sum_invariant_and_library_softmax():
+    B, S, nq, Hq, Hkv, hd = 2, 11, 6, 4, 2, 3
+    q, kc, vc, idx, offsets = _attn_inputs(B, S, nq, Hq, Hkv, hd, 13)
+    scale = 0.7
+    _, lse = O.partial_attention(q, idx, offsets, kc, vc, Hq, Hkv, scale)
+    c = O.column_sums(q, offsets, kc, lse, Hq, Hkv, scale)
+    assert np.allclose(c.sum(axis=1), Hq * nq, atol=1e-12)          # each query row sums to 1 per head
+    for b in range(B):
+        Q = torch.tensor(q[b * nq:(b + 1) * nq]).transpose(0, 1)      # [Hq, nq, hd]
+        K = torch.tensor(kc[b]).transpose(0, 1).repeat_interleave(Hq // Hkv, 0)
+        P = torch.softmax(scale * Q @ K.transpose(1, 2), dim=-1)      # [Hq, nq, S]
+        assert np.allclose(c[b], P.sum(dim=(0, 1)).numpy(), atol=1e-12)
+
+
+def test_colsum_zero_queries_uniform_and_topk_tiebreak():
+    B, S, nq, Hq, Hkv, hd = 2, 16, 12, 3, 3, 4
+    q, kc, vc, idx, offsets = _attn_inputs(B, S, nq, Hq, Hkv, hd, 14)
+    q[:] = 0.0
+    _, lse = O.partial_attention(q, idx, offsets, kc, vc, Hq, Hkv, 0.5)
+    c = O.column_sums(q, offsets, kc, lse, Hq, Hkv, 0.5)
+    assert np.allclose(c, Hq * nq / S, atol=1e-13)
+    ti, tv = O.topk_keys(np.full((B, S), Hq * nq / S), 4, 16, 5)       # all equal -> lowest indices
+    assert ti.tolist() == [[4, 5, 6, 7, 8]] * 2
+
+
+def test_topk_brute_force():
+    rng = np.random.default_rng(15)
+    c = rng.integers(0, 4, size=(3, 20)).astype(np.float64)          # many ties
+    ti, tv = O.topk_keys(c, 3, 18, 7)
+    for b in range(3):
+        exp = sorted(range(3, 18), key=lambda j: (-c[b, j], j))[:7]
+        assert ti[b].tolist() == exp and tv[b].tolist() == [c[b, j] for j in exp]
+
+
+# --------------------------------------------------------------------------
+# stable prefix
+# --------------------------------------------------------------------------
+def bf_prefix(argmax_hist, maxprob, L, conf, min_commit, S_gen, W):
+    """Brute force: argmax_hist is the list of per-step argmax rows (carry-forward
+    already applied), newest last."""
+    last = argmax_hist[-W:]
+    if len(last) < W:
+        last = [[-1] * S_gen] * (W - len(last)) + last
+    i = L
+    while i < S_gen:
+        col = [row[i] for row in last]
+        if not (all(v == col[0] for v in col) and col[0] != -1 and maxprob[i] >= conf):
+            break
+        i += 1
+    if min_commit and i == L and L < S_gen:
+        i = L + 1
+    return i
+
+
+def test_stable_prefix_brute_force_random_histories():
+    rng = np.random.default_rng(16)
+    B, S, gen_lo, W = 4, 30, 6, 3
+    S_gen = S - gen_lo
+    for trial in range(20):
+        ring = np.full((B, S_gen, W), -1, np.int64)
+        committed = np.zeros(B, np.int64)
+        hist = [[] for _ in range(B)]
+        min_commit = trial % 2
+        for t in range(6):
+            am = rng.integers(0, 2, size=(B, S)).astype(np.int64)     # few tokens -> frequent repeats
+            mp = rng.choice([0.5, 0.9, 0.95], size=(B, S))
+            ring, new = O.stable_prefix_step(am, mp, ring, t, gen_lo, S, 0.9, min_commit, committed)
+            for b in range(B):
+                hist[b].append(am[b, gen_lo:].tolist())
+                exp = bf_prefix(hist[b], mp[b, gen_lo:].tolist(), int(committed[b]), 0.9, min_commit, S_gen, W)
+                assert new[b] == exp
+            committed = new
+
+
+def test_stable_prefix_closed_forms():
+    B, S, W = 2, 10, 3
+    ring = np.full((B, S, W), 7, np.int64)
+    am = np.full((B, S), 7)
+    mp = np.full((B, S), 0.95)
+    _, new = O.stable_prefix_step(am, mp, ring, 5, 0, S, 0.9, 0, np.array([0, 4]))
+    assert new.tolist() == [S, S]                                    # all stable
+    mp[:] = 0.5
+    _, new = O.stable_prefix_step(am, mp, ring, 5, 0, S, 0.9, 0, np.array([3, S]))
+    assert new.tolist() == [3, S]                                    # none stable
+    _, new = O.stable_prefix_step(am, mp, ring, 5, 0, S, 0.9, 1, np.array([3, S]))
+    assert new.tolist() == [4, S]                                    # fallback commits one, never past S_gen
+    mp[:] = 0.9
+    _, new = O.stable_prefix_step(am, mp, ring, 5, 0, S, 0.9, 0, np.array([0, 0]))
+    assert new.tolist() == [S, S]                                    # >= is inclusive
+
+
+def test_admissible_frontiers():
+    st = np.array([1, 1, 2, 1, 0, 1])
+    assert O.admissible_frontiers({0}, st, 6, 0) == {2, 4}
+    assert O.admissible_frontiers({4}, st, 6, 1) == {5}
+    assert O.admissible_frontiers({5}, st, 6, 0) == {6}
+
+
+def test_lsp_planted_closed_form():
+    """Planted rows before P_b have a dominant token: argmax = target and
+    max-prob >= 0.9; row P_b is diffuse.  Then L_t = min(P_b, first i >= L_{t-1}
+    whose first evaluation step e_i > t-2)."""
+    D = 256
+    sh = W.LspShape(**{**W.LSP_COMMIT.__dict__, "B": 3, "S": 160, "prompt": 32, "D": D, "V": 2048,
+                       "w_std": 0.02 * math.sqrt(4096 / D), "steps": 8})
+    inp = W.lsp_inputs(sh)
+    S_gen = inp.S_gen
+    ring = np.full((sh.B, S_gen, sh.W), -1, np.int64)
+    argmax = np.full((sh.B, sh.S), -1, np.int64)
+    maxprob = np.zeros((sh.B, sh.S))
+    committed = np.zeros(sh.B, np.int64)
+    first_eval = np.full((sh.B, S_gen), 10 ** 9)
+    for t in range(sh.steps):
+        h = inp.hidden(t)
+        rows = inp.active_rows(t)
+        for b in range(sh.B):
+            mp, a, _ = O.confidence(h[b, rows[b]], inp.w_lm)
+            argmax[b, rows[b]] = a
+            maxprob[b, rows[b]] = mp
+            g = rows[b] - sh.prompt
+            first_eval[b, g] = np.minimum(first_eval[b, g], t)
+            planted = g < inp.frontier[b]
+            assert np.array_equal(a[planted], inp.targets[b, g[planted]])
+            assert np.all(mp[planted] >= 0.9)
+            assert np.all(mp[g == inp.frontier[b]] < 0.9)
+        ring, new = O.stable_prefix_step(argmax, maxprob, ring, t, sh.prompt, sh.S, sh.conf, 0, committed)
+        for b in range(sh.B):
+            i = int(committed[b])
+            while i < S_gen and first_eval[b, i] <= t - 2:
+                i += 1
+            assert new[b] == min(int(inp.frontier[b]), i)
+        committed = new
+    assert committed.max() > 0
+
+
+# --------------------------------------------------------------------------
+# hand-derived fixtures
+# --------------------------------------------------------------------------
+def test_golden_hand_fixtures():
+    with open(os.path.join(GOLDEN, "hand_cases.json")) as f:
+        cases = json.load(f)
+    for c in cases["attention"]:
+        q = np.array(c["q"], dtype=np.float64)[None, None]
+        k = np.array(c["k"], dtype=np.float64)[None, :, None]
+        v = np.array(c["v"], dtype=np.float64)[None, :, None]
+        o, lse = O.partial_attention(q, [0], [0, 1], k, v, 1, 1, c["scale"])
+        assert np.allclose(o[0, 0], c["o"], atol=1e-12), c["name"]
+        assert lse[0, 0] == pytest.approx(c["lse"], abs=1e-12), c["name"]
+    for c in cases["cosine"]:
+        assert O.cosine_scores(np.array(c["a"]), np.array(c["b"])) == pytest.approx(c["cos"], abs=1e-15)
+    for c in cases["colsum"]:
+        q = np.array(c["q"], dtype=np.float64)[:, None]
+        k = np.array(c["k"], dtype=np.float64)[None, :, None]
+        nq = q.shape[0]
+        v = np.zeros_like(k)
+        _, lse = O.partial_attention(q, list(range(nq)), [0, nq], k, v, 1, 1, c["scale"])
+        col = O.column_sums(q, [0, nq], k, lse, 1, 1, c["scale"])
+        assert np.allclose(col[0], c["c"], atol=1e-12), c["name"]
