@@ -1,0 +1,218 @@
+/*
+ * dlm.h - C ABI of the sparse-query denoising step for MI355X (gfx950).
+ *
+ * One denoising step of a masked diffusion LM that re-processes only the
+ * tokens that are still changing:
+ *   1. score every token's stability (cosine against the previous step, or the
+ *      model's max-softmax confidence)                 -> dlm_saliency_select
+ *   2. compact the selected positions into an index list (same call)
+ *   3. recompute Q/K/V for only those rows and scatter K/V into the
+ *      persistent full-length cache                     -> dlm_gather_qkv_scatter_kv
+ *   4. bidirectional attention of the selected queries over all keys, with
+ *      the outputs scattered back into the cached activations
+ *                                                       -> dlm_partial_attn
+ *      optional: per-key attention column sums + top-k  -> dlm_attn_colsum
+ *      optional: longest-stable-prefix commit           -> dlm_stable_prefix
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or retains caller memory.  Tensors are
+ *     dense, row-major, in the layouts stated per argument, and 16-byte
+ *     aligned.
+ *   - `dtype` is DLM_F32 (float) or DLM_BF16 (bfloat16 storage, float32
+ *     accumulation, bf16 results rounded to nearest-even).
+ *   - Weights are stored output-major: row n holds the D input weights of
+ *     output feature n (so y = x . W^T).
+ *   - Selected rows are passed as (idx, offsets): idx int32 holds positions
+ *     in ascending order per batch row, packed batch-major; offsets int32
+ *     [B+1] is the exclusive prefix sum of the per-row counts.  Both live on
+ *     the device; `max_rows` is a host-side upper bound on offsets[B] used to
+ *     size launch grids (work beyond the device count is skipped on the GPU),
+ *     so no call synchronises with the host.  With max_rows == 0 a call
+ *     does nothing and its row arrays (idx, offsets, per-row outputs) may be NULL.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the null stream), allocates nothing, and returns a status code.
+ *     Argument validation happens on the host before any launch: on failure
+ *     nothing has been enqueued.  dlm_last_error() gives a thread-local text
+ *     describing the last failure.
+ *   - `workspace` is caller-owned device scratch of at least the size the
+ *     matching *_workspace_size() query returns.  It must be zero-filled once
+ *     after allocation; every call leaves its internal counters at zero
+ *     again.  Calls that overlap in time must not share a workspace.
+ */
+#ifndef DLM_H
+#define DLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DLM_OK 0
+#define DLM_ERR_INVALID_ARG 1   /* null pointer, bad shape, misalignment       */
+#define DLM_ERR_UNSUPPORTED 2   /* valid request this build does not implement  */
+#define DLM_ERR_WORKSPACE 3     /* workspace missing or too small               */
+#define DLM_ERR_HIP 4           /* a HIP launch or runtime call failed          */
+
+/* element types */
+#define DLM_F32 0
+#define DLM_BF16 1
+
+/* scoring modes of dlm_saliency_select */
+#define DLM_SCORE_COSINE 0
+#define DLM_SCORE_CONFIDENCE 1
+#define DLM_SCORE_GIVEN 2
+
+const char* dlm_status_string(int status);
+const char* dlm_last_error(void);
+/* Version string of the library build. */
+const char* dlm_version(void);
+
+/* ------------------------------------------------------------------------
+ * dlm_saliency_select
+ *
+ * Scores token stability and compacts the positions to recompute.
+ * Follows: "DyLLM: Efficient Diffusion LLM Inference via Saliency-based
+ * Token Selection and Partial Attention", Methodologie 1 (temporal cosine
+ * similarity per token between consecutive steps; low similarity = salient
+ * = recomputed); "Accelerating Diffusion Large Language Models with SlowFast
+ * Sampling", Metodologia, certainty principle (max predicted confidence);
+ * "Stopping Computation for Converged Tokens in Masked Diffusion-LM
+ * Decoding", Methodik (unlocked positions are recomputed).
+ *
+ * mode DLM_SCORE_COSINE:  a = cur [B,S,D], b = prev [B,S,D] (dtype).
+ *     scores[b,i] = <cur,prev> / (|cur| |prev|) for i in [lo,hi) (0 when a
+ *     norm is 0), float32 accumulation.  `scores` may be NULL (then the
+ *     scores live in the workspace only).  Other entries are not written.
+ * mode DLM_SCORE_CONFIDENCE (dtype must be DLM_BF16):  a = hidden [B,S,D],
+ *     b = W_lm [V,D].  For the rows listed by (eval_idx, eval_offsets)
+ *     (at most max_eval of them) the logits z = h . W_lm^T are formed on the
+ *     matrix cores and reduced on the fly (never stored): scores[b,i] =
+ *     1 / sum_v exp(z_v - max z) (the max softmax probability) and
+ *     argmax[b,i] = lowest v attaining max z.  `scores` [B,S] f32 and
+ *     `argmax` [B,S] i32 are required and act as caches: entries of rows
+ *     not evaluated keep their values.  D % 64 == 0, V % 128 == 0.
+ * mode DLM_SCORE_GIVEN:  a = scores f32 [B,S] supplied by the caller
+ *     (e.g. 1 = locked, 0 = unlocked); b, scores, argmax unused.
+ *
+ * Compaction (all modes): position i in [lo,hi) of row b is selected iff
+ * score < threshold (strict).  idx int32 (capacity B*(hi-lo)) receives the
+ * selected positions ascending per row, packed batch-major; counts int32 [B];
+ * offsets int32 [B+1].
+ * ------------------------------------------------------------------------ */
+size_t dlm_select_workspace_size(int mode, int B, int S, int V, int max_eval);
+int dlm_saliency_select(int mode, int dtype, const void* a, const void* b,
+                        int B, int S, int D, int V,
+                        const int32_t* eval_idx, const int32_t* eval_offsets, int max_eval,
+                        int lo, int hi, float threshold,
+                        float* scores, int32_t* argmax,
+                        int32_t* idx, int32_t* counts, int32_t* offsets,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dlm_gather_qkv_scatter_kv
+ *
+ * Q/K/V projection of the selected rows only; K/V scattered into the
+ * persistent cache.  Follows: "Stopping Computation for Converged Tokens in
+ * Masked Diffusion-LM Decoding", Methodik, Kernprinzipien (locked positions
+ * skip their projections, their K/V stay cached); "DyLLM ...", Methodologie 1
+ * (stable tokens reuse cached activations).
+ *
+ * x [B,S,D]; w_qkv [(Hq+2*Hkv)*hd, D] output-major with rows [0,Hq*hd) =
+ * W_q, then W_k, then W_v; head h owns rows [h*hd,(h+1)*hd) of its block.
+ * For every selected row r = (b, i = idx[r]):
+ *   q_out[r, :, :]       = x[b,i] . W_q^T        q_out [max_rows, Hq, hd]
+ *   k_cache[b, i, :, :]  = x[b,i] . W_k^T        k_cache, v_cache [B,S,Hkv,hd]
+ *   v_cache[b, i, :, :]  = x[b,i] . W_v^T
+ * Cache rows that are not selected are not touched (byte-identical).
+ * bf16: D % 64 == 0, hd in {64,128}.  f32: D % 4 == 0.
+ * ------------------------------------------------------------------------ */
+int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D,
+                              const int32_t* idx, const int32_t* offsets, int max_rows,
+                              const void* w_qkv, int Hq, int Hkv, int hd,
+                              void* q_out, void* k_cache, void* v_cache,
+                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * dlm_partial_attn
+ *
+ * Bidirectional (unmasked) attention of the selected queries over all S
+ * keys, outputs scattered back.  Follows: "DyLLM ...", Methodologie 2 (salient
+ * path: attention rows fully recomputed for the selected tokens); "Stopping
+ * Computation ...", Methodik, Kernprinzipien (active tokens attend to the
+ * cached K/V of locked tokens; cost O(M N d)).
+ *
+ * q_sel [max_rows, Hq, hd] (rows in idx order); k_cache, v_cache
+ * [B,S,Hkv,hd]; query head h reads KV head h / (Hq/Hkv).  For each selected
+ * row r of batch row b and head h:
+ *   o_sel[r,h,:] = softmax_j(scale * q.K[b,j]) . V[b,j]   over all j < S
+ *   lse[r,h]     = natural-log log-sum-exp of the scaled scores (lse may be NULL)
+ * Output scatter (optional):
+ *   w_o == NULL, out_cache != NULL:  out_cache[b, idx[r], :] = concat_h o_sel[r,h,:]
+ *                                    (D_out must equal Hq*hd)
+ *   w_o != NULL:  out_cache[b, idx[r], :] = concat_h o_sel[r,h,:] . W_o^T,
+ *                 w_o [D_out, Hq*hd] output-major; out_cache required.
+ * Other out_cache rows are not touched.  hd in {64,128}.
+ * ------------------------------------------------------------------------ */
+size_t dlm_partial_attn_workspace_size(int dtype, int max_rows, int B, int S, int Hq, int Hkv,
+                                       int hd);
+int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int32_t* offsets,
+                     int max_rows, const void* k_cache, const void* v_cache,
+                     int B, int S, int Hq, int Hkv, int hd, float scale,
+                     void* o_sel, float* lse,
+                     const void* w_o, int D_out, void* out_cache,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dlm_attn_colsum
+ *
+ * Per-key attention column sums and the top-k keys.  Follows: "Attention-
+ * Based Sampler for Diffusion Language Models", Methodologie 1-2 (decode
+ * tokens in descending order of the column sums of the attention matrix,
+ * aggregated over heads).
+ *
+ * colsum[b,j] = sum over the selected rows r of b and all heads h of
+ *               exp(scale * q_sel[r,h] . K[b,j,h/(Hq/Hkv)] - lse[r,h])
+ * for every j < S (bf16 only, float32 throughout).  lse [max_rows, Hq] is
+ * the natural-log LSE of the same queries (from dlm_partial_attn).
+ * If k > 0: topk_idx [B,k] i32 / topk_val [B,k] f32 receive the k keys of
+ * [key_lo,key_hi) with the largest sums, ordered by (-colsum, j): equal sums
+ * go to the lower position.  k <= key_hi-key_lo <= 8192.
+ * ------------------------------------------------------------------------ */
+size_t dlm_attn_colsum_workspace_size(int B, int S, int Hkv);
+int dlm_attn_colsum(int dtype, const void* q_sel, const int32_t* offsets, int max_rows,
+                    const void* k_cache, const float* lse,
+                    int B, int S, int Hq, int Hkv, int hd, float scale,
+                    float* colsum, int key_lo, int key_hi, int k,
+                    int32_t* topk_idx, float* topk_val,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dlm_stable_prefix
+ *
+ * Longest-stable-prefix commit.  Follows: "Beyond Scattered Acceptance: Fast
+ * and Coherent Inference for DLMs via Longest Stable Prefixes", Methodologie
+ * (commit the longest contiguous stable block at the start of the remaining
+ * active region in one step; commit at least one token as a fallback).
+ *
+ * argmax [B,S] i32 and maxprob [B,S] f32 hold each position's latest values
+ * (-1 / anything before its first evaluation).  ring [B, gen_hi-gen_lo, W]
+ * i32 keeps the last W pushes per generated position (initialise to -1).
+ * Step `step` first pushes argmax[b, gen_lo+i] into slot step % W for every
+ * generated position i, then, from the frontier L = committed[b] (a count
+ * of committed generated positions), advances over positions whose W ring
+ * entries are equal and not -1 and whose maxprob >= conf_threshold; if none
+ * advanced, min_commit != 0 and L < gen_hi-gen_lo, it advances by one.
+ * committed [B] i32 is updated in place.
+ * ------------------------------------------------------------------------ */
+int dlm_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
+                      int gen_lo, int gen_hi, int32_t* ring, int W, int step,
+                      float conf_threshold, int min_commit, int32_t* committed, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLM_H */

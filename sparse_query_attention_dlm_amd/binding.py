@@ -1,0 +1,199 @@
+"""Thin ctypes binding of libdlm (include/dlm.h).
+
+Argument marshalling only: tensors become device pointers, shapes become ints,
+the current torch stream becomes the hipStream_t.  Every computation runs in
+the library's HIP kernels; there is no fallback path.  Importing this module
+fails loudly if libdlm.so has not been built.
+
+Function names match the C entry points."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+DLM_OK, DLM_ERR_INVALID_ARG, DLM_ERR_UNSUPPORTED, DLM_ERR_WORKSPACE, DLM_ERR_HIP = range(5)
+DLM_F32, DLM_BF16 = 0, 1
+DLM_SCORE_COSINE, DLM_SCORE_CONFIDENCE, DLM_SCORE_GIVEN = 0, 1, 2
+
+
+class DlmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    return ctypes.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+lib.dlm_status_string.restype = ctypes.c_char_p
+lib.dlm_status_string.argtypes = [_I]
+lib.dlm_last_error.restype = ctypes.c_char_p
+lib.dlm_version.restype = ctypes.c_char_p
+lib.dlm_select_workspace_size.restype = _Z
+lib.dlm_select_workspace_size.argtypes = [_I, _I, _I, _I, _I]
+lib.dlm_saliency_select.restype = _I
+lib.dlm_saliency_select.argtypes = [_I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _F,
+                                    _P, _P, _P, _P, _P, _P, _Z, _P]
+lib.dlm_gather_qkv_scatter_kv.restype = _I
+lib.dlm_gather_qkv_scatter_kv.argtypes = [_I, _P, _I, _I, _I, _P, _P, _I, _P, _I, _I, _I,
+                                          _P, _P, _P, _P]
+lib.dlm_partial_attn_workspace_size.restype = _Z
+lib.dlm_partial_attn_workspace_size.argtypes = [_I] * 7
+lib.dlm_partial_attn.restype = _I
+lib.dlm_partial_attn.argtypes = [_I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P,
+                                 _P, _I, _P, _P, _Z, _P]
+lib.dlm_attn_colsum_workspace_size.restype = _Z
+lib.dlm_attn_colsum_workspace_size.argtypes = [_I, _I, _I]
+lib.dlm_attn_colsum.restype = _I
+lib.dlm_attn_colsum.argtypes = [_I, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _I,
+                                _P, _P, _P, _Z, _P]
+lib.dlm_stable_prefix.restype = _I
+lib.dlm_stable_prefix.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _I, _F, _I, _P, _P]
+
+
+def version() -> str:
+    return lib.dlm_version().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != DLM_OK:
+        raise DlmError(rc, f"{lib.dlm_status_string(rc).decode()}: {lib.dlm_last_error().decode()}")
+
+
+def _ptr(t, name, dtype=None, required=True):
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _dt(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return DLM_BF16
+    if t.dtype == torch.float32:
+        return DLM_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return _ptr(ws, "workspace"), ws.numel() * ws.element_size()
+
+
+def dlm_select_workspace_size(mode, B, S, V=0, max_eval=0) -> int:
+    return int(lib.dlm_select_workspace_size(mode, B, S, V, max_eval))
+
+
+def dlm_partial_attn_workspace_size(dtype, max_rows, B, S, Hq, Hkv, hd) -> int:
+    return int(lib.dlm_partial_attn_workspace_size(dtype, max_rows, B, S, Hq, Hkv, hd))
+
+
+def dlm_attn_colsum_workspace_size(B, S, Hkv) -> int:
+    return int(lib.dlm_attn_colsum_workspace_size(B, S, Hkv))
+
+
+def dlm_saliency_select(mode, a, b, *, lo, hi, threshold, idx, counts, offsets, workspace=None,
+                        scores=None, argmax=None, eval_idx=None, eval_offsets=None, max_eval=0,
+                        stream=None):
+    """a, b: COSINE cur/prev [B,S,D]; CONFIDENCE hidden [B,S,D] / W_lm [V,D];
+    GIVEN scores f32 [B,S] (b None)."""
+    if mode == DLM_SCORE_GIVEN:
+        B, S = a.shape
+        D = V = 0
+        dtype = DLM_F32
+        _ptr(a, "scores", torch.float32)
+    else:
+        B, S, D = a.shape
+        dtype = _dt(a)
+        V = b.shape[0] if mode == DLM_SCORE_CONFIDENCE else 0
+    wp, wn = _ws(workspace)
+    rc = lib.dlm_saliency_select(
+        mode, dtype, _ptr(a, "a"), _ptr(b, "b", required=False), B, S, D, V,
+        _ptr(eval_idx, "eval_idx", torch.int32, False), _ptr(eval_offsets, "eval_offsets", torch.int32, False),
+        int(max_eval), int(lo), int(hi), float(threshold),
+        _ptr(scores, "scores", torch.float32, False), _ptr(argmax, "argmax", torch.int32, False),
+        _ptr(idx, "idx", torch.int32), _ptr(counts, "counts", torch.int32),
+        _ptr(offsets, "offsets", torch.int32), wp, wn, _stream(stream))
+    _check(rc)
+
+
+def dlm_gather_qkv_scatter_kv(x, idx, offsets, max_rows, w_qkv, Hq, Hkv, hd, q_out, k_cache,
+                              v_cache, stream=None):
+    B, S, D = x.shape
+    rc = lib.dlm_gather_qkv_scatter_kv(
+        _dt(x), _ptr(x, "x"), B, S, D, _ptr(idx, "idx", torch.int32),
+        _ptr(offsets, "offsets", torch.int32), int(max_rows), _ptr(w_qkv, "w_qkv", x.dtype),
+        Hq, Hkv, hd, _ptr(q_out, "q_out", x.dtype), _ptr(k_cache, "k_cache", x.dtype),
+        _ptr(v_cache, "v_cache", x.dtype), _stream(stream))
+    _check(rc)
+
+
+def dlm_partial_attn(q_sel, idx, offsets, max_rows, k_cache, v_cache, scale, o_sel, lse=None,
+                     w_o=None, out_cache=None, workspace=None, stream=None):
+    B, S, Hkv, hd = k_cache.shape
+    Hq = q_sel.shape[1]
+    D_out = out_cache.shape[-1] if out_cache is not None else 0
+    wp, wn = _ws(workspace)
+    rc = lib.dlm_partial_attn(
+        _dt(q_sel), _ptr(q_sel, "q_sel"), _ptr(idx, "idx", torch.int32),
+        _ptr(offsets, "offsets", torch.int32), int(max_rows), _ptr(k_cache, "k_cache", q_sel.dtype),
+        _ptr(v_cache, "v_cache", q_sel.dtype), B, S, Hq, Hkv, hd, float(scale),
+        _ptr(o_sel, "o_sel", q_sel.dtype), _ptr(lse, "lse", torch.float32, False),
+        _ptr(w_o, "w_o", q_sel.dtype, False), D_out, _ptr(out_cache, "out_cache", q_sel.dtype, False),
+        wp, wn, _stream(stream))
+    _check(rc)
+
+
+def dlm_attn_colsum(q_sel, offsets, max_rows, k_cache, lse, scale, colsum, key_lo=0, key_hi=None,
+                    k=0, topk_idx=None, topk_val=None, workspace=None, stream=None):
+    B, S, Hkv, hd = k_cache.shape
+    Hq = q_sel.shape[1]
+    key_hi = S if key_hi is None else key_hi
+    wp, wn = _ws(workspace)
+    rc = lib.dlm_attn_colsum(
+        _dt(q_sel), _ptr(q_sel, "q_sel"), _ptr(offsets, "offsets", torch.int32), int(max_rows),
+        _ptr(k_cache, "k_cache", q_sel.dtype), _ptr(lse, "lse", torch.float32), B, S, Hq, Hkv, hd,
+        float(scale), _ptr(colsum, "colsum", torch.float32), int(key_lo), int(key_hi), int(k),
+        _ptr(topk_idx, "topk_idx", torch.int32, False), _ptr(topk_val, "topk_val", torch.float32, False),
+        wp, wn, _stream(stream))
+    _check(rc)
+
+
+def dlm_stable_prefix(argmax, maxprob, gen_lo, gen_hi, ring, step, conf_threshold, committed,
+                      min_commit=0, stream=None):
+    B, S = argmax.shape
+    W = ring.shape[-1]
+    rc = lib.dlm_stable_prefix(
+        _ptr(argmax, "argmax", torch.int32), _ptr(maxprob, "maxprob", torch.float32), B, S,
+        int(gen_lo), int(gen_hi), _ptr(ring, "ring", torch.int32), W, int(step),
+        float(conf_threshold), int(min_commit), _ptr(committed, "committed", torch.int32),
+        _stream(stream))
+    _check(rc)

@@ -1,0 +1,338 @@
+// C ABI of libdlm (declared in include/dlm.h): host-side argument validation
+// and dispatch to the gfx950 kernels.  Validation runs before any HIP call, so
+// a rejected request enqueues nothing and works without a GPU present.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dlm.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DLM_OK;
+  return fail(DLM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+size_t elt(int dtype) { return dtype == DLM_BF16 ? 2 : 4; }
+
+#define REQUIRE(cond, ...)                                  \
+  do {                                                      \
+    if (!(cond)) return fail(DLM_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+#define REQUIRE_PTR(p) REQUIRE((p) != nullptr, "%s must not be NULL", #p)
+#define REQUIRE_ALIGNED(p) REQUIRE(aligned16(p), "%s must be 16-byte aligned", #p)
+
+constexpr size_t kTicketBytes = 256;
+
+}  // namespace
+
+extern "C" {
+
+const char* dlm_status_string(int status) {
+  switch (status) {
+    case DLM_OK: return "DLM_OK";
+    case DLM_ERR_INVALID_ARG: return "DLM_ERR_INVALID_ARG";
+    case DLM_ERR_UNSUPPORTED: return "DLM_ERR_UNSUPPORTED";
+    case DLM_ERR_WORKSPACE: return "DLM_ERR_WORKSPACE";
+    case DLM_ERR_HIP: return "DLM_ERR_HIP";
+    default: return "DLM_ERR_UNKNOWN";
+  }
+}
+
+const char* dlm_last_error(void) { return g_last_error.c_str(); }
+const char* dlm_version(void) { return "libdlm 0.1 (gfx950)"; }
+
+// ---------------------------------------------------------------------------
+size_t dlm_select_workspace_size(int mode, int B, int S, int V, int max_eval) {
+  size_t n = kTicketBytes;
+  if (B > 0 && S > 0) n += round_up((size_t)B * S * sizeof(float), 256);
+  if (mode == DLM_SCORE_CONFIDENCE && V > 0 && max_eval > 0)
+    n += (size_t)max_eval * dlm::gemm_lmhead_ntile(V) * sizeof(float4);
+  return n;
+}
+
+int dlm_saliency_select(int mode, int dtype, const void* a, const void* b, int B, int S, int D,
+                        int V, const int32_t* eval_idx, const int32_t* eval_offsets, int max_eval,
+                        int lo, int hi, float threshold, float* scores, int32_t* argmax,
+                        int32_t* idx, int32_t* counts, int32_t* offsets, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  REQUIRE(mode == DLM_SCORE_COSINE || mode == DLM_SCORE_CONFIDENCE || mode == DLM_SCORE_GIVEN,
+          "unknown scoring mode %d", mode);
+  REQUIRE(dtype == DLM_F32 || dtype == DLM_BF16, "unknown dtype %d", dtype);
+  REQUIRE(B > 0 && S > 0, "B and S must be positive (B=%d S=%d)", B, S);
+  REQUIRE(0 <= lo && lo <= hi && hi <= S, "window [lo,hi) = [%d,%d) outside [0,%d]", lo, hi, S);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(counts);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(a);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mode == DLM_SCORE_GIVEN) {
+    REQUIRE_ALIGNED(a);
+    return hip_status(dlm::launch_given_select(static_cast<const float*>(a), B, S, lo, hi,
+                                               threshold, idx, counts, offsets, st),
+                      "given-score select");
+  }
+  REQUIRE_PTR(b);
+  REQUIRE(D > 0, "D must be positive");
+  REQUIRE_ALIGNED(a);
+  REQUIRE_ALIGNED(b);
+  const size_t need = dlm_select_workspace_size(mode, B, S, V, max_eval);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  REQUIRE_ALIGNED(workspace);
+  unsigned* ticket = static_cast<unsigned*>(workspace);
+  float* scratch = reinterpret_cast<float*>(static_cast<char*>(workspace) + kTicketBytes);
+  if (mode == DLM_SCORE_COSINE) {
+    REQUIRE(D % (dtype == DLM_BF16 ? 8 : 4) == 0, "D=%d must be a multiple of %d", D,
+            dtype == DLM_BF16 ? 8 : 4);
+    float* sc = scores ? scores : scratch;
+    return hip_status(dlm::launch_cosine_select(dtype, a, b, B, S, D, lo, hi, threshold, sc, idx,
+                                                counts, offsets, ticket, st),
+                      "cosine select");
+  }
+  // confidence
+  REQUIRE(dtype == DLM_BF16, "confidence scoring needs bf16 hidden states and W_lm");
+  REQUIRE_PTR(eval_idx);
+  REQUIRE_PTR(eval_offsets);
+  REQUIRE_PTR(scores);
+  REQUIRE_PTR(argmax);
+  REQUIRE(D % 64 == 0, "D=%d must be a multiple of 64", D);
+  REQUIRE(V > 0 && V % 128 == 0, "V=%d must be a positive multiple of 128", V);
+  REQUIRE(max_eval >= 0 && (long long)max_eval <= (long long)B * S, "max_eval=%d out of range",
+          max_eval);
+  const int ntile = dlm::gemm_lmhead_ntile(V);
+  float4* part = reinterpret_cast<float4*>(static_cast<char*>(workspace) + kTicketBytes +
+                                           round_up((size_t)B * S * sizeof(float), 256));
+  if (max_eval > 0) {
+    dlm::GemmArgs g{};
+    g.w = b;
+    g.x = a;
+    g.K = D;
+    g.N = V;
+    g.B = B;
+    g.S = S;
+    g.idx = eval_idx;
+    g.offsets = eval_offsets;
+    g.max_rows = max_eval;
+    g.part = part;
+    g.ntile = ntile;
+    int rc = hip_status(dlm::launch_gemm(DLM_BF16, dlm::EPI_LMHEAD, dlm::A_GATHER, g, st),
+                        "LM-head GEMM");
+    if (rc != DLM_OK) return rc;
+  }
+  return hip_status(dlm::launch_lmhead_combine(part, ntile, eval_idx, eval_offsets, max_eval, B, S,
+                                               lo, hi, threshold, scores, argmax, idx, counts,
+                                               offsets, ticket, st),
+                    "LM-head combine");
+}
+
+// ---------------------------------------------------------------------------
+int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D, const int32_t* idx,
+                              const int32_t* offsets, int max_rows, const void* w_qkv, int Hq,
+                              int Hkv, int hd, void* q_out, void* k_cache, void* v_cache,
+                              void* stream) {
+  REQUIRE(dtype == DLM_F32 || dtype == DLM_BF16, "unknown dtype %d", dtype);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_qkv);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  if (max_rows != 0) {  // with no rows to process, the row arrays may be empty (NULL)
+    REQUIRE_PTR(idx);
+    REQUIRE_PTR(offsets);
+    REQUIRE_PTR(q_out);
+  }
+  REQUIRE(B > 0 && S > 0 && D > 0, "B, S, D must be positive");
+  REQUIRE(Hq > 0 && Hkv > 0 && Hq % Hkv == 0, "Hq=%d must be a positive multiple of Hkv=%d", Hq,
+          Hkv);
+  REQUIRE(hd == 64 || hd == 128, "head dim %d not supported (64 or 128)", hd);
+  REQUIRE(max_rows >= 0 && (long long)max_rows <= (long long)B * S, "max_rows=%d out of range",
+          max_rows);
+  REQUIRE(D % (dtype == DLM_BF16 ? 64 : 4) == 0, "D=%d must be a multiple of %d", D,
+          dtype == DLM_BF16 ? 64 : 4);
+  REQUIRE_ALIGNED(x);
+  REQUIRE_ALIGNED(w_qkv);
+  REQUIRE_ALIGNED(q_out);
+  REQUIRE_ALIGNED(k_cache);
+  REQUIRE_ALIGNED(v_cache);
+  if (max_rows == 0) return DLM_OK;
+  dlm::GemmArgs g{};
+  g.w = w_qkv;
+  g.x = x;
+  g.K = D;
+  g.N = (Hq + 2 * Hkv) * hd;
+  g.B = B;
+  g.S = S;
+  g.idx = idx;
+  g.offsets = offsets;
+  g.max_rows = max_rows;
+  g.q_out = q_out;
+  g.k_cache = k_cache;
+  g.v_cache = v_cache;
+  g.nq = Hq * hd;
+  g.nk = Hkv * hd;
+  return hip_status(dlm::launch_gemm(dtype, dlm::EPI_QKV, dlm::A_GATHER, g,
+                                     static_cast<hipStream_t>(stream)),
+                    "gathered QKV GEMM");
+}
+
+// ---------------------------------------------------------------------------
+size_t dlm_partial_attn_workspace_size(int dtype, int max_rows, int B, int S, int Hq, int Hkv,
+                                       int hd) {
+  if (max_rows <= 0 || B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || hd <= 0) return 0;
+  return dlm::attn_workspace_bytes(dtype, max_rows, B, S, Hq, Hkv, hd);
+}
+
+int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int32_t* offsets,
+                     int max_rows, const void* k_cache, const void* v_cache, int B, int S, int Hq,
+                     int Hkv, int hd, float scale, void* o_sel, float* lse, const void* w_o,
+                     int D_out, void* out_cache, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  REQUIRE(dtype == DLM_F32 || dtype == DLM_BF16, "unknown dtype %d", dtype);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  if (max_rows != 0) {  // with no rows to process, the row arrays may be empty (NULL)
+    REQUIRE_PTR(q_sel);
+    REQUIRE_PTR(idx);
+    REQUIRE_PTR(offsets);
+    REQUIRE_PTR(o_sel);
+  }
+  REQUIRE(B > 0 && S > 0, "B and S must be positive");
+  REQUIRE(Hq > 0 && Hkv > 0 && Hq % Hkv == 0, "Hq=%d must be a positive multiple of Hkv=%d", Hq,
+          Hkv);
+  REQUIRE(hd == 64 || hd == 128, "head dim %d not supported (64 or 128)", hd);
+  REQUIRE(max_rows >= 0 && (long long)max_rows <= (long long)B * S, "max_rows=%d out of range",
+          max_rows);
+  REQUIRE(scale > 0.f, "scale must be positive");
+  REQUIRE_ALIGNED(q_sel);
+  REQUIRE_ALIGNED(k_cache);
+  REQUIRE_ALIGNED(v_cache);
+  REQUIRE_ALIGNED(o_sel);
+  if (w_o) {
+    REQUIRE(out_cache != nullptr, "w_o given but out_cache is NULL");
+    REQUIRE(D_out > 0, "D_out must be positive");
+    if (dtype == DLM_BF16)
+      REQUIRE(D_out % 64 == 0 && (Hq * hd) % 64 == 0, "bf16 W_o needs D_out %% 64 == 0");
+    REQUIRE_ALIGNED(w_o);
+  } else if (out_cache) {
+    REQUIRE(D_out == Hq * hd, "without W_o, D_out (%d) must equal Hq*hd (%d)", D_out, Hq * hd);
+  }
+  if (out_cache) REQUIRE_ALIGNED(out_cache);
+  const size_t need = dlm::attn_workspace_bytes(dtype, max_rows, B, S, Hq, Hkv, hd);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0) REQUIRE_ALIGNED(workspace);
+  if (max_rows == 0) return DLM_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  dlm::AttnArgs a{};
+  a.q = q_sel;
+  a.idx = idx;
+  a.offsets = offsets;
+  a.max_rows = max_rows;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.B = B;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.hd = hd;
+  a.scale = scale;
+  a.o = o_sel;
+  a.lse = lse;
+  a.ctx_out = w_o ? nullptr : out_cache;
+  int rc = hip_status(dlm::launch_attn(dtype, a, workspace, st), "partial attention");
+  if (rc != DLM_OK || !w_o) return rc;
+  dlm::GemmArgs g{};
+  g.w = w_o;
+  g.x = o_sel;
+  g.K = Hq * hd;
+  g.N = D_out;
+  g.B = B;
+  g.S = S;
+  g.idx = idx;
+  g.offsets = offsets;
+  g.max_rows = max_rows;
+  g.out = out_cache;
+  g.ld_out = D_out;
+  return hip_status(dlm::launch_gemm(dtype, dlm::EPI_ROWS, dlm::A_COMPACT, g, st),
+                    "output projection");
+}
+
+// ---------------------------------------------------------------------------
+size_t dlm_attn_colsum_workspace_size(int B, int S, int Hkv) {
+  if (B <= 0 || S <= 0 || Hkv <= 0) return 0;
+  return (size_t)Hkv * B * S * sizeof(float);
+}
+
+int dlm_attn_colsum(int dtype, const void* q_sel, const int32_t* offsets, int max_rows,
+                    const void* k_cache, const float* lse, int B, int S, int Hq, int Hkv, int hd,
+                    float scale, float* colsum, int key_lo, int key_hi, int k, int32_t* topk_idx,
+                    float* topk_val, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != DLM_BF16)
+    return fail(DLM_ERR_UNSUPPORTED, "attention column sums are implemented for bf16 only");
+  REQUIRE_PTR(q_sel);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(colsum);
+  REQUIRE(B > 0 && S > 0, "B and S must be positive");
+  REQUIRE(Hq > 0 && Hkv > 0 && Hq % Hkv == 0, "Hq=%d must be a positive multiple of Hkv=%d", Hq,
+          Hkv);
+  REQUIRE(hd == 64 || hd == 128, "head dim %d not supported (64 or 128)", hd);
+  REQUIRE(max_rows >= 0 && (long long)max_rows <= (long long)B * S, "max_rows=%d out of range",
+          max_rows);
+  REQUIRE(0 <= key_lo && key_lo <= key_hi && key_hi <= S, "key window [%d,%d) outside [0,%d]",
+          key_lo, key_hi, S);
+  REQUIRE(k >= 0 && k <= key_hi - key_lo, "k=%d exceeds the key window", k);
+  REQUIRE(k == 0 || key_hi - key_lo <= 8192, "top-k key window limited to 8192 keys");
+  REQUIRE(k == 0 || topk_idx != nullptr || topk_val != nullptr, "k > 0 needs an output");
+  REQUIRE_ALIGNED(q_sel);
+  REQUIRE_ALIGNED(k_cache);
+  const size_t need = dlm_attn_colsum_workspace_size(B, S, Hkv);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  return hip_status(dlm::launch_colsum(q_sel, offsets, max_rows, k_cache, lse, B, S, Hq, Hkv, hd,
+                                       scale, static_cast<float*>(workspace), colsum, key_lo,
+                                       key_hi, k, topk_idx, topk_val,
+                                       static_cast<hipStream_t>(stream)),
+                    "attention column sums");
+}
+
+// ---------------------------------------------------------------------------
+int dlm_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S, int gen_lo,
+                      int gen_hi, int32_t* ring, int W, int step, float conf_threshold,
+                      int min_commit, int32_t* committed, void* stream) {
+  REQUIRE_PTR(argmax);
+  REQUIRE_PTR(maxprob);
+  REQUIRE_PTR(ring);
+  REQUIRE_PTR(committed);
+  REQUIRE(B > 0 && S > 0, "B and S must be positive");
+  REQUIRE(0 <= gen_lo && gen_lo < gen_hi && gen_hi <= S, "generated region [%d,%d) invalid",
+          gen_lo, gen_hi);
+  REQUIRE(W >= 1 && W <= 64, "ring depth W=%d out of range [1,64]", W);
+  REQUIRE(step >= 0, "step must be non-negative");
+  return hip_status(dlm::launch_stable_prefix(argmax, maxprob, B, S, gen_lo, gen_hi, ring, W, step,
+                                              conf_threshold, min_commit, committed,
+                                              static_cast<hipStream_t>(stream)),
+                    "stable prefix");
+}
+
+}  // extern "C"

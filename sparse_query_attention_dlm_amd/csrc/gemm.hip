@@ -1,0 +1,319 @@
+// Gathered-row GEMM on the gfx950 matrix cores, with fused epilogues.
+//
+// SureLock (Stopping Computation for Converged Tokens), Methodik,
+// Kernprinzipien: only the active positions compute Q/K/V, locked positions
+// keep their cached K/V.  DyLLM, Methodologie 1: recomputed tokens overwrite
+// their cached activations.  SlowFast Sampling, Metodologia (certainty
+// principle): the max softmax probability of the LM head is the confidence.
+//
+// Computes D^T[n][m] = sum_k W[n][k] * A[row(m)][k] with W output-major, so
+// both MFMA operands are K-contiguous and come straight from LDS rows:
+//   A-operand = a 32-row block of W (output features), B-operand = 32 gathered
+//   token rows.  The gather happens on load (row pointers resolved once per
+//   tile from idx/offsets), so no compacted copy of the hidden states is made.
+// Epilogues:
+//   EPI_QKV    - Q rows written compact, K/V rows scattered into the caches
+//                (8-byte bf16x4 stores of 4 consecutive features)
+//   EPI_ROWS   - rows scattered into an output cache (W_o projection)
+//   EPI_LMHEAD - per (token, 128-column vocabulary tile): max logit, sum of
+//                exp(z - max) and the lowest argmax; logits never stored.
+// Tiles: TP (features) x TT (tokens) x 64 (k), 4 waves, 32x32x16 bf16 MFMA,
+// double-buffered LDS with 16-byte row padding, register-staged prefetch.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dlm {
+
+template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, int m_tiles_max) {
+  constexpr int BK = 64, PITCH = BK + 8;  // u16 elements per LDS row (144 bytes)
+  constexpr int ROWS = TP + TT;
+  constexpr int CHUNKS = ROWS * (BK / 8);
+  static_assert(CHUNKS % 256 == 0, "tile rows must fill the workgroup");
+  constexpr int CPT = CHUNKS / 256;
+  constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
+  static_assert(WP * WT == 4 && FP >= 1 && FT >= 1, "wave layout");
+  static_assert(PF >= 1, "prefetch depth");
+
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * ROWS * PITCH];
+  __shared__ long long s_arow[TT];
+  __shared__ int s_drow[TT];
+
+  const int n_rows = min(g.offsets[g.B], g.max_rows);
+  const int m_tiles = (n_rows + TT - 1) / TT;
+  const int nt = blockIdx.x / m_tiles_max, mt = blockIdx.x % m_tiles_max;
+  if (mt >= m_tiles) return;
+  const int m0 = mt * TT, n0 = nt * TP;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int t = tid; t < TT; t += 256) {
+    const int m = m0 + t;
+    long long arow = -1;
+    int drow = -1;
+    if (m < n_rows) {
+      const int b = batch_of(g.offsets, g.B, m);
+      drow = b * g.S + g.idx[m];
+      arow = (AMODE == A_GATHER) ? (long long)drow * g.K : (long long)m * g.K;
+    }
+    s_arow[t] = arow;
+    s_drow[t] = drow;
+  }
+  __syncthreads();
+
+  // Chunk j of this thread covers LDS row (tid/8 + 32 j), 16-byte column tid%8.
+  // Rows [0,TP) are weight rows (one base pointer, constant stride); rows
+  // [TP, TP+TT) are gathered token rows (32-bit element offsets).
+  constexpr int CW = TP / 32;  // chunks of weight rows per thread
+  constexpr int CX = CPT - CW;  // chunks of token rows per thread
+  const int r0 = tid >> 3, kc = tid & 7;
+  const u16* gW = static_cast<const u16*>(g.w) + (size_t)(n0 + r0) * g.K + kc * 8;
+  const u16* gX = static_cast<const u16*>(g.x) + kc * 8;
+  const size_t wstride = (size_t)32 * g.K;
+  uint32_t xoff[CX];
+#pragma unroll
+  for (int j = 0; j < CX; ++j) {
+    long long ar = s_arow[r0 + 32 * j];
+    if (ar < 0) ar = s_arow[0];  // padding rows of a ragged tile reuse a valid row
+    xoff[j] = (uint32_t)ar;
+  }
+  u16* const ldsw = lds + r0 * PITCH + kc * 8;
+  auto gload = [&](int j, int kstep) -> u32x4 {
+    const u16* p = (j < CW) ? gW + j * wstride : gX + xoff[j - CW];
+    return *reinterpret_cast<const u32x4*>(p + (size_t)kstep * BK);
+  };
+
+  f32x16 acc[FP][FT];
+#pragma unroll
+  for (int a = 0; a < FP; ++a)
+#pragma unroll
+    for (int b = 0; b < FT; ++b) acc[a][b] = f32x16{};
+
+  // Register ring of PF k-steps in flight; slot s holds k-step j with j % PF == s.
+  // The steady-state loop is branch-free (loads past the end re-read the last
+  // k-step, stores past the end go to the idle LDS buffer) and nk % PF == 0,
+  // so the compiler can count outstanding loads exactly and waits only for
+  // the oldest slot instead of draining the queue every k-step.
+  u32x4 stg[PF][CPT];
+  const int nk = g.K / BK;
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) stg[p][j] = gload(j, min(p, nk - 1));
+  }
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(ldsw + 32 * j * PITCH) = stg[0][j];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) stg[0][j] = gload(j, min(PF, nk - 1));
+  __syncthreads();
+
+  const int wp = wave / WT, wt = wave % WT;
+  const int lr = lane & 31, lg = lane >> 5;
+  for (int kt0 = 0; kt0 < nk; kt0 += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int kt = kt0 + u;
+      const int buf = (PF % 2 == 0) ? (u & 1) : (kt & 1);
+      const u16* sW = lds + buf * ROWS * PITCH;
+      const u16* sX = sW + TP * PITCH;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 af[FP], bfr[FT];
+#pragma unroll
+        for (int a = 0; a < FP; ++a)
+          af[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(sW + (wp * WTP + a * 32 + lr) * PITCH +
+                                                            kk * 16 + lg * 8));
+#pragma unroll
+        for (int b = 0; b < FT; ++b)
+          bfr[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(sX + (wt * WTT + b * 32 + lr) * PITCH +
+                                                             kk * 16 + lg * 8));
+#pragma unroll
+        for (int a = 0; a < FP; ++a)
+#pragma unroll
+          for (int b = 0; b < FT; ++b) acc[a][b] = mfma32x32x16(af[a], bfr[b], acc[a][b]);
+      }
+      const int slot = (u + 1) % PF;  // compile-time after unrolling
+      u16* dst = ldsw + (buf ^ 1) * ROWS * PITCH;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(dst + 32 * j * PITCH) = stg[slot][j];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) stg[slot][j] = gload(j, min(kt + 1 + PF, nk - 1));
+      __syncthreads();
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  if constexpr (EPI == EPI_QKV || EPI == EPI_ROWS) {
+#pragma unroll
+    for (int b = 0; b < FT; ++b) {
+      const int ml = wt * WTT + b * 32 + lr;
+      const int drow = s_drow[ml];
+      if (drow < 0) continue;
+      const int m = m0 + ml;
+#pragma unroll
+      for (int a = 0; a < FP; ++a) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int n = n0 + wp * WTP + a * 32 + 8 * q4 + 4 * lg;
+          u32x2 pk;
+          pk[0] = pack_bf16x2(acc[a][b][4 * q4 + 0], acc[a][b][4 * q4 + 1]);
+          pk[1] = pack_bf16x2(acc[a][b][4 * q4 + 2], acc[a][b][4 * q4 + 3]);
+          u16* dst;
+          if constexpr (EPI == EPI_QKV) {
+            if (n < g.nq)
+              dst = static_cast<u16*>(g.q_out) + (size_t)m * g.nq + n;
+            else if (n < g.nq + g.nk)
+              dst = static_cast<u16*>(g.k_cache) + (size_t)drow * g.nk + (n - g.nq);
+            else
+              dst = static_cast<u16*>(g.v_cache) + (size_t)drow * g.nk + (n - g.nq - g.nk);
+          } else {
+            dst = static_cast<u16*>(g.out) + (size_t)drow * g.ld_out + n;
+          }
+          *reinterpret_cast<u32x2*>(dst) = pk;
+        }
+      }
+    }
+  } else {
+    __shared__ float s_pm[WP][TT], s_ps[WP][TT];
+    __shared__ int s_pa[WP][TT];
+#pragma unroll
+    for (int b = 0; b < FT; ++b) {
+      const int ml = wt * WTT + b * 32 + lr;
+      // running (max, sum exp(z - max), argmax) merged 16 logits at a time
+      float m = -INFINITY, s = 0.f;
+      int am = 0x7fffffff;
+#pragma unroll
+      for (int a = 0; a < FP; ++a) {
+        float cm = acc[a][b][0];
+        int ca = n0 + wp * WTP + a * 32 + 4 * lg;
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+          const int n = n0 + wp * WTP + a * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
+          const float v = acc[a][b][i];
+          if (v > cm) {  // rows grow with i, so ties keep the lower index
+            cm = v;
+            ca = n;
+          }
+        }
+        const float cm2 = cm * kLog2e;
+        float cs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cs += __builtin_amdgcn_exp2f(fmaf(acc[a][b][i], kLog2e, -cm2));
+        merge_part(m, s, am, cm, cs, ca);
+      }
+      const float m2 = __shfl_xor(m, 32, 64), s2 = __shfl_xor(s, 32, 64);
+      const int a2 = __shfl_xor(am, 32, 64);
+      merge_part(m, s, am, m2, s2, a2);
+      if (lg == 0) {
+        s_pm[wp][ml] = m;
+        s_ps[wp][ml] = s;
+        s_pa[wp][ml] = am;
+      }
+    }
+    __syncthreads();
+    for (int t = tid; t < TT; t += 256) {
+      if (s_drow[t] < 0) continue;
+      float m = s_pm[0][t], s = s_ps[0][t];
+      int am = s_pa[0][t];
+#pragma unroll
+      for (int w = 1; w < WP; ++w) merge_part(m, s, am, s_pm[w][t], s_ps[w][t], s_pa[w][t]);
+      g.part[(size_t)(m0 + t) * g.ntile + nt] = make_float4(m, s, __int_as_float(am), 0.f);
+    }
+  }
+}
+
+// fp32 path (small fp32 layers): one thread per output element, float4 loads,
+// sequential float32 accumulation over k.
+template <int EPI, int AMODE>
+__global__ __launch_bounds__(64) void gemm_f32_kernel(GemmArgs g) {
+  const int m = blockIdx.y, n = blockIdx.x * 64 + threadIdx.x;
+  const int n_rows = min(g.offsets[g.B], g.max_rows);
+  if (m >= n_rows || n >= g.N) return;
+  const int b = batch_of(g.offsets, g.B, m);
+  const int drow = b * g.S + g.idx[m];
+  const float* xr = static_cast<const float*>(g.x) +
+                    (AMODE == A_GATHER ? (size_t)drow * g.K : (size_t)m * g.K);
+  const float* wr = static_cast<const float*>(g.w) + (size_t)n * g.K;
+  float acc = 0.f;
+  for (int k = 0; k < g.K; k += 4) {
+    const float4 xv = *reinterpret_cast<const float4*>(xr + k);
+    const float4 wv = *reinterpret_cast<const float4*>(wr + k);
+    acc = fmaf(xv.x, wv.x, acc);
+    acc = fmaf(xv.y, wv.y, acc);
+    acc = fmaf(xv.z, wv.z, acc);
+    acc = fmaf(xv.w, wv.w, acc);
+  }
+  float* dst;
+  if constexpr (EPI == EPI_QKV) {
+    if (n < g.nq)
+      dst = static_cast<float*>(g.q_out) + (size_t)m * g.nq + n;
+    else if (n < g.nq + g.nk)
+      dst = static_cast<float*>(g.k_cache) + (size_t)drow * g.nk + (n - g.nq);
+    else
+      dst = static_cast<float*>(g.v_cache) + (size_t)drow * g.nk + (n - g.nq - g.nk);
+  } else {
+    dst = static_cast<float*>(g.out) + (size_t)drow * g.ld_out + n;
+  }
+  *dst = acc;
+}
+
+// Tile shapes (features x tokens, prefetch depth):
+//   LM head and large selections: 256 x 256, each wave a 128 x 128 block, so
+//     every LDS fragment feeds four MFMAs; 1 k-step of prefetch.
+//   medium selections (<= 1024 rows): 128 x 128, 2 k-steps of prefetch (two
+//     workgroups per CU).
+//   short selections (<= 128 rows): 64 features x 128 tokens, 4 k-steps of
+//     prefetch, so the weight stream keeps enough bytes in flight per CU.
+// The prefetch depth is reduced to 2 or 1 when it does not divide K / 64.
+constexpr int kLmTP = 256;
+int gemm_lmhead_ntile(int V) { return V / kLmTP; }
+
+template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE>
+static void launch_bf16(const GemmArgs& g, hipStream_t st) {
+  const int m_tiles_max = (g.max_rows + TT - 1) / TT;
+  const int grid = (g.N / TP) * m_tiles_max;
+  hipLaunchKernelGGL((gemm_bf16_kernel<TP, TT, WP, WT, PF, EPI, AMODE>), dim3(grid), dim3(256), 0,
+                     st, g, m_tiles_max);
+}
+
+template <int TP, int TT, int PFMAX, int EPI, int AMODE>
+static void launch_pf(const GemmArgs& g, hipStream_t st) {
+  // the prefetch depth must divide the number of 64-wide k-steps
+  const int nk = g.K / 64;
+  if (PFMAX >= 4 && nk % 4 == 0)
+    launch_bf16<TP, TT, 2, 2, (PFMAX >= 4 ? 4 : 1), EPI, AMODE>(g, st);
+  else if (PFMAX >= 2 && nk % 2 == 0)
+    launch_bf16<TP, TT, 2, 2, (PFMAX >= 2 ? 2 : 1), EPI, AMODE>(g, st);
+  else
+    launch_bf16<TP, TT, 2, 2, 1, EPI, AMODE>(g, st);
+}
+
+template <int EPI, int AMODE>
+static void launch_by_rows(const GemmArgs& g, hipStream_t st) {
+  if (g.max_rows <= 128 || g.N % 128 != 0)
+    launch_pf<64, 128, 4, EPI, AMODE>(g, st);
+  else if (g.max_rows <= 1024 || g.N % 256 != 0)
+    launch_pf<128, 128, 2, EPI, AMODE>(g, st);
+  else
+    launch_pf<256, 256, 1, EPI, AMODE>(g, st);
+}
+
+hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStream_t st) {
+  if (g.max_rows <= 0) return hipSuccess;
+  if (dtype == 0) {
+    const dim3 grid((g.N + 63) / 64, g.max_rows);
+    if (epi == EPI_QKV)
+      hipLaunchKernelGGL((gemm_f32_kernel<EPI_QKV, A_GATHER>), grid, dim3(64), 0, st, g);
+    else
+      hipLaunchKernelGGL((gemm_f32_kernel<EPI_ROWS, A_COMPACT>), grid, dim3(64), 0, st, g);
+    return hipGetLastError();
+  }
+  if (epi == EPI_LMHEAD)
+    launch_pf<kLmTP, 256, 1, EPI_LMHEAD, A_GATHER>(g, st);
+  else if (epi == EPI_QKV)
+    launch_by_rows<EPI_QKV, A_GATHER>(g, st);
+  else
+    launch_by_rows<EPI_ROWS, A_COMPACT>(g, st);
+  return hipGetLastError();
+}
+
+}  // namespace dlm

@@ -1,0 +1,78 @@
+// Host-side launchers of the gfx950 kernels (internal to libdlm; the public
+// surface is include/dlm.h).  Every launcher enqueues on `st`, performs no
+// synchronisation and returns hipGetLastError() after its launches.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dlm {
+
+// select.hip
+hipError_t launch_cosine_select(int dtype, const void* cur, const void* prev, int B, int S, int D,
+                                int lo, int hi, float thr, float* scores, int32_t* idx,
+                                int32_t* counts, int32_t* offsets, unsigned* ticket,
+                                hipStream_t st);
+hipError_t launch_given_select(const float* scores, int B, int S, int lo, int hi, float thr,
+                               int32_t* idx, int32_t* counts, int32_t* offsets, hipStream_t st);
+hipError_t launch_lmhead_combine(const float4* part, int ntile, const int32_t* eval_idx,
+                                 const int32_t* eval_offsets, int max_eval, int B, int S, int lo,
+                                 int hi, float thr, float* scores, int32_t* argmax, int32_t* idx,
+                                 int32_t* counts, int32_t* offsets, unsigned* ticket,
+                                 hipStream_t st);
+
+// gemm.hip -- D^T[n][m] = sum_k W[n][k] * A[row(m)][k]; W output-major [N][K].
+enum GemmEpilogue { EPI_QKV = 0, EPI_ROWS = 1, EPI_LMHEAD = 2 };
+enum GemmAMode { A_GATHER = 0, A_COMPACT = 1 };
+struct GemmArgs {
+  const void* w;            // [N][K]
+  const void* x;            // A_GATHER: x[B][S][K], row (b, idx[m]); A_COMPACT: x[m][K]
+  int K, N, B, S;
+  const int32_t* idx;       // selected positions (packed)
+  const int32_t* offsets;   // [B+1]
+  int max_rows;
+  // EPI_QKV: columns [0,nq) -> q_out[m][nq], [nq,nq+nk) -> k_cache row, then v_cache row
+  void* q_out;
+  void* k_cache;
+  void* v_cache;
+  int nq, nk;
+  // EPI_ROWS: out[(b*S + idx[m])*ld_out + n]
+  void* out;
+  int ld_out;
+  // EPI_LMHEAD: part[m*ntile + tile] = {max, sum exp(z-max), argmax bits, 0}
+  float4* part;
+  int ntile;
+};
+hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStream_t st);
+int gemm_lmhead_ntile(int V);
+
+// attn.hip
+struct AttnArgs {
+  const void* q;            // [max_rows][Hq][hd]
+  const int32_t* idx;
+  const int32_t* offsets;
+  int max_rows;
+  const void* k;            // [B][S][Hkv][hd]
+  const void* v;
+  int B, S, Hq, Hkv, hd;
+  float scale;
+  void* o;                  // [max_rows][Hq][hd]
+  float* lse;               // [max_rows][Hq] or null
+  void* ctx_out;            // out_cache [B][S][Hq*hd] or null (no W_o)
+  float* part_o;            // split-KV partials (workspace)
+  float* part_lse;
+};
+size_t attn_workspace_bytes(int dtype, int max_rows, int B, int S, int Hq, int Hkv, int hd);
+hipError_t launch_attn(int dtype, const AttnArgs& a, void* workspace, hipStream_t st);
+
+// colsum.hip
+hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, const void* k,
+                         const float* lse, int B, int S, int Hq, int Hkv, int hd, float scale,
+                         float* partial, float* colsum, int key_lo, int key_hi, int kk,
+                         int32_t* topk_idx, float* topk_val, hipStream_t st);
+
+// prefix.hip
+hipError_t launch_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
+                                int gen_lo, int gen_hi, int32_t* ring, int W, int step, float thr,
+                                int min_commit, int32_t* committed, hipStream_t st);
+
+}  // namespace dlm

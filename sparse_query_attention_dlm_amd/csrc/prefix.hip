@@ -1,0 +1,59 @@
+// Longest-stable-prefix commit.
+//
+// Beyond Scattered Acceptance (Longest Stable Prefixes), Methodologie: the
+// scheduler commits, in one step, the longest contiguous run of stable
+// positions at the start of the remaining active region, and commits at
+// least one position when none is stable.  Stability here: the per-step
+// argmax stayed the same over the last W steps (SlowFast Sampling,
+// Metodologia, convergence principle) and the max probability is at least
+// the confidence threshold.
+//
+// One workgroup per sequence: every thread pushes the latest argmax of its
+// positions into the W-deep ring, tests stability on the ring it just
+// updated, and the first unstable position at or after the frontier is found
+// with an LDS atomicMin.  Integer work only; the one float comparison uses the
+// float32 max-prob given.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dlm {
+
+__global__ __launch_bounds__(256) void stable_prefix_kernel(const int32_t* __restrict__ argmax,
+                                                            const float* __restrict__ maxprob,
+                                                            int S, int gen_lo, int gen_hi,
+                                                            int32_t* __restrict__ ring, int W,
+                                                            int step, float thr, int min_commit,
+                                                            int32_t* __restrict__ committed) {
+  __shared__ int s_first;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int S_gen = gen_hi - gen_lo;
+  const int L = committed[b];
+  if (tid == 0) s_first = S_gen;
+  __syncthreads();
+  const int slot = step % W;
+  for (int i = tid; i < S_gen; i += 256) {
+    const size_t pos = (size_t)b * S + gen_lo + i;
+    const int a = argmax[pos];
+    int32_t* rr = ring + ((size_t)b * S_gen + i) * W;
+    rr[slot] = a;
+    bool stable = (a != -1) && (maxprob[pos] >= thr);
+    for (int w = 0; w < W; ++w) stable = stable && (rr[w] == a);
+    if (i >= L && !stable) atomicMin(&s_first, i);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int e = s_first;
+    if (min_commit && e == L && L < S_gen) e = L + 1;
+    committed[b] = e;
+  }
+}
+
+hipError_t launch_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
+                                int gen_lo, int gen_hi, int32_t* ring, int W, int step, float thr,
+                                int min_commit, int32_t* committed, hipStream_t st) {
+  hipLaunchKernelGGL(stable_prefix_kernel, dim3(B), dim3(256), 0, st, argmax, maxprob, S, gen_lo,
+                     gen_hi, ring, W, step, thr, min_commit, committed);
+  return hipGetLastError();
+}
+
+}  // namespace dlm

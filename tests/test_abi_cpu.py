@@ -1,0 +1,166 @@
+"""CPU-side checks of the C-ABI library: it loads without a GPU, exports every
+entry point declared in include/dlm.h, and rejects invalid requests on the host
+(before any launch) with the documented status codes.  No compute call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dlm.h")
+LIB = os.path.join(ROOT, "sparse_query_attention_dlm_amd", "libdlm.so")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+COSINE, CONFIDENCE, GIVEN = 0, 1, 2
+FAKE = 0x10000          # a 16-byte aligned non-null pointer value; never dereferenced here
+MISALIGNED = 0x10008
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libdlm.so not built")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    L = ctypes.CDLL(LIB)
+    L.dlm_last_error.restype = ctypes.c_char_p
+    L.dlm_status_string.restype = ctypes.c_char_p
+    L.dlm_select_workspace_size.restype = ctypes.c_size_t
+    L.dlm_partial_attn_workspace_size.restype = ctypes.c_size_t
+    L.dlm_attn_colsum_workspace_size.restype = ctypes.c_size_t
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(dlm_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for fn in ["dlm_saliency_select", "dlm_gather_qkv_scatter_kv", "dlm_partial_attn",
+               "dlm_attn_colsum", "dlm_stable_prefix"]:
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.dlm_status_string(OK) == b"DLM_OK"
+    assert lib.dlm_status_string(INVALID) == b"DLM_ERR_INVALID_ARG"
+    assert lib.dlm_status_string(WORKSPACE) == b"DLM_ERR_WORKSPACE"
+    assert lib.dlm_status_string(99) == b"DLM_ERR_UNKNOWN"
+
+
+def p(v):
+    return ctypes.c_void_p(v)
+
+
+def f(v):
+    return ctypes.c_float(v)
+
+
+def select(lib, mode=COSINE, dtype=BF16, a=FAKE, b=FAKE, B=1, S=16, D=64, V=0, ev=0, evo=0,
+           max_eval=0, lo=0, hi=16, scores=0, argmax=0, idx=FAKE, counts=FAKE, offsets=FAKE,
+           ws=FAKE, ws_bytes=1 << 20):
+    return lib.dlm_saliency_select(mode, dtype, p(a), p(b), B, S, D, V, p(ev), p(evo), max_eval, lo, hi,
+                                   f(0.5), p(scores), p(argmax), p(idx), p(counts), p(offsets), p(ws),
+                                   ctypes.c_size_t(ws_bytes), p(0))
+
+
+def test_select_rejections(lib):
+    assert select(lib, mode=7) == INVALID
+    assert select(lib, dtype=5) == INVALID
+    assert select(lib, B=0) == INVALID
+    assert select(lib, lo=5, hi=4) == INVALID
+    assert select(lib, hi=17) == INVALID
+    assert select(lib, idx=0) == INVALID
+    assert b"idx" in lib.dlm_last_error()
+    assert select(lib, a=0) == INVALID
+    assert select(lib, b=0) == INVALID
+    assert select(lib, a=MISALIGNED) == INVALID
+    assert select(lib, D=12) == INVALID                      # bf16 rows must be 16-byte chunks
+    assert select(lib, ws=0) == WORKSPACE
+    assert select(lib, ws_bytes=8) == WORKSPACE
+    assert select(lib, mode=CONFIDENCE, dtype=F32, V=128, ev=FAKE, evo=FAKE, scores=FAKE, argmax=FAKE) == INVALID
+    assert select(lib, mode=CONFIDENCE, V=100, ev=FAKE, evo=FAKE, scores=FAKE, argmax=FAKE, max_eval=4) == INVALID
+    assert select(lib, mode=CONFIDENCE, V=128, ev=FAKE, evo=FAKE, scores=0, argmax=FAKE) == INVALID
+    assert select(lib, mode=CONFIDENCE, V=128, ev=0, evo=FAKE, scores=FAKE, argmax=FAKE) == INVALID
+
+
+def test_select_workspace_size_covers_partials(lib):
+    small = lib.dlm_select_workspace_size(COSINE, 2, 100, 0, 0)
+    assert small >= 2 * 100 * 4
+    big = lib.dlm_select_workspace_size(CONFIDENCE, 2, 100, 32768, 50)
+    assert big >= small + 50 * (32768 // 128) * 16
+
+
+def gqkv(lib, dtype=BF16, x=FAKE, B=1, S=8, D=64, idx=FAKE, off=FAKE, max_rows=8, w=FAKE, Hq=2, Hkv=1,
+         hd=64, q=FAKE, k=FAKE, v=FAKE):
+    return lib.dlm_gather_qkv_scatter_kv(dtype, p(x), B, S, D, p(idx), p(off), max_rows, p(w), Hq, Hkv,
+                                         hd, p(q), p(k), p(v), p(0))
+
+
+def test_gather_qkv_rejections(lib):
+    assert gqkv(lib, x=0) == INVALID
+    assert gqkv(lib, w=0) == INVALID
+    assert gqkv(lib, Hq=3, Hkv=2) == INVALID                 # Hq % Hkv != 0
+    assert gqkv(lib, hd=96) == INVALID                       # unsupported head dim
+    assert gqkv(lib, D=96) == INVALID                        # bf16 needs D % 64 == 0
+    assert gqkv(lib, max_rows=9) == INVALID                  # more rows than B*S
+    assert gqkv(lib, max_rows=-1) == INVALID
+    assert gqkv(lib, k=MISALIGNED) == INVALID
+
+
+def attn(lib, dtype=BF16, q=FAKE, idx=FAKE, off=FAKE, max_rows=4, k=FAKE, v=FAKE, B=1, S=64, Hq=2,
+         Hkv=1, hd=128, scale=0.1, o=FAKE, lse=0, wo=0, D_out=0, out=0, ws=0, ws_bytes=0):
+    return lib.dlm_partial_attn(dtype, p(q), p(idx), p(off), max_rows, p(k), p(v), B, S, Hq, Hkv, hd,
+                                f(scale), p(o), p(lse), p(wo), D_out, p(out), p(ws),
+                                ctypes.c_size_t(ws_bytes), p(0))
+
+
+def test_partial_attn_rejections(lib):
+    assert attn(lib, q=0) == INVALID
+    assert attn(lib, o=0) == INVALID
+    assert attn(lib, hd=32) == INVALID
+    assert attn(lib, Hq=3, Hkv=2) == INVALID
+    assert attn(lib, scale=0.0) == INVALID
+    assert attn(lib, wo=FAKE, out=0, D_out=64) == INVALID    # W_o without an output cache
+    assert attn(lib, out=FAKE, D_out=100) == INVALID         # no W_o: D_out must be Hq*hd
+    assert attn(lib, wo=FAKE, out=FAKE, D_out=100) == INVALID  # bf16 W_o: D_out % 64
+    # a short selection needs split-KV scratch: refused without it
+    need = lib.dlm_partial_attn_workspace_size(BF16, 4, 1, 4096, 2, 1, 128)
+    assert need > 0
+    assert attn(lib, S=4096) == WORKSPACE
+    assert attn(lib, S=4096, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+
+
+def colsum(lib, dtype=BF16, q=FAKE, off=FAKE, max_rows=4, k=FAKE, lse=FAKE, B=1, S=64, Hq=2, Hkv=1,
+           hd=128, cs=FAKE, lo=0, hi=64, kk=4, ti=FAKE, tv=0, ws=FAKE, ws_bytes=1 << 20):
+    return lib.dlm_attn_colsum(dtype, p(q), p(off), max_rows, p(k), p(lse), B, S, Hq, Hkv, hd, f(0.1),
+                               p(cs), lo, hi, kk, p(ti), p(tv), p(ws), ctypes.c_size_t(ws_bytes), p(0))
+
+
+def test_colsum_rejections(lib):
+    assert colsum(lib, dtype=F32) == UNSUPPORTED
+    assert colsum(lib, lse=0) == INVALID
+    assert colsum(lib, lo=10, hi=5) == INVALID
+    assert colsum(lib, kk=65) == INVALID                     # k larger than the key window
+    assert colsum(lib, S=10000, hi=10000) == INVALID         # top-k window over 8192 keys
+    assert colsum(lib, ti=0, tv=0) == INVALID                # k > 0 but nowhere to write
+    assert colsum(lib, ws_bytes=4) == WORKSPACE
+    assert lib.dlm_attn_colsum_workspace_size(4, 4096, 32) == 32 * 4 * 4096 * 4
+
+
+def test_stable_prefix_rejections(lib):
+    def sp(argmax=FAKE, mp=FAKE, B=2, S=32, lo=8, hi=32, ring=FAKE, W=3, step=0, com=FAKE):
+        return lib.dlm_stable_prefix(p(argmax), p(mp), B, S, lo, hi, p(ring), W, step, f(0.9), 0, p(com), p(0))
+    assert sp(argmax=0) == INVALID
+    assert sp(ring=0) == INVALID
+    assert sp(lo=8, hi=8) == INVALID
+    assert sp(hi=33) == INVALID
+    assert sp(W=0) == INVALID
+    assert sp(step=-1) == INVALID

@@ -1,0 +1,343 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on the same
+seeded inputs, element by element.
+
+Bars: index sets exact outside the 1e-4 threshold band; float outputs within
+1e-4 (fp32 storage) or 2e-2 (bf16 storage) max-abs; cache rows that a step does
+not select must be byte-identical.  Downstream calls receive the oracle's index
+set, so each stage is compared on identical inputs."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dlm_oracle as O
+from sparse_query_attention_dlm_amd import workloads as W
+from helpers import (BAND, TOL, check_selection, check_topk, dev, host, i32, maxabs, rows_mask,
+                     workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dlm():
+    from sparse_query_attention_dlm_amd import binding
+    return binding
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ---------------------------------------------------------------------------
+# cosine-selected single steps (tiny fp32 layer, bf16 S=1024 layer)
+# ---------------------------------------------------------------------------
+def run_cosine_step(dlm, shape, tau=None, **override):
+    inp = W.cosine_step_inputs(shape, **override)
+    s = inp.shape
+    dt = s.dtype
+    tau = s.tau if tau is None else tau
+    scale = 1.0 / math.sqrt(s.hd)
+    say(f"[cosine step] {s.name} B={s.B} S={s.S} D={s.D} Hq={s.Hq} Hkv={s.Hkv} tau={tau}")
+    kc0, vc0, out0 = O.full_recompute_caches(inp.prev, inp.w_qkv, s.Hq, s.Hkv, s.hd, scale, inp.w_o)
+    kc0, vc0, out0 = (W.to_storage(a, dt) for a in (kc0, vc0, out0))
+    ref = O.cosine_step(inp.cur, inp.prev, inp.w_qkv, s.Hq, s.Hkv, s.hd, tau, kc0, vc0, out0, w_o=inp.w_o)
+
+    cur, prev = dev(inp.cur, dt), dev(inp.prev, dt)
+    B, S = s.B, s.S
+    idx = torch.zeros(B * S, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(B, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    scores = torch.zeros(B, S, dtype=torch.float32, device="cuda")
+    ws = workspace(dlm.dlm_select_workspace_size(dlm.DLM_SCORE_COSINE, B, S))
+    dlm.dlm_saliency_select(dlm.DLM_SCORE_COSINE, cur, prev, lo=0, hi=S, threshold=tau, idx=idx,
+                            counts=counts, offsets=offsets, scores=scores, workspace=ws)
+    torch.cuda.synchronize()
+    assert maxabs(host(scores), ref["scores"]) <= 1e-5
+    off_g = offsets.cpu().numpy()
+    check_selection(idx.cpu().numpy(), counts.cpu().numpy(), off_g, ref["scores"], 0, S, tau)
+    assert int(torch.count_nonzero(ws)) == 0, "workspace ticket not restored to zero"
+
+    n = int(ref["offsets"][-1])
+    idx_o, off_o = i32(ref["idx"]), i32(ref["offsets"])
+    q = torch.zeros(max(n, 1), s.Hq, s.hd, dtype=cur.dtype, device="cuda")
+    kc, vc = dev(kc0, dt), dev(vc0, dt)
+    dlm.dlm_gather_qkv_scatter_kv(cur, idx_o, off_o, n, dev(inp.w_qkv, dt), s.Hq, s.Hkv, s.hd, q, kc, vc)
+    o = torch.zeros_like(q)
+    lse = torch.zeros(max(n, 1), s.Hq, dtype=torch.float32, device="cuda")
+    out = dev(out0, dt)
+    wo = dev(inp.w_o, dt) if inp.w_o is not None else None
+    wsa = workspace(dlm.dlm_partial_attn_workspace_size(
+        dlm.DLM_BF16 if dt == "bf16" else dlm.DLM_F32, max(n, 1), B, S, s.Hq, s.Hkv, s.hd))
+    dlm.dlm_partial_attn(q, idx_o, off_o, n, kc, vc, scale, o, lse, w_o=wo, out_cache=out, workspace=wsa)
+    torch.cuda.synchronize()
+
+    tol = TOL[dt]
+    sel = rows_mask(B, S, ref["idx"], ref["offsets"])
+    errs = {
+        "q": maxabs(host(q)[:n], ref["q"]),
+        "k": maxabs(host(kc)[sel], ref["k_cache"][sel]),
+        "v": maxabs(host(vc)[sel], ref["v_cache"][sel]),
+        "o": maxabs(host(o)[:n], ref["o"]),
+        "lse": maxabs(host(lse)[:n], ref["lse"]),
+        "out": maxabs(host(out)[sel], ref["out_cache"][sel]),
+    }
+    say(f"  n={n} max-abs errors: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k_, v_ in errs.items():
+        assert v_ <= tol, f"{k_}: {v_} > {tol}"
+    # untouched rows byte-identical
+    k_ref, v_ref, out_ref = dev(kc0, dt), dev(vc0, dt), dev(out0, dt)
+    keep = torch.from_numpy(~sel).cuda()
+    assert torch.equal(kc[keep], k_ref[keep]) and torch.equal(vc[keep], v_ref[keep])
+    assert torch.equal(out[keep], out_ref[keep])
+    return ref, n
+
+
+def test_tiny_fp32_step(dlm):
+    ref, n = run_cosine_step(dlm, W.TINY_FP32)
+    assert n == 16
+
+
+def test_bf16_s1024_step_full_size(dlm):
+    ref, n = run_cosine_step(dlm, W.BF16_S1024)
+    assert n == 102
+
+
+def test_bf16_step_ragged_multi_batch(dlm):
+    # several batch rows, a ragged selection count and tiles that do not divide evenly
+    run_cosine_step(dlm, W.BF16_S1024, B=3, S=200, D=512, Hq=4, Hkv=2, hd=128, n_redrawn=37)
+
+
+def test_bf16_step_head_dim_64(dlm):
+    run_cosine_step(dlm, W.BF16_S1024, B=2, S=130, D=256, Hq=4, Hkv=4, hd=64, n_redrawn=19)
+
+
+def test_all_selected_equals_full_recompute(dlm):
+    # tau above every cosine: all rows recomputed -> the step equals a full pass on cur
+    ref, n = run_cosine_step(dlm, W.BF16_S1024, tau=2.0, B=1, S=96, D=256, Hq=2, Hkv=2, hd=128, n_redrawn=5)
+    assert n == 96
+
+
+def test_none_selected_returns_cache(dlm):
+    ref, n = run_cosine_step(dlm, W.BF16_S1024, tau=-2.0, B=2, S=64, D=256, Hq=2, Hkv=2, hd=128, n_redrawn=5)
+    assert n == 0
+
+
+# ---------------------------------------------------------------------------
+# lock loop (GQA, given scores, several steps carrying the caches)
+# ---------------------------------------------------------------------------
+def test_gqa_lock_loop_reduced(dlm):
+    inp = W.lock_loop_inputs(W.GQA_LOCK_LOOP, B=2, S=320, D=512, Hq=8, Hkv=2, steps=5)
+    s = inp.shape
+    B, S = s.B, s.S
+    scale = 1.0 / math.sqrt(s.hd)
+    say(f"[lock loop] B={B} S={S} D={s.D} Hq={s.Hq} Hkv={s.Hkv} steps={s.steps}")
+    kc_o = np.zeros((B, S, s.Hkv, s.hd))
+    vc_o = np.zeros_like(kc_o)
+    out_o = np.zeros((B, S, s.Hq * s.hd))
+    kc = torch.zeros(B, S, s.Hkv, s.hd, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    out = torch.zeros(B, S, s.Hq * s.hd, dtype=torch.bfloat16, device="cuda")
+    w = dev(inp.w_qkv, "bf16")
+    max_rows = B * S
+    q = torch.zeros(max_rows, s.Hq, s.hd, dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros_like(q)
+    lse = torch.zeros(max_rows, s.Hq, dtype=torch.float32, device="cuda")
+    idx = torch.zeros(B * S, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(B, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    wsa = workspace(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, max_rows, B, S, s.Hq, s.Hkv, s.hd))
+    for t in range(s.steps):
+        sc = inp.unlocked_scores(t)
+        x = inp.hidden(t)
+        ridx, rcounts, roff = O.compact(sc, 0, S, 0.5)
+        q_o, kc_o, vc_o = O.qkv_project_scatter(x, ridx, roff, inp.w_qkv, s.Hq, s.Hkv, s.hd, kc_o, vc_o)
+        o_o, lse_o = O.partial_attention(q_o, ridx, roff, kc_o, vc_o, s.Hq, s.Hkv, scale)
+        out_o = O.output_scatter(o_o, ridx, roff, out_o)
+
+        dlm.dlm_saliency_select(dlm.DLM_SCORE_GIVEN, dev(sc, "f32"), None, lo=0, hi=S, threshold=0.5,
+                                idx=idx, counts=counts, offsets=offsets)
+        xd = dev(x, "bf16")
+        dlm.dlm_gather_qkv_scatter_kv(xd, idx, offsets, max_rows, w, s.Hq, s.Hkv, s.hd, q, kc, vc)
+        dlm.dlm_partial_attn(q, idx, offsets, max_rows, kc, vc, scale, o, lse, out_cache=out, workspace=wsa)
+        torch.cuda.synchronize()
+        n = int(roff[-1])
+        assert np.array_equal(offsets.cpu().numpy(), roff) and np.array_equal(idx.cpu().numpy()[:n], ridx)
+        errs = dict(q=maxabs(host(q)[:n], q_o), k=maxabs(host(kc), kc_o), v=maxabs(host(vc), vc_o),
+                    o=maxabs(host(o)[:n], o_o), lse=maxabs(host(lse)[:n], lse_o), out=maxabs(host(out), out_o))
+        say(f"  step {t}: n={n} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        for k_, v_ in errs.items():
+            assert v_ <= TOL["bf16"], f"step {t} {k_}: {v_}"
+
+
+# ---------------------------------------------------------------------------
+# attention column sums + top-k
+# ---------------------------------------------------------------------------
+def run_colsum(dlm, zero_q=False, **override):
+    inp = W.colsum_inputs(W.COLSUM_TOP64, zero_q=zero_q, **override)
+    s = inp.shape
+    B, S, nq = s.B, s.S, s.S - s.prompt
+    scale = 1.0 / math.sqrt(s.hd)
+    say(f"[colsum] B={B} S={S} prompt={s.prompt} Hq={s.Hq} Hkv={s.Hkv} k={s.k} zero_q={zero_q}")
+    sc = inp.masked_scores()
+    idx = torch.zeros(B * S, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(B, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    dlm.dlm_saliency_select(dlm.DLM_SCORE_GIVEN, dev(sc), None, lo=0, hi=S, threshold=0.5, idx=idx,
+                            counts=counts, offsets=offsets)
+    ridx, _, roff = O.compact(sc, 0, S, 0.5)
+    q_np = inp.q.reshape(B * nq, s.Hq, s.hd)
+    o_o, lse_o = O.partial_attention(q_np, ridx, roff, inp.k_cache, inp.v_cache, s.Hq, s.Hkv, scale)
+    c_o = O.column_sums(q_np, roff, inp.k_cache, lse_o, s.Hq, s.Hkv, scale)
+    q = dev(q_np, "bf16")
+    kc, vc = dev(inp.k_cache, "bf16"), dev(inp.v_cache, "bf16")
+    n = B * nq
+    o = torch.zeros_like(q)
+    lse = torch.zeros(n, s.Hq, dtype=torch.float32, device="cuda")
+    wsa = workspace(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, n, B, S, s.Hq, s.Hkv, s.hd))
+    dlm.dlm_partial_attn(q, idx, offsets, n, kc, vc, scale, o, lse, workspace=wsa)
+    colsum = torch.zeros(B, S, dtype=torch.float32, device="cuda")
+    ti = torch.zeros(B, s.k, dtype=torch.int32, device="cuda")
+    tv = torch.zeros(B, s.k, dtype=torch.float32, device="cuda")
+    wsc = workspace(dlm.dlm_attn_colsum_workspace_size(B, S, s.Hkv))
+    dlm.dlm_attn_colsum(q, offsets, n, kc, lse, scale, colsum, key_lo=s.prompt, key_hi=S, k=s.k,
+                        topk_idx=ti, topk_val=tv, workspace=wsc)
+    torch.cuda.synchronize()
+    assert np.array_equal(offsets.cpu().numpy(), roff)
+    c_g = host(colsum)
+    errs = dict(o=maxabs(host(o), o_o), lse=maxabs(host(lse), lse_o), colsum=maxabs(c_g, c_o))
+    say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k_, v_ in errs.items():
+        assert v_ <= TOL["bf16"], f"{k_}: {v_}"
+    # column sums total the number of selected queries times the heads
+    assert np.allclose(c_g.sum(axis=1), s.Hq * nq, rtol=1e-5)
+    ti_g = ti.cpu().numpy()
+    check_topk(ti_g, c_o, s.prompt, S, s.k)
+    tv_g = tv.cpu().numpy()
+    assert np.all(np.diff(tv_g, axis=1) <= 0)
+    for b in range(B):
+        assert np.array_equal(tv_g[b], c_g[b, ti_g[b]].astype(np.float32))
+    # determinism: a second run is bit-identical
+    c2 = torch.zeros_like(colsum)
+    ti2 = torch.zeros_like(ti)
+    dlm.dlm_attn_colsum(q, offsets, n, kc, lse, scale, c2, key_lo=s.prompt, key_hi=S, k=s.k,
+                        topk_idx=ti2, workspace=wsc)
+    torch.cuda.synchronize()
+    assert torch.equal(c2, colsum) and torch.equal(ti2, ti)
+    return ti_g, c_g
+
+
+def test_colsum_topk_reduced(dlm):
+    run_colsum(dlm, B=2, S=1024, prompt=256, Hq=4, Hkv=4, k=16)
+
+
+def test_colsum_topk_gqa_ragged(dlm):
+    run_colsum(dlm, B=3, S=520, prompt=77, Hq=8, Hkv=2, k=24)
+
+
+def test_colsum_uniform_ties_pick_lowest_positions(dlm):
+    ti, c = run_colsum(dlm, zero_q=True, B=2, S=512, prompt=128, Hq=4, Hkv=4, k=20)
+    assert ti.tolist() == [list(range(128, 148))] * 2
+
+
+# ---------------------------------------------------------------------------
+# confidence + longest stable prefix
+# ---------------------------------------------------------------------------
+def lsp_shape(**kw):
+    D = kw.get("D", 256)
+    base = dict(B=3, S=160, prompt=32, D=D, V=2048, w_std=0.02 * math.sqrt(4096 / D), steps=8)
+    base.update(kw)
+    return W.LspShape(**{**W.LSP_COMMIT.__dict__, **base})
+
+
+def stability_state(ring, amb_ring, mp, conf, band=BAND):
+    """1 stable / 0 not / 2 ambiguous, per generated position of one batch row."""
+    eq = np.all(ring == ring[:, :1], axis=1) & (ring[:, 0] != -1)
+    amb_arg = np.any(amb_ring, axis=1)
+    st = np.where(eq & (mp >= conf), 1, 0)
+    amb = amb_arg | (np.abs(mp - conf) <= band)
+    return np.where(amb, 2, st)
+
+
+def test_confidence_and_stable_prefix_loop(dlm):
+    sh = lsp_shape()
+    inp = W.lsp_inputs(sh)
+    B, S, S_gen = sh.B, sh.S, inp.S_gen
+    say(f"[lsp] B={B} S={S} D={sh.D} V={sh.V} steps={sh.steps}")
+    w = dev(inp.w_lm, "bf16")
+    scores = torch.zeros(B, S, dtype=torch.float32, device="cuda")
+    argmax = torch.full((B, S), -1, dtype=torch.int32, device="cuda")
+    ring = torch.full((B, S_gen, sh.W), -1, dtype=torch.int32, device="cuda")
+    committed = torch.zeros(B, dtype=torch.int32, device="cuda")
+    idx = torch.zeros(B * S, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(B, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    n_act = inp.n_active()
+    ws = workspace(dlm.dlm_select_workspace_size(dlm.DLM_SCORE_CONFIDENCE, B, S, sh.V, B * n_act))
+    ring_o = np.full((B, S_gen, sh.W), -1, np.int64)
+    amb_o = np.zeros((B, S_gen, sh.W), bool)
+    arg_o = np.full((B, S), -1, np.int64)
+    mp_o = np.zeros((B, S))
+    amb_now = np.zeros((B, S), bool)
+    for t in range(sh.steps):
+        rows = inp.active_rows(t)
+        h = inp.hidden(t)
+        ev_idx, ev_off = W.pack_rows(rows)
+        dlm.dlm_saliency_select(dlm.DLM_SCORE_CONFIDENCE, dev(h, "bf16"), w, lo=sh.prompt, hi=S,
+                                threshold=sh.conf, idx=idx, counts=counts, offsets=offsets,
+                                scores=scores, argmax=argmax, eval_idx=i32(ev_idx),
+                                eval_offsets=i32(ev_off), max_eval=len(ev_idx), workspace=ws)
+        torch.cuda.synchronize()
+        sc_g, am_g = scores.cpu().numpy(), argmax.cpu().numpy()
+        worst = 0.0
+        for b in range(B):
+            mp, a, gap = O.confidence(h[b, rows[b]], inp.w_lm)
+            arg_o[b, rows[b]] = a
+            mp_o[b, rows[b]] = mp
+            amb_now[b, rows[b]] = gap <= BAND
+            clear = gap > BAND
+            assert np.array_equal(am_g[b, rows[b]][clear], a[clear]), f"step {t} b {b}: argmax"
+            worst = max(worst, maxabs(sc_g[b, rows[b]], mp))
+        assert worst <= TOL["bf16"]
+        check_selection(idx.cpu().numpy(), counts.cpu().numpy(), offsets.cpu().numpy(), mp_o,
+                        sh.prompt, S, sh.conf) if t == 0 else None
+        prev_L = committed.cpu().numpy().copy()
+        dlm.dlm_stable_prefix(argmax, scores, sh.prompt, S, ring, t, sh.conf, committed)
+        torch.cuda.synchronize()
+        ring_o[:, :, t % sh.W] = arg_o[:, sh.prompt:]
+        amb_o[:, :, t % sh.W] = amb_now[:, sh.prompt:]
+        L_g = committed.cpu().numpy()
+        for b in range(B):
+            st = stability_state(ring_o[b], amb_o[b], mp_o[b, sh.prompt:], sh.conf)
+            adm = O.admissible_frontiers({int(prev_L[b])}, st, S_gen, 0)
+            assert int(L_g[b]) in adm, f"step {t} b {b}: frontier {L_g[b]} not in {sorted(adm)}"
+        say(f"  step {t}: frontiers {L_g.tolist()} max-prob err {worst:.2e}")
+    assert committed.cpu().numpy().max() > 0
+
+
+def test_stable_prefix_bit_exact_on_given_inputs(dlm):
+    """Prefix step alone, fed identical float32 max-probs: the frontiers and the
+    ring must match the oracle bit for bit (decisions in the same precision)."""
+    rng = np.random.default_rng(21)
+    B, S, gen_lo, Wd = 5, 700, 60, 3
+    S_gen = S - gen_lo
+    ring_o = np.full((B, S_gen, Wd), -1, np.int64)
+    com_o = np.zeros(B, np.int64)
+    ring = torch.full((B, S_gen, Wd), -1, dtype=torch.int32, device="cuda")
+    com = torch.zeros(B, dtype=torch.int32, device="cuda")
+    say(f"[prefix] B={B} S={S} gen_lo={gen_lo}")
+    for t in range(12):
+        am = rng.integers(0, 2, size=(B, S)).astype(np.int64)
+        am[:, : gen_lo + 40 * t] = 1                                    # a growing stable head
+        mp = rng.choice(np.array([0.5, 0.9, 0.95, 0.8999999], np.float32), size=(B, S), p=[0.05, 0.3, 0.6, 0.05])
+        min_commit = t % 2
+        ring_o, com_new = O.stable_prefix_step(am, mp, ring_o, t, gen_lo, S, 0.9, min_commit, com_o)
+        dlm.dlm_stable_prefix(i32(am), torch.from_numpy(mp).cuda(), gen_lo, S, ring, t, 0.9, com,
+                              min_commit=min_commit)
+        torch.cuda.synchronize()
+        assert np.array_equal(com.cpu().numpy(), com_new), f"step {t}"
+        assert np.array_equal(ring.cpu().numpy(), ring_o)
+        com_o = com_new
+    assert com_o.max() > 0
