@@ -95,12 +95,14 @@ class StepSet:
                                   dtype=torch.uint8, device="cuda")
         self.ws_attn = torch.zeros(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, max_rows, B, S, s.Hq, s.Hkv, s.hd),
                                    dtype=torch.uint8, device="cuda")
+        self.ws_qkv = torch.zeros(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, max_rows, s.Hq, s.Hkv, s.hd),
+                                  dtype=torch.uint8, device="cuda")
         # cache state of the previous step: a full pass (every row selected) on prev
         all_rows = torch.zeros(B, S, dtype=torch.float32, device="cuda")
         dlm.dlm_saliency_select(dlm.DLM_SCORE_GIVEN, all_rows, None, lo=0, hi=S, threshold=0.5,
                                 idx=self.idx, counts=self.counts, offsets=self.offsets)
         dlm.dlm_gather_qkv_scatter_kv(self.prev, self.idx, self.offsets, B * S, self.w, s.Hq, s.Hkv,
-                                      s.hd, self.q, self.kc, self.vc)
+                                      s.hd, self.q, self.kc, self.vc, workspace=self.ws_qkv)
         dlm.dlm_partial_attn(self.q, self.idx, self.offsets, B * S, self.kc, self.vc,
                              1.0 / math.sqrt(s.hd), self.o, self.lse, out_cache=self.out,
                              workspace=self.ws_attn)
@@ -142,7 +144,7 @@ def main():
                                             threshold=sh.tau, idx=st.idx, counts=st.counts,
                                             offsets=st.offsets, workspace=st.ws_sel),
             lambda: dlm.dlm_gather_qkv_scatter_kv(st.cur, st.idx, st.offsets, max_rows, st.w, s.Hq,
-                                                  s.Hkv, s.hd, st.q, st.kc, st.vc),
+                                                  s.Hkv, s.hd, st.q, st.kc, st.vc, workspace=st.ws_qkv),
             lambda: dlm.dlm_partial_attn(st.q, st.idx, st.offsets, max_rows, st.kc, st.vc, scale,
                                          st.o, st.lse, out_cache=st.out, workspace=st.ws_attn),
         ]
@@ -155,50 +157,67 @@ def main():
     n_sel = int(sets[0].offsets[-1].item())
     ref_o = [st.o[:n_sel].clone() for st in sets]
 
+    # one HIP graph holds one step of every rotating set (a replay = a.sets
+    # steps); single-step graphs cover a remainder so exactly --steps run
     capture_stream = torch.cuda.Stream()
-    graphs = []
-    for st in sets:
-        gs = []
-        for f in stages(st):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=capture_stream):
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=capture_stream):
+        for st in sets:
+            for f in stages(st):
                 f()
-            gs.append(g)
-        graphs.append(gs)
+    singles = []
+    for st in sets:
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1, stream=capture_stream):
+            for f in stages(st):
+                f()
+        singles.append(g1)
     torch.cuda.synchronize()
-
-    names = ["select", "qkv", "attn"]
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
-
-    def run_step(i, events=None):
-        gs = graphs[i % a.sets]
-        for k, g in enumerate(gs):
-            if events is not None:
-                events[k].record(stream)
-            g.replay()
-        if events is not None:
-            events[3].record(stream)
+    per_replay = a.sets
+    reps, rem = divmod(a.steps, per_replay)
+    steps = a.steps
 
     print(f"[bench] warmup {a.warmup} steps", file=sys.stderr, flush=True)
-    for i in range(a.warmup):
-        run_step(i)
+    for _ in range(max(1, a.warmup // per_replay)):
+        graph.replay()
     torch.cuda.synchronize()
     for r, st in enumerate(sets):   # graph replays reproduce the eager results
         assert int(st.offsets[-1].item()) == n_sel
         assert torch.equal(st.o[:n_sel], ref_o[r]), "graph replay differs from the eager step"
 
-    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] timing {steps} steps", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(a.steps):
-        run_step(i, ev[i])
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    for i in range(rem):
+        singles[i].replay()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage_ms = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)] for i in range(a.steps)])
-    step_ms = float(np.array([ev[i][0].elapsed_time(ev[i][3]) for i in range(a.steps)]).mean())
-    ms_per_step = wall * 1e3 / a.steps
+    step_ms = e0.elapsed_time(e1) / steps
+    ms_per_step = wall * 1e3 / steps
     value = n_sel / (ms_per_step / 1e3)
+
+    # stage durations: the same calls launched eagerly, bracketed by HIP events
+    # on the launch stream; a GPU sleep queued first lets the host enqueue far
+    # ahead, so the events see GPU time only (not Python call overhead)
+    names = ["select", "qkv", "attn"]
+    kreps = min(a.steps, 100)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(kreps)]
+    sleep_gpu(0.2 + kreps * 0.0005)
+    host0 = time.perf_counter()
+    for i in range(kreps):
+        fs = stages(sets[i % a.sets])
+        for k in range(3):
+            ev[i][k].record()
+            fs[k]()
+        ev[i][3].record()
+    host_enqueue_ms = (time.perf_counter() - host0) * 1e3
+    torch.cuda.synchronize()
+    stage_ms = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)] for i in range(kreps)])
 
     # algorithmic work per stage (bytes the method must move / flops it must do)
     D, N = sh.D, (s.Hq + 2 * s.Hkv) * s.hd
@@ -228,9 +247,10 @@ def main():
         "data": "synthetic (seeded N(0,1) hidden states, N(0,1/64) weights; random init, no checkpoint)",
         "config": {"workload": sh.name + " cosine-select step", "B": B, "S": S, "D": D,
                    "Hq": s.Hq, "Hkv": s.Hkv, "hd": s.hd, "n_selected": n_sel, "tau": sh.tau,
-                   "max_rows_bound": max_rows, "rotating_input_sets": a.sets, "launch": "hip graphs per stage"},
+                   "max_rows_bound": max_rows, "rotating_input_sets": a.sets, "launch": "one hip graph per round of the input sets"},
         "stages_ms": {k: float(v) for k, v in zip(names, mean)},
         "step_gpu_ms": step_ms,
+        "stage_timing": f"{kreps} eager steps behind a queued GPU sleep (host enqueue {host_enqueue_ms:.1f} ms)",
         "roofline": {"kernel": "gemm_bf16_kernel (gathered QKV + K/V scatter)", "bound": "hbm",
                      "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM, "traffic": traffic,
@@ -246,7 +266,7 @@ def main():
     }
     if not a.no_extras:
         print("[bench] other workloads", file=sys.stderr, flush=True)
-        del sets, graphs
+        del sets, graph, singles
         torch.cuda.empty_cache()
         out["other_workloads"] = {}
         for name, fn in EXTRAS:
@@ -271,12 +291,32 @@ def _gen(shape, seed, scale=1.0, dtype=None):
     return t.to(dtype or torch.bfloat16)
 
 
+_SLEEP_CYCLES_PER_S = None
+
+
+def sleep_gpu(seconds):
+    """Queue a GPU spin of about `seconds` (calibrated once) so that work the host
+    enqueues next starts back to back on the GPU."""
+    import torch
+    global _SLEEP_CYCLES_PER_S
+    if _SLEEP_CYCLES_PER_S is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(10_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_S = 10_000_000 / (a.elapsed_time(b) / 1e3)
+    torch.cuda._sleep(int(seconds * _SLEEP_CYCLES_PER_S))
+
+
 def _time(fn, reps, warmup=2):
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    sleep_gpu(0.05 + 0.002 * reps)
     for a, b in ev:
         a.record()
         fn()
@@ -392,6 +432,7 @@ def extra_lock_loop(dlm, W):
     counts = torch.empty(B, dtype=torch.int32, device="cuda")
     offsets = torch.empty(B + 1, dtype=torch.int32, device="cuda")
     wsa = torch.zeros(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, B * S, B, S, Hq, Hkv, hd), dtype=torch.uint8, device="cuda")
+    wsq = torch.zeros(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, B * S, Hq, Hkv, hd), dtype=torch.uint8, device="cuda")
     scale = 1.0 / math.sqrt(hd)
 
     def stage(t, k):
@@ -400,7 +441,8 @@ def extra_lock_loop(dlm, W):
             dlm.dlm_saliency_select(dlm.DLM_SCORE_GIVEN, s_t, None, lo=0, hi=S, threshold=0.5,
                                     idx=idx, counts=counts, offsets=offsets)
         elif k == 1:
-            dlm.dlm_gather_qkv_scatter_kv(xs[t % 2], idx, offsets, n, w, Hq, Hkv, hd, q, kc, vc)
+            dlm.dlm_gather_qkv_scatter_kv(xs[t % 2], idx, offsets, n, w, Hq, Hkv, hd, q, kc, vc,
+                                          workspace=wsq)
         else:
             dlm.dlm_partial_attn(q, idx, offsets, n, kc, vc, scale, o, lse, out_cache=out, workspace=wsa)
 

@@ -36,9 +36,9 @@
  *     nothing has been enqueued.  dlm_last_error() gives a thread-local text
  *     describing the last failure.
  *   - `workspace` is caller-owned device scratch of at least the size the
- *     matching *_workspace_size() query returns.  It must be zero-filled once
- *     after allocation; every call leaves its internal counters at zero
- *     again.  Calls that overlap in time must not share a workspace.
+ *     matching *_workspace_size() query returns (any contents; nothing in it
+ *     survives a call).  Calls that overlap in time must not share a
+ *     workspace.
  */
 #ifndef DLM_H
 #define DLM_H
@@ -94,7 +94,7 @@ const char* dlm_version(void);
  *     1 / sum_v exp(z_v - max z) (the max softmax probability) and
  *     argmax[b,i] = lowest v attaining max z.  `scores` [B,S] f32 and
  *     `argmax` [B,S] i32 are required and act as caches: entries of rows
- *     not evaluated keep their values.  D % 64 == 0, V % 128 == 0.
+ *     not evaluated keep their values.  D % 64 == 0, V % 256 == 0.
  * mode DLM_SCORE_GIVEN:  a = scores f32 [B,S] supplied by the caller
  *     (e.g. 1 = locked, 0 = unlocked); b, scores, argmax unused.
  *
@@ -128,13 +128,16 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b,
  *   k_cache[b, i, :, :]  = x[b,i] . W_k^T        k_cache, v_cache [B,S,Hkv,hd]
  *   v_cache[b, i, :, :]  = x[b,i] . W_v^T
  * Cache rows that are not selected are not touched (byte-identical).
- * bf16: D % 64 == 0, hd in {64,128}.  f32: D % 4 == 0.
+ * bf16: D % 64 == 0, hd in {64,128}, B*S*D < 2^31; the workspace (size from
+ * dlm_gather_qkv_workspace_size) holds split-K partial tiles, used when the
+ * selection is too short to fill the GPU.  f32: D % 4 == 0, no workspace.
  * ------------------------------------------------------------------------ */
+size_t dlm_gather_qkv_workspace_size(int dtype, int max_rows, int Hq, int Hkv, int hd);
 int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D,
                               const int32_t* idx, const int32_t* offsets, int max_rows,
                               const void* w_qkv, int Hq, int Hkv, int hd,
                               void* q_out, void* k_cache, void* v_cache,
-                              void* stream);
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * dlm_partial_attn
@@ -157,8 +160,9 @@ int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D,
  *                 w_o [D_out, Hq*hd] output-major; out_cache required.
  * Other out_cache rows are not touched.  hd in {64,128}.
  * ------------------------------------------------------------------------ */
+/* D_out_wo: D_out when a W_o projection will be passed, else 0 */
 size_t dlm_partial_attn_workspace_size(int dtype, int max_rows, int B, int S, int Hq, int Hkv,
-                                       int hd);
+                                       int hd, int D_out_wo);
 int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int32_t* offsets,
                      int max_rows, const void* k_cache, const void* v_cache,
                      int B, int S, int Hq, int Hkv, int hd, float scale,

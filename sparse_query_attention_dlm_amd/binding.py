@@ -46,11 +46,13 @@ lib.dlm_select_workspace_size.argtypes = [_I, _I, _I, _I, _I]
 lib.dlm_saliency_select.restype = _I
 lib.dlm_saliency_select.argtypes = [_I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _F,
                                     _P, _P, _P, _P, _P, _P, _Z, _P]
+lib.dlm_gather_qkv_workspace_size.restype = _Z
+lib.dlm_gather_qkv_workspace_size.argtypes = [_I] * 5
 lib.dlm_gather_qkv_scatter_kv.restype = _I
 lib.dlm_gather_qkv_scatter_kv.argtypes = [_I, _P, _I, _I, _I, _P, _P, _I, _P, _I, _I, _I,
-                                          _P, _P, _P, _P]
+                                          _P, _P, _P, _P, _Z, _P]
 lib.dlm_partial_attn_workspace_size.restype = _Z
-lib.dlm_partial_attn_workspace_size.argtypes = [_I] * 7
+lib.dlm_partial_attn_workspace_size.argtypes = [_I] * 8
 lib.dlm_partial_attn.restype = _I
 lib.dlm_partial_attn.argtypes = [_I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P,
                                  _P, _I, _P, _P, _Z, _P]
@@ -112,8 +114,12 @@ def dlm_select_workspace_size(mode, B, S, V=0, max_eval=0) -> int:
     return int(lib.dlm_select_workspace_size(mode, B, S, V, max_eval))
 
 
-def dlm_partial_attn_workspace_size(dtype, max_rows, B, S, Hq, Hkv, hd) -> int:
-    return int(lib.dlm_partial_attn_workspace_size(dtype, max_rows, B, S, Hq, Hkv, hd))
+def dlm_partial_attn_workspace_size(dtype, max_rows, B, S, Hq, Hkv, hd, D_out_wo=0) -> int:
+    return int(lib.dlm_partial_attn_workspace_size(dtype, max_rows, B, S, Hq, Hkv, hd, D_out_wo))
+
+
+def dlm_gather_qkv_workspace_size(dtype, max_rows, Hq, Hkv, hd) -> int:
+    return int(lib.dlm_gather_qkv_workspace_size(dtype, max_rows, Hq, Hkv, hd))
 
 
 def dlm_attn_colsum_workspace_size(B, S, Hkv) -> int:
@@ -146,13 +152,14 @@ def dlm_saliency_select(mode, a, b, *, lo, hi, threshold, idx, counts, offsets, 
 
 
 def dlm_gather_qkv_scatter_kv(x, idx, offsets, max_rows, w_qkv, Hq, Hkv, hd, q_out, k_cache,
-                              v_cache, stream=None):
+                              v_cache, workspace=None, stream=None):
     B, S, D = x.shape
+    wp, wn = _ws(workspace)
     rc = lib.dlm_gather_qkv_scatter_kv(
-        _dt(x), _ptr(x, "x"), B, S, D, _ptr(idx, "idx", torch.int32),
-        _ptr(offsets, "offsets", torch.int32), int(max_rows), _ptr(w_qkv, "w_qkv", x.dtype),
-        Hq, Hkv, hd, _ptr(q_out, "q_out", x.dtype), _ptr(k_cache, "k_cache", x.dtype),
-        _ptr(v_cache, "v_cache", x.dtype), _stream(stream))
+        _dt(x), _ptr(x, "x"), B, S, D, _ptr(idx, "idx", torch.int32, False),
+        _ptr(offsets, "offsets", torch.int32, False), int(max_rows), _ptr(w_qkv, "w_qkv", x.dtype),
+        Hq, Hkv, hd, _ptr(q_out, "q_out", x.dtype, False), _ptr(k_cache, "k_cache", x.dtype),
+        _ptr(v_cache, "v_cache", x.dtype), wp, wn, _stream(stream))
     _check(rc)
 
 

@@ -280,32 +280,38 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 }
 
 // Combine split-KV partials: O = sum_s exp(lse_s - L) O_s with L = logsumexp_s lse_s.
-template <int HD>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  const AttnPlan plan = attn_plan(a);
-  const int nsplit = plan.nsplit;
-  if (nsplit <= 1) return;  // the attention kernel already wrote the outputs
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int pr = blockIdx.x * 4 + wave;
-  const int n_rows = plan.n_rows;
-  if (pr >= n_rows * a.Hq) return;
-  const int row = pr / a.Hq, h = pr % a.Hq;
-  const size_t split_stride = (size_t)n_rows * a.Hq;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_lse[s * split_stride + pr]);
-  float tot = 0.f;
-  for (int s = 0; s < nsplit; ++s) tot += __expf(a.part_lse[s * split_stride + pr] - M);
-  const float L = M + __logf(tot);
+// One wave per (row, head): lane s < nsplit reads split s's LSE, the weights are
+// broadcast, and all splits' partial rows are loaded before any accumulation
+// (NS2 = 8 or 16 slots, branch-free; unused slots re-read a valid split with
+// weight 0).
+template <int HD, int NS2>
+__device__ __forceinline__ void merge_row(const AttnArgs& a, const AttnPlan& plan, int pr, int lane) {
   constexpr int E = HD / 64;
+  const int nsplit = plan.nsplit;
+  const size_t split_stride = (size_t)plan.n_rows * a.Hq;
+  const float ls = lane < nsplit ? a.part_lse[lane * split_stride + pr] : -INFINITY;
+  const float M = wave_max(ls);
+  const float wl = lane < nsplit ? __expf(ls - M) : 0.f;
+  const float tot = wave_sum(wl);
+  const float L = M + __logf(tot);
+  float v[NS2][E];
+#pragma unroll
+  for (int s = 0; s < NS2; ++s) {
+    const int sc = min(s, nsplit - 1);
+    const float* po = a.part_o + (sc * split_stride + pr) * HD + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[s][e] = po[e];
+  }
   float o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float w = __expf(a.part_lse[s * split_stride + pr] - L);
-    const float* po = a.part_o + (s * split_stride + pr) * HD;
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = fmaf(w, po[lane * E + e], o[e]);
+  for (int s = 0; s < NS2; ++s) {
+    const float w = __shfl(wl, s, 64) / tot;  // zero for slots past nsplit
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = fmaf(w, v[s][e], o[e]);
   }
+  const int row = pr / a.Hq, h = pr % a.Hq;
   u16* op = static_cast<u16*>(a.o) + (size_t)pr * HD + lane * E;
   u16* cp = nullptr;
   if (a.ctx_out) {
@@ -314,11 +320,24 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const u16 v = f32_to_bf16(o[e]);
-    op[e] = v;
-    if (cp) cp[e] = v;
+    const u16 bv = f32_to_bf16(o[e]);
+    op[e] = bv;
+    if (cp) cp[e] = bv;
   }
   if (lane == 0 && a.lse) a.lse[pr] = L;
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  const AttnPlan plan = attn_plan(a);
+  if (plan.nsplit <= 1) return;  // the attention kernel already wrote the outputs
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int pr = blockIdx.x * 4 + wave;
+  if (pr >= plan.n_rows * a.Hq) return;
+  if (plan.nsplit <= 8)
+    merge_row<HD, 8>(a, plan, pr, lane);
+  else
+    merge_row<HD, 16>(a, plan, pr, lane);
 }
 
 template <int HD>

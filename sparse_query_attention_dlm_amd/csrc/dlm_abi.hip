@@ -38,7 +38,7 @@ size_t elt(int dtype) { return dtype == DLM_BF16 ? 2 : 4; }
 #define REQUIRE_PTR(p) REQUIRE((p) != nullptr, "%s must not be NULL", #p)
 #define REQUIRE_ALIGNED(p) REQUIRE(aligned16(p), "%s must be 16-byte aligned", #p)
 
-constexpr size_t kTicketBytes = 256;
+constexpr size_t kSelectTicketBytes = 256;
 
 }  // namespace
 
@@ -60,10 +60,12 @@ const char* dlm_version(void) { return "libdlm 0.1 (gfx950)"; }
 
 // ---------------------------------------------------------------------------
 size_t dlm_select_workspace_size(int mode, int B, int S, int V, int max_eval) {
-  size_t n = kTicketBytes;
+  size_t n = kSelectTicketBytes;
   if (B > 0 && S > 0) n += round_up((size_t)B * S * sizeof(float), 256);
-  if (mode == DLM_SCORE_CONFIDENCE && V > 0 && max_eval > 0)
-    n += (size_t)max_eval * dlm::gemm_lmhead_ntile(V) * sizeof(float4);
+  if (mode == DLM_SCORE_CONFIDENCE && V > 0 && max_eval > 0) {
+    n += round_up((size_t)max_eval * dlm::gemm_lmhead_ntile(V) * sizeof(float4), 256);
+    n += dlm::gemm_workspace_bytes(dlm::EPI_LMHEAD, max_eval, V);
+  }
   return n;
 }
 
@@ -92,34 +94,37 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b, int B
   REQUIRE(D > 0, "D must be positive");
   REQUIRE_ALIGNED(a);
   REQUIRE_ALIGNED(b);
+  if (mode == DLM_SCORE_COSINE) {
+    REQUIRE(D % (dtype == DLM_BF16 ? 8 : 4) == 0, "D=%d must be a multiple of %d", D,
+            dtype == DLM_BF16 ? 8 : 4);
+  } else {
+    REQUIRE(dtype == DLM_BF16, "confidence scoring needs bf16 hidden states and W_lm");
+    REQUIRE_PTR(eval_idx);
+    REQUIRE_PTR(eval_offsets);
+    REQUIRE_PTR(scores);
+    REQUIRE_PTR(argmax);
+    REQUIRE(D % 64 == 0, "D=%d must be a multiple of 64", D);
+    REQUIRE(V > 0 && V % 256 == 0, "V=%d must be a positive multiple of 256", V);
+    REQUIRE(max_eval >= 0 && (long long)max_eval <= (long long)B * S, "max_eval=%d out of range",
+            max_eval);
+    REQUIRE((long long)B * S * D < (1ll << 31), "hidden states larger than 2^31 elements");
+  }
   const size_t need = dlm_select_workspace_size(mode, B, S, V, max_eval);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   REQUIRE_ALIGNED(workspace);
-  unsigned* ticket = static_cast<unsigned*>(workspace);
-  float* scratch = reinterpret_cast<float*>(static_cast<char*>(workspace) + kTicketBytes);
+  float* scratch = reinterpret_cast<float*>(static_cast<char*>(workspace) + kSelectTicketBytes);
   if (mode == DLM_SCORE_COSINE) {
-    REQUIRE(D % (dtype == DLM_BF16 ? 8 : 4) == 0, "D=%d must be a multiple of %d", D,
-            dtype == DLM_BF16 ? 8 : 4);
     float* sc = scores ? scores : scratch;
     return hip_status(dlm::launch_cosine_select(dtype, a, b, B, S, D, lo, hi, threshold, sc, idx,
-                                                counts, offsets, ticket, st),
+                                                counts, offsets, st),
                       "cosine select");
   }
-  // confidence
-  REQUIRE(dtype == DLM_BF16, "confidence scoring needs bf16 hidden states and W_lm");
-  REQUIRE_PTR(eval_idx);
-  REQUIRE_PTR(eval_offsets);
-  REQUIRE_PTR(scores);
-  REQUIRE_PTR(argmax);
-  REQUIRE(D % 64 == 0, "D=%d must be a multiple of 64", D);
-  REQUIRE(V > 0 && V % 128 == 0, "V=%d must be a positive multiple of 128", V);
-  REQUIRE(max_eval >= 0 && (long long)max_eval <= (long long)B * S, "max_eval=%d out of range",
-          max_eval);
   const int ntile = dlm::gemm_lmhead_ntile(V);
-  float4* part = reinterpret_cast<float4*>(static_cast<char*>(workspace) + kTicketBytes +
-                                           round_up((size_t)B * S * sizeof(float), 256));
+  char* wsb = static_cast<char*>(workspace) + kSelectTicketBytes + round_up((size_t)B * S * sizeof(float), 256);
+  float4* part = reinterpret_cast<float4*>(wsb);
+  char* gws = wsb + round_up((size_t)max_eval * ntile * sizeof(float4), 256);
   if (max_eval > 0) {
     dlm::GemmArgs g{};
     g.w = b;
@@ -131,23 +136,29 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b, int B
     g.idx = eval_idx;
     g.offsets = eval_offsets;
     g.max_rows = max_eval;
-    g.part = part;
+    g.lm_part = part;
     g.ntile = ntile;
+    g.part = reinterpret_cast<float*>(gws);
     int rc = hip_status(dlm::launch_gemm(DLM_BF16, dlm::EPI_LMHEAD, dlm::A_GATHER, g, st),
                         "LM-head GEMM");
     if (rc != DLM_OK) return rc;
   }
   return hip_status(dlm::launch_lmhead_combine(part, ntile, eval_idx, eval_offsets, max_eval, B, S,
                                                lo, hi, threshold, scores, argmax, idx, counts,
-                                               offsets, ticket, st),
+                                               offsets, st),
                     "LM-head combine");
 }
 
 // ---------------------------------------------------------------------------
+size_t dlm_gather_qkv_workspace_size(int dtype, int max_rows, int Hq, int Hkv, int hd) {
+  if (dtype != DLM_BF16 || max_rows <= 0 || Hq <= 0 || Hkv <= 0 || hd <= 0) return 0;
+  return dlm::gemm_workspace_bytes(dlm::EPI_QKV, max_rows, (Hq + 2 * Hkv) * hd);
+}
+
 int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D, const int32_t* idx,
                               const int32_t* offsets, int max_rows, const void* w_qkv, int Hq,
                               int Hkv, int hd, void* q_out, void* k_cache, void* v_cache,
-                              void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream) {
   REQUIRE(dtype == DLM_F32 || dtype == DLM_BF16, "unknown dtype %d", dtype);
   REQUIRE_PTR(x);
   REQUIRE_PTR(w_qkv);
@@ -172,8 +183,15 @@ int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D, con
   REQUIRE_ALIGNED(k_cache);
   REQUIRE_ALIGNED(v_cache);
   if (max_rows == 0) return DLM_OK;
+  const size_t need = dlm_gather_qkv_workspace_size(dtype, max_rows, Hq, Hkv, hd);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0) REQUIRE_ALIGNED(workspace);
+  REQUIRE((long long)B * S * D < (1ll << 31), "x larger than 2^31 elements is not supported");
   dlm::GemmArgs g{};
   g.w = w_qkv;
+  g.part = static_cast<float*>(workspace);
   g.x = x;
   g.K = D;
   g.N = (Hq + 2 * Hkv) * hd;
@@ -194,9 +212,11 @@ int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D, con
 
 // ---------------------------------------------------------------------------
 size_t dlm_partial_attn_workspace_size(int dtype, int max_rows, int B, int S, int Hq, int Hkv,
-                                       int hd) {
+                                       int hd, int D_out_wo) {
   if (max_rows <= 0 || B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || hd <= 0) return 0;
-  return dlm::attn_workspace_bytes(dtype, max_rows, B, S, Hq, Hkv, hd);
+  size_t n = round_up(dlm::attn_workspace_bytes(dtype, max_rows, B, S, Hq, Hkv, hd), 256);
+  if (dtype == DLM_BF16 && D_out_wo > 0) n += dlm::gemm_workspace_bytes(dlm::EPI_ROWS, max_rows, D_out_wo);
+  return n;
 }
 
 int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int32_t* offsets,
@@ -234,7 +254,7 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
     REQUIRE(D_out == Hq * hd, "without W_o, D_out (%d) must equal Hq*hd (%d)", D_out, Hq * hd);
   }
   if (out_cache) REQUIRE_ALIGNED(out_cache);
-  const size_t need = dlm::attn_workspace_bytes(dtype, max_rows, B, S, Hq, Hkv, hd);
+  const size_t need = dlm_partial_attn_workspace_size(dtype, max_rows, B, S, Hq, Hkv, hd, w_o ? D_out : 0);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -271,6 +291,11 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
   g.max_rows = max_rows;
   g.out = out_cache;
   g.ld_out = D_out;
+  if (dtype == DLM_BF16) {
+    char* gws = static_cast<char*>(workspace) +
+                round_up(dlm::attn_workspace_bytes(dtype, max_rows, B, S, Hq, Hkv, hd), 256);
+    g.part = reinterpret_cast<float*>(gws);
+  }
   return hip_status(dlm::launch_gemm(dtype, dlm::EPI_ROWS, dlm::A_COMPACT, g, st),
                     "output projection");
 }

@@ -24,124 +24,16 @@
 
 namespace dlm {
 
-template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, int m_tiles_max) {
-  constexpr int BK = 64, PITCH = BK + 8;  // u16 elements per LDS row (144 bytes)
-  constexpr int ROWS = TP + TT;
-  constexpr int CHUNKS = ROWS * (BK / 8);
-  static_assert(CHUNKS % 256 == 0, "tile rows must fill the workgroup");
-  constexpr int CPT = CHUNKS / 256;
+// Epilogues on the accumulated tile.  Register i of acc[a][b] in lane l holds
+// feature n0 + wp*WTP + 32a + 8(i/4) + 4(l/32) + i%4 of token m0 + wt*WTT + 32b + l%32.
+template <int TP, int TT, int WP, int WT, int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
+                                              f32x16 (&acc)[TP / WP / 32][TT / WT / 32], int m0,
+                                              int n0, int nt, const int* s_drow) {
   constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
-  static_assert(WP * WT == 4 && FP >= 1 && FT >= 1, "wave layout");
-  static_assert(PF >= 1, "prefetch depth");
-
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * ROWS * PITCH];
-  __shared__ long long s_arow[TT];
-  __shared__ int s_drow[TT];
-
-  const int n_rows = min(g.offsets[g.B], g.max_rows);
-  const int m_tiles = (n_rows + TT - 1) / TT;
-  const int nt = blockIdx.x / m_tiles_max, mt = blockIdx.x % m_tiles_max;
-  if (mt >= m_tiles) return;
-  const int m0 = mt * TT, n0 = nt * TP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  for (int t = tid; t < TT; t += 256) {
-    const int m = m0 + t;
-    long long arow = -1;
-    int drow = -1;
-    if (m < n_rows) {
-      const int b = batch_of(g.offsets, g.B, m);
-      drow = b * g.S + g.idx[m];
-      arow = (AMODE == A_GATHER) ? (long long)drow * g.K : (long long)m * g.K;
-    }
-    s_arow[t] = arow;
-    s_drow[t] = drow;
-  }
-  __syncthreads();
-
-  // Chunk j of this thread covers LDS row (tid/8 + 32 j), 16-byte column tid%8.
-  // Rows [0,TP) are weight rows (one base pointer, constant stride); rows
-  // [TP, TP+TT) are gathered token rows (32-bit element offsets).
-  constexpr int CW = TP / 32;  // chunks of weight rows per thread
-  constexpr int CX = CPT - CW;  // chunks of token rows per thread
-  const int r0 = tid >> 3, kc = tid & 7;
-  const u16* gW = static_cast<const u16*>(g.w) + (size_t)(n0 + r0) * g.K + kc * 8;
-  const u16* gX = static_cast<const u16*>(g.x) + kc * 8;
-  const size_t wstride = (size_t)32 * g.K;
-  uint32_t xoff[CX];
-#pragma unroll
-  for (int j = 0; j < CX; ++j) {
-    long long ar = s_arow[r0 + 32 * j];
-    if (ar < 0) ar = s_arow[0];  // padding rows of a ragged tile reuse a valid row
-    xoff[j] = (uint32_t)ar;
-  }
-  u16* const ldsw = lds + r0 * PITCH + kc * 8;
-  auto gload = [&](int j, int kstep) -> u32x4 {
-    const u16* p = (j < CW) ? gW + j * wstride : gX + xoff[j - CW];
-    return *reinterpret_cast<const u32x4*>(p + (size_t)kstep * BK);
-  };
-
-  f32x16 acc[FP][FT];
-#pragma unroll
-  for (int a = 0; a < FP; ++a)
-#pragma unroll
-    for (int b = 0; b < FT; ++b) acc[a][b] = f32x16{};
-
-  // Register ring of PF k-steps in flight; slot s holds k-step j with j % PF == s.
-  // The steady-state loop is branch-free (loads past the end re-read the last
-  // k-step, stores past the end go to the idle LDS buffer) and nk % PF == 0,
-  // so the compiler can count outstanding loads exactly and waits only for
-  // the oldest slot instead of draining the queue every k-step.
-  u32x4 stg[PF][CPT];
-  const int nk = g.K / BK;
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) stg[p][j] = gload(j, min(p, nk - 1));
-  }
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(ldsw + 32 * j * PITCH) = stg[0][j];
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) stg[0][j] = gload(j, min(PF, nk - 1));
-  __syncthreads();
-
   const int wp = wave / WT, wt = wave % WT;
   const int lr = lane & 31, lg = lane >> 5;
-  for (int kt0 = 0; kt0 < nk; kt0 += PF) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int kt = kt0 + u;
-      const int buf = (PF % 2 == 0) ? (u & 1) : (kt & 1);
-      const u16* sW = lds + buf * ROWS * PITCH;
-      const u16* sX = sW + TP * PITCH;
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 af[FP], bfr[FT];
-#pragma unroll
-        for (int a = 0; a < FP; ++a)
-          af[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(sW + (wp * WTP + a * 32 + lr) * PITCH +
-                                                            kk * 16 + lg * 8));
-#pragma unroll
-        for (int b = 0; b < FT; ++b)
-          bfr[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(sX + (wt * WTT + b * 32 + lr) * PITCH +
-                                                             kk * 16 + lg * 8));
-#pragma unroll
-        for (int a = 0; a < FP; ++a)
-#pragma unroll
-          for (int b = 0; b < FT; ++b) acc[a][b] = mfma32x32x16(af[a], bfr[b], acc[a][b]);
-      }
-      const int slot = (u + 1) % PF;  // compile-time after unrolling
-      u16* dst = ldsw + (buf ^ 1) * ROWS * PITCH;
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(dst + 32 * j * PITCH) = stg[slot][j];
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) stg[slot][j] = gload(j, min(kt + 1 + PF, nk - 1));
-      __syncthreads();
-    }
-  }
-
-  // ---------------------------------------------------------------- epilogue
   if constexpr (EPI == EPI_QKV || EPI == EPI_ROWS) {
 #pragma unroll
     for (int b = 0; b < FT; ++b) {
@@ -216,9 +108,233 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g, int m_tiles_
       int am = s_pa[0][t];
 #pragma unroll
       for (int w = 1; w < WP; ++w) merge_part(m, s, am, s_pm[w][t], s_ps[w][t], s_pa[w][t]);
-      g.part[(size_t)(m0 + t) * g.ntile + nt] = make_float4(m, s, __int_as_float(am), 0.f);
+      g.lm_part[(size_t)(m0 + t) * g.ntile + nt] = make_float4(m, s, __int_as_float(am), 0.f);
     }
   }
+}
+
+// Split-K plan, computed on the device from the real row count.  When the
+// output tiles are fewer than split_units, K is split over spare workgroups of
+// the grid: ks is a power of two that divides the k-steps into whole prefetch
+// rings (at least two rings per split), grown while units * ks stays below
+// kSplitTarget and within kSplitCap (the workspace) and the grid.
+constexpr int kSplitTarget = 768;
+constexpr int kSplitCap = 1024;
+
+// GATE: 0 = always run; 1 = run only when the device row count is <= kSkinnyRows;
+// 2 = run only when it is larger.  A host that only knows a loose upper bound
+// launches a GATE 1 and a GATE 2 kernel and the device picks the tiling.
+constexpr int kSkinnyRows = 128;
+struct GemmSplit {
+  int units;
+  int ks;
+};
+__device__ __forceinline__ GemmSplit gemm_split(int units, int grid, int nk, int pf,
+                                                int split_units) {
+  GemmSplit s{units, 1};
+  if (units <= 0 || units >= split_units) return s;
+  while (true) {
+    const int k2 = s.ks * 2;
+    if (units * k2 > kSplitCap || units * k2 > grid || units * s.ks >= kSplitTarget) break;
+    if (k2 > 8 || nk % k2 != 0 || (nk / k2) % pf != 0 || nk / k2 < 2 * pf) break;
+    s.ks = k2;
+  }
+  return s;
+}
+
+template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SPLIT_UNITS>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int BK = 64, PITCH = BK + 8;  // u16 elements per LDS row (144 bytes)
+  constexpr int ROWS = TP + TT;
+  constexpr int CHUNKS = ROWS * (BK / 8);
+  static_assert(CHUNKS % 256 == 0, "tile rows must fill the workgroup");
+  constexpr int CPT = CHUNKS / 256;
+  constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
+  static_assert(WP * WT == 4 && FP >= 1 && FT >= 1, "wave layout");
+  static_assert(PF >= 1, "prefetch depth");
+
+  __shared__ __attribute__((aligned(16))) u16 lds[2 * ROWS * PITCH];
+  __shared__ long long s_arow[TT];
+  __shared__ int s_drow[TT];
+
+  const int n_rows = min(g.offsets[g.B], g.max_rows);
+  if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
+  const int m_tiles = (n_rows + TT - 1) / TT;
+  const int n_tiles = g.N / TP;
+  const int nk_all = g.K / BK;
+  const GemmSplit sp = gemm_split(m_tiles * n_tiles, (int)gridDim.x, nk_all, PF, SPLIT_UNITS);
+  if ((int)blockIdx.x >= sp.units * sp.ks) return;
+  const int unit = (int)blockIdx.x % sp.units, ksi = (int)blockIdx.x / sp.units;
+  const int nt = unit / m_tiles, mt = unit % m_tiles;
+  const int m0 = mt * TT, n0 = nt * TP;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nk = nk_all / sp.ks;        // k-steps of this split
+  const int kbase = ksi * nk;           // first k-step of this split
+
+  for (int t = tid; t < TT; t += 256) {
+    const int m = m0 + t;
+    long long arow = -1;
+    int drow = -1;
+    if (m < n_rows) {
+      const int b = batch_of(g.offsets, g.B, m);
+      drow = b * g.S + g.idx[m];
+      arow = (AMODE == A_GATHER) ? (long long)drow * g.K : (long long)m * g.K;
+    }
+    s_arow[t] = arow;
+    s_drow[t] = drow;
+  }
+  __syncthreads();
+
+  // Chunk j of this thread covers LDS row (tid/8 + 32 j), 16-byte column tid%8.
+  // Rows [0,TP) are weight rows (one base pointer, constant stride); rows
+  // [TP, TP+TT) are gathered token rows (32-bit element offsets).
+  constexpr int CW = TP / 32;  // chunks of weight rows per thread
+  constexpr int CX = CPT - CW;  // chunks of token rows per thread
+  const int r0 = tid >> 3, kc = tid & 7;
+  const u16* gW = static_cast<const u16*>(g.w) + (size_t)(n0 + r0) * g.K + kc * 8;
+  const u16* gX = static_cast<const u16*>(g.x) + kc * 8;
+  const size_t wstride = (size_t)32 * g.K;
+  uint32_t xoff[CX];
+#pragma unroll
+  for (int j = 0; j < CX; ++j) {
+    long long ar = s_arow[r0 + 32 * j];
+    if (ar < 0) ar = s_arow[0];  // padding rows of a ragged tile reuse a valid row
+    xoff[j] = (uint32_t)ar;
+  }
+  u16* const ldsw = lds + r0 * PITCH + kc * 8;
+  auto gload = [&](int j, int kstep) -> u32x4 {
+    const u16* p = (j < CW) ? gW + j * wstride : gX + xoff[j - CW];
+    return *reinterpret_cast<const u32x4*>(p + (size_t)(kbase + kstep) * BK);
+  };
+
+  f32x16 acc[FP][FT];
+#pragma unroll
+  for (int a = 0; a < FP; ++a)
+#pragma unroll
+    for (int b = 0; b < FT; ++b) acc[a][b] = f32x16{};
+
+  // Register ring of PF k-steps in flight; slot s holds k-step j with j % PF == s.
+  // The steady-state loop is branch-free (loads past the end re-read the last
+  // k-step, stores past the end go to the idle LDS buffer) and nk % PF == 0,
+  // so the compiler can count outstanding loads exactly and waits only for
+  // the oldest slot instead of draining the queue every k-step.
+  u32x4 stg[PF][CPT];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) stg[p][j] = gload(j, min(p, nk - 1));
+  }
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(ldsw + 32 * j * PITCH) = stg[0][j];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) stg[0][j] = gload(j, min(PF, nk - 1));
+  __syncthreads();
+
+  const int wp = wave / WT, wt = wave % WT;
+  const int lr = lane & 31, lg = lane >> 5;
+  for (int kt0 = 0; kt0 < nk; kt0 += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int kt = kt0 + u;
+      const int buf = (PF % 2 == 0) ? (u & 1) : (kt & 1);
+      const u16* sW = lds + buf * ROWS * PITCH;
+      const u16* sX = sW + TP * PITCH;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 af[FP], bfr[FT];
+#pragma unroll
+        for (int a = 0; a < FP; ++a)
+          af[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(sW + (wp * WTP + a * 32 + lr) * PITCH +
+                                                            kk * 16 + lg * 8));
+#pragma unroll
+        for (int b = 0; b < FT; ++b)
+          bfr[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(sX + (wt * WTT + b * 32 + lr) * PITCH +
+                                                             kk * 16 + lg * 8));
+#pragma unroll
+        for (int a = 0; a < FP; ++a)
+#pragma unroll
+          for (int b = 0; b < FT; ++b) acc[a][b] = mfma32x32x16(af[a], bfr[b], acc[a][b]);
+      }
+      const int slot = (u + 1) % PF;  // compile-time after unrolling
+      u16* dst = ldsw + (buf ^ 1) * ROWS * PITCH;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(dst + 32 * j * PITCH) = stg[slot][j];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) stg[slot][j] = gload(j, min(kt + 1 + PF, nk - 1));
+      __syncthreads();
+    }
+  }
+
+  if (sp.ks > 1) {
+    // split-K: store the partial tile in register order (16-byte vectors,
+    // consecutive threads adjacent); gemm_splitk_reduce_kernel sums the
+    // splits in a fixed order after this kernel has finished
+    constexpr int NQ = FP * FT * 4;
+    float4* mine = reinterpret_cast<float4*>(g.part) + ((size_t)unit * sp.ks + ksi) * (NQ * 256);
+#pragma unroll
+    for (int a = 0; a < FP; ++a)
+#pragma unroll
+      for (int b = 0; b < FT; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          mine[((a * FT + b) * 4 + q) * 256 + tid] = make_float4(
+              acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
+    return;
+  }
+  gemm_epilogue<TP, TT, WP, WT, EPI>(g, acc, m0, n0, nt, s_drow);
+}
+
+// Second pass of split-K: one workgroup per output tile sums the partial tiles
+// of its splits in split order and runs the epilogue.  Exits at once when the
+// device plan did not split (the plan is recomputed from the same inputs).
+template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SPLIT_UNITS>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g, int main_grid) {
+  constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
+  constexpr int NQ = FP * FT * 4;
+  __shared__ int s_drow[TT];
+  const int n_rows = min(g.offsets[g.B], g.max_rows);
+  if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
+  const int m_tiles = (n_rows + TT - 1) / TT;
+  const int n_tiles = g.N / TP;
+  const GemmSplit sp = gemm_split(m_tiles * n_tiles, main_grid, g.K / 64, PF, SPLIT_UNITS);
+  if (sp.ks <= 1 || (int)blockIdx.x >= sp.units) return;
+  const int unit = blockIdx.x;
+  const int nt = unit / m_tiles, mt = unit % m_tiles;
+  const int m0 = mt * TT, n0 = nt * TP;
+  const int tid = threadIdx.x;
+  for (int t = tid; t < TT; t += 256) {
+    const int m = m0 + t;
+    s_drow[t] = m < n_rows ? batch_of(g.offsets, g.B, m) * g.S + g.idx[m] : -1;
+  }
+  __syncthreads();
+  const float4* all = reinterpret_cast<const float4*>(g.part) + (size_t)unit * sp.ks * (NQ * 256);
+  f32x16 acc[FP][FT];
+#pragma unroll
+  for (int a = 0; a < FP; ++a)
+#pragma unroll
+    for (int b = 0; b < FT; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int o = ((a * FT + b) * 4 + q) * 256 + tid;
+        float4 v[8];
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2)  // splits past ks re-read split 0 (weight 0 below)
+          v[k2] = all[(size_t)(k2 < sp.ks ? k2 : 0) * (NQ * 256) + o];
+        float4 sum = v[0];
+#pragma unroll
+        for (int k2 = 1; k2 < 8; ++k2)
+          if (k2 < sp.ks) {
+            sum.x += v[k2].x;
+            sum.y += v[k2].y;
+            sum.z += v[k2].z;
+            sum.w += v[k2].w;
+          }
+        acc[a][b][4 * q] = sum.x;
+        acc[a][b][4 * q + 1] = sum.y;
+        acc[a][b][4 * q + 2] = sum.z;
+        acc[a][b][4 * q + 3] = sum.w;
+      }
+  gemm_epilogue<TP, TT, WP, WT, EPI>(g, acc, m0, n0, nt, s_drow);
 }
 
 // fp32 path (small fp32 layers): one thread per output element, float4 loads,
@@ -257,44 +373,72 @@ __global__ __launch_bounds__(64) void gemm_f32_kernel(GemmArgs g) {
 }
 
 // Tile shapes (features x tokens, prefetch depth):
+//   short selections (<= 128 rows): 64 features x 128 tokens with an 8-deep
+//     register ring, one workgroup per CU and no split-K (measured: splitting
+//     K here costs more in partial-tile traffic than it gains in parallelism).
+//   medium selections: 128 x 128, 2-deep ring (two workgroups per CU).
 //   LM head and large selections: 256 x 256, each wave a 128 x 128 block, so
-//     every LDS fragment feeds four MFMAs; 1 k-step of prefetch.
-//   medium selections (<= 1024 rows): 128 x 128, 2 k-steps of prefetch (two
-//     workgroups per CU).
-//   short selections (<= 128 rows): 64 features x 128 tokens, 4 k-steps of
-//     prefetch, so the weight stream keeps enough bytes in flight per CU.
-// The prefetch depth is reduced to 2 or 1 when it does not divide K / 64.
+//     every LDS fragment feeds four MFMAs; 1-deep ring.
+// The ring depth is reduced when it does not divide K / 64.  When the device
+// finds fewer than SPLIT_UNITS output tiles it splits K (partials in the
+// workspace, summed by gemm_splitk_reduce_kernel).
 constexpr int kLmTP = 256;
 int gemm_lmhead_ntile(int V) { return V / kLmTP; }
 
-template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE>
-static void launch_bf16(const GemmArgs& g, hipStream_t st) {
-  const int m_tiles_max = (g.max_rows + TT - 1) / TT;
-  const int grid = (g.N / TP) * m_tiles_max;
-  hipLaunchKernelGGL((gemm_bf16_kernel<TP, TT, WP, WT, PF, EPI, AMODE>), dim3(grid), dim3(256), 0,
-                     st, g, m_tiles_max);
+static void tile_of(int epi, int max_rows, int N, int* TP, int* TT) {
+  if (epi == EPI_LMHEAD) { *TP = kLmTP; *TT = 256; return; }
+  if (max_rows <= 128 || N % 128 != 0) { *TP = 64; *TT = 128; return; }
+  if (max_rows <= 1024 || N % 256 != 0) { *TP = 128; *TT = 128; return; }
+  *TP = 256; *TT = 256;
 }
 
-template <int TP, int TT, int PFMAX, int EPI, int AMODE>
+size_t gemm_workspace_bytes(int epi, int max_rows, int N) {
+  if (max_rows <= 0) return 0;
+  int TP, TT;
+  tile_of(epi, max_rows, N, &TP, &TT);
+  return (size_t)kSplitCap * TP * TT * sizeof(float);
+}
+
+template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SU>
+static void launch_bf16(const GemmArgs& g, hipStream_t st) {
+  // one workgroup per possible output tile, and at least kSplitCap so that the
+  // device can split K when the real selection turns out to be short
+  const int m_tiles_max = (g.max_rows + TT - 1) / TT;
+  int grid = (g.N / TP) * m_tiles_max;
+  if (SU > 0 && grid < kSplitCap) grid = kSplitCap;
+  hipLaunchKernelGGL((gemm_bf16_kernel<TP, TT, WP, WT, PF, EPI, AMODE, GATE, SU>), dim3(grid),
+                     dim3(256), 0, st, g);
+  if (SU > 0)  // the split-K reduction pass (exits at once when the device did not split)
+    hipLaunchKernelGGL((gemm_splitk_reduce_kernel<TP, TT, WP, WT, PF, EPI, AMODE, GATE, SU>),
+                       dim3(SU), dim3(256), 0, st, g, grid);
+}
+
+template <int TP, int TT, int PFMAX, int EPI, int AMODE, int GATE, int SU>
 static void launch_pf(const GemmArgs& g, hipStream_t st) {
-  // the prefetch depth must divide the number of 64-wide k-steps
+  // the ring depth must divide the number of 64-wide k-steps
   const int nk = g.K / 64;
-  if (PFMAX >= 4 && nk % 4 == 0)
-    launch_bf16<TP, TT, 2, 2, (PFMAX >= 4 ? 4 : 1), EPI, AMODE>(g, st);
+  if (PFMAX >= 8 && nk % 8 == 0)
+    launch_bf16<TP, TT, 2, 2, (PFMAX >= 8 ? 8 : 1), EPI, AMODE, GATE, SU>(g, st);
+  else if (PFMAX >= 4 && nk % 4 == 0)
+    launch_bf16<TP, TT, 2, 2, (PFMAX >= 4 ? 4 : 1), EPI, AMODE, GATE, SU>(g, st);
   else if (PFMAX >= 2 && nk % 2 == 0)
-    launch_bf16<TP, TT, 2, 2, (PFMAX >= 2 ? 2 : 1), EPI, AMODE>(g, st);
+    launch_bf16<TP, TT, 2, 2, (PFMAX >= 2 ? 2 : 1), EPI, AMODE, GATE, SU>(g, st);
   else
-    launch_bf16<TP, TT, 2, 2, 1, EPI, AMODE>(g, st);
+    launch_bf16<TP, TT, 2, 2, 1, EPI, AMODE, GATE, SU>(g, st);
 }
 
 template <int EPI, int AMODE>
 static void launch_by_rows(const GemmArgs& g, hipStream_t st) {
-  if (g.max_rows <= 128 || g.N % 128 != 0)
-    launch_pf<64, 128, 4, EPI, AMODE>(g, st);
-  else if (g.max_rows <= 1024 || g.N % 256 != 0)
-    launch_pf<128, 128, 2, EPI, AMODE>(g, st);
+  if (g.max_rows <= kSkinnyRows || g.N % 128 != 0) {
+    launch_pf<64, 128, 8, EPI, AMODE, 0, 0>(g, st);
+    return;
+  }
+  // loose bound: the device decides between the skinny and the large tiling
+  launch_pf<64, 128, 8, EPI, AMODE, 1, 0>(g, st);
+  if (g.max_rows <= 1024 || g.N % 256 != 0)
+    launch_pf<128, 128, 2, EPI, AMODE, 2, 256>(g, st);
   else
-    launch_pf<256, 256, 1, EPI, AMODE>(g, st);
+    launch_pf<256, 256, 1, EPI, AMODE, 2, 256>(g, st);
 }
 
 hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStream_t st) {
@@ -308,7 +452,7 @@ hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStre
     return hipGetLastError();
   }
   if (epi == EPI_LMHEAD)
-    launch_pf<kLmTP, 256, 1, EPI_LMHEAD, A_GATHER>(g, st);
+    launch_pf<kLmTP, 256, 1, EPI_LMHEAD, A_GATHER, 0, 256>(g, st);
   else if (epi == EPI_QKV)
     launch_by_rows<EPI_QKV, A_GATHER>(g, st);
   else

@@ -10,15 +10,13 @@ namespace dlm {
 // select.hip
 hipError_t launch_cosine_select(int dtype, const void* cur, const void* prev, int B, int S, int D,
                                 int lo, int hi, float thr, float* scores, int32_t* idx,
-                                int32_t* counts, int32_t* offsets, unsigned* ticket,
-                                hipStream_t st);
+                                int32_t* counts, int32_t* offsets, hipStream_t st);
 hipError_t launch_given_select(const float* scores, int B, int S, int lo, int hi, float thr,
                                int32_t* idx, int32_t* counts, int32_t* offsets, hipStream_t st);
 hipError_t launch_lmhead_combine(const float4* part, int ntile, const int32_t* eval_idx,
                                  const int32_t* eval_offsets, int max_eval, int B, int S, int lo,
                                  int hi, float thr, float* scores, int32_t* argmax, int32_t* idx,
-                                 int32_t* counts, int32_t* offsets, unsigned* ticket,
-                                 hipStream_t st);
+                                 int32_t* counts, int32_t* offsets, hipStream_t st);
 
 // gemm.hip -- D^T[n][m] = sum_k W[n][k] * A[row(m)][k]; W output-major [N][K].
 enum GemmEpilogue { EPI_QKV = 0, EPI_ROWS = 1, EPI_LMHEAD = 2 };
@@ -38,10 +36,13 @@ struct GemmArgs {
   // EPI_ROWS: out[(b*S + idx[m])*ld_out + n]
   void* out;
   int ld_out;
-  // EPI_LMHEAD: part[m*ntile + tile] = {max, sum exp(z-max), argmax bits, 0}
-  float4* part;
+  // EPI_LMHEAD: lm_part[m*ntile + tile] = {max, sum exp(z-max), argmax bits, 0}
+  float4* lm_part;
   int ntile;
+  // split-K scratch (workspace): partial tiles
+  float* part;
 };
+size_t gemm_workspace_bytes(int epi, int max_rows, int N);
 hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStream_t st);
 int gemm_lmhead_ntile(int V);
 

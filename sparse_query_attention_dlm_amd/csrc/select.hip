@@ -6,11 +6,10 @@
 // softmax probability is the confidence signal; SureLock, Methodik: unlocked
 // positions are the ones recomputed.  Selected iff score < threshold.
 //
-// Layout: one wave64 per scored row, 16-byte vector loads, float32
-// accumulation, wave reductions.  The compaction (flag -> prefix sum ->
-// ascending index list, counts, offsets) runs in the last workgroup to finish
-// (atomic ticket in the caller's zeroed workspace; the ticket wraps back to
-// zero, so the workspace is left zeroed for the next call).
+// Layout: one wave64 per scored row, 16-byte vector loads (a lane's whole
+// batch of loads is issued before any arithmetic), float32 accumulation, wave
+// reductions.  The compaction (flag -> prefix sum -> ascending index list,
+// counts, offsets) is a single-workgroup pass launched after the scores.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -69,24 +68,11 @@ __device__ void compact_rows(const float* scores, int B, int S, int lo, int hi, 
   if (tid == 0) offsets[B] = base;
 }
 
-// Returns true in every thread of the workgroup that finished last.
-__device__ __forceinline__ bool last_block_done(unsigned* ticket) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicInc(ticket, gridDim.x - 1) == gridDim.x - 1);
-  __syncthreads();
-  if (s_last) __threadfence();  // acquire: other workgroups' scores are visible
-  return s_last;
-}
-
 template <int DT>
 __global__ __launch_bounds__(256) void cosine_select_kernel(const void* __restrict__ cur,
                                                             const void* __restrict__ prev, int B,
                                                             int S, int D, int lo, int hi, float thr,
-                                                            float* scores, int32_t* idx,
-                                                            int32_t* counts, int32_t* offsets,
-                                                            unsigned* ticket) {
+                                                            float* scores) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int W = hi - lo;
   const int r = blockIdx.x * 4 + wave;
@@ -144,8 +130,6 @@ __global__ __launch_bounds__(256) void cosine_select_kernel(const void* __restri
       scores[(size_t)b * S + i] = den > 0.f ? dot / den : 0.f;
     }
   }
-  if (!last_block_done(ticket)) return;
-  compact_rows(scores, B, S, lo, hi, thr, idx, counts, offsets);
 }
 
 __global__ __launch_bounds__(256) void given_select_kernel(const float* __restrict__ scores, int B,
@@ -159,9 +143,8 @@ __global__ __launch_bounds__(256) void given_select_kernel(const float* __restri
 // into max-prob and argmax per evaluated row, then the compaction.
 __global__ __launch_bounds__(256) void lmhead_combine_kernel(
     const float4* __restrict__ part, int ntile, const int32_t* __restrict__ eval_idx,
-    const int32_t* __restrict__ eval_offsets, int max_eval, int B, int S, int lo, int hi,
-    float thr, float* scores, int32_t* argmax, int32_t* idx, int32_t* counts, int32_t* offsets,
-    unsigned* ticket) {
+    const int32_t* __restrict__ eval_offsets, int max_eval, int B, int S, float* scores,
+    int32_t* argmax) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + wave;
   const int n_eval = min(eval_offsets[B], max_eval);
@@ -185,28 +168,11 @@ __global__ __launch_bounds__(256) void lmhead_combine_kernel(
       argmax[pos] = a;
     }
   }
-  if (!last_block_done(ticket)) return;
-  compact_rows(scores, B, S, lo, hi, thr, idx, counts, offsets);
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_cosine_select(int dtype, const void* cur, const void* prev, int B, int S, int D,
-                                int lo, int hi, float thr, float* scores, int32_t* idx,
-                                int32_t* counts, int32_t* offsets, unsigned* ticket,
-                                hipStream_t st) {
-  const int rows = B * (hi - lo);
-  const int grid = rows > 0 ? (rows + 3) / 4 : 1;
-  if (dtype == 1)
-    hipLaunchKernelGGL(cosine_select_kernel<1>, dim3(grid), dim3(256), 0, st, cur, prev, B, S, D,
-                       lo, hi, thr, scores, idx, counts, offsets, ticket);
-  else
-    hipLaunchKernelGGL(cosine_select_kernel<0>, dim3(grid), dim3(256), 0, st, cur, prev, B, S, D,
-                       lo, hi, thr, scores, idx, counts, offsets, ticket);
-  return hipGetLastError();
-}
-
 hipError_t launch_given_select(const float* scores, int B, int S, int lo, int hi, float thr,
                                int32_t* idx, int32_t* counts, int32_t* offsets, hipStream_t st) {
   hipLaunchKernelGGL(given_select_kernel, dim3(1), dim3(256), 0, st, scores, B, S, lo, hi, thr,
@@ -214,15 +180,39 @@ hipError_t launch_given_select(const float* scores, int B, int S, int lo, int hi
   return hipGetLastError();
 }
 
+// Scoring runs over many workgroups; the compaction is a second, single-
+// workgroup launch.  (Ordering the two inside one kernel would need agent-scope
+// fences, which on this multi-XCD part write back and invalidate whole L2s.)
+hipError_t launch_cosine_select(int dtype, const void* cur, const void* prev, int B, int S, int D,
+                                int lo, int hi, float thr, float* scores, int32_t* idx,
+                                int32_t* counts, int32_t* offsets, hipStream_t st) {
+  const int rows = B * (hi - lo);
+  if (rows > 0) {
+    const int grid = (rows + 3) / 4;
+    if (dtype == 1)
+      hipLaunchKernelGGL(cosine_select_kernel<1>, dim3(grid), dim3(256), 0, st, cur, prev, B, S, D,
+                         lo, hi, thr, scores);
+    else
+      hipLaunchKernelGGL(cosine_select_kernel<0>, dim3(grid), dim3(256), 0, st, cur, prev, B, S, D,
+                         lo, hi, thr, scores);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_given_select(scores, B, S, lo, hi, thr, idx, counts, offsets, st);
+}
+
 hipError_t launch_lmhead_combine(const float4* part, int ntile, const int32_t* eval_idx,
                                  const int32_t* eval_offsets, int max_eval, int B, int S, int lo,
                                  int hi, float thr, float* scores, int32_t* argmax, int32_t* idx,
-                                 int32_t* counts, int32_t* offsets, unsigned* ticket,
-                                 hipStream_t st) {
-  const int grid = max_eval > 0 ? (max_eval + 3) / 4 : 1;
-  hipLaunchKernelGGL(lmhead_combine_kernel, dim3(grid), dim3(256), 0, st, part, ntile, eval_idx,
-                     eval_offsets, max_eval, B, S, lo, hi, thr, scores, argmax, idx, counts, offsets, ticket);
-  return hipGetLastError();
+                                 int32_t* counts, int32_t* offsets, hipStream_t st) {
+  if (max_eval > 0) {
+    const int grid = (max_eval + 3) / 4;
+    hipLaunchKernelGGL(lmhead_combine_kernel, dim3(grid), dim3(256), 0, st, part, ntile, eval_idx,
+                       eval_offsets, max_eval, B, S, scores, argmax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_given_select(scores, B, S, lo, hi, thr, idx, counts, offsets, st);
 }
 
 }  // namespace dlm

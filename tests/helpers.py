@@ -21,9 +21,10 @@ def host(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def workspace(nbytes):
-    """Zero-filled device scratch (the library requires zero-filled workspaces)."""
-    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device="cuda")
+def workspace(nbytes, fill=0x5A):
+    """Device scratch of the requested size, filled with junk: the library must
+    not depend on workspace contents."""
+    return torch.full((max(int(nbytes), 16),), fill, dtype=torch.uint8, device="cuda")
 
 
 def maxabs(a, b):

@@ -85,23 +85,23 @@ def test_select_rejections(lib):
     assert select(lib, D=12) == INVALID                      # bf16 rows must be 16-byte chunks
     assert select(lib, ws=0) == WORKSPACE
     assert select(lib, ws_bytes=8) == WORKSPACE
-    assert select(lib, mode=CONFIDENCE, dtype=F32, V=128, ev=FAKE, evo=FAKE, scores=FAKE, argmax=FAKE) == INVALID
-    assert select(lib, mode=CONFIDENCE, V=100, ev=FAKE, evo=FAKE, scores=FAKE, argmax=FAKE, max_eval=4) == INVALID
-    assert select(lib, mode=CONFIDENCE, V=128, ev=FAKE, evo=FAKE, scores=0, argmax=FAKE) == INVALID
-    assert select(lib, mode=CONFIDENCE, V=128, ev=0, evo=FAKE, scores=FAKE, argmax=FAKE) == INVALID
+    assert select(lib, mode=CONFIDENCE, dtype=F32, V=256, ev=FAKE, evo=FAKE, scores=FAKE, argmax=FAKE) == INVALID
+    assert select(lib, mode=CONFIDENCE, V=128, ev=FAKE, evo=FAKE, scores=FAKE, argmax=FAKE, max_eval=4) == INVALID
+    assert select(lib, mode=CONFIDENCE, V=256, ev=FAKE, evo=FAKE, scores=0, argmax=FAKE) == INVALID
+    assert select(lib, mode=CONFIDENCE, V=256, ev=0, evo=FAKE, scores=FAKE, argmax=FAKE) == INVALID
 
 
 def test_select_workspace_size_covers_partials(lib):
     small = lib.dlm_select_workspace_size(COSINE, 2, 100, 0, 0)
     assert small >= 2 * 100 * 4
     big = lib.dlm_select_workspace_size(CONFIDENCE, 2, 100, 32768, 50)
-    assert big >= small + 50 * (32768 // 128) * 16
+    assert big >= small + 50 * (32768 // 256) * 16
 
 
 def gqkv(lib, dtype=BF16, x=FAKE, B=1, S=8, D=64, idx=FAKE, off=FAKE, max_rows=8, w=FAKE, Hq=2, Hkv=1,
          hd=64, q=FAKE, k=FAKE, v=FAKE):
     return lib.dlm_gather_qkv_scatter_kv(dtype, p(x), B, S, D, p(idx), p(off), max_rows, p(w), Hq, Hkv,
-                                         hd, p(q), p(k), p(v), p(0))
+                                         hd, p(q), p(k), p(v), p(FAKE), ctypes.c_size_t(1 << 30), p(0))
 
 
 def test_gather_qkv_rejections(lib):
@@ -113,6 +113,13 @@ def test_gather_qkv_rejections(lib):
     assert gqkv(lib, max_rows=9) == INVALID                  # more rows than B*S
     assert gqkv(lib, max_rows=-1) == INVALID
     assert gqkv(lib, k=MISALIGNED) == INVALID
+    # bf16 needs split-K scratch sized by dlm_gather_qkv_workspace_size
+    lib.dlm_gather_qkv_workspace_size.restype = ctypes.c_size_t
+    need = lib.dlm_gather_qkv_workspace_size(BF16, 8, 2, 1, 64)
+    assert need > 0
+    assert lib.dlm_gather_qkv_scatter_kv(BF16, p(FAKE), 1, 8, 64, p(FAKE), p(FAKE), 8, p(FAKE), 2, 1, 64,
+                                         p(FAKE), p(FAKE), p(FAKE), p(FAKE), ctypes.c_size_t(need - 1),
+                                         p(0)) == WORKSPACE
 
 
 def attn(lib, dtype=BF16, q=FAKE, idx=FAKE, off=FAKE, max_rows=4, k=FAKE, v=FAKE, B=1, S=64, Hq=2,
@@ -132,7 +139,7 @@ def test_partial_attn_rejections(lib):
     assert attn(lib, out=FAKE, D_out=100) == INVALID         # no W_o: D_out must be Hq*hd
     assert attn(lib, wo=FAKE, out=FAKE, D_out=100) == INVALID  # bf16 W_o: D_out % 64
     # a short selection needs split-KV scratch: refused without it
-    need = lib.dlm_partial_attn_workspace_size(BF16, 4, 1, 4096, 2, 1, 128)
+    need = lib.dlm_partial_attn_workspace_size(BF16, 4, 1, 4096, 2, 1, 128, 0)
     assert need > 0
     assert attn(lib, S=4096) == WORKSPACE
     assert attn(lib, S=4096, ws=FAKE, ws_bytes=need - 1) == WORKSPACE

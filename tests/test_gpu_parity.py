@@ -58,19 +58,21 @@ def run_cosine_step(dlm, shape, tau=None, **override):
     assert maxabs(host(scores), ref["scores"]) <= 1e-5
     off_g = offsets.cpu().numpy()
     check_selection(idx.cpu().numpy(), counts.cpu().numpy(), off_g, ref["scores"], 0, S, tau)
-    assert int(torch.count_nonzero(ws)) == 0, "workspace ticket not restored to zero"
 
     n = int(ref["offsets"][-1])
     idx_o, off_o = i32(ref["idx"]), i32(ref["offsets"])
     q = torch.zeros(max(n, 1), s.Hq, s.hd, dtype=cur.dtype, device="cuda")
     kc, vc = dev(kc0, dt), dev(vc0, dt)
-    dlm.dlm_gather_qkv_scatter_kv(cur, idx_o, off_o, n, dev(inp.w_qkv, dt), s.Hq, s.Hkv, s.hd, q, kc, vc)
+    dcode = dlm.DLM_BF16 if dt == "bf16" else dlm.DLM_F32
+    wsq = workspace(dlm.dlm_gather_qkv_workspace_size(dcode, n, s.Hq, s.Hkv, s.hd))
+    dlm.dlm_gather_qkv_scatter_kv(cur, idx_o, off_o, n, dev(inp.w_qkv, dt), s.Hq, s.Hkv, s.hd, q, kc, vc,
+                                  workspace=wsq)
     o = torch.zeros_like(q)
     lse = torch.zeros(max(n, 1), s.Hq, dtype=torch.float32, device="cuda")
     out = dev(out0, dt)
     wo = dev(inp.w_o, dt) if inp.w_o is not None else None
     wsa = workspace(dlm.dlm_partial_attn_workspace_size(
-        dlm.DLM_BF16 if dt == "bf16" else dlm.DLM_F32, max(n, 1), B, S, s.Hq, s.Hkv, s.hd))
+        dcode, max(n, 1), B, S, s.Hq, s.Hkv, s.hd, out0.shape[-1] if inp.w_o is not None else 0))
     dlm.dlm_partial_attn(q, idx_o, off_o, n, kc, vc, scale, o, lse, w_o=wo, out_cache=out, workspace=wsa)
     torch.cuda.synchronize()
 
@@ -114,6 +116,16 @@ def test_bf16_step_head_dim_64(dlm):
     run_cosine_step(dlm, W.BF16_S1024, B=2, S=130, D=256, Hq=4, Hkv=4, hd=64, n_redrawn=19)
 
 
+def test_bf16_step_deep_split_k(dlm):
+    # few output tiles and a long reduction: the GEMM splits K eight ways on the device
+    run_cosine_step(dlm, W.BF16_S1024, B=1, S=256, D=4096, Hq=4, Hkv=4, hd=128, n_redrawn=40)
+
+
+def test_bf16_step_with_output_projection(dlm):
+    # bf16 layer with a W_o projection before the output scatter (ragged, two batch rows)
+    run_cosine_step(dlm, W.BF16_S1024, B=2, S=150, D=256, Hq=4, Hkv=4, hd=64, n_redrawn=23, with_wo=True)
+
+
 def test_all_selected_equals_full_recompute(dlm):
     # tau above every cosine: all rows recomputed -> the step equals a full pass on cur
     ref, n = run_cosine_step(dlm, W.BF16_S1024, tau=2.0, B=1, S=96, D=256, Hq=2, Hkv=2, hd=128, n_redrawn=5)
@@ -149,6 +161,7 @@ def test_gqa_lock_loop_reduced(dlm):
     counts = torch.zeros(B, dtype=torch.int32, device="cuda")
     offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
     wsa = workspace(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, max_rows, B, S, s.Hq, s.Hkv, s.hd))
+    wsq = workspace(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, max_rows, s.Hq, s.Hkv, s.hd))
     for t in range(s.steps):
         sc = inp.unlocked_scores(t)
         x = inp.hidden(t)
@@ -160,7 +173,8 @@ def test_gqa_lock_loop_reduced(dlm):
         dlm.dlm_saliency_select(dlm.DLM_SCORE_GIVEN, dev(sc, "f32"), None, lo=0, hi=S, threshold=0.5,
                                 idx=idx, counts=counts, offsets=offsets)
         xd = dev(x, "bf16")
-        dlm.dlm_gather_qkv_scatter_kv(xd, idx, offsets, max_rows, w, s.Hq, s.Hkv, s.hd, q, kc, vc)
+        dlm.dlm_gather_qkv_scatter_kv(xd, idx, offsets, max_rows, w, s.Hq, s.Hkv, s.hd, q, kc, vc,
+                                      workspace=wsq)
         dlm.dlm_partial_attn(q, idx, offsets, max_rows, kc, vc, scale, o, lse, out_cache=out, workspace=wsa)
         torch.cuda.synchronize()
         n = int(roff[-1])
