@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the dominant-kernel measurements of the other four workloads")
     ap.add_argument("--only-extras", action="store_true", help="measure only the other workloads")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="measure a plain streaming read and a 1 GiB copy (the reference for the "
+                         "FETCH_SIZE / WRITE_SIZE byte counters) and exit")
     return ap.parse_args()
 
 
@@ -122,6 +125,9 @@ def main():
     from sparse_query_attention_dlm_amd import workloads as W
 
     torch.cuda.set_device(0)
+    if a.hbm_ceiling:
+        print(json.dumps(hbm_ceiling()), flush=True)
+        return
     if a.only_extras:
         res = {}
         for name, fn in EXTRAS:
@@ -502,6 +508,19 @@ def extra_tiny(dlm, W):
     t = _time(g.replay, 50, warmup=5)
     n = int(offsets[-1].item())
     return {"workload": sh.name, "n_selected": n, "step_us": t * 1e3, "tokens_per_s": n / (t / 1e3)}
+
+
+def hbm_ceiling():
+    """Measured HBM ceilings on this GPU: a streaming read (torch sum over 2 GiB,
+    more than the Infinity Cache) and a plain 1 GiB device copy."""
+    import torch
+    n = (2 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty(n // 2, dtype=torch.float32, device="cuda")
+    t_sum = _time(lambda: x.sum(), 10)
+    t_copy = _time(lambda: y.copy_(x[: n // 2]), 10)
+    return {"stream_read_GBps": n * 4 / t_sum / 1e6, "copy_1GiB_GBps_read_plus_write": 2 * (n // 2) * 4 / t_copy / 1e6,
+            "copy_bytes_each_way": (n // 2) * 4}
 
 
 EXTRAS = (("tiny_fp32", extra_tiny), ("colsum_top64", extra_colsum), ("lsp_commit", extra_lsp),

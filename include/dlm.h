@@ -128,9 +128,10 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b,
  *   k_cache[b, i, :, :]  = x[b,i] . W_k^T        k_cache, v_cache [B,S,Hkv,hd]
  *   v_cache[b, i, :, :]  = x[b,i] . W_v^T
  * Cache rows that are not selected are not touched (byte-identical).
- * bf16: D % 64 == 0, hd in {64,128}, B*S*D < 2^31; the workspace (size from
- * dlm_gather_qkv_workspace_size) holds split-K partial tiles, used when the
- * selection is too short to fill the GPU.  f32: D % 4 == 0, no workspace.
+ * bf16: D % 64 == 0, hd in {64,128}, B*S*D < 2^31.  The workspace (size from
+ * dlm_gather_qkv_workspace_size) holds split-K partial tiles; only bounds
+ * above 1024 rows with (Hq+2*Hkv)*hd % 256 == 0 need one (size 0 otherwise,
+ * and then workspace may be NULL).  f32: D % 4 == 0, no workspace.
  * ------------------------------------------------------------------------ */
 size_t dlm_gather_qkv_workspace_size(int dtype, int max_rows, int Hq, int Hkv, int hd);
 int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D,

@@ -142,8 +142,14 @@ __device__ __forceinline__ GemmSplit gemm_split(int units, int grid, int nk, int
   return s;
 }
 
-template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SPLIT_UNITS>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+// u16 elements of the double-buffered LDS tile (rows padded to 72 elements)
+constexpr int gemm_lds_u16(int TP, int TT) { return 2 * (TP + TT) * 72; }
+
+// One output tile (or one K-split of it) of the gathered GEMM; the caller
+// provides the LDS buffers so that several tilings can share one allocation.
+template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int SPLIT_UNITS>
+__device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u16* lds,
+                                               long long* s_arow, int* s_drow) {
   constexpr int BK = 64, PITCH = BK + 8;  // u16 elements per LDS row (144 bytes)
   constexpr int ROWS = TP + TT;
   constexpr int CHUNKS = ROWS * (BK / 8);
@@ -152,13 +158,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
   static_assert(WP * WT == 4 && FP >= 1 && FT >= 1, "wave layout");
   static_assert(PF >= 1, "prefetch depth");
+  static_assert(2 * ROWS * PITCH == gemm_lds_u16(TP, TT), "LDS size");
 
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * ROWS * PITCH];
-  __shared__ long long s_arow[TT];
-  __shared__ int s_drow[TT];
-
-  const int n_rows = min(g.offsets[g.B], g.max_rows);
-  if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
   const int m_tiles = (n_rows + TT - 1) / TT;
   const int n_tiles = g.N / TP;
   const int nk_all = g.K / BK;
@@ -284,6 +285,34 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   gemm_epilogue<TP, TT, WP, WT, EPI>(g, acc, m0, n0, nt, s_drow);
 }
 
+template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SPLIT_UNITS>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) u16 lds[gemm_lds_u16(TP, TT)];
+  __shared__ long long s_arow[TT];
+  __shared__ int s_drow[TT];
+  const int n_rows = min(g.offsets[g.B], g.max_rows);
+  if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
+  gemm_tile_body<TP, TT, WP, WT, PF, EPI, AMODE, SPLIT_UNITS>(g, n_rows, lds, s_arow, s_drow);
+}
+
+// One launch for a host that only knows a loose row bound: the device row
+// count picks the weight-streaming tiling (<= kSkinnyRows rows) or the large
+// tiling, so no second launch has to start just to exit.  Both bodies share
+// one LDS allocation sized for the larger of the two.
+template <int TP, int TT, int PF, int TP2, int TT2, int PF2, int EPI, int AMODE, int SU2>
+__global__ __launch_bounds__(256) void gemm_dual_kernel(GemmArgs g) {
+  constexpr int L1 = gemm_lds_u16(TP, TT), L2 = gemm_lds_u16(TP2, TT2);
+  constexpr int TTM = TT > TT2 ? TT : TT2;
+  __shared__ __attribute__((aligned(16))) u16 lds[L1 > L2 ? L1 : L2];
+  __shared__ long long s_arow[TTM];
+  __shared__ int s_drow[TTM];
+  const int n_rows = min(g.offsets[g.B], g.max_rows);
+  if (n_rows <= kSkinnyRows)
+    gemm_tile_body<TP, TT, 2, 2, PF, EPI, AMODE, 0>(g, n_rows, lds, s_arow, s_drow);
+  else
+    gemm_tile_body<TP2, TT2, 2, 2, PF2, EPI, AMODE, SU2>(g, n_rows, lds, s_arow, s_drow);
+}
+
 // Second pass of split-K: one workgroup per output tile sums the partial tiles
 // of its splits in split order and runs the epilogue.  Exits at once when the
 // device plan did not split (the plan is recomputed from the same inputs).
@@ -385,18 +414,13 @@ __global__ __launch_bounds__(64) void gemm_f32_kernel(GemmArgs g) {
 constexpr int kLmTP = 256;
 int gemm_lmhead_ntile(int V) { return V / kLmTP; }
 
-static void tile_of(int epi, int max_rows, int N, int* TP, int* TT) {
-  if (epi == EPI_LMHEAD) { *TP = kLmTP; *TT = 256; return; }
-  if (max_rows <= 128 || N % 128 != 0) { *TP = 64; *TT = 128; return; }
-  if (max_rows <= 1024 || N % 256 != 0) { *TP = 128; *TT = 128; return; }
-  *TP = 256; *TT = 256;
-}
-
+// Split-K scratch: only the LM head and the 256 x 256 tiling (loose bounds
+// above 1024 rows) may split K; the other tilings never need scratch.
 size_t gemm_workspace_bytes(int epi, int max_rows, int N) {
   if (max_rows <= 0) return 0;
-  int TP, TT;
-  tile_of(epi, max_rows, N, &TP, &TT);
-  return (size_t)kSplitCap * TP * TT * sizeof(float);
+  if (epi == EPI_LMHEAD) return (size_t)kSplitCap * kLmTP * 256 * sizeof(float);
+  if (max_rows <= 1024 || N % 256 != 0) return 0;
+  return (size_t)kSplitCap * 256 * 256 * sizeof(float);
 }
 
 template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SU>
@@ -427,18 +451,47 @@ static void launch_pf(const GemmArgs& g, hipStream_t st) {
     launch_bf16<TP, TT, 2, 2, 1, EPI, AMODE, GATE, SU>(g, st);
 }
 
+// Skinny tiling 64 x 128 (PF k-steps in flight) for <= kSkinnyRows rows, a
+// large tiling above; split-K only for the 256 x 256 tiling (its reduction
+// pass exits at once unless the device split).
+template <int PF1, int TP2, int TT2, int PF2, int EPI, int AMODE, int SU2>
+static void launch_dual(const GemmArgs& g, hipStream_t st) {
+  const int grid1 = (g.N / 64) * ((kSkinnyRows + 127) / 128);
+  int grid2 = (g.N / TP2) * ((g.max_rows + TT2 - 1) / TT2);
+  if (SU2 > 0 && grid2 < kSplitCap) grid2 = kSplitCap;
+  const int grid = grid1 > grid2 ? grid1 : grid2;
+  hipLaunchKernelGGL((gemm_dual_kernel<64, 128, PF1, TP2, TT2, PF2, EPI, AMODE, SU2>),
+                     dim3(grid), dim3(256), 0, st, g);
+  if (SU2 > 0)
+    hipLaunchKernelGGL((gemm_splitk_reduce_kernel<TP2, TT2, 2, 2, PF2, EPI, AMODE, 2, SU2>), dim3(SU2),
+                       dim3(256), 0, st, g, grid);
+}
+
 template <int EPI, int AMODE>
 static void launch_by_rows(const GemmArgs& g, hipStream_t st) {
+  const int nk = g.K / 64;
   if (g.max_rows <= kSkinnyRows || g.N % 128 != 0) {
-    launch_pf<64, 128, 8, EPI, AMODE, 0, 0>(g, st);
+    launch_pf<64, 128, 4, EPI, AMODE, 0, 0>(g, st);
     return;
   }
-  // loose bound: the device decides between the skinny and the large tiling
-  launch_pf<64, 128, 8, EPI, AMODE, 1, 0>(g, st);
-  if (g.max_rows <= 1024 || g.N % 256 != 0)
-    launch_pf<128, 128, 2, EPI, AMODE, 2, 256>(g, st);
-  else
-    launch_pf<256, 256, 1, EPI, AMODE, 2, 256>(g, st);
+  // loose bound: one launch; the device picks the tiling from the real count
+  const bool mid = g.max_rows <= 1024 || g.N % 256 != 0;
+  if (nk % 4 == 0) {
+    if (mid)
+      launch_dual<4, 128, 128, 4, EPI, AMODE, 0>(g, st);
+    else
+      launch_dual<4, 256, 256, 1, EPI, AMODE, 256>(g, st);
+  } else if (nk % 2 == 0) {
+    if (mid)
+      launch_dual<2, 128, 128, 2, EPI, AMODE, 0>(g, st);
+    else
+      launch_dual<2, 256, 256, 1, EPI, AMODE, 256>(g, st);
+  } else {
+    if (mid)
+      launch_dual<1, 128, 128, 1, EPI, AMODE, 0>(g, st);
+    else
+      launch_dual<1, 256, 256, 1, EPI, AMODE, 256>(g, st);
+  }
 }
 
 hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStream_t st) {

@@ -113,12 +113,17 @@ def test_gather_qkv_rejections(lib):
     assert gqkv(lib, max_rows=9) == INVALID                  # more rows than B*S
     assert gqkv(lib, max_rows=-1) == INVALID
     assert gqkv(lib, k=MISALIGNED) == INVALID
-    # bf16 needs split-K scratch sized by dlm_gather_qkv_workspace_size
+    # bounds up to 1024 rows never split K: no scratch
     lib.dlm_gather_qkv_workspace_size.restype = ctypes.c_size_t
-    need = lib.dlm_gather_qkv_workspace_size(BF16, 8, 2, 1, 64)
+    assert lib.dlm_gather_qkv_workspace_size(BF16, 1024, 2, 1, 64) == 0
+    # a looser bound may split K on the device: scratch sized by the query
+    need = lib.dlm_gather_qkv_workspace_size(BF16, 2048, 2, 1, 64)
     assert need > 0
-    assert lib.dlm_gather_qkv_scatter_kv(BF16, p(FAKE), 1, 8, 64, p(FAKE), p(FAKE), 8, p(FAKE), 2, 1, 64,
-                                         p(FAKE), p(FAKE), p(FAKE), p(FAKE), ctypes.c_size_t(need - 1),
+    assert lib.dlm_gather_qkv_scatter_kv(BF16, p(FAKE), 1, 2048, 64, p(FAKE), p(FAKE), 2048, p(FAKE), 2,
+                                         1, 64, p(FAKE), p(FAKE), p(FAKE), p(FAKE),
+                                         ctypes.c_size_t(need - 1), p(0)) == WORKSPACE
+    assert lib.dlm_gather_qkv_scatter_kv(BF16, p(FAKE), 1, 2048, 64, p(FAKE), p(FAKE), 2048, p(FAKE), 2,
+                                         1, 64, p(FAKE), p(FAKE), p(FAKE), p(0), ctypes.c_size_t(0),
                                          p(0)) == WORKSPACE
 
 

@@ -186,6 +186,55 @@ def test_gqa_lock_loop_reduced(dlm):
             assert v_ <= TOL["bf16"], f"step {t} {k_}: {v_}"
 
 
+def test_loose_row_bound_picks_every_tiling(dlm):
+    """The host passes max_rows = B*S > 1024 while the device count is 50, 600
+    or 2000: the one GEMM launch must take the weight-streaming tiling, then
+    the 256 x 256 tiling with K split over spare workgroups, and the attention
+    its matching plans; every result against the oracle."""
+    B, S, D, Hq, Hkv, hd = 2, 1100, 1024, 4, 2, 64
+    N = (Hq + 2 * Hkv) * hd
+    scale = 1.0 / math.sqrt(hd)
+    rng = np.random.default_rng(11)
+    x = W.round_bf16(rng.standard_normal((B, S, D)))
+    w = W.round_bf16(rng.standard_normal((N, D)) / 32.0)
+    kc0 = W.round_bf16(rng.standard_normal((B, S, Hkv, hd)))
+    vc0 = W.round_bf16(rng.standard_normal((B, S, Hkv, hd)))
+    out0 = W.round_bf16(rng.standard_normal((B, S, Hq * hd)))
+    max_rows = B * S
+    q = torch.zeros(max_rows, Hq, hd, dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros_like(q)
+    lse = torch.zeros(max_rows, Hq, dtype=torch.float32, device="cuda")
+    idx = torch.zeros(B * S, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(B, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    wsq = workspace(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, max_rows, Hq, Hkv, hd))
+    wsa = workspace(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, max_rows, B, S, Hq, Hkv, hd))
+    xd, wd = dev(x, "bf16"), dev(w, "bf16")
+    for per_b in (25, 300, 1000):
+        sc = np.ones((B, S))
+        for b in range(B):
+            sc[b, rng.choice(S, per_b, replace=False)] = 0.0
+        ridx, _, roff = O.compact(sc, 0, S, 0.5)
+        q_o, kc_o, vc_o = O.qkv_project_scatter(x, ridx, roff, w, Hq, Hkv, hd, kc0, vc0)
+        o_o, lse_o = O.partial_attention(q_o, ridx, roff, kc_o, vc_o, Hq, Hkv, scale)
+        out_o = O.output_scatter(o_o, ridx, roff, out0)
+        say(f"[loose bound] max_rows={max_rows} n={int(roff[-1])} D={D} N={N}")
+        kc, vc, out = dev(kc0, "bf16"), dev(vc0, "bf16"), dev(out0, "bf16")
+        dlm.dlm_saliency_select(dlm.DLM_SCORE_GIVEN, dev(sc, "f32"), None, lo=0, hi=S, threshold=0.5,
+                                idx=idx, counts=counts, offsets=offsets)
+        dlm.dlm_gather_qkv_scatter_kv(xd, idx, offsets, max_rows, wd, Hq, Hkv, hd, q, kc, vc,
+                                      workspace=wsq)
+        dlm.dlm_partial_attn(q, idx, offsets, max_rows, kc, vc, scale, o, lse, out_cache=out, workspace=wsa)
+        torch.cuda.synchronize()
+        n = int(roff[-1])
+        assert np.array_equal(idx.cpu().numpy()[:n], ridx)
+        errs = dict(q=maxabs(host(q)[:n], q_o), k=maxabs(host(kc), kc_o), v=maxabs(host(vc), vc_o),
+                    o=maxabs(host(o)[:n], o_o), lse=maxabs(host(lse)[:n], lse_o), out=maxabs(host(out), out_o))
+        say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        for k_, v_ in errs.items():
+            assert v_ <= TOL["bf16"], f"n={n} {k_}: {v_}"
+
+
 # ---------------------------------------------------------------------------
 # attention column sums + top-k
 # ---------------------------------------------------------------------------
