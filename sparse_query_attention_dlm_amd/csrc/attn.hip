@@ -36,13 +36,16 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const u16* p) {
 // from the selection counts (the host only knows an upper bound):
 //   units  = sum_b ceil(n_b * G / 128) query tiles, times Hkv
 //   nsplit = 1 when units >= kSplitTarget, else ceil(kSplitTarget / units)
-//            capped at 16 and at S/128, so short selections still fill the chip.
+//            capped at 16 and at S/128, so short selections still spread
+//            their K/V reads over the whole GPU (one CU streams only a few
+//            tens of GB/s, so a few workgroups cannot read a long cache fast);
+//            the merge pass combines the split partials by their LSE.
 // With nsplit > 1, units < kSplitTarget implies nsplit * n_rows * Hq <=
 // 2 * kSplitTarget * 128 = kPartRows, the bound the workspace is sized for.
 constexpr int kSplitTarget = 512;
 constexpr int kPartRows = 2 * kSplitTarget * 128;
-
-constexpr int kAttnKT = 64;  // keys per K/V tile of the bf16 kernel
+constexpr int kAttnKT = 64;      // keys per K/V tile
+constexpr int kMergeGrid = 1024; // workgroups of the merge pass (grid-stride)
 
 struct AttnPlan {
   int units;
@@ -68,15 +71,132 @@ __device__ __forceinline__ AttnPlan attn_plan(const AttnArgs& a) {
     ns = min(ns, max(1, a.S / 128));
     if (p.n_rows > 0) ns = min(ns, max(1, kPartRows / (p.n_rows * a.Hq)));
   }
-  // keys per split are rounded up to whole 64-key tiles; recount the splits
-  // from that size so that none of them is empty
+  // keys per split are rounded up to whole tiles; recount the splits from that
+  // size so that none of them is empty
   p.kps = ((a.S + ns - 1) / ns + kAttnKT - 1) / kAttnKT * kAttnKT;
   p.nsplit = (a.S + p.kps - 1) / p.kps;
   return p;
 }
 
+// LDS of the attention kernel (u16 elements)
 template <int HD>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
+struct AttnLds {
+  static constexpr int PITCH = HD + 8;
+  static constexpr int WIDE = 2 * kAttnKT * PITCH;
+};
+
+// Locate the (batch row, kv head, query tile) of a unit: tiles of QT query
+// vectors are counted per batch row, Hkv units per tile.
+struct AttnUnit {
+  int b, nb, row_base, g, t, split;
+};
+__device__ __forceinline__ AttnUnit attn_unit(const AttnArgs& a, const AttnPlan& plan, int QT) {
+  AttnUnit u;
+  u.split = blockIdx.x % plan.nsplit;
+  const int rest = blockIdx.x / plan.nsplit;
+  u.g = rest % a.Hkv;
+  int t = rest / a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  u.b = -1;
+  u.nb = 0;
+  u.row_base = 0;
+  for (int bb = 0; bb < a.B; ++bb) {
+    const int lo_b = min(a.offsets[bb], a.max_rows), hi_b = min(a.offsets[bb + 1], a.max_rows);
+    const int n_b = hi_b - lo_b;
+    const int tb = (n_b * G + QT - 1) / QT;
+    if (t < tb) {
+      u.b = bb;
+      u.nb = n_b;
+      u.row_base = lo_b;
+      break;
+    }
+    t -= tb;
+  }
+  u.t = t;
+  return u;
+}
+
+// Store 32 rows d0..d0+31 (one O^T block) of a query vector, already divided
+// by the softmax sum: bf16 to o (and the context row of the output cache), or
+// fp32 to the split partials.  Register i of the block holds d = 8(i/4) +
+// 4*lg + i%4 of the query in column lr.
+template <int HD>
+__device__ __forceinline__ void attn_store_block(const AttnArgs& a, const AttnPlan& plan, int split,
+                                                 int b, int row, int h, int dblk, const f32x16& o,
+                                                 float inv, int lg) {
+  if (plan.nsplit == 1) {
+    u16* op = static_cast<u16*>(a.o) + ((size_t)row * a.Hq + h) * HD;
+    u16* cp = a.ctx_out ? static_cast<u16*>(a.ctx_out) + ((size_t)(b * a.S + a.idx[row]) * a.Hq + h) * HD
+                        : nullptr;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dblk + 8 * q4 + 4 * lg;
+      u32x2 pk;
+      pk[0] = pack_bf16x2(o[4 * q4] * inv, o[4 * q4 + 1] * inv);
+      pk[1] = pack_bf16x2(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(op + d0) = pk;
+      if (cp) *reinterpret_cast<u32x2*>(cp + d0) = pk;
+    }
+  } else {
+    float* po = a.part_o + (((size_t)split * plan.n_rows + row) * a.Hq + h) * HD;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * dblk + 8 * q4 + 4 * lg;
+      *reinterpret_cast<float4*>(po + d0) =
+          make_float4(o[4 * q4] * inv, o[4 * q4 + 1] * inv, o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv);
+    }
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void attn_store_lse(const AttnArgs& a, const AttnPlan& plan, int split,
+                                               int row, int h, float lse_nat) {
+  if (plan.nsplit == 1) {
+    if (a.lse) a.lse[(size_t)row * a.Hq + h] = lse_nat;
+  } else {
+    a.part_lse[((size_t)split * plan.n_rows + row) * a.Hq + h] = lse_nat;
+  }
+}
+
+// Multiply P^T into O^T for one 32-key block whose first LDS row is kb0:
+// O^T[d] += V^T(32 d x 16 keys) . P^T(16 keys x 32 queries), two 16-key chunks.
+// P^T register i of the block is key 8(i/4) + 4*lg + i%4; the V^T operand is
+// read with ds_read_b64_tr_b16 in the matching key-slot order: k-slots
+// 8*ga+0..3 <-> keys 16cc+4ga+0..3, slots 8*ga+4..7 <-> keys 16cc+8+4ga+0..3.
+template <int HD>
+__device__ __forceinline__ void attn_pv_block(const u16* sV, int kb0, const float (&p)[16],
+                                              f32x16 (&acc)[HD / 32], int lane) {
+  constexpr int PITCH = HD + 8, NDB = HD / 32;
+  const int g16 = lane >> 4, j16 = lane & 15, ga = g16 >> 1;
+  bf16x8 pb[2];
+  {
+    u32x4 w0, w1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w0[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+      w1[j] = pack_bf16x2(p[8 + 2 * j], p[8 + 2 * j + 1]);
+    }
+    pb[0] = as_bf16x8(w0);
+    pb[1] = as_bf16x8(w1);
+  }
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    const int m0 = 32 * d + 16 * (g16 & 1);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const u16* pa = sV + (kb0 + 16 * cc + 4 * ga + (j16 >> 2)) * PITCH + m0 + 4 * (j16 & 3);
+      const i16x4 va = lds_read_tr16(pa);
+      const i16x4 vb = lds_read_tr16(pa + 8 * PITCH);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[d] = mfma32x32x16(av, pb[cc], acc[d]);
+    }
+  }
+}
+
+// 128 query vectors per workgroup (wave w owns vectors 32w..32w+31) that
+// share every 64-key tile of the split.
+template <int HD>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& plan, u16* smem) {
   constexpr int QT = 128;        // query vectors per workgroup
   constexpr int KT = kAttnKT;    // keys per tile (two 32-key MFMA blocks)
   constexpr int PITCH = HD + 8;  // u16 per LDS row
@@ -84,39 +204,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int NDB = HD / 32;   // 32-row blocks of O^T
   constexpr int CPR = HD / 8;    // 16-byte chunks per K/V row
   constexpr int CPT = 2 * KT * CPR / 256;
-  __shared__ __attribute__((aligned(16))) u16 sK[KT * PITCH];
-  __shared__ __attribute__((aligned(16))) u16 sV[KT * PITCH];
+  u16* sK = smem;
+  u16* sV = smem + KT * PITCH;
 
-  const AttnPlan plan = attn_plan(a);
-  const int nsplit = plan.nsplit;
-  if ((int)blockIdx.x >= plan.units * nsplit) return;
-  const int split = blockIdx.x % nsplit;
-  const int rest = blockIdx.x / nsplit;
-  const int g = rest % a.Hkv;
-  int t = rest / a.Hkv;
+  if ((int)blockIdx.x >= plan.units * plan.nsplit) return;
+  const AttnUnit u = attn_unit(a, plan, QT);
+  if (u.b < 0) return;
   const int G = a.Hq / a.Hkv;
-  int b = -1, nb = 0, row_base = 0;
-  for (int bb = 0; bb < a.B; ++bb) {
-    const int lo_b = min(a.offsets[bb], a.max_rows), hi_b = min(a.offsets[bb + 1], a.max_rows);
-    const int n_b = hi_b - lo_b;
-    const int tb = (n_b * G + QT - 1) / QT;
-    if (t < tb) {
-      b = bb;
-      nb = n_b;
-      row_base = lo_b;
-      break;
-    }
-    t -= tb;
-  }
-  if (b < 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
-  const int nvec = nb * G;
-  const int vq = t * QT + wave * 32 + lr;
+  const int nvec = u.nb * G;
+  const int vq = u.t * QT + wave * 32 + lr;
   const bool qvalid = vq < nvec;
   const int vqc = qvalid ? vq : (nvec - 1);
-  const int row = row_base + vqc / G;
-  const int h = g * G + vqc % G;
+  const int row = u.row_base + vqc / G;
+  const int h = u.g * G + vqc % G;
 
   bf16x8 qf[NS];
   {
@@ -125,18 +227,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
     for (int s = 0; s < NS; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s));
   }
 
-  const int kbeg = split * plan.kps, kend = min(a.S, kbeg + plan.kps);
+  const int kbeg = u.split * plan.kps, kend = min(a.S, kbeg + plan.kps);
   const size_t kstride = (size_t)a.Hkv * HD;
-  const u16* kbase = static_cast<const u16*>(a.k) + ((size_t)b * a.S * a.Hkv + g) * HD;
-  const u16* vbase = static_cast<const u16*>(a.v) + ((size_t)b * a.S * a.Hkv + g) * HD;
+  const u16* kbase = static_cast<const u16*>(a.k) + ((size_t)u.b * a.S * a.Hkv + u.g) * HD;
+  const u16* vbase = static_cast<const u16*>(a.v) + ((size_t)u.b * a.S * a.Hkv + u.g) * HD;
   const float c = a.scale * kLog2e;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 acc[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) acc[d] = f32x16{};
-
-  const int g16 = lane >> 4, j16 = lane & 15, ga = g16 >> 1;
 
   // K/V tile loads: chunk j of this thread is (tensor, key row, 16-byte column)
   u32x4 st[CPT];
@@ -194,6 +294,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
     mt = pair_max(mt);
+    // the first tile of a split always holds a valid key, so m_new is finite
     const float m_new = fmaxf(m_run, mt * c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float p[2][16];
@@ -211,72 +312,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[d][i] *= alpha;
     m_run = m_new;
-
-    // P^T in B-operand layout: register i of key block kb is key 32kb+8(i/4)+4*lg+(i%4)
-    bf16x8 pb[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      u32x4 w0, w1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w0[j] = pack_bf16x2(p[kb][2 * j], p[kb][2 * j + 1]);
-        w1[j] = pack_bf16x2(p[kb][8 + 2 * j], p[kb][8 + 2 * j + 1]);
-      }
-      pb[kb][0] = as_bf16x8(w0);
-      pb[kb][1] = as_bf16x8(w1);
-    }
-#pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      const int m0 = 32 * d + 16 * (g16 & 1);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          // k-slots 8*ga+0..3 <-> keys 16cc+4ga+0..3, slots 8*ga+4..7 <-> keys 16cc+8+4ga+0..3
-          const u16* pa = sV + (32 * kb + 16 * cc + 4 * ga + (j16 >> 2)) * PITCH + m0 + 4 * (j16 & 3);
-          const i16x4 va = lds_read_tr16(pa);
-          const i16x4 vb = lds_read_tr16(pa + 8 * PITCH);
-          const bf16x8 av =
-              __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[d] = mfma32x32x16(av, pb[kb][cc], acc[d]);
-        }
-    }
+    for (int kb = 0; kb < 2; ++kb) attn_pv_block<HD>(sV, 32 * kb, p[kb], acc, lane);
   }
 
   const float l_tot = pair_sum(l_run);
   const float inv = 1.f / l_tot;
   const float lse_nat = (m_run + __log2f(l_tot)) * kLn2;
   if (!qvalid) return;
-  if (nsplit == 1) {
-    u16* op = static_cast<u16*>(a.o) + ((size_t)row * a.Hq + h) * HD;
-    u16* cp = a.ctx_out ? static_cast<u16*>(a.ctx_out) +
-                              ((size_t)(b * a.S + a.idx[row]) * a.Hq + h) * HD
-                        : nullptr;
 #pragma unroll
-    for (int d = 0; d < NDB; ++d)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * d + 8 * q4 + 4 * lg;
-        u32x2 pk;
-        pk[0] = pack_bf16x2(acc[d][4 * q4] * inv, acc[d][4 * q4 + 1] * inv);
-        pk[1] = pack_bf16x2(acc[d][4 * q4 + 2] * inv, acc[d][4 * q4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + d0) = pk;
-        if (cp) *reinterpret_cast<u32x2*>(cp + d0) = pk;
-      }
-    if (lg == 0 && a.lse) a.lse[(size_t)row * a.Hq + h] = lse_nat;
-  } else {
-    float* po = a.part_o + (((size_t)split * plan.n_rows + row) * a.Hq + h) * HD;
-#pragma unroll
-    for (int d = 0; d < NDB; ++d)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * d + 8 * q4 + 4 * lg;
-        *reinterpret_cast<float4*>(po + d0) =
-            make_float4(acc[d][4 * q4] * inv, acc[d][4 * q4 + 1] * inv, acc[d][4 * q4 + 2] * inv,
-                        acc[d][4 * q4 + 3] * inv);
-      }
-    if (lg == 0) a.part_lse[((size_t)split * plan.n_rows + row) * a.Hq + h] = lse_nat;
-  }
+  for (int d = 0; d < NDB; ++d) attn_store_block<HD>(a, plan, u.split, u.b, row, h, d, acc[d], inv, lg);
+  if (lg == 0) attn_store_lse<HD>(a, plan, u.split, row, h, lse_nat);
+}
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 smem[AttnLds<HD>::WIDE];
+  const AttnPlan plan = attn_plan(a);
+  attn_body<HD>(a, plan, smem);
 }
 
 // Combine split-KV partials: O = sum_s exp(lse_s - L) O_s with L = logsumexp_s lse_s.
@@ -332,12 +385,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const AttnPlan plan = attn_plan(a);
   if (plan.nsplit <= 1) return;  // the attention kernel already wrote the outputs
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int pr = blockIdx.x * 4 + wave;
-  if (pr >= plan.n_rows * a.Hq) return;
-  if (plan.nsplit <= 8)
-    merge_row<HD, 8>(a, plan, pr, lane);
-  else
-    merge_row<HD, 16>(a, plan, pr, lane);
+  const int pairs = plan.n_rows * a.Hq;
+  for (int pr = blockIdx.x * 4 + wave; pr < pairs; pr += gridDim.x * 4) {
+    if (plan.nsplit <= 8)
+      merge_row<HD, 8>(a, plan, pr, lane);
+    else
+      merge_row<HD, 16>(a, plan, pr, lane);
+  }
 }
 
 template <int HD>
@@ -409,10 +463,10 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-static int attn_tiles_max(int max_rows, int B, int G) { return (max_rows * G + 127) / 128 + B - 1; }
+static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 size_t attn_workspace_bytes(int dtype, int max_rows, int B, int S, int Hq, int Hkv, int hd) {
-  if (dtype != 1) return 0;
+  if (dtype != 1 || S < 256) return 0;  // fewer than 256 keys are never split
   return (size_t)kPartRows * (hd + 1) * sizeof(float);
 }
 
@@ -428,20 +482,21 @@ hipError_t launch_attn(int dtype, const AttnArgs& a0, void* workspace, hipStream
     return hipGetLastError();
   }
   const int G = a.Hq / a.Hkv;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_lse = a.part_o + (size_t)kPartRows * a.hd;
-  // enough workgroups for every tile and for the split factor the device may choose
-  const int grid = attn_tiles_max(a.max_rows, a.B, G) * a.Hkv + 2 * kSplitTarget;
+  const bool may_split = a.S >= 256;
+  a.part_o = may_split ? static_cast<float*>(workspace) : nullptr;
+  a.part_lse = may_split ? a.part_o + (size_t)kPartRows * a.hd : nullptr;
+  // enough workgroups for every tile and for the split factor the device may
+  // choose (units < kSplitTarget splits into fewer than 2 * kSplitTarget)
+  const int grid = (ceil_div((long long)a.max_rows * G, 128) + a.B - 1) * a.Hkv + 2 * kSplitTarget;
   if (a.hd == 64)
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3(grid), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3(grid), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !may_split) return e;
   // the merge runs only when the device chose to split; otherwise it exits at once
-  const long long pairs = (long long)a.max_rows * a.Hq;
-  const long long cap = (long long)kPartRows;
-  const int mgrid = (int)(((pairs < cap ? pairs : cap) + 3) / 4);
+  const long long quads = ((long long)a.max_rows * a.Hq + 3) / 4;
+  const int mgrid = (int)(quads < kMergeGrid ? quads : kMergeGrid);
   if (a.hd == 64)
     hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(mgrid), dim3(256), 0, st, a);
   else

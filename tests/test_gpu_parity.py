@@ -235,6 +235,59 @@ def test_loose_row_bound_picks_every_tiling(dlm):
             assert v_ <= TOL["bf16"], f"n={n} {k_}: {v_}"
 
 
+def run_attention_plan(dlm, B, S, Hq, Hkv, hd, rows_per_b, sample=None, seed=21):
+    """Partial attention on given q/k/v (bf16) against the oracle; with
+    `sample`, only that many selected rows (spread over the batch rows) are
+    recomputed by the oracle, over all S keys."""
+    rng = np.random.default_rng(seed)
+    scale = 1.0 / math.sqrt(hd)
+    kc = W.round_bf16(rng.standard_normal((B, S, Hkv, hd)))
+    vc = W.round_bf16(rng.standard_normal((B, S, Hkv, hd)))
+    sc = np.ones((B, S))
+    for b in range(B):
+        sc[b, rng.choice(S, rows_per_b[b], replace=False)] = 0.0
+    ridx, _, roff = O.compact(sc, 0, S, 0.5)
+    n = int(roff[-1])
+    q = W.round_bf16(rng.standard_normal((n, Hq, hd)))
+    say(f"[attention plan] B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} n={n} sample={sample}")
+    o = torch.zeros(n, Hq, hd, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(n, Hq, dtype=torch.float32, device="cuda")
+    wsa = workspace(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, n, B, S, Hq, Hkv, hd))
+    dlm.dlm_partial_attn(dev(q, "bf16"), i32(ridx), i32(roff), n, dev(kc, "bf16"), dev(vc, "bf16"), scale,
+                         o, lse, workspace=wsa)
+    torch.cuda.synchronize()
+    if sample is None:
+        pick = np.arange(n)
+    else:
+        pick = np.unique(np.linspace(0, n - 1, sample).astype(np.int64))
+    # the oracle on the picked rows only: each keeps its own batch row
+    counts = np.array([np.sum((pick >= roff[b]) & (pick < roff[b + 1])) for b in range(B)])
+    poff = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    o_o, lse_o = O.partial_attention(q[pick], ridx[pick], poff, kc, vc, Hq, Hkv, scale)
+    eo, el = maxabs(host(o)[pick], o_o), maxabs(host(lse)[pick], lse_o)
+    say(f"  rows checked {len(pick)}: o={eo:.2e} lse={el:.2e}")
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+
+
+def test_attention_many_tiles_gqa_ragged(dlm):
+    """>= 512 tiles of 128 query vectors: no key split (GQA 4:1, ragged last
+    query tile and last 64-key tile); sampled rows against the oracle."""
+    run_attention_plan(dlm, B=2, S=1500, Hq=32, Hkv=8, hd=128, rows_per_b=[1500, 1436], sample=48)
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+def test_attention_few_tiles_split_keys(dlm, hd):
+    """Four query tiles over S = 4200 keys: the keys split over 14 workgroups
+    (more than 8, the merge's second register layout) and the LSE merge pass;
+    every row against the oracle."""
+    run_attention_plan(dlm, B=2, S=4200, Hq=4, Hkv=2, hd=hd, rows_per_b=[37, 5])
+
+
+def test_attention_short_sequence(dlm):
+    """S = 70: one ragged 64-key tile and a 6-key tail tile, never split."""
+    run_attention_plan(dlm, B=3, S=70, Hq=4, Hkv=4, hd=128, rows_per_b=[70, 1, 33])
+
+
 # ---------------------------------------------------------------------------
 # attention column sums + top-k
 # ---------------------------------------------------------------------------
