@@ -98,7 +98,7 @@ class StepSet:
                                   dtype=torch.uint8, device="cuda")
         self.ws_attn = torch.zeros(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, max_rows, B, S, s.Hq, s.Hkv, s.hd),
                                    dtype=torch.uint8, device="cuda")
-        self.ws_qkv = torch.zeros(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, max_rows, s.Hq, s.Hkv, s.hd),
+        self.ws_qkv = torch.zeros(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, max_rows, s.D, s.Hq, s.Hkv, s.hd),
                                   dtype=torch.uint8, device="cuda")
         # cache state of the previous step: a full pass (every row selected) on prev
         all_rows = torch.zeros(B, S, dtype=torch.float32, device="cuda")
@@ -438,7 +438,7 @@ def extra_lock_loop(dlm, W):
     counts = torch.empty(B, dtype=torch.int32, device="cuda")
     offsets = torch.empty(B + 1, dtype=torch.int32, device="cuda")
     wsa = torch.zeros(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, B * S, B, S, Hq, Hkv, hd), dtype=torch.uint8, device="cuda")
-    wsq = torch.zeros(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, B * S, Hq, Hkv, hd), dtype=torch.uint8, device="cuda")
+    wsq = torch.zeros(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, B * S, D, Hq, Hkv, hd), dtype=torch.uint8, device="cuda")
     scale = 1.0 / math.sqrt(hd)
 
     def stage(t, k):

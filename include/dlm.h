@@ -128,12 +128,13 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b,
  *   k_cache[b, i, :, :]  = x[b,i] . W_k^T        k_cache, v_cache [B,S,Hkv,hd]
  *   v_cache[b, i, :, :]  = x[b,i] . W_v^T
  * Cache rows that are not selected are not touched (byte-identical).
- * bf16: D % 64 == 0, hd in {64,128}, B*S*D < 2^31.  The workspace (size from
- * dlm_gather_qkv_workspace_size) holds split-K partial tiles; only bounds
- * above 1024 rows with (Hq+2*Hkv)*hd % 256 == 0 need one (size 0 otherwise,
- * and then workspace may be NULL).  f32: D % 4 == 0, no workspace.
+ * bf16: D % 64 == 0, hd in {64,128}, x under 2 GiB, w_qkv under 4 GiB.  The
+ * workspace (size from dlm_gather_qkv_workspace_size) holds split-K partial
+ * tiles; only bounds above 1024 rows with (Hq+2*Hkv)*hd % 256 == 0 need one
+ * (size 0 otherwise, and then workspace may be NULL).  f32: D % 4 == 0, no
+ * workspace.
  * ------------------------------------------------------------------------ */
-size_t dlm_gather_qkv_workspace_size(int dtype, int max_rows, int Hq, int Hkv, int hd);
+size_t dlm_gather_qkv_workspace_size(int dtype, int max_rows, int D, int Hq, int Hkv, int hd);
 int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D,
                               const int32_t* idx, const int32_t* offsets, int max_rows,
                               const void* w_qkv, int Hq, int Hkv, int hd,

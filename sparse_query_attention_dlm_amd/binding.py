@@ -47,7 +47,7 @@ lib.dlm_saliency_select.restype = _I
 lib.dlm_saliency_select.argtypes = [_I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _F,
                                     _P, _P, _P, _P, _P, _P, _Z, _P]
 lib.dlm_gather_qkv_workspace_size.restype = _Z
-lib.dlm_gather_qkv_workspace_size.argtypes = [_I] * 5
+lib.dlm_gather_qkv_workspace_size.argtypes = [_I] * 6
 lib.dlm_gather_qkv_scatter_kv.restype = _I
 lib.dlm_gather_qkv_scatter_kv.argtypes = [_I, _P, _I, _I, _I, _P, _P, _I, _P, _I, _I, _I,
                                           _P, _P, _P, _P, _Z, _P]
@@ -118,8 +118,8 @@ def dlm_partial_attn_workspace_size(dtype, max_rows, B, S, Hq, Hkv, hd, D_out_wo
     return int(lib.dlm_partial_attn_workspace_size(dtype, max_rows, B, S, Hq, Hkv, hd, D_out_wo))
 
 
-def dlm_gather_qkv_workspace_size(dtype, max_rows, Hq, Hkv, hd) -> int:
-    return int(lib.dlm_gather_qkv_workspace_size(dtype, max_rows, Hq, Hkv, hd))
+def dlm_gather_qkv_workspace_size(dtype, max_rows, D, Hq, Hkv, hd) -> int:
+    return int(lib.dlm_gather_qkv_workspace_size(dtype, max_rows, D, Hq, Hkv, hd))
 
 
 def dlm_attn_colsum_workspace_size(B, S, Hkv) -> int:

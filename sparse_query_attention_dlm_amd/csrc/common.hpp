@@ -65,13 +65,16 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_b
 // (partner, own): in both the low-half value comes first, so the two lanes
 // compute bit-identical results.
 // Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3):
-// loads whose VGPR offset lies past the end return zeros.  The range check
-// covers the VGPR offset only, so every offset goes there (soffset = 0).
+// loads past the end return zeros without touching memory.  Callers keep
+// `bytes` below 2^31 wherever they rely on that, put the per-lane part of an
+// offset in the VGPR (voff) and a wave-uniform part in soff, and mark a lane
+// out of range with voff >= 2^31: then voff alone and voff + soff (< 2^32)
+// are both past the end, whichever of the two the range check uses.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
 __device__ __forceinline__ float pair_max(float v) {

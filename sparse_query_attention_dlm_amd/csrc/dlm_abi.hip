@@ -64,7 +64,7 @@ size_t dlm_select_workspace_size(int mode, int B, int S, int V, int max_eval) {
   if (B > 0 && S > 0) n += round_up((size_t)B * S * sizeof(float), 256);
   if (mode == DLM_SCORE_CONFIDENCE && V > 0 && max_eval > 0) {
     n += round_up((size_t)max_eval * dlm::gemm_lmhead_ntile(V) * sizeof(float4), 256);
-    n += dlm::gemm_workspace_bytes(dlm::EPI_LMHEAD, max_eval, V);
+    n += dlm::gemm_workspace_bytes(dlm::EPI_LMHEAD, max_eval, V, 0);
   }
   return n;
 }
@@ -107,7 +107,8 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b, int B
     REQUIRE(V > 0 && V % 256 == 0, "V=%d must be a positive multiple of 256", V);
     REQUIRE(max_eval >= 0 && (long long)max_eval <= (long long)B * S, "max_eval=%d out of range",
             max_eval);
-    REQUIRE((long long)B * S * D < (1ll << 31), "hidden states larger than 2^31 elements");
+    REQUIRE((long long)B * S * D * 2 < (1ll << 31), "hidden states of 2 GiB or more");
+    REQUIRE((long long)V * D * 2 < (1ll << 32), "W_lm of 4 GiB or more");
   }
   const size_t need = dlm_select_workspace_size(mode, B, S, V, max_eval);
   if (workspace == nullptr || workspace_bytes < need)
@@ -129,6 +130,7 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b, int B
     dlm::GemmArgs g{};
     g.w = b;
     g.x = a;
+    g.x_bytes = (uint32_t)((size_t)B * S * D * 2);
     g.K = D;
     g.N = V;
     g.B = B;
@@ -150,9 +152,9 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b, int B
 }
 
 // ---------------------------------------------------------------------------
-size_t dlm_gather_qkv_workspace_size(int dtype, int max_rows, int Hq, int Hkv, int hd) {
-  if (dtype != DLM_BF16 || max_rows <= 0 || Hq <= 0 || Hkv <= 0 || hd <= 0) return 0;
-  return dlm::gemm_workspace_bytes(dlm::EPI_QKV, max_rows, (Hq + 2 * Hkv) * hd);
+size_t dlm_gather_qkv_workspace_size(int dtype, int max_rows, int D, int Hq, int Hkv, int hd) {
+  if (dtype != DLM_BF16 || max_rows <= 0 || D <= 0 || Hq <= 0 || Hkv <= 0 || hd <= 0) return 0;
+  return dlm::gemm_workspace_bytes(dlm::EPI_QKV, max_rows, (Hq + 2 * Hkv) * hd, D);
 }
 
 int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D, const int32_t* idx,
@@ -183,7 +185,11 @@ int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D, con
   REQUIRE_ALIGNED(k_cache);
   REQUIRE_ALIGNED(v_cache);
   if (max_rows == 0) return DLM_OK;
-  const size_t need = dlm_gather_qkv_workspace_size(dtype, max_rows, Hq, Hkv, hd);
+  if (dtype == DLM_BF16) {
+    REQUIRE((long long)B * S * D * 2 < (1ll << 31), "x of 2 GiB or more is not supported");
+    REQUIRE((long long)(Hq + 2 * Hkv) * hd * D * 2 < (1ll << 32), "w_qkv of 4 GiB or more");
+  }
+  const size_t need = dlm_gather_qkv_workspace_size(dtype, max_rows, D, Hq, Hkv, hd);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -193,6 +199,7 @@ int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D, con
   g.w = w_qkv;
   g.part = static_cast<float*>(workspace);
   g.x = x;
+  g.x_bytes = (uint32_t)((size_t)B * S * D * 2);
   g.K = D;
   g.N = (Hq + 2 * Hkv) * hd;
   g.B = B;
@@ -215,7 +222,8 @@ size_t dlm_partial_attn_workspace_size(int dtype, int max_rows, int B, int S, in
                                        int hd, int D_out_wo) {
   if (max_rows <= 0 || B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || hd <= 0) return 0;
   size_t n = round_up(dlm::attn_workspace_bytes(dtype, max_rows, B, S, Hq, Hkv, hd), 256);
-  if (dtype == DLM_BF16 && D_out_wo > 0) n += dlm::gemm_workspace_bytes(dlm::EPI_ROWS, max_rows, D_out_wo);
+  if (dtype == DLM_BF16 && D_out_wo > 0)
+    n += dlm::gemm_workspace_bytes(dlm::EPI_ROWS, max_rows, D_out_wo, Hq * hd);
   return n;
 }
 
@@ -247,8 +255,11 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
   if (w_o) {
     REQUIRE(out_cache != nullptr, "w_o given but out_cache is NULL");
     REQUIRE(D_out > 0, "D_out must be positive");
-    if (dtype == DLM_BF16)
+    if (dtype == DLM_BF16) {
       REQUIRE(D_out % 64 == 0 && (Hq * hd) % 64 == 0, "bf16 W_o needs D_out %% 64 == 0");
+      REQUIRE((long long)D_out * Hq * hd * 2 < (1ll << 32), "W_o of 4 GiB or more");
+      REQUIRE((long long)max_rows * Hq * hd * 2 < (1ll << 31), "o_sel of 2 GiB or more");
+    }
     REQUIRE_ALIGNED(w_o);
   } else if (out_cache) {
     REQUIRE(D_out == Hq * hd, "without W_o, D_out (%d) must equal Hq*hd (%d)", D_out, Hq * hd);
@@ -282,6 +293,7 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
   dlm::GemmArgs g{};
   g.w = w_o;
   g.x = o_sel;
+  g.x_bytes = (uint32_t)((size_t)max_rows * Hq * hd * 2);
   g.K = Hq * hd;
   g.N = D_out;
   g.B = B;

@@ -9,20 +9,44 @@
 // Computes D^T[n][m] = sum_k W[n][k] * A[row(m)][k] with W output-major, so
 // both MFMA operands are K-contiguous and come straight from LDS rows:
 //   A-operand = a 32-row block of W (output features), B-operand = 32 gathered
-//   token rows.  The gather happens on load (row pointers resolved once per
+//   token rows.  The gather happens on load (row offsets resolved once per
 //   tile from idx/offsets), so no compacted copy of the hidden states is made.
 // Epilogues:
 //   EPI_QKV    - Q rows written compact, K/V rows scattered into the caches
 //                (8-byte bf16x4 stores of 4 consecutive features)
 //   EPI_ROWS   - rows scattered into an output cache (W_o projection)
-//   EPI_LMHEAD - per (token, 128-column vocabulary tile): max logit, sum of
+//   EPI_LMHEAD - per (token, 256-column vocabulary tile): max logit, sum of
 //                exp(z - max) and the lowest argmax; logits never stored.
 // Tiles: TP (features) x TT (tokens) x 64 (k), 4 waves, 32x32x16 bf16 MFMA,
-// double-buffered LDS with 16-byte row padding, register-staged prefetch.
+// double-buffered LDS with 16-byte row padding, a branch-free register ring
+// of PF k-steps, operands fetched with buffer loads (one VGPR offset per
+// chunk; padding token rows point past the end of the buffer and read zeros
+// without touching memory).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace dlm {
+
+// Store four consecutive features n..n+3 of token m (cache row drow) as bf16.
+template <int EPI>
+__device__ __forceinline__ void epi_store4(const GemmArgs& g, int m, int drow, int n, float v0, float v1,
+                                           float v2, float v3) {
+  u32x2 pk;
+  pk[0] = pack_bf16x2(v0, v1);
+  pk[1] = pack_bf16x2(v2, v3);
+  u16* dst;
+  if constexpr (EPI == EPI_QKV) {
+    if (n < g.nq)
+      dst = static_cast<u16*>(g.q_out) + (size_t)m * g.nq + n;
+    else if (n < g.nq + g.nk)
+      dst = static_cast<u16*>(g.k_cache) + (size_t)drow * g.nk + (n - g.nq);
+    else
+      dst = static_cast<u16*>(g.v_cache) + (size_t)drow * g.nk + (n - g.nq - g.nk);
+  } else {
+    dst = static_cast<u16*>(g.out) + (size_t)drow * g.ld_out + n;
+  }
+  *reinterpret_cast<u32x2*>(dst) = pk;
+}
 
 // Epilogues on the accumulated tile.  Register i of acc[a][b] in lane l holds
 // feature n0 + wp*WTP + 32a + 8(i/4) + 4(l/32) + i%4 of token m0 + wt*WTT + 32b + l%32.
@@ -40,29 +64,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
       const int ml = wt * WTT + b * 32 + lr;
       const int drow = s_drow[ml];
       if (drow < 0) continue;
-      const int m = m0 + ml;
 #pragma unroll
-      for (int a = 0; a < FP; ++a) {
+      for (int a = 0; a < FP; ++a)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int n = n0 + wp * WTP + a * 32 + 8 * q4 + 4 * lg;
-          u32x2 pk;
-          pk[0] = pack_bf16x2(acc[a][b][4 * q4 + 0], acc[a][b][4 * q4 + 1]);
-          pk[1] = pack_bf16x2(acc[a][b][4 * q4 + 2], acc[a][b][4 * q4 + 3]);
-          u16* dst;
-          if constexpr (EPI == EPI_QKV) {
-            if (n < g.nq)
-              dst = static_cast<u16*>(g.q_out) + (size_t)m * g.nq + n;
-            else if (n < g.nq + g.nk)
-              dst = static_cast<u16*>(g.k_cache) + (size_t)drow * g.nk + (n - g.nq);
-            else
-              dst = static_cast<u16*>(g.v_cache) + (size_t)drow * g.nk + (n - g.nq - g.nk);
-          } else {
-            dst = static_cast<u16*>(g.out) + (size_t)drow * g.ld_out + n;
-          }
-          *reinterpret_cast<u32x2*>(dst) = pk;
-        }
-      }
+        for (int q4 = 0; q4 < 4; ++q4)
+          epi_store4<EPI>(g, m0 + ml, drow, n0 + wp * WTP + a * 32 + 8 * q4 + 4 * lg, acc[a][b][4 * q4],
+                          acc[a][b][4 * q4 + 1], acc[a][b][4 * q4 + 2], acc[a][b][4 * q4 + 3]);
     }
   } else {
     __shared__ float s_pm[WP][TT], s_ps[WP][TT];
@@ -113,29 +120,34 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
   }
 }
 
-// Split-K plan, computed on the device from the real row count.  When the
-// output tiles are fewer than split_units, K is split over spare workgroups of
-// the grid: ks is a power of two that divides the k-steps into whole prefetch
-// rings (at least two rings per split), grown while units * ks stays below
-// kSplitTarget and within kSplitCap (the workspace) and the grid.
-constexpr int kSplitTarget = 768;
+// Split-K plan, computed on the device from the real row count.  When there
+// are fewer than SB output tiles, K is split over spare workgroups of the
+// grid: ks is a power of two (<= 8) that divides the k-steps into whole
+// prefetch rings (at least two rings per split), doubled while units * ks
+// stays below ST and within kSplitCap (the workspace) and the grid.
 constexpr int kSplitCap = 1024;
 
-// GATE: 0 = always run; 1 = run only when the device row count is <= kSkinnyRows;
-// 2 = run only when it is larger.  A host that only knows a loose upper bound
-// launches a GATE 1 and a GATE 2 kernel and the device picks the tiling.
+// The weight-streaming case (<= kSkinnyRows rows): 64-feature tiles, no
+// split-K.  Measured on this GPU (n = 102, N = 12288, K = 4096): splitting K
+// over 192-feature tiles (one workgroup per CU, 1/4 of the rows each) ran the
+// product in 31.8 us against 35 us, but its partial tiles cost a 9.8 us
+// reduction pass; with all CUs streaming from HBM each gets only ~20 GB/s, so
+// the partials cost about what the saved row reads gain.
 constexpr int kSkinnyRows = 128;
+// Reduction pass: workgroups per split tile are chosen so that about
+// kReduceTarget of them share the partials.
+constexpr int kReduceTarget = 256;
+
 struct GemmSplit {
   int units;
   int ks;
 };
-__device__ __forceinline__ GemmSplit gemm_split(int units, int grid, int nk, int pf,
-                                                int split_units) {
+__host__ __device__ inline GemmSplit gemm_split(int units, int grid, int nk, int pf, int SB, int ST) {
   GemmSplit s{units, 1};
-  if (units <= 0 || units >= split_units) return s;
+  if (units <= 0 || units >= SB) return s;
   while (true) {
     const int k2 = s.ks * 2;
-    if (units * k2 > kSplitCap || units * k2 > grid || units * s.ks >= kSplitTarget) break;
+    if (units * k2 > kSplitCap || units * k2 > grid || units * s.ks >= ST) break;
     if (k2 > 8 || nk % k2 != 0 || (nk / k2) % pf != 0 || nk / k2 < 2 * pf) break;
     s.ks = k2;
   }
@@ -145,11 +157,31 @@ __device__ __forceinline__ GemmSplit gemm_split(int units, int grid, int nk, int
 // u16 elements of the double-buffered LDS tile (rows padded to 72 elements)
 constexpr int gemm_lds_u16(int TP, int TT) { return 2 * (TP + TT) * 72; }
 
+// Resolve the tile's token rows: cache row (b*S + idx[m], -1 for padding) and
+// the byte offset of the operand row (past the end of the buffer for padding,
+// so that its loads return zeros).
+template <int TT, int AMODE>
+__device__ __forceinline__ void gemm_rows(const GemmArgs& g, int n_rows, int m0, uint32_t* s_xoff,
+                                          int* s_drow) {
+  for (int t = threadIdx.x; t < TT; t += 256) {
+    const int m = m0 + t;
+    uint32_t xo = 0x80000000u;
+    int drow = -1;
+    if (m < n_rows) {
+      const int b = batch_of(g.offsets, g.B, m);
+      drow = b * g.S + g.idx[m];
+      xo = (uint32_t)((AMODE == A_GATHER ? (size_t)drow : (size_t)m) * g.K * 2);
+    }
+    s_xoff[t] = xo;
+    s_drow[t] = drow;
+  }
+}
+
 // One output tile (or one K-split of it) of the gathered GEMM; the caller
 // provides the LDS buffers so that several tilings can share one allocation.
-template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int SPLIT_UNITS>
+template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int SB, int ST>
 __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u16* lds,
-                                               long long* s_arow, int* s_drow) {
+                                               uint32_t* s_xoff, int* s_drow) {
   constexpr int BK = 64, PITCH = BK + 8;  // u16 elements per LDS row (144 bytes)
   constexpr int ROWS = TP + TT;
   constexpr int CHUNKS = ROWS * (BK / 8);
@@ -163,7 +195,7 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
   const int m_tiles = (n_rows + TT - 1) / TT;
   const int n_tiles = g.N / TP;
   const int nk_all = g.K / BK;
-  const GemmSplit sp = gemm_split(m_tiles * n_tiles, (int)gridDim.x, nk_all, PF, SPLIT_UNITS);
+  const GemmSplit sp = gemm_split(m_tiles * n_tiles, (int)gridDim.x, nk_all, PF, SB, ST);
   if ((int)blockIdx.x >= sp.units * sp.ks) return;
   const int unit = (int)blockIdx.x % sp.units, ksi = (int)blockIdx.x / sp.units;
   const int nt = unit / m_tiles, mt = unit % m_tiles;
@@ -172,40 +204,30 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
   const int nk = nk_all / sp.ks;        // k-steps of this split
   const int kbase = ksi * nk;           // first k-step of this split
 
-  for (int t = tid; t < TT; t += 256) {
-    const int m = m0 + t;
-    long long arow = -1;
-    int drow = -1;
-    if (m < n_rows) {
-      const int b = batch_of(g.offsets, g.B, m);
-      drow = b * g.S + g.idx[m];
-      arow = (AMODE == A_GATHER) ? (long long)drow * g.K : (long long)m * g.K;
-    }
-    s_arow[t] = arow;
-    s_drow[t] = drow;
-  }
+  gemm_rows<TT, AMODE>(g, n_rows, m0, s_xoff, s_drow);
   __syncthreads();
 
   // Chunk j of this thread covers LDS row (tid/8 + 32 j), 16-byte column tid%8.
-  // Rows [0,TP) are weight rows (one base pointer, constant stride); rows
-  // [TP, TP+TT) are gathered token rows (32-bit element offsets).
+  // Rows [0,TP) are weight rows (VGPR offset of row tid/8, the rest of the
+  // offset uniform); rows [TP, TP+TT) are gathered token rows.
   constexpr int CW = TP / 32;  // chunks of weight rows per thread
   constexpr int CX = CPT - CW;  // chunks of token rows per thread
   const int r0 = tid >> 3, kc = tid & 7;
-  const u16* gW = static_cast<const u16*>(g.w) + (size_t)(n0 + r0) * g.K + kc * 8;
-  const u16* gX = static_cast<const u16*>(g.x) + kc * 8;
-  const size_t wstride = (size_t)32 * g.K;
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.w, (uint32_t)((size_t)g.N * g.K * 2));
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.x, g.x_bytes);
+  const uint32_t woff = (uint32_t)(((size_t)(n0 + r0) * g.K + kc * 8) * 2);
+  const uint32_t wstride = (uint32_t)(32 * g.K * 2);
   uint32_t xoff[CX];
 #pragma unroll
   for (int j = 0; j < CX; ++j) {
-    long long ar = s_arow[r0 + 32 * j];
-    if (ar < 0) ar = s_arow[0];  // padding rows of a ragged tile reuse a valid row
-    xoff[j] = (uint32_t)ar;
+    const uint32_t o = s_xoff[r0 + 32 * j];
+    xoff[j] = o + (o & 0x80000000u ? 0u : (uint32_t)(kc * 16));
   }
   u16* const ldsw = lds + r0 * PITCH + kc * 8;
   auto gload = [&](int j, int kstep) -> u32x4 {
-    const u16* p = (j < CW) ? gW + j * wstride : gX + xoff[j - CW];
-    return *reinterpret_cast<const u32x4*>(p + (size_t)(kbase + kstep) * BK);
+    const uint32_t ko = (uint32_t)(kbase + kstep) * (BK * 2);
+    if (j < CW) return buffer_load16(rW, woff, ko + (uint32_t)j * wstride);
+    return buffer_load16(rX, xoff[j - CW], ko);
   };
 
   f32x16 acc[FP][FT];
@@ -268,102 +290,142 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
 
   if (sp.ks > 1) {
     // split-K: store the partial tile in register order (16-byte vectors,
-    // consecutive threads adjacent); gemm_splitk_reduce_kernel sums the
-    // splits in a fixed order after this kernel has finished
+    // consecutive threads adjacent; padding tokens are skipped, the reduction
+    // skips them too); gemm_splitk_reduce_kernel sums the splits in a fixed
+    // order after this kernel has finished
     constexpr int NQ = FP * FT * 4;
     float4* mine = reinterpret_cast<float4*>(g.part) + ((size_t)unit * sp.ks + ksi) * (NQ * 256);
 #pragma unroll
-    for (int a = 0; a < FP; ++a)
+    for (int b = 0; b < FT; ++b) {
+      if (s_drow[wt * WTT + b * 32 + lr] < 0) continue;
 #pragma unroll
-      for (int b = 0; b < FT; ++b)
+      for (int a = 0; a < FP; ++a)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           mine[((a * FT + b) * 4 + q) * 256 + tid] = make_float4(
               acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
+    }
     return;
   }
   gemm_epilogue<TP, TT, WP, WT, EPI>(g, acc, m0, n0, nt, s_drow);
 }
 
-template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SPLIT_UNITS>
+// GATE: 0 = always run; 1 = run only when the device row count is <= kSkinnyRows;
+// 2 = run only when it is larger.
+template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) u16 lds[gemm_lds_u16(TP, TT)];
-  __shared__ long long s_arow[TT];
+  __shared__ uint32_t s_xoff[TT];
   __shared__ int s_drow[TT];
   const int n_rows = min(g.offsets[g.B], g.max_rows);
   if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
-  gemm_tile_body<TP, TT, WP, WT, PF, EPI, AMODE, SPLIT_UNITS>(g, n_rows, lds, s_arow, s_drow);
+  gemm_tile_body<TP, TT, WP, WT, PF, EPI, AMODE, SB, ST>(g, n_rows, lds, s_xoff, s_drow);
 }
 
 // One launch for a host that only knows a loose row bound: the device row
 // count picks the weight-streaming tiling (<= kSkinnyRows rows) or the large
 // tiling, so no second launch has to start just to exit.  Both bodies share
 // one LDS allocation sized for the larger of the two.
-template <int TP, int TT, int PF, int TP2, int TT2, int PF2, int EPI, int AMODE, int SU2>
+template <int TP, int TT, int PF, int SB, int ST, int TP2, int TT2, int PF2, int SB2, int ST2, int EPI,
+          int AMODE>
 __global__ __launch_bounds__(256) void gemm_dual_kernel(GemmArgs g) {
   constexpr int L1 = gemm_lds_u16(TP, TT), L2 = gemm_lds_u16(TP2, TT2);
   constexpr int TTM = TT > TT2 ? TT : TT2;
   __shared__ __attribute__((aligned(16))) u16 lds[L1 > L2 ? L1 : L2];
-  __shared__ long long s_arow[TTM];
+  __shared__ uint32_t s_xoff[TTM];
   __shared__ int s_drow[TTM];
   const int n_rows = min(g.offsets[g.B], g.max_rows);
   if (n_rows <= kSkinnyRows)
-    gemm_tile_body<TP, TT, 2, 2, PF, EPI, AMODE, 0>(g, n_rows, lds, s_arow, s_drow);
+    gemm_tile_body<TP, TT, 2, 2, PF, EPI, AMODE, SB, ST>(g, n_rows, lds, s_xoff, s_drow);
   else
-    gemm_tile_body<TP2, TT2, 2, 2, PF2, EPI, AMODE, SU2>(g, n_rows, lds, s_arow, s_drow);
+    gemm_tile_body<TP2, TT2, 2, 2, PF2, EPI, AMODE, SB2, ST2>(g, n_rows, lds, s_xoff, s_drow);
 }
 
-// Second pass of split-K: one workgroup per output tile sums the partial tiles
-// of its splits in split order and runs the epilogue.  Exits at once when the
-// device plan did not split (the plan is recomputed from the same inputs).
-template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SPLIT_UNITS>
+// Second pass of split-K.  The plan is recomputed from the same inputs (the
+// pass exits at once when the device did not split).  For the row epilogues a
+// tile's 16-byte register groups are shared out over several workgroups
+// (about kReduceTarget in all), each summing its groups over the splits in
+// split order and storing them; the LM-head epilogue needs whole rows, so one
+// workgroup reduces one tile.
+template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g, int main_grid) {
   constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
   constexpr int NQ = FP * FT * 4;
   __shared__ int s_drow[TT];
+  __shared__ uint32_t s_xoff[TT];
   const int n_rows = min(g.offsets[g.B], g.max_rows);
   if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
   const int m_tiles = (n_rows + TT - 1) / TT;
   const int n_tiles = g.N / TP;
-  const GemmSplit sp = gemm_split(m_tiles * n_tiles, main_grid, g.K / 64, PF, SPLIT_UNITS);
-  if (sp.ks <= 1 || (int)blockIdx.x >= sp.units) return;
-  const int unit = blockIdx.x;
+  const GemmSplit sp = gemm_split(m_tiles * n_tiles, main_grid, g.K / 64, PF, SB, ST);
+  if (sp.ks <= 1) return;
+  const int RS = EPI == EPI_LMHEAD ? 1 : min(NQ, (kReduceTarget + sp.units - 1) / sp.units);
+  if ((int)blockIdx.x >= sp.units * RS) return;
+  const int unit = (int)blockIdx.x / RS, slice = (int)blockIdx.x % RS;
   const int nt = unit / m_tiles, mt = unit % m_tiles;
   const int m0 = mt * TT, n0 = nt * TP;
-  const int tid = threadIdx.x;
-  for (int t = tid; t < TT; t += 256) {
-    const int m = m0 + t;
-    s_drow[t] = m < n_rows ? batch_of(g.offsets, g.B, m) * g.S + g.idx[m] : -1;
-  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  const int wp = wave / WT, wt = wave % WT;
+  gemm_rows<TT, AMODE>(g, n_rows, m0, s_xoff, s_drow);
   __syncthreads();
   const float4* all = reinterpret_cast<const float4*>(g.part) + (size_t)unit * sp.ks * (NQ * 256);
-  f32x16 acc[FP][FT];
+  auto sum_splits = [&](int gi) {
+    const int o = gi * 256 + tid;
+    float4 v[8];
 #pragma unroll
-  for (int a = 0; a < FP; ++a)
+    for (int k2 = 0; k2 < 8; ++k2)  // splits past ks re-read split 0 (not added below)
+      v[k2] = all[(size_t)(k2 < sp.ks ? k2 : 0) * (NQ * 256) + o];
+    float4 sum = v[0];
 #pragma unroll
-    for (int b = 0; b < FT; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int o = ((a * FT + b) * 4 + q) * 256 + tid;
-        float4 v[8];
-#pragma unroll
-        for (int k2 = 0; k2 < 8; ++k2)  // splits past ks re-read split 0 (weight 0 below)
-          v[k2] = all[(size_t)(k2 < sp.ks ? k2 : 0) * (NQ * 256) + o];
-        float4 sum = v[0];
-#pragma unroll
-        for (int k2 = 1; k2 < 8; ++k2)
-          if (k2 < sp.ks) {
-            sum.x += v[k2].x;
-            sum.y += v[k2].y;
-            sum.z += v[k2].z;
-            sum.w += v[k2].w;
-          }
-        acc[a][b][4 * q] = sum.x;
-        acc[a][b][4 * q + 1] = sum.y;
-        acc[a][b][4 * q + 2] = sum.z;
-        acc[a][b][4 * q + 3] = sum.w;
+    for (int k2 = 1; k2 < 8; ++k2)
+      if (k2 < sp.ks) {
+        sum.x += v[k2].x;
+        sum.y += v[k2].y;
+        sum.z += v[k2].z;
+        sum.w += v[k2].w;
       }
-  gemm_epilogue<TP, TT, WP, WT, EPI>(g, acc, m0, n0, nt, s_drow);
+    return sum;
+  };
+  if constexpr (EPI == EPI_LMHEAD) {
+    f32x16 acc[FP][FT];
+#pragma unroll
+    for (int a = 0; a < FP; ++a)
+#pragma unroll
+      for (int b = 0; b < FT; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // padding tokens hold no partials: their sums are never used
+          const float4 s = s_drow[wt * WTT + b * 32 + lr] >= 0 ? sum_splits((a * FT + b) * 4 + q)
+                                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+          acc[a][b][4 * q] = s.x;
+          acc[a][b][4 * q + 1] = s.y;
+          acc[a][b][4 * q + 2] = s.z;
+          acc[a][b][4 * q + 3] = s.w;
+        }
+    gemm_epilogue<TP, TT, WP, WT, EPI>(g, acc, m0, n0, nt, s_drow);
+  } else {
+    const int per = (NQ + RS - 1) / RS;
+    const int g_end = min(NQ, (slice + 1) * per);
+    // four groups at a time, so that their partial loads are in flight together
+    for (int g0 = slice * per; g0 < g_end; g0 += 4) {
+      float4 sv[4];
+      int drow[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int gi = min(g0 + u, g_end - 1);
+        drow[u] = g0 + u < g_end ? s_drow[wt * WTT + ((gi / 4) % FT) * 32 + lr] : -1;
+        sv[u] = sum_splits(gi);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (drow[u] < 0) continue;  // padding token or past the slice
+        const int gi = g0 + u;
+        const int a = gi / (FT * 4), b = (gi / 4) % FT, q = gi % 4;
+        epi_store4<EPI>(g, m0 + wt * WTT + b * 32 + lr, drow[u], n0 + wp * WTP + a * 32 + 8 * q + 4 * lg,
+                        sv[u].x, sv[u].y, sv[u].z, sv[u].w);
+      }
+    }
+  }
 }
 
 // fp32 path (small fp32 layers): one thread per output element, float4 loads,
@@ -401,97 +463,87 @@ __global__ __launch_bounds__(64) void gemm_f32_kernel(GemmArgs g) {
   *dst = acc;
 }
 
-// Tile shapes (features x tokens, prefetch depth):
-//   short selections (<= 128 rows): 64 features x 128 tokens with an 8-deep
-//     register ring, one workgroup per CU and no split-K (measured: splitting
-//     K here costs more in partial-tile traffic than it gains in parallelism).
-//   medium selections: 128 x 128, 2-deep ring (two workgroups per CU).
-//   LM head and large selections: 256 x 256, each wave a 128 x 128 block, so
-//     every LDS fragment feeds four MFMAs; 1-deep ring.
-// The ring depth is reduced when it does not divide K / 64.  When the device
-// finds fewer than SPLIT_UNITS output tiles it splits K (partials in the
-// workspace, summed by gemm_splitk_reduce_kernel).
+// ---------------------------------------------------------------------------
+// Host dispatch.  Tile shapes (features x tokens, prefetch depth):
+//   <= kSkinnyRows rows: 64 x 128, 4-deep ring, one workgroup per CU.
+//   loose bounds up to 1024 rows: 128 x 128 for the large case, 4-deep ring.
+//   LM head and looser bounds: 256 x 256, each wave a 128 x 128 block, so
+//     every LDS fragment feeds four MFMAs; 1-deep ring; K split when the
+//     device finds fewer than 256 output tiles.
 constexpr int kLmTP = 256;
 int gemm_lmhead_ntile(int V) { return V / kLmTP; }
 
-// Split-K scratch: only the LM head and the 256 x 256 tiling (loose bounds
-// above 1024 rows) may split K; the other tilings never need scratch.
-size_t gemm_workspace_bytes(int epi, int max_rows, int N) {
+static int pf_for(int nk, int pfmax) {
+  for (int pf = pfmax; pf > 1; pf /= 2)
+    if (nk % pf == 0) return pf;
+  return 1;
+}
+
+size_t gemm_workspace_bytes(int epi, int max_rows, int N, int K) {
   if (max_rows <= 0) return 0;
   if (epi == EPI_LMHEAD) return (size_t)kSplitCap * kLmTP * 256 * sizeof(float);
-  if (max_rows <= 1024 || N % 256 != 0) return 0;
-  return (size_t)kSplitCap * 256 * 256 * sizeof(float);
+  if (max_rows > 1024 && N % 256 == 0) return (size_t)kSplitCap * 256 * 256 * sizeof(float);
+  return 0;
 }
 
-template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SU>
+template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
+static void launch_reduce(const GemmArgs& g, int main_grid, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_splitk_reduce_kernel<TP, TT, WP, WT, PF, EPI, AMODE, GATE, SB, ST>),
+                     dim3(SB + kReduceTarget), dim3(256), 0, st, g, main_grid);
+}
+
+template <int TP, int TT, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
 static void launch_bf16(const GemmArgs& g, hipStream_t st) {
-  // one workgroup per possible output tile, and at least kSplitCap so that the
-  // device can split K when the real selection turns out to be short
+  // one workgroup per possible output tile, and at least enough for the
+  // split the device may choose when the real selection turns out short
   const int m_tiles_max = (g.max_rows + TT - 1) / TT;
   int grid = (g.N / TP) * m_tiles_max;
-  if (SU > 0 && grid < kSplitCap) grid = kSplitCap;
-  hipLaunchKernelGGL((gemm_bf16_kernel<TP, TT, WP, WT, PF, EPI, AMODE, GATE, SU>), dim3(grid),
+  if (SB > 0) {
+    const int cap = ST < kSplitCap ? 2 * ST : kSplitCap;
+    if (grid < cap) grid = cap;
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<TP, TT, 2, 2, PF, EPI, AMODE, GATE, SB, ST>), dim3(grid),
                      dim3(256), 0, st, g);
-  if (SU > 0)  // the split-K reduction pass (exits at once when the device did not split)
-    hipLaunchKernelGGL((gemm_splitk_reduce_kernel<TP, TT, WP, WT, PF, EPI, AMODE, GATE, SU>),
-                       dim3(SU), dim3(256), 0, st, g, grid);
+  if (SB > 0) launch_reduce<TP, TT, 2, 2, PF, EPI, AMODE, GATE, SB, ST>(g, grid, st);
 }
 
-template <int TP, int TT, int PFMAX, int EPI, int AMODE, int GATE, int SU>
-static void launch_pf(const GemmArgs& g, hipStream_t st) {
-  // the ring depth must divide the number of 64-wide k-steps
+// the weight-streaming tiling alone (GATE 0 or 1)
+template <int EPI, int AMODE, int GATE>
+static void launch_skinny(const GemmArgs& g, hipStream_t st) {
   const int nk = g.K / 64;
-  if (PFMAX >= 8 && nk % 8 == 0)
-    launch_bf16<TP, TT, 2, 2, (PFMAX >= 8 ? 8 : 1), EPI, AMODE, GATE, SU>(g, st);
-  else if (PFMAX >= 4 && nk % 4 == 0)
-    launch_bf16<TP, TT, 2, 2, (PFMAX >= 4 ? 4 : 1), EPI, AMODE, GATE, SU>(g, st);
-  else if (PFMAX >= 2 && nk % 2 == 0)
-    launch_bf16<TP, TT, 2, 2, (PFMAX >= 2 ? 2 : 1), EPI, AMODE, GATE, SU>(g, st);
+  if (pf_for(nk, 4) == 4)
+    launch_bf16<64, 128, 4, EPI, AMODE, GATE, 0, 0>(g, st);
+  else if (pf_for(nk, 4) == 2)
+    launch_bf16<64, 128, 2, EPI, AMODE, GATE, 0, 0>(g, st);
   else
-    launch_bf16<TP, TT, 2, 2, 1, EPI, AMODE, GATE, SU>(g, st);
+    launch_bf16<64, 128, 1, EPI, AMODE, GATE, 0, 0>(g, st);
 }
 
-// Skinny tiling 64 x 128 (PF k-steps in flight) for <= kSkinnyRows rows, a
-// large tiling above; split-K only for the 256 x 256 tiling (its reduction
-// pass exits at once unless the device split).
-template <int PF1, int TP2, int TT2, int PF2, int EPI, int AMODE, int SU2>
+// loose bound: one launch whose device row count picks the body, then the
+// split-K pass(es) of the bodies that may split
+template <int TP2, int TT2, int PF2, int SB2, int ST2, int EPI, int AMODE>
 static void launch_dual(const GemmArgs& g, hipStream_t st) {
-  const int grid1 = (g.N / 64) * ((kSkinnyRows + 127) / 128);
   int grid2 = (g.N / TP2) * ((g.max_rows + TT2 - 1) / TT2);
-  if (SU2 > 0 && grid2 < kSplitCap) grid2 = kSplitCap;
+  if (SB2 > 0 && grid2 < kSplitCap) grid2 = kSplitCap;
+  const int grid1 = g.N / 64;
   const int grid = grid1 > grid2 ? grid1 : grid2;
-  hipLaunchKernelGGL((gemm_dual_kernel<64, 128, PF1, TP2, TT2, PF2, EPI, AMODE, SU2>),
-                     dim3(grid), dim3(256), 0, st, g);
-  if (SU2 > 0)
-    hipLaunchKernelGGL((gemm_splitk_reduce_kernel<TP2, TT2, 2, 2, PF2, EPI, AMODE, 2, SU2>), dim3(SU2),
-                       dim3(256), 0, st, g, grid);
+  hipLaunchKernelGGL((gemm_dual_kernel<64, 128, 4, 0, 0, TP2, TT2, PF2, SB2, ST2, EPI, AMODE>), dim3(grid),
+                     dim3(256), 0, st, g);
+  if (SB2 > 0) launch_reduce<TP2, TT2, 2, 2, PF2, EPI, AMODE, 2, SB2, ST2>(g, grid, st);
 }
 
 template <int EPI, int AMODE>
 static void launch_by_rows(const GemmArgs& g, hipStream_t st) {
-  const int nk = g.K / 64;
   if (g.max_rows <= kSkinnyRows || g.N % 128 != 0) {
-    launch_pf<64, 128, 4, EPI, AMODE, 0, 0>(g, st);
+    launch_skinny<EPI, AMODE, 0>(g, st);
     return;
   }
-  // loose bound: one launch; the device picks the tiling from the real count
-  const bool mid = g.max_rows <= 1024 || g.N % 256 != 0;
-  if (nk % 4 == 0) {
-    if (mid)
-      launch_dual<4, 128, 128, 4, EPI, AMODE, 0>(g, st);
-    else
-      launch_dual<4, 256, 256, 1, EPI, AMODE, 256>(g, st);
-  } else if (nk % 2 == 0) {
-    if (mid)
-      launch_dual<2, 128, 128, 2, EPI, AMODE, 0>(g, st);
-    else
-      launch_dual<2, 256, 256, 1, EPI, AMODE, 256>(g, st);
-  } else {
-    if (mid)
-      launch_dual<1, 128, 128, 1, EPI, AMODE, 0>(g, st);
-    else
-      launch_dual<1, 256, 256, 1, EPI, AMODE, 256>(g, st);
-  }
+  // the ring depth must divide the k-steps; the skinny body keeps depth 4
+  // (launch_dual is only used when K / 64 is a multiple of 4)
+  if (g.max_rows <= 1024 || g.N % 256 != 0)
+    launch_dual<128, 128, 4, 0, 0, EPI, AMODE>(g, st);
+  else
+    launch_dual<256, 256, 1, 256, 768, EPI, AMODE>(g, st);
 }
 
 hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStream_t st) {
@@ -504,12 +556,19 @@ hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStre
       hipLaunchKernelGGL((gemm_f32_kernel<EPI_ROWS, A_COMPACT>), grid, dim3(64), 0, st, g);
     return hipGetLastError();
   }
-  if (epi == EPI_LMHEAD)
-    launch_pf<kLmTP, 256, 1, EPI_LMHEAD, A_GATHER, 0, 256>(g, st);
-  else if (epi == EPI_QKV)
+  if (epi == EPI_LMHEAD) {
+    launch_bf16<kLmTP, 256, 1, EPI_LMHEAD, A_GATHER, 0, 256, 768>(g, st);
+  } else if ((g.K / 64) % 4 != 0 && g.max_rows > kSkinnyRows) {
+    // short K: the 4-deep skinny ring does not divide it; one large tiling
+    if (epi == EPI_QKV)
+      launch_bf16<128, 128, 1, EPI_QKV, A_GATHER, 0, 0, 0>(g, st);
+    else
+      launch_bf16<128, 128, 1, EPI_ROWS, A_COMPACT, 0, 0, 0>(g, st);
+  } else if (epi == EPI_QKV) {
     launch_by_rows<EPI_QKV, A_GATHER>(g, st);
-  else
+  } else {
     launch_by_rows<EPI_ROWS, A_COMPACT>(g, st);
+  }
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ enum GemmAMode { A_GATHER = 0, A_COMPACT = 1 };
 struct GemmArgs {
   const void* w;            // [N][K]
   const void* x;            // A_GATHER: x[B][S][K], row (b, idx[m]); A_COMPACT: x[m][K]
+  uint32_t x_bytes;         // size of x (operand loads are range-checked against it)
   int K, N, B, S;
   const int32_t* idx;       // selected positions (packed)
   const int32_t* offsets;   // [B+1]
@@ -42,7 +43,7 @@ struct GemmArgs {
   // split-K scratch (workspace): partial tiles
   float* part;
 };
-size_t gemm_workspace_bytes(int epi, int max_rows, int N);
+size_t gemm_workspace_bytes(int epi, int max_rows, int N, int K);
 hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStream_t st);
 int gemm_lmhead_ntile(int V);
 

@@ -113,11 +113,12 @@ def test_gather_qkv_rejections(lib):
     assert gqkv(lib, max_rows=9) == INVALID                  # more rows than B*S
     assert gqkv(lib, max_rows=-1) == INVALID
     assert gqkv(lib, k=MISALIGNED) == INVALID
-    # bounds up to 1024 rows never split K: no scratch
     lib.dlm_gather_qkv_workspace_size.restype = ctypes.c_size_t
-    assert lib.dlm_gather_qkv_workspace_size(BF16, 1024, 2, 1, 64) == 0
-    # a looser bound may split K on the device: scratch sized by the query
-    need = lib.dlm_gather_qkv_workspace_size(BF16, 2048, 2, 1, 64)
+    # 256 features, bounds up to 1024 rows: no tiling splits K, no scratch
+    assert lib.dlm_gather_qkv_workspace_size(BF16, 1024, 64, 2, 1, 64) == 0
+    assert lib.dlm_gather_qkv_workspace_size(BF16, 1024, 4096, 32, 32, 128) == 0
+    # a looser bound may split the large tiling on the device
+    need = lib.dlm_gather_qkv_workspace_size(BF16, 2048, 64, 2, 1, 64)
     assert need > 0
     assert lib.dlm_gather_qkv_scatter_kv(BF16, p(FAKE), 1, 2048, 64, p(FAKE), p(FAKE), 2048, p(FAKE), 2,
                                          1, 64, p(FAKE), p(FAKE), p(FAKE), p(FAKE),

@@ -64,7 +64,7 @@ def run_cosine_step(dlm, shape, tau=None, **override):
     q = torch.zeros(max(n, 1), s.Hq, s.hd, dtype=cur.dtype, device="cuda")
     kc, vc = dev(kc0, dt), dev(vc0, dt)
     dcode = dlm.DLM_BF16 if dt == "bf16" else dlm.DLM_F32
-    wsq = workspace(dlm.dlm_gather_qkv_workspace_size(dcode, n, s.Hq, s.Hkv, s.hd))
+    wsq = workspace(dlm.dlm_gather_qkv_workspace_size(dcode, n, s.D, s.Hq, s.Hkv, s.hd))
     dlm.dlm_gather_qkv_scatter_kv(cur, idx_o, off_o, n, dev(inp.w_qkv, dt), s.Hq, s.Hkv, s.hd, q, kc, vc,
                                   workspace=wsq)
     o = torch.zeros_like(q)
@@ -161,7 +161,7 @@ def test_gqa_lock_loop_reduced(dlm):
     counts = torch.zeros(B, dtype=torch.int32, device="cuda")
     offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
     wsa = workspace(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, max_rows, B, S, s.Hq, s.Hkv, s.hd))
-    wsq = workspace(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, max_rows, s.Hq, s.Hkv, s.hd))
+    wsq = workspace(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, max_rows, s.D, s.Hq, s.Hkv, s.hd))
     for t in range(s.steps):
         sc = inp.unlocked_scores(t)
         x = inp.hidden(t)
@@ -207,7 +207,7 @@ def test_loose_row_bound_picks_every_tiling(dlm):
     idx = torch.zeros(B * S, dtype=torch.int32, device="cuda")
     counts = torch.zeros(B, dtype=torch.int32, device="cuda")
     offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
-    wsq = workspace(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, max_rows, Hq, Hkv, hd))
+    wsq = workspace(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, max_rows, D, Hq, Hkv, hd))
     wsa = workspace(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, max_rows, B, S, Hq, Hkv, hd))
     xd, wd = dev(x, "bf16"), dev(w, "bf16")
     for per_b in (25, 300, 1000):
