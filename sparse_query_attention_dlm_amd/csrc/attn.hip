@@ -45,6 +45,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const u16* p) {
 constexpr int kSplitTarget = 512;
 constexpr int kPartRows = 2 * kSplitTarget * 128;
 constexpr int kAttnKT = 64;      // keys per K/V tile
+constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag
 constexpr int kMergeGrid = 1024; // workgroups of the merge pass (grid-stride)
 
 struct AttnPlan {
@@ -80,9 +81,16 @@ __device__ __forceinline__ AttnPlan attn_plan(const AttnArgs& a) {
 
 // LDS of the attention kernel (u16 elements)
 template <int HD>
+// Row pitches (u16) chosen for conflict-free LDS access:
+//   K rows are read as 16-byte A-fragments by 16 lanes on 16 consecutive rows:
+//     a pitch of HD + 8 moves each row by 4 banks (HD = 128) or 36 banks (64).
+//   V rows are read transposed (ds_read_b64_tr_b16): 32 lanes touch 4
+//     consecutive rows x 32 elements (16 banks each), so consecutive rows must
+//     sit 16 banks apart: a pitch of HD + 32 (320 or 192 bytes).
 struct AttnLds {
-  static constexpr int PITCH = HD + 8;
-  static constexpr int WIDE = 2 * kAttnKT * PITCH;
+  static constexpr int KPITCH = HD + 8;
+  static constexpr int VPITCH = HD + 32;
+  static constexpr int WIDE = kAttnKT * (KPITCH + VPITCH);
 };
 
 // Locate the (batch row, kv head, query tile) of a unit: tiles of QT query
@@ -166,7 +174,7 @@ __device__ __forceinline__ void attn_store_lse(const AttnArgs& a, const AttnPlan
 template <int HD>
 __device__ __forceinline__ void attn_pv_block(const u16* sV, int kb0, const float (&p)[16],
                                               f32x16 (&acc)[HD / 32], int lane) {
-  constexpr int PITCH = HD + 8, NDB = HD / 32;
+  constexpr int PITCH = AttnLds<HD>::VPITCH, NDB = HD / 32;
   const int g16 = lane >> 4, j16 = lane & 15, ga = g16 >> 1;
   bf16x8 pb[2];
   {
@@ -199,13 +207,13 @@ template <int HD>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& plan, u16* smem) {
   constexpr int QT = 128;        // query vectors per workgroup
   constexpr int KT = kAttnKT;    // keys per tile (two 32-key MFMA blocks)
-  constexpr int PITCH = HD + 8;  // u16 per LDS row
+  constexpr int PITCH = AttnLds<HD>::KPITCH, VPITCH = AttnLds<HD>::VPITCH;  // u16 per LDS row
   constexpr int NS = HD / 16;    // k-chunks of Q.K^T
   constexpr int NDB = HD / 32;   // 32-row blocks of O^T
   constexpr int CPR = HD / 8;    // 16-byte chunks per K/V row
   constexpr int CPT = 2 * KT * CPR / 256;
   u16* sK = smem;
-  u16* sV = smem + KT * PITCH;
+  u16* sV = smem + KT * PITCH;  // V rows at VPITCH
 
   if ((int)blockIdx.x >= plan.units * plan.nsplit) return;
   const AttnUnit u = attn_unit(a, plan, QT);
@@ -263,7 +271,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
       const int cidx = tid + 256 * j;
       const int tensor = cidx / (KT * CPR), rem = cidx % (KT * CPR);
       const int r = rem / CPR, ch = rem % CPR;
-      *reinterpret_cast<u32x4*>((tensor ? sV : sK) + r * PITCH + ch * 8) = st[j];
+      *reinterpret_cast<u32x4*>(tensor ? sV + r * VPITCH + ch * 8 : sK + r * PITCH + ch * 8) = st[j];
     }
     __syncthreads();
     if (k0 + KT < kend) load_tile(k0 + KT);  // next tile streams in during this tile's math
@@ -294,24 +302,34 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
     mt = pair_max(mt);
-    // the first tile of a split always holds a valid key, so m_new is finite
-    const float m_new = fmaxf(m_run, mt * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // Lazy rescaling: the reference max m_run (log2 units) moves only when a
+    // tile's max exceeds it by more than kRescaleSlack.  Until then every
+    // probability exp2(s*c - m_run) stays <= 2^kRescaleSlack, which fp32 sums
+    // and bf16 P carry with the same relative precision, and the normalised
+    // output and the LSE are unchanged; the rescale of O (64 multiplies) is
+    // then skipped by the whole wave.  The first tile of a split always holds
+    // a valid key, so m_run leaves -inf there (alpha = 0 on the empty sums).
+    const bool move = mt * c > m_run + kRescaleSlack;
+    if (__any(move)) {
+      const float m_new = move ? mt * c : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[d][i] *= alpha;
+      m_run = m_new;
+    }
     float p[2][16];
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_new));
+        p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_run));
         ls += p[kb][i];
       }
-    l_run = fmaf(l_run, alpha, ls);
-#pragma unroll
-    for (int d = 0; d < NDB; ++d)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[d][i] *= alpha;
-    m_run = m_new;
+    l_run += ls;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) attn_pv_block<HD>(sV, 32 * kb, p[kb], acc, lane);
   }

@@ -154,8 +154,8 @@ __host__ __device__ inline GemmSplit gemm_split(int units, int grid, int nk, int
   return s;
 }
 
-// u16 elements of the double-buffered LDS tile (rows padded to 72 elements)
-constexpr int gemm_lds_u16(int TP, int TT) { return 2 * (TP + TT) * 72; }
+// u16 elements of the double-buffered LDS tile (rows padded by 8 elements)
+constexpr int gemm_lds_u16(int TP, int TT, int BK) { return 2 * (TP + TT) * (BK + 8); }
 
 // Resolve the tile's token rows: cache row (b*S + idx[m], -1 for padding) and
 // the byte offset of the operand row (past the end of the buffer for padding,
@@ -179,18 +179,27 @@ __device__ __forceinline__ void gemm_rows(const GemmArgs& g, int n_rows, int m0,
 
 // One output tile (or one K-split of it) of the gathered GEMM; the caller
 // provides the LDS buffers so that several tilings can share one allocation.
-template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int SB, int ST>
+// WK = 2: eight waves; waves 4..7 repeat the layout of waves 0..3 on the
+// other half of every k-step's 16-wide sub-steps, two waves per SIMD hide each
+// other's LDS and barrier latency, and the halves are added through LDS.
+template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK = 1>
 __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u16* lds,
                                                uint32_t* s_xoff, int* s_drow) {
-  constexpr int BK = 64, PITCH = BK + 8;  // u16 elements per LDS row (144 bytes)
+  constexpr int NT = 256 * WK;   // threads
+  constexpr int PITCH = BK + 8;  // u16 elements per LDS row (16 bytes of padding)
   constexpr int ROWS = TP + TT;
-  constexpr int CHUNKS = ROWS * (BK / 8);
-  static_assert(CHUNKS % 256 == 0, "tile rows must fill the workgroup");
-  constexpr int CPT = CHUNKS / 256;
+  constexpr int CPR = BK / 8;    // 16-byte chunks per row and k-step
+  constexpr int RPJ = NT / CPR;  // rows covered by one chunk index of the workgroup
+  constexpr int CHUNKS = ROWS * CPR;
+  static_assert(CHUNKS % NT == 0 && TP % RPJ == 0, "tile rows must fill the workgroup");
+  constexpr int CPT = CHUNKS / NT;
   constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
   static_assert(WP * WT == 4 && FP >= 1 && FT >= 1, "wave layout");
   static_assert(PF >= 1, "prefetch depth");
-  static_assert(2 * ROWS * PITCH == gemm_lds_u16(TP, TT), "LDS size");
+  static_assert(2 * ROWS * PITCH == gemm_lds_u16(TP, TT, BK), "LDS size");
+  static_assert(WK == 1 || (WK == 2 && EPI != EPI_LMHEAD && (BK / 16) % 2 == 0 &&
+                            FP * FT * 16 * 256 * 4 <= 2 * ROWS * PITCH * 2),
+                "two k-halves: row epilogues only, partial sums fit the tile's LDS");
 
   const int m_tiles = (n_rows + TT - 1) / TT;
   const int n_tiles = g.N / TP;
@@ -200,27 +209,27 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
   const int unit = (int)blockIdx.x % sp.units, ksi = (int)blockIdx.x / sp.units;
   const int nt = unit / m_tiles, mt = unit % m_tiles;
   const int m0 = mt * TT, n0 = nt * TP;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, wk = tid >> 8;
   const int nk = nk_all / sp.ks;        // k-steps of this split
   const int kbase = ksi * nk;           // first k-step of this split
 
   gemm_rows<TT, AMODE>(g, n_rows, m0, s_xoff, s_drow);
   __syncthreads();
 
-  // Chunk j of this thread covers LDS row (tid/8 + 32 j), 16-byte column tid%8.
-  // Rows [0,TP) are weight rows (VGPR offset of row tid/8, the rest of the
-  // offset uniform); rows [TP, TP+TT) are gathered token rows.
-  constexpr int CW = TP / 32;  // chunks of weight rows per thread
+  // Chunk j of this thread covers LDS row (tid/CPR + RPJ j), 16-byte column
+  // tid%CPR.  Rows [0,TP) are weight rows (VGPR offset of row tid/CPR, the
+  // rest of the offset uniform); rows [TP, TP+TT) are gathered token rows.
+  constexpr int CW = TP / RPJ;  // chunks of weight rows per thread
   constexpr int CX = CPT - CW;  // chunks of token rows per thread
-  const int r0 = tid >> 3, kc = tid & 7;
+  const int r0 = tid / CPR, kc = tid % CPR;
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.w, (uint32_t)((size_t)g.N * g.K * 2));
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.x, g.x_bytes);
   const uint32_t woff = (uint32_t)(((size_t)(n0 + r0) * g.K + kc * 8) * 2);
-  const uint32_t wstride = (uint32_t)(32 * g.K * 2);
+  const uint32_t wstride = (uint32_t)(RPJ * g.K * 2);
   uint32_t xoff[CX];
 #pragma unroll
   for (int j = 0; j < CX; ++j) {
-    const uint32_t o = s_xoff[r0 + 32 * j];
+    const uint32_t o = s_xoff[r0 + RPJ * j];
     xoff[j] = o + (o & 0x80000000u ? 0u : (uint32_t)(kc * 16));
   }
   u16* const ldsw = lds + r0 * PITCH + kc * 8;
@@ -248,7 +257,7 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
     for (int j = 0; j < CPT; ++j) stg[p][j] = gload(j, min(p, nk - 1));
   }
 #pragma unroll
-  for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(ldsw + 32 * j * PITCH) = stg[0][j];
+  for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(ldsw + RPJ * j * PITCH) = stg[0][j];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) stg[0][j] = gload(j, min(PF, nk - 1));
   __syncthreads();
@@ -263,7 +272,8 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
       const u16* sW = lds + buf * ROWS * PITCH;
       const u16* sX = sW + TP * PITCH;
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
+      for (int kh = 0; kh < BK / 16 / WK; ++kh) {
+        const int kk = wk * (BK / 16 / WK) + kh;
         bf16x8 af[FP], bfr[FT];
 #pragma unroll
         for (int a = 0; a < FP; ++a)
@@ -281,11 +291,33 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
       const int slot = (u + 1) % PF;  // compile-time after unrolling
       u16* dst = ldsw + (buf ^ 1) * ROWS * PITCH;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(dst + 32 * j * PITCH) = stg[slot][j];
+      for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(dst + RPJ * j * PITCH) = stg[slot][j];
 #pragma unroll
       for (int j = 0; j < CPT; ++j) stg[slot][j] = gload(j, min(kt + 1 + PF, nk - 1));
       __syncthreads();
     }
+  }
+
+  if constexpr (WK == 2) {
+    // add the second k-half into the first: waves 4..7 park their sums in the
+    // (now idle) tile LDS in register order, waves 0..3 add them
+    float* red = reinterpret_cast<float*>(lds);
+    if (wk == 1) {
+#pragma unroll
+      for (int a = 0; a < FP; ++a)
+#pragma unroll
+        for (int b = 0; b < FT; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) red[(((a * FT + b) * 16 + i) * 4 + wave) * 64 + lane] = acc[a][b][i];
+    }
+    __syncthreads();
+    if (wk == 1) return;
+#pragma unroll
+    for (int a = 0; a < FP; ++a)
+#pragma unroll
+      for (int b = 0; b < FT; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] += red[(((a * FT + b) * 16 + i) * 4 + wave) * 64 + lane];
   }
 
   if (sp.ks > 1) {
@@ -312,33 +344,34 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
 
 // GATE: 0 = always run; 1 = run only when the device row count is <= kSkinnyRows;
 // 2 = run only when it is larger.
-template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) u16 lds[gemm_lds_u16(TP, TT)];
+template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST,
+          int WK = 1>
+__global__ __launch_bounds__(256 * WK) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) u16 lds[gemm_lds_u16(TP, TT, BK)];
   __shared__ uint32_t s_xoff[TT];
   __shared__ int s_drow[TT];
   const int n_rows = min(g.offsets[g.B], g.max_rows);
   if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
-  gemm_tile_body<TP, TT, WP, WT, PF, EPI, AMODE, SB, ST>(g, n_rows, lds, s_xoff, s_drow);
+  gemm_tile_body<TP, TT, WP, WT, BK, PF, EPI, AMODE, SB, ST, WK>(g, n_rows, lds, s_xoff, s_drow);
 }
 
 // One launch for a host that only knows a loose row bound: the device row
 // count picks the weight-streaming tiling (<= kSkinnyRows rows) or the large
 // tiling, so no second launch has to start just to exit.  Both bodies share
 // one LDS allocation sized for the larger of the two.
-template <int TP, int TT, int PF, int SB, int ST, int TP2, int TT2, int PF2, int SB2, int ST2, int EPI,
-          int AMODE>
+template <int TP, int TT, int BK, int PF, int SB, int ST, int TP2, int TT2, int BK2, int PF2, int SB2,
+          int ST2, int EPI, int AMODE>
 __global__ __launch_bounds__(256) void gemm_dual_kernel(GemmArgs g) {
-  constexpr int L1 = gemm_lds_u16(TP, TT), L2 = gemm_lds_u16(TP2, TT2);
+  constexpr int L1 = gemm_lds_u16(TP, TT, BK), L2 = gemm_lds_u16(TP2, TT2, BK2);
   constexpr int TTM = TT > TT2 ? TT : TT2;
   __shared__ __attribute__((aligned(16))) u16 lds[L1 > L2 ? L1 : L2];
   __shared__ uint32_t s_xoff[TTM];
   __shared__ int s_drow[TTM];
   const int n_rows = min(g.offsets[g.B], g.max_rows);
   if (n_rows <= kSkinnyRows)
-    gemm_tile_body<TP, TT, 2, 2, PF, EPI, AMODE, SB, ST>(g, n_rows, lds, s_xoff, s_drow);
+    gemm_tile_body<TP, TT, 2, 2, BK, PF, EPI, AMODE, SB, ST>(g, n_rows, lds, s_xoff, s_drow);
   else
-    gemm_tile_body<TP2, TT2, 2, 2, PF2, EPI, AMODE, SB2, ST2>(g, n_rows, lds, s_xoff, s_drow);
+    gemm_tile_body<TP2, TT2, 2, 2, BK2, PF2, EPI, AMODE, SB2, ST2>(g, n_rows, lds, s_xoff, s_drow);
 }
 
 // Second pass of split-K.  The plan is recomputed from the same inputs (the
@@ -347,7 +380,7 @@ __global__ __launch_bounds__(256) void gemm_dual_kernel(GemmArgs g) {
 // (about kReduceTarget in all), each summing its groups over the splits in
 // split order and storing them; the LM-head epilogue needs whole rows, so one
 // workgroup reduces one tile.
-template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
+template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g, int main_grid) {
   constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
   constexpr int NQ = FP * FT * 4;
@@ -357,7 +390,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g, int
   if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
   const int m_tiles = (n_rows + TT - 1) / TT;
   const int n_tiles = g.N / TP;
-  const GemmSplit sp = gemm_split(m_tiles * n_tiles, main_grid, g.K / 64, PF, SB, ST);
+  const GemmSplit sp = gemm_split(m_tiles * n_tiles, main_grid, g.K / BK, PF, SB, ST);
   if (sp.ks <= 1) return;
   const int RS = EPI == EPI_LMHEAD ? 1 : min(NQ, (kReduceTarget + sp.units - 1) / sp.units);
   if ((int)blockIdx.x >= sp.units * RS) return;
@@ -486,13 +519,13 @@ size_t gemm_workspace_bytes(int epi, int max_rows, int N, int K) {
   return 0;
 }
 
-template <int TP, int TT, int WP, int WT, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
+template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
 static void launch_reduce(const GemmArgs& g, int main_grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_splitk_reduce_kernel<TP, TT, WP, WT, PF, EPI, AMODE, GATE, SB, ST>),
+  hipLaunchKernelGGL((gemm_splitk_reduce_kernel<TP, TT, WP, WT, BK, PF, EPI, AMODE, GATE, SB, ST>),
                      dim3(SB + kReduceTarget), dim3(256), 0, st, g, main_grid);
 }
 
-template <int TP, int TT, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
+template <int TP, int TT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST, int WK = 1>
 static void launch_bf16(const GemmArgs& g, hipStream_t st) {
   // one workgroup per possible output tile, and at least enough for the
   // split the device may choose when the real selection turns out short
@@ -502,34 +535,35 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
     const int cap = ST < kSplitCap ? 2 * ST : kSplitCap;
     if (grid < cap) grid = cap;
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<TP, TT, 2, 2, PF, EPI, AMODE, GATE, SB, ST>), dim3(grid),
-                     dim3(256), 0, st, g);
-  if (SB > 0) launch_reduce<TP, TT, 2, 2, PF, EPI, AMODE, GATE, SB, ST>(g, grid, st);
+  hipLaunchKernelGGL((gemm_bf16_kernel<TP, TT, 2, 2, BK, PF, EPI, AMODE, GATE, SB, ST, WK>), dim3(grid),
+                     dim3(256 * WK), 0, st, g);
+  if (SB > 0) launch_reduce<TP, TT, 2, 2, BK, PF, EPI, AMODE, GATE, SB, ST>(g, grid, st);
 }
 
-// the weight-streaming tiling alone (GATE 0 or 1)
+// the weight-streaming tiling alone (GATE 0 or 1).  Measured at n = 102:
+// 128-wide k-steps with a 2-deep ring (half the barriers, same bytes in
+// flight) ran 36.7 us against 34.7 us for 64-wide steps with a 4-deep ring.
 template <int EPI, int AMODE, int GATE>
 static void launch_skinny(const GemmArgs& g, hipStream_t st) {
-  const int nk = g.K / 64;
-  if (pf_for(nk, 4) == 4)
-    launch_bf16<64, 128, 4, EPI, AMODE, GATE, 0, 0>(g, st);
-  else if (pf_for(nk, 4) == 2)
-    launch_bf16<64, 128, 2, EPI, AMODE, GATE, 0, 0>(g, st);
+  if (pf_for(g.K / 64, 4) == 4)
+    launch_bf16<64, 128, 64, 4, EPI, AMODE, GATE, 0, 0, 2>(g, st);
+  else if (pf_for(g.K / 64, 4) == 2)
+    launch_bf16<64, 128, 64, 2, EPI, AMODE, GATE, 0, 0>(g, st);
   else
-    launch_bf16<64, 128, 1, EPI, AMODE, GATE, 0, 0>(g, st);
+    launch_bf16<64, 128, 64, 1, EPI, AMODE, GATE, 0, 0>(g, st);
 }
 
 // loose bound: one launch whose device row count picks the body, then the
-// split-K pass(es) of the bodies that may split
-template <int TP2, int TT2, int PF2, int SB2, int ST2, int EPI, int AMODE>
+// split-K pass of the large body when it may split
+template <int BK1, int PF1, int TP2, int TT2, int PF2, int SB2, int ST2, int EPI, int AMODE>
 static void launch_dual(const GemmArgs& g, hipStream_t st) {
   int grid2 = (g.N / TP2) * ((g.max_rows + TT2 - 1) / TT2);
   if (SB2 > 0 && grid2 < kSplitCap) grid2 = kSplitCap;
   const int grid1 = g.N / 64;
   const int grid = grid1 > grid2 ? grid1 : grid2;
-  hipLaunchKernelGGL((gemm_dual_kernel<64, 128, 4, 0, 0, TP2, TT2, PF2, SB2, ST2, EPI, AMODE>), dim3(grid),
-                     dim3(256), 0, st, g);
-  if (SB2 > 0) launch_reduce<TP2, TT2, 2, 2, PF2, EPI, AMODE, 2, SB2, ST2>(g, grid, st);
+  hipLaunchKernelGGL((gemm_dual_kernel<64, 128, BK1, PF1, 0, 0, TP2, TT2, 64, PF2, SB2, ST2, EPI, AMODE>),
+                     dim3(grid), dim3(256), 0, st, g);
+  if (SB2 > 0) launch_reduce<TP2, TT2, 2, 2, 64, PF2, EPI, AMODE, 2, SB2, ST2>(g, grid, st);
 }
 
 template <int EPI, int AMODE>
@@ -538,12 +572,11 @@ static void launch_by_rows(const GemmArgs& g, hipStream_t st) {
     launch_skinny<EPI, AMODE, 0>(g, st);
     return;
   }
-  // the ring depth must divide the k-steps; the skinny body keeps depth 4
-  // (launch_dual is only used when K / 64 is a multiple of 4)
+  // loose bound (K / 64 is a multiple of 4 here)
   if (g.max_rows <= 1024 || g.N % 256 != 0)
-    launch_dual<128, 128, 4, 0, 0, EPI, AMODE>(g, st);
+    launch_dual<64, 4, 128, 128, 4, 0, 0, EPI, AMODE>(g, st);
   else
-    launch_dual<256, 256, 1, 256, 768, EPI, AMODE>(g, st);
+    launch_dual<64, 4, 256, 256, 1, 256, 768, EPI, AMODE>(g, st);
 }
 
 hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStream_t st) {
@@ -557,13 +590,13 @@ hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStre
     return hipGetLastError();
   }
   if (epi == EPI_LMHEAD) {
-    launch_bf16<kLmTP, 256, 1, EPI_LMHEAD, A_GATHER, 0, 256, 768>(g, st);
+    launch_bf16<kLmTP, 256, 64, 1, EPI_LMHEAD, A_GATHER, 0, 256, 768>(g, st);
   } else if ((g.K / 64) % 4 != 0 && g.max_rows > kSkinnyRows) {
     // short K: the 4-deep skinny ring does not divide it; one large tiling
     if (epi == EPI_QKV)
-      launch_bf16<128, 128, 1, EPI_QKV, A_GATHER, 0, 0, 0>(g, st);
+      launch_bf16<128, 128, 64, 1, EPI_QKV, A_GATHER, 0, 0, 0>(g, st);
     else
-      launch_bf16<128, 128, 1, EPI_ROWS, A_COMPACT, 0, 0, 0>(g, st);
+      launch_bf16<128, 128, 64, 1, EPI_ROWS, A_COMPACT, 0, 0, 0>(g, st);
   } else if (epi == EPI_QKV) {
     launch_by_rows<EPI_QKV, A_GATHER>(g, st);
   } else {
