@@ -160,10 +160,12 @@ int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D,
  *                                    (D_out must equal Hq*hd)
  *   w_o != NULL:  out_cache[b, idx[r], :] = concat_h o_sel[r,h,:] . W_o^T,
  *                 w_o [D_out, Hq*hd] output-major; out_cache required.
- * Other out_cache rows are not touched.  hd in {64,128}.
+ * Other out_cache rows are not touched.  hd in {64,128}.  bf16: one
+ * sequence's K (or V) slice plus 64 rows, (S+64)*Hkv*hd*2 bytes, stays under
+ * 2 GiB, else DLM_ERR_INVALID_ARG.
  * Workspace (size from dlm_partial_attn_workspace_size, D_out_wo = D_out when
  * a W_o projection will be passed, else 0): bf16 needs split-KV partials only
- * for S >= 256 and the W_o GEMM's split-K tiles only for loose bounds above
+ * for S >= 512 and the W_o GEMM's split-K tiles only for loose bounds above
  * 1024 rows; when the size is 0, workspace may be NULL.
  * ------------------------------------------------------------------------ */
 size_t dlm_partial_attn_workspace_size(int dtype, int max_rows, int B, int S, int Hq, int Hkv,

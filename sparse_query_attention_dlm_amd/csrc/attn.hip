@@ -21,6 +21,8 @@
 //   * Few queries (short selections): the key range is split over workgroups
 //     and a merge pass combines the partial outputs by their LSE.
 // fp32 kernel (small fp32 layers): one wave per (row, head), float32 FMA.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -36,15 +38,18 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const u16* p) {
 // from the selection counts (the host only knows an upper bound):
 //   units  = sum_b ceil(n_b * G / 128) query tiles, times Hkv
 //   nsplit = 1 when units >= kSplitTarget, else ceil(kSplitTarget / units)
-//            capped at 16 and at S/128, so short selections still spread
+//            capped at 16 and at S/256, so short selections still spread
 //            their K/V reads over the whole GPU (one CU streams only a few
 //            tens of GB/s, so a few workgroups cannot read a long cache fast);
-//            the merge pass combines the split partials by their LSE.
+//            the merge pass combines the split partials by their LSE.  Each
+//            split keeps at least 256 keys: shorter ones cost more in partial
+//            outputs (written and merged) than they gain in spread.
 // With nsplit > 1, units < kSplitTarget implies nsplit * n_rows * Hq <=
 // 2 * kSplitTarget * 128 = kPartRows, the bound the workspace is sized for.
 constexpr int kSplitTarget = 512;
 constexpr int kPartRows = 2 * kSplitTarget * 128;
 constexpr int kAttnKT = 64;      // keys per K/V tile
+constexpr int kMinSplitKeys = 256;  // keys per split at least
 constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag
 constexpr int kMergeGrid = 1024; // workgroups of the merge pass (grid-stride)
 
@@ -69,7 +74,7 @@ __device__ __forceinline__ AttnPlan attn_plan(const AttnArgs& a) {
   if (p.units > 0 && p.units < kSplitTarget) {
     ns = (kSplitTarget + p.units - 1) / p.units;
     ns = min(ns, 16);
-    ns = min(ns, max(1, a.S / 128));
+    ns = min(ns, max(1, a.S / kMinSplitKeys));
     if (p.n_rows > 0) ns = min(ns, max(1, kPartRows / (p.n_rows * a.Hq)));
   }
   // keys per split are rounded up to whole tiles; recount the splits from that
@@ -236,9 +241,18 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
   }
 
   const int kbeg = u.split * plan.kps, kend = min(a.S, kbeg + plan.kps);
-  const size_t kstride = (size_t)a.Hkv * HD;
-  const u16* kbase = static_cast<const u16*>(a.k) + ((size_t)u.b * a.S * a.Hkv + u.g) * HD;
-  const u16* vbase = static_cast<const u16*>(a.v) + ((size_t)u.b * a.S * a.Hkv + u.g) * HD;
+  // K/V of this (sequence, kv head) through buffer loads: key j at j*rowbytes
+  // from the base; the resource ends after key S-1, so rows past the end of
+  // the sequence read zeros (the whole offset sits in the VGPR)
+  const uint32_t rowbytes = (uint32_t)a.Hkv * HD * 2;
+  const size_t base_el = ((size_t)u.b * a.S * a.Hkv + u.g) * HD;
+  const uint32_t nbytes = (uint32_t)(a.S - 1) * rowbytes + HD * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const u16*>(a.k) + base_el, nbytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const u16*>(a.v) + base_el, nbytes);
+  constexpr int RPJ = 256 / CPR;       // key rows between a thread's chunks
+  constexpr int JT = KT * CPR / 256;   // chunks per tensor per thread
+  static_assert(2 * JT == CPT, "K and V chunks");
+  const uint32_t voff = (uint32_t)(tid / CPR) * rowbytes + (tid % CPR) * 16;
   const float c = a.scale * kLog2e;
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -246,36 +260,21 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
 #pragma unroll
   for (int d = 0; d < NDB; ++d) acc[d] = f32x16{};
 
-  // K/V tile loads: chunk j of this thread is (tensor, key row, 16-byte column)
+  // K/V tile loads: chunk j < JT of this thread is K row (tid/CPR + RPJ j),
+  // 16-byte column tid%CPR; chunk JT + j the same V row.  Keys of the tile
+  // past the split's end (but inside the sequence) are loaded and masked.
   u32x4 st[CPT];
   auto load_tile = [&](int k0) {
-    const int nvalid = min(KT, kend - k0);
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int cidx = tid + 256 * j;
-      const int tensor = cidx / (KT * CPR), rem = cidx % (KT * CPR);
-      const int r = rem / CPR, ch = rem % CPR;
-      if (r < nvalid)
-        st[j] = *reinterpret_cast<const u32x4*>((tensor ? vbase : kbase) + (size_t)(k0 + r) * kstride + ch * 8);
-      else
-        st[j] = u32x4{0, 0, 0, 0};
+    for (int j = 0; j < JT; ++j) {
+      const uint32_t o = voff + (uint32_t)(k0 + RPJ * j) * rowbytes;
+      st[j] = buffer_load16(rk, o);
+      st[JT + j] = buffer_load16(rv, o);
     }
   };
-  if (kbeg < kend) load_tile(kbeg);
-
-  for (int k0 = kbeg; k0 < kend; k0 += KT) {
-    const int nvalid = min(KT, kend - k0);
-    __syncthreads();  // every wave is done reading the previous tile
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int cidx = tid + 256 * j;
-      const int tensor = cidx / (KT * CPR), rem = cidx % (KT * CPR);
-      const int r = rem / CPR, ch = rem % CPR;
-      *reinterpret_cast<u32x4*>(tensor ? sV + r * VPITCH + ch * 8 : sK + r * PITCH + ch * 8) = st[j];
-    }
-    __syncthreads();
-    if (k0 + KT < kend) load_tile(k0 + KT);  // next tile streams in during this tile's math
-
+  // One K/V tile's scores, online softmax and P.V.  `masked` (a
+  // std::integral_constant) compiles the key mask in for the last, partial tile.
+  auto tile_math = [&](int nvalid, auto masked) {
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -287,7 +286,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
         sacc[kb] = mfma32x32x16(kf, qf[s], sacc[kb]);
       }
     }
-    if (nvalid < KT) {
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -332,6 +331,33 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
     l_run += ls;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) attn_pv_block<HD>(sV, 32 * kb, p[kb], acc, lane);
+  };
+
+  if (kbeg < kend) load_tile(kbeg);
+
+  // Stage tile k0 from registers into LDS and start loading the next one,
+  // which streams in during this tile's math.
+  auto stage = [&](int k0) {
+    __syncthreads();  // every wave is done reading the previous tile
+#pragma unroll
+    for (int j = 0; j < JT; ++j) {
+      const int r = tid / CPR + RPJ * j, ch = tid % CPR;
+      *reinterpret_cast<u32x4*>(sK + r * PITCH + ch * 8) = st[j];
+      *reinterpret_cast<u32x4*>(sV + r * VPITCH + ch * 8) = st[JT + j];
+    }
+    __syncthreads();
+    if (k0 + KT < kend) load_tile(k0 + KT);
+  };
+  // Full tiles run a copy of the math without the key mask; the partial last
+  // tile of the split (if any) runs the masked copy after the loop.
+  int k0 = kbeg;
+  for (; k0 + KT <= kend; k0 += KT) {
+    stage(k0);
+    tile_math(KT, std::false_type{});
+  }
+  if (k0 < kend) {
+    stage(k0);
+    tile_math(kend - k0, std::true_type{});
   }
 
   const float l_tot = pair_sum(l_run);
@@ -484,7 +510,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
 static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 size_t attn_workspace_bytes(int dtype, int max_rows, int B, int S, int Hq, int Hkv, int hd) {
-  if (dtype != 1 || S < 256) return 0;  // fewer than 256 keys are never split
+  if (dtype != 1 || S < 2 * kMinSplitKeys) return 0;  // such sequences are never split
   return (size_t)kPartRows * (hd + 1) * sizeof(float);
 }
 
@@ -500,7 +526,7 @@ hipError_t launch_attn(int dtype, const AttnArgs& a0, void* workspace, hipStream
     return hipGetLastError();
   }
   const int G = a.Hq / a.Hkv;
-  const bool may_split = a.S >= 256;
+  const bool may_split = a.S >= 2 * kMinSplitKeys;
   a.part_o = may_split ? static_cast<float*>(workspace) : nullptr;
   a.part_lse = may_split ? a.part_o + (size_t)kPartRows * a.hd : nullptr;
   // enough workgroups for every tile and for the split factor the device may

@@ -60,10 +60,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Reductions over the lane pair (l, l^32) with v_permlane32_swap.  With both
-// operands equal, lanes < 32 receive (own, partner) and lanes >= 32 receive
-// (partner, own): in both the low-half value comes first, so the two lanes
-// compute bit-identical results.
 // Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3):
 // loads past the end return zeros without touching memory.  Callers keep
 // `bytes` below 2^31 wherever they rely on that, put the per-lane part of an
@@ -77,6 +73,10 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
+// Reductions over the lane pair (l, l^32) with v_permlane32_swap.  With both
+// operands equal, lanes < 32 receive (own, partner) and lanes >= 32 receive
+// (partner, own): in both the low-half value comes first, so the two lanes
+// compute bit-identical results.
 __device__ __forceinline__ float pair_max(float v) {
   unsigned u = __float_as_uint(v);
   auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);

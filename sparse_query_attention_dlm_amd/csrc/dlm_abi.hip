@@ -248,6 +248,8 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
   REQUIRE(max_rows >= 0 && (long long)max_rows <= (long long)B * S, "max_rows=%d out of range",
           max_rows);
   REQUIRE(scale > 0.f, "scale must be positive");
+  REQUIRE(dtype != DLM_BF16 || (long long)(S + 64) * Hkv * hd * 2 < (1ll << 31),
+          "one sequence's K or V cache slice reaches 2 GiB");
   REQUIRE_ALIGNED(q_sel);
   REQUIRE_ALIGNED(k_cache);
   REQUIRE_ALIGNED(v_cache);

@@ -144,6 +144,8 @@ def test_partial_attn_rejections(lib):
     assert attn(lib, wo=FAKE, out=0, D_out=64) == INVALID    # W_o without an output cache
     assert attn(lib, out=FAKE, D_out=100) == INVALID         # no W_o: D_out must be Hq*hd
     assert attn(lib, wo=FAKE, out=FAKE, D_out=100) == INVALID  # bf16 W_o: D_out % 64
+    # bf16 addresses one sequence's K/V slice with 32-bit offsets: under 2 GiB
+    assert attn(lib, S=(1 << 20) - 64, Hq=8, Hkv=8) == INVALID
     # a short selection needs split-KV scratch: refused without it
     need = lib.dlm_partial_attn_workspace_size(BF16, 4, 1, 4096, 2, 1, 128, 0)
     assert need > 0
