@@ -233,8 +233,15 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
     xoff[j] = o + (o & 0x80000000u ? 0u : (uint32_t)(kc * 16));
   }
   u16* const ldsw = lds + r0 * PITCH + kc * 8;
+  // Every workgroup walks its k-steps from its own starting point (wrapping
+  // around): workgroups are dealt round-robin to the 8 XCDs, so the ~nk
+  // workgroups sharing an XCD's L2 read different k-slices of the gathered
+  // rows at any moment instead of all hitting the same lines.
+  const int krot = ((int)blockIdx.x >> 3) % nk;
   auto gload = [&](int j, int kstep) -> u32x4 {
-    const uint32_t ko = (uint32_t)(kbase + kstep) * (BK * 2);
+    int kp = kstep + krot;
+    kp -= kp >= nk ? nk : 0;
+    const uint32_t ko = (uint32_t)(kbase + kp) * (BK * 2);
     if (j < CW) return buffer_load16(rW, woff, ko + (uint32_t)j * wstride);
     return buffer_load16(rX, xoff[j - CW], ko);
   };
