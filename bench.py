@@ -33,6 +33,14 @@ if ROOT not in sys.path:
 
 PEAK_HBM = 8.0e12      # MI355X HBM3E, bytes/s
 PEAK_BF16 = 2.5e15     # MI355X dense bf16 MFMA, flop/s
+# ceilings measured on this GPU at the start of the run (measured_ceilings):
+# "mfma_bf16" flop/s of the MFMA-loop probe, "hbm_copy" bytes/s of a 1 GiB copy
+MEASURED = {}
+
+
+def of_measured(rate, key):
+    """rate as a fraction of the ceiling measured on this GPU (None if not measured)."""
+    return rate / MEASURED[key] if MEASURED.get(key) else None
 
 
 def parse():
@@ -129,13 +137,16 @@ def main():
         print(json.dumps(hbm_ceiling()), flush=True)
         return
     if a.only_extras:
+        ceil = measured_ceilings(dlm)
         res = {}
         for name, fn in EXTRAS:
             print(f"[bench]   {name}", file=sys.stderr, flush=True)
             res[name] = fn(dlm, W)
             torch.cuda.empty_cache()
-        print(json.dumps({"other_workloads": res}), flush=True)
+        print(json.dumps({"measured_ceilings": ceil, "other_workloads": res}), flush=True)
         return
+    print("[bench] measuring HBM and MFMA ceilings", file=sys.stderr, flush=True)
+    ceilings = measured_ceilings(dlm)
     sh = W.BF16_S1024
     B, S, s = sh.B, sh.S, sh
     max_rows = B * S            # the host does not know the selection count
@@ -259,18 +270,22 @@ def main():
                    "Hq": s.Hq, "Hkv": s.Hkv, "hd": s.hd, "n_selected": n_sel, "tau": sh.tau,
                    "max_rows_bound": max_rows, "rotating_input_sets": a.sets, "launch": "one hip graph per round of the input sets"},
         "stages_ms": {k: float(v) for k, v in zip(names, mean)},
+        "measured_ceilings": ceilings,
         "step_gpu_ms": step_ms,
         "stage_timing": f"{kreps} back-to-back launches per stage between two HIP events, behind a queued GPU sleep (host enqueue {host_enqueue_ms:.1f} ms)",
         "roofline": {"kernel": "gemm_dual_kernel, 64x128 weight-streaming body (gathered QKV + K/V scatter)", "bound": "hbm",
                      "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM, "traffic": traffic,
-                     "algorithmic_bytes": qkv_bytes},
+                     "algorithmic_bytes": qkv_bytes,
+                     "frac_of_measured_ceiling": of_measured(achieved, "hbm_copy")},
         "stage_roofline": {
             "select": {"bound": "hbm", "GB/s": sel_bytes / (mean[0] / 1e3) / 1e9,
-                       "frac": sel_bytes / (mean[0] / 1e3) / PEAK_HBM},
+                       "frac": sel_bytes / (mean[0] / 1e3) / PEAK_HBM,
+                       "frac_of_measured_ceiling": of_measured(sel_bytes / (mean[0] / 1e3), "hbm_copy")},
             "qkv": {"TFLOP/s": qkv_flops / qkv_s / 1e12, "mfma_frac": qkv_flops / qkv_s / PEAK_BF16},
             "attn": {"bound": "hbm", "GB/s": attn_bytes / (mean[2] / 1e3) / 1e9,
                      "frac": attn_bytes / (mean[2] / 1e3) / PEAK_HBM,
+                     "frac_of_measured_ceiling": of_measured(attn_bytes / (mean[2] / 1e3), "hbm_copy"),
                      "TFLOP/s": attn_flops / (mean[2] / 1e3) / 1e12},
         },
     }
@@ -370,8 +385,10 @@ def extra_colsum(dlm, W):
     f_attn = 4.0 * n * S * hd * Hq
     f_col = 2.0 * n * S * hd * Hq
     return {"workload": sh.name, "n_selected": n,
-            "partial_attn": {"ms": t_attn, "TFLOP/s": f_attn / t_attn / 1e9, "frac": f_attn / (t_attn / 1e3) / PEAK_BF16},
-            "colsum_topk": {"ms": t_col, "TFLOP/s": f_col / t_col / 1e9, "frac": f_col / (t_col / 1e3) / PEAK_BF16},
+            "partial_attn": {"ms": t_attn, "TFLOP/s": f_attn / t_attn / 1e9, "frac": f_attn / (t_attn / 1e3) / PEAK_BF16,
+                             "frac_of_measured_ceiling": of_measured(f_attn / (t_attn / 1e3), "mfma_bf16")},
+            "colsum_topk": {"ms": t_col, "TFLOP/s": f_col / t_col / 1e9, "frac": f_col / (t_col / 1e3) / PEAK_BF16,
+                            "frac_of_measured_ceiling": of_measured(f_col / (t_col / 1e3), "mfma_bf16")},
             "tokens_per_s": n / ((t_attn + t_col) / 1e3)}
 
 
@@ -410,7 +427,8 @@ def extra_lsp(dlm, W):
     t_pre = _time(prefix, 10)
     f = 2.0 * n * D * V
     return {"workload": sh.name, "n_selected": n,
-            "confidence_lm_head": {"ms": t_conf, "TFLOP/s": f / t_conf / 1e9, "frac": f / (t_conf / 1e3) / PEAK_BF16},
+            "confidence_lm_head": {"ms": t_conf, "TFLOP/s": f / t_conf / 1e9, "frac": f / (t_conf / 1e3) / PEAK_BF16,
+                                   "frac_of_measured_ceiling": of_measured(f / (t_conf / 1e3), "mfma_bf16")},
             "stable_prefix": {"ms": t_pre},
             "tokens_per_s": n / ((t_conf + t_pre) / 1e3)}
 
@@ -471,10 +489,12 @@ def extra_lock_loop(dlm, W):
         fq = 2.0 * n * D * N
         fa = 4.0 * n * S * hd * Hq
         per[f"t{t}"] = {"rows": n, "qkv_ms": tq, "qkv_frac": fq / (tq / 1e3) / PEAK_BF16,
-                        "attn_ms": ta, "attn_frac": fa / (ta / 1e3) / PEAK_BF16}
+                        "attn_ms": ta, "attn_frac": fa / (ta / 1e3) / PEAK_BF16,
+                        "attn_frac_of_measured_ceiling": of_measured(fa / (ta / 1e3), "mfma_bf16")}
     fl = sum(2.0 * n * D * N + 4.0 * n * S * hd * Hq for _, n in sc)
     return {"workload": sh.name, "rows_total": rows, "loop_ms": t_loop,
             "tokens_per_s": rows / (t_loop / 1e3), "loop_frac_mfma": fl / (t_loop / 1e3) / PEAK_BF16,
+            "loop_frac_of_measured_ceiling": of_measured(fl / (t_loop / 1e3), "mfma_bf16"),
             "steps": per}
 
 
@@ -527,8 +547,56 @@ def hbm_ceiling():
             "copy_bytes_each_way": (n // 2) * 4}
 
 
+def mfma_ceiling(dlm, grid=512, iters=2000):
+    """Measured bf16 MFMA ceiling: the library's MFMA-loop probe (eight
+    independent 32x32x16 chains per wave on registers, no memory traffic)."""
+    import torch
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    t = _time(lambda: dlm.dlm_probe_mfma_bf16(iters, grid, sink), 5)
+    flops = grid * 4 * iters * 8 * 32768
+    return {"mfma_bf16_TFLOPs": flops / (t / 1e3) / 1e12,
+            "mfma_probe": f"{grid} workgroups x 4 waves x {iters} rounds of 8 independent 32x32x16 bf16 MFMAs"}
+
+
+def measured_ceilings(dlm):
+    """HBM (streaming read, 1 GiB copy) and MFMA ceilings measured on this GPU;
+    also fills MEASURED for the *_of_measured_ceiling fractions."""
+    import torch
+    c = {**hbm_ceiling(), **mfma_ceiling(dlm)}
+    torch.cuda.empty_cache()
+    MEASURED["mfma_bf16"] = c["mfma_bf16_TFLOPs"] * 1e12
+    MEASURED["hbm_copy"] = c["copy_1GiB_GBps_read_plus_write"] * 1e9
+    return c
+
+
+def extra_select_b8(dlm, W):
+    """Not a configuration of the pages: the C2 cosine select at B = 8 (134 MB
+    per call, two rotating input sets of 268 MB, more than the Infinity
+    Cache), the asymptote of the select kernel's HBM rate."""
+    import torch
+    B, S, D = 8, 1024, 4096
+    sets = [(_gen((B, S, D), 601 + 2 * r, dtype=torch.bfloat16), _gen((B, S, D), 602 + 2 * r, dtype=torch.bfloat16))
+            for r in range(2)]
+    idx = torch.empty(B * S, dtype=torch.int32, device="cuda")
+    counts = torch.empty(B, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(dlm.dlm_select_workspace_size(dlm.DLM_SCORE_COSINE, B, S, 0, 0), dtype=torch.uint8, device="cuda")
+    calls = [lambda c=c, p=p: dlm.dlm_saliency_select(dlm.DLM_SCORE_COSINE, c, p, lo=0, hi=S, threshold=0.95, idx=idx,
+                                                      counts=counts, offsets=offsets, workspace=ws) for c, p in sets]
+    state = {"i": 0}
+
+    def call():
+        calls[state["i"] % 2]()
+        state["i"] += 1
+    t = _time(call, 20)
+    nbytes = 2 * B * S * D * 2
+    return {"workload": "bf16_select_b8_s1024_d4096 (not a configuration of the pages)", "ms": t,
+            "GB/s": nbytes / (t / 1e3) / 1e9, "frac": nbytes / (t / 1e3) / PEAK_HBM,
+            "frac_of_measured_ceiling": of_measured(nbytes / (t / 1e3), "hbm_copy")}
+
+
 EXTRAS = (("tiny_fp32", extra_tiny), ("colsum_top64", extra_colsum), ("lsp_commit", extra_lsp),
-          ("gqa_lock_loop", extra_lock_loop))
+          ("gqa_lock_loop", extra_lock_loop), ("select_b8_asymptote", extra_select_b8))
 
 
 def cpu_baseline(W, sh, seconds):

@@ -223,6 +223,19 @@ int dlm_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
                       int gen_lo, int gen_hi, int32_t* ring, int W, int step,
                       float conf_threshold, int min_commit, int32_t* committed, void* stream);
 
+/* ------------------------------------------------------------------------
+ * dlm_probe_mfma_bf16  (measurement aid, not a step of the method)
+ *
+ * Runs grid workgroups of 256 threads in which every wave issues `iters`
+ * rounds of eight independent 32x32x16 bf16 MFMAs on register operands (no
+ * memory traffic): grid * 4 * iters * 8 * 32768 flop.  Timing it gives the
+ * matrix pipes' peak at the clock the chip holds under MFMA load, the
+ * measured ceiling that roofline fractions are also reported against.
+ * sink [grid*256] f32 (device) receives one value per thread.  iters > 0,
+ * grid > 0, else DLM_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------ */
+int dlm_probe_mfma_bf16(int iters, int grid, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

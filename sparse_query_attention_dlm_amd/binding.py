@@ -63,6 +63,8 @@ lib.dlm_attn_colsum.argtypes = [_I, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, 
                                 _P, _P, _P, _Z, _P]
 lib.dlm_stable_prefix.restype = _I
 lib.dlm_stable_prefix.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _I, _F, _I, _P, _P]
+lib.dlm_probe_mfma_bf16.restype = _I
+lib.dlm_probe_mfma_bf16.argtypes = [_I, _I, _P, _P]
 
 
 def version() -> str:
@@ -204,3 +206,10 @@ def dlm_stable_prefix(argmax, maxprob, gen_lo, gen_hi, ring, step, conf_threshol
         float(conf_threshold), int(min_commit), _ptr(committed, "committed", torch.int32),
         _stream(stream))
     _check(rc)
+
+
+def dlm_probe_mfma_bf16(iters, grid, sink, stream=None):
+    """Measurement aid: grid*4 waves each run iters x 8 bf16 32x32x16 MFMAs
+    on registers (grid*4*iters*8*32768 flop); sink f32 [grid*256]."""
+    assert sink.numel() >= grid * 256, "sink needs grid*256 floats"
+    _check(lib.dlm_probe_mfma_bf16(int(iters), int(grid), _ptr(sink, "sink", torch.float32), _stream(stream)))

@@ -374,4 +374,12 @@ int dlm_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
                     "stable prefix");
 }
 
+// ---------------------------------------------------------------------------
+int dlm_probe_mfma_bf16(int iters, int grid, float* sink, void* stream) {
+  REQUIRE(iters > 0 && grid > 0, "iters=%d and grid=%d must be positive", iters, grid);
+  REQUIRE_PTR(sink);
+  return hip_status(dlm::launch_probe_mfma(iters, grid, sink, static_cast<hipStream_t>(stream)),
+                    "MFMA probe");
+}
+
 }  // extern "C"

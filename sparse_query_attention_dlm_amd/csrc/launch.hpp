@@ -65,6 +65,7 @@ struct AttnArgs {
 };
 size_t attn_workspace_bytes(int dtype, int max_rows, int B, int S, int Hq, int Hkv, int hd);
 hipError_t launch_attn(int dtype, const AttnArgs& a, void* workspace, hipStream_t st);
+hipError_t launch_probe_mfma(int iters, int grid, float* sink, hipStream_t st);
 
 // colsum.hip
 hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, const void* k,

@@ -170,6 +170,12 @@ def test_colsum_rejections(lib):
     assert lib.dlm_attn_colsum_workspace_size(4, 4096, 32) == 32 * 4 * 4096 * 4
 
 
+def test_probe_rejections(lib):
+    assert lib.dlm_probe_mfma_bf16(0, 1, p(FAKE), p(0)) == INVALID
+    assert lib.dlm_probe_mfma_bf16(1, 0, p(FAKE), p(0)) == INVALID
+    assert lib.dlm_probe_mfma_bf16(1, 1, p(0), p(0)) == INVALID
+
+
 def test_stable_prefix_rejections(lib):
     def sp(argmax=FAKE, mp=FAKE, B=2, S=32, lo=8, hi=32, ring=FAKE, W=3, step=0, com=FAKE):
         return lib.dlm_stable_prefix(p(argmax), p(mp), B, S, lo, hi, p(ring), W, step, f(0.9), 0, p(com), p(0))

@@ -457,3 +457,38 @@ def test_stable_prefix_bit_exact_on_given_inputs(dlm):
         assert np.array_equal(ring.cpu().numpy(), ring_o)
         com_o = com_new
     assert com_o.max() > 0
+
+
+# ---------------------------------------------------------------------------
+# measurement aid: the MFMA ceiling probe
+# ---------------------------------------------------------------------------
+def test_mfma_probe_matches_closed_form(dlm):
+    """The MFMA ceiling probe does the work it is timed for: each thread's
+    sink value equals 8 chains x iters x the sum of its 16 result registers of
+    A.B, built on the host from the probe's operand values and the 32x32x16
+    fragment layout (A: row lane%32, k = 8*(lane/32)+e; B: column lane%32, same
+    k; C register r: row 8(r/4) + 4*(lane/32) + r%4, column lane%32)."""
+    iters, grid = 3, 2
+    say(f"[mfma probe] iters={iters} grid={grid}")
+    sink = torch.zeros(grid * 256, dtype=torch.float32, device="cuda")
+    dlm.dlm_probe_mfma_bf16(iters, grid, sink)
+    torch.cuda.synchronize()
+    f32 = np.float32
+    bf = lambda v: float(W.round_bf16(np.array([v], dtype=np.float32))[0])
+    A = np.zeros((32, 16))
+    Bm = np.zeros((16, 32))
+    for m in range(32):
+        for k in range(16):
+            la, e = m + 32 * (k // 8), k % 8
+            A[m, k] = bf(f32(1) + f32(1e-3) * f32(la)) if e % 2 == 0 else bf(f32(1) - f32(1e-3) * f32(e // 2))
+    for k in range(16):
+        for n in range(32):
+            lb, e = n + 32 * (k // 8), k % 8
+            Bm[k, n] = bf(f32(1e-3) * f32(e // 2)) if e % 2 == 0 else bf(f32(1e-3) * f32(lb))
+    C = A @ Bm
+    exp = np.array([sum(C[8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32] for r in range(16)) for l in range(64)])
+    exp = 8 * iters * exp
+    got = host(sink).reshape(grid * 4, 64)
+    err = float(np.max(np.abs(got - exp[None, :]) / np.abs(exp[None, :])))
+    say(f"  max relative error {err:.2e}")
+    assert err <= 1e-4
