@@ -36,7 +36,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const u16* p) {
 
 // Work plan shared by the attention and merge kernels, computed on the device
 // from the selection counts (the host only knows an upper bound):
-//   units  = sum_b ceil(n_b * G / 128) query tiles, times Hkv
+//   units  = sum_b ceil(n_b * G / QT) query tiles of QT vectors, times Hkv
 //   nsplit = 1 when units >= kSplitTarget, else ceil(kSplitTarget / units)
 //            capped at 16 and at S/256, so short selections still spread
 //            their K/V reads over the whole GPU (one CU streams only a few
@@ -44,8 +44,8 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const u16* p) {
 //            the merge pass combines the split partials by their LSE.  Each
 //            split keeps at least 256 keys: shorter ones cost more in partial
 //            outputs (written and merged) than they gain in spread.
-// With nsplit > 1, units < kSplitTarget implies nsplit * n_rows * Hq <=
-// 2 * kSplitTarget * 128 = kPartRows, the bound the workspace is sized for.
+// A last cap keeps nsplit * n_rows * Hq <= kPartRows, the bound the
+// workspace is sized for.
 constexpr int kSplitTarget = 512;
 constexpr int kPartRows = 2 * kSplitTarget * 128;
 constexpr int kAttnKT = 64;      // keys per K/V tile
@@ -60,12 +60,12 @@ struct AttnPlan {
   int n_rows;
 };
 
-__device__ __forceinline__ AttnPlan attn_plan(const AttnArgs& a) {
+__device__ __forceinline__ AttnPlan attn_plan(const AttnArgs& a, int QT) {
   const int G = a.Hq / a.Hkv;
   int tiles = 0;
   for (int bb = 0; bb < a.B; ++bb) {
     const int n_b = min(a.offsets[bb + 1], a.max_rows) - min(a.offsets[bb], a.max_rows);
-    tiles += (n_b * G + 127) / 128;
+    tiles += (n_b * G + QT - 1) / QT;
   }
   AttnPlan p;
   p.units = tiles * a.Hkv;
@@ -206,17 +206,19 @@ __device__ __forceinline__ void attn_pv_block(const u16* sV, int kb0, const floa
   }
 }
 
-// 128 query vectors per workgroup (wave w owns vectors 32w..32w+31) that
-// share every 64-key tile of the split.
-template <int HD>
+// QT = 128*WQ query vectors per workgroup of 4*WQ waves (wave w owns vectors
+// 32w..32w+31) share every 64-key tile of the split: each tile is read from
+// L2 once per QT vectors, so WQ = 2 halves the K/V bytes a CU pulls per flop.
+template <int HD, int WQ>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& plan, u16* smem) {
-  constexpr int QT = 128;        // query vectors per workgroup
+  constexpr int QT = 128 * WQ;   // query vectors per workgroup
+  constexpr int NT = 256 * WQ;   // threads per workgroup
   constexpr int KT = kAttnKT;    // keys per tile (two 32-key MFMA blocks)
   constexpr int PITCH = AttnLds<HD>::KPITCH, VPITCH = AttnLds<HD>::VPITCH;  // u16 per LDS row
   constexpr int NS = HD / 16;    // k-chunks of Q.K^T
   constexpr int NDB = HD / 32;   // 32-row blocks of O^T
   constexpr int CPR = HD / 8;    // 16-byte chunks per K/V row
-  constexpr int CPT = 2 * KT * CPR / 256;
+  constexpr int CPT = 2 * KT * CPR / NT;
   u16* sK = smem;
   u16* sV = smem + KT * PITCH;  // V rows at VPITCH
 
@@ -249,8 +251,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
   const uint32_t nbytes = (uint32_t)(a.S - 1) * rowbytes + HD * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const u16*>(a.k) + base_el, nbytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const u16*>(a.v) + base_el, nbytes);
-  constexpr int RPJ = 256 / CPR;       // key rows between a thread's chunks
-  constexpr int JT = KT * CPR / 256;   // chunks per tensor per thread
+  constexpr int RPJ = NT / CPR;        // key rows between a thread's chunks
+  constexpr int JT = KT * CPR / NT;    // chunks per tensor per thread
   static_assert(2 * JT == CPT, "K and V chunks");
   const uint32_t voff = (uint32_t)(tid / CPR) * rowbytes + (tid % CPR) * 16;
   const float c = a.scale * kLog2e;
@@ -275,12 +277,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
   // One K/V tile's scores, online softmax and P.V.  `masked` (a
   // std::integral_constant) compiles the key mask in for the last, partial tile.
   auto tile_math = [&](int nvalid, auto masked) {
-    f32x16 sacc[2];
+    // the two 32-key blocks' MFMA chains alternate, so each MFMA issues two
+    // slots after the one it depends on (a lone chain waits out its latency)
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int s = 0; s < NS; ++s) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
+      for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kf = as_bf16x8(
             *reinterpret_cast<const u32x4*>(sK + (32 * kb + lr) * PITCH + 16 * s + 8 * lg));
         sacc[kb] = mfma32x32x16(kf, qf[s], sacc[kb]);
@@ -295,11 +298,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
           if (key >= nvalid) sacc[kb][i] = -INFINITY;
         }
     }
-    float mt = sacc[0][0];
+    // tile max: four independent partial maxima (short dependency chains)
+    float mq[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < 4; ++j) mq[j] = fmaxf(sacc[j >> 1][8 * (j & 1)], sacc[j >> 1][8 * (j & 1) + 1]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 2; i < 8; ++i) mq[j] = fmaxf(mq[j], sacc[j >> 1][8 * (j & 1) + i]);
+    float mt = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mt = pair_max(mt);
     // Lazy rescaling: the reference max m_run (log2 units) moves only when a
     // tile's max exceeds it by more than kRescaleSlack.  Until then every
@@ -320,15 +327,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
       m_run = m_new;
     }
     float p[2][16];
-    float ls = 0.f;
+    float lq[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums (short dependency chains)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_run));
-        ls += p[kb][i];
+        lq[i & 3] += p[kb][i];
       }
-    l_run += ls;
+    l_run += (lq[0] + lq[1]) + (lq[2] + lq[3]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) attn_pv_block<HD>(sV, 32 * kb, p[kb], acc, lane);
   };
@@ -369,11 +376,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
   if (lg == 0) attn_store_lse<HD>(a, plan, u.split, row, h, lse_nat);
 }
 
-template <int HD>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
+// WQ = 1: 128 query vectors, two workgroups per CU (short selections, whose
+// splits spread the K/V stream over the CUs); WQ = 2: 256 query vectors in
+// eight waves, one workgroup per CU (many query tiles, where every tile of
+// K/V is re-read by each query tile of its head from L2).
+template <int HD, int WQ>
+__global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) u16 smem[AttnLds<HD>::WIDE];
-  const AttnPlan plan = attn_plan(a);
-  attn_body<HD>(a, plan, smem);
+  const AttnPlan plan = attn_plan(a, 128 * WQ);
+  attn_body<HD, WQ>(a, plan, smem);
 }
 
 // Combine split-KV partials: O = sum_s exp(lse_s - L) O_s with L = logsumexp_s lse_s.
@@ -424,9 +435,9 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, const AttnPlan& pla
   if (lane == 0 && a.lse) a.lse[pr] = L;
 }
 
-template <int HD>
+template <int HD, int QT>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  const AttnPlan plan = attn_plan(a);
+  const AttnPlan plan = attn_plan(a, QT);
   if (plan.nsplit <= 1) return;  // the attention kernel already wrote the outputs
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int pairs = plan.n_rows * a.Hq;
@@ -529,22 +540,45 @@ hipError_t launch_attn(int dtype, const AttnArgs& a0, void* workspace, hipStream
   const bool may_split = a.S >= 2 * kMinSplitKeys;
   a.part_o = may_split ? static_cast<float*>(workspace) : nullptr;
   a.part_lse = may_split ? a.part_o + (size_t)kPartRows * a.hd : nullptr;
+  // A bound of fewer than kSplitTarget 128-vector tiles means the device
+  // always splits the keys (short selections): 128-vector workgroups.
+  // Otherwise 256-vector workgroups, which halve the K/V re-reads.
+  auto max_units = [&](int QT) {
+    return (ceil_div((long long)a.max_rows * G, QT) + a.B - 1) * (long long)a.Hkv;
+  };
+  const bool wide = !(may_split && max_units(128) < kSplitTarget);
+  const int QT = wide ? 256 : 128;
   // enough workgroups for every tile and for the split factor the device may
   // choose (units < kSplitTarget splits into fewer than 2 * kSplitTarget)
-  const int grid = (ceil_div((long long)a.max_rows * G, 128) + a.B - 1) * a.Hkv + 2 * kSplitTarget;
-  if (a.hd == 64)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3(grid), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3(grid), dim3(256), 0, st, a);
+  const int grid = (int)max_units(QT) + 2 * kSplitTarget;
+  const int threads = wide ? 512 : 256;
+  if (a.hd == 64) {
+    if (wide)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 2>), dim3(grid), dim3(threads), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 1>), dim3(grid), dim3(threads), 0, st, a);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 2>), dim3(grid), dim3(threads), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 1>), dim3(grid), dim3(threads), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !may_split) return e;
   // the merge runs only when the device chose to split; otherwise it exits at once
   const long long quads = ((long long)a.max_rows * a.Hq + 3) / 4;
   const int mgrid = (int)(quads < kMergeGrid ? quads : kMergeGrid);
-  if (a.hd == 64)
-    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(mgrid), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(mgrid), dim3(256), 0, st, a);
+  if (a.hd == 64) {
+    if (wide)
+      hipLaunchKernelGGL((attn_merge_kernel<64, 256>), dim3(mgrid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_merge_kernel<64, 128>), dim3(mgrid), dim3(256), 0, st, a);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((attn_merge_kernel<128, 256>), dim3(mgrid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_merge_kernel<128, 128>), dim3(mgrid), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
