@@ -142,12 +142,12 @@ struct GemmSplit {
   int units;
   int ks;
 };
-__host__ __device__ inline GemmSplit gemm_split(int units, int grid, int nk, int pf, int SB, int ST) {
+__host__ __device__ inline GemmSplit gemm_split(int units, int nk, int pf, int SB, int ST) {
   GemmSplit s{units, 1};
   if (units <= 0 || units >= SB) return s;
   while (true) {
     const int k2 = s.ks * 2;
-    if (units * k2 > kSplitCap || units * k2 > grid || units * s.ks >= ST) break;
+    if (units * k2 > kSplitCap || units * s.ks >= ST) break;
     if (k2 > 8 || nk % k2 != 0 || (nk / k2) % pf != 0 || nk / k2 < 2 * pf) break;
     s.ks = k2;
   }
@@ -182,6 +182,10 @@ __device__ __forceinline__ void gemm_rows(const GemmArgs& g, int n_rows, int m0,
 // WK = 2: eight waves; waves 4..7 repeat the layout of waves 0..3 on the
 // other half of every k-step's 16-wide sub-steps, two waves per SIMD hide each
 // other's LDS and barrier latency, and the halves are added through LDS.
+template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK>
+__device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u16* lds, uint32_t* s_xoff,
+                                               int* s_drow, const GemmSplit sp, int unit, int ksi);
+
 template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK = 1>
 __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u16* lds,
                                                uint32_t* s_xoff, int* s_drow) {
@@ -204,9 +208,32 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
   const int m_tiles = (n_rows + TT - 1) / TT;
   const int n_tiles = g.N / TP;
   const int nk_all = g.K / BK;
-  const GemmSplit sp = gemm_split(m_tiles * n_tiles, (int)gridDim.x, nk_all, PF, SB, ST);
-  if ((int)blockIdx.x >= sp.units * sp.ks) return;
-  const int unit = (int)blockIdx.x % sp.units, ksi = (int)blockIdx.x / sp.units;
+  const GemmSplit sp = gemm_split(m_tiles * n_tiles, nk_all, PF, SB, ST);
+  const int total = sp.units * sp.ks;
+  // Work items (tile, k-split) go to workgroups round-robin: item w runs on
+  // workgroup w % gridDim.x, so a grid of one workgroup per CU keeps every
+  // workgroup on the same k-step of its current tile and the tiles running
+  // together on an XCD share their weight and row slices in its L2.
+  for (int work = (int)blockIdx.x; work < total; work += (WK == 1 ? (int)gridDim.x : total)) {
+    gemm_tile_work<TP, TT, WP, WT, BK, PF, EPI, AMODE, SB, ST, WK>(g, n_rows, lds, s_xoff, s_drow, sp,
+                                                                   work % sp.units, work / sp.units);
+    if constexpr (WK == 1) __syncthreads();  // the next item rewrites the row table and tiles
+  }
+}
+
+template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK>
+__device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u16* lds, uint32_t* s_xoff,
+                                               int* s_drow, const GemmSplit sp, int unit, int ksi) {
+  constexpr int NT = 256 * WK;   // threads
+  constexpr int PITCH = BK + 8;  // u16 elements per LDS row (16 bytes of padding)
+  constexpr int ROWS = TP + TT;
+  constexpr int CPR = BK / 8;    // 16-byte chunks per row and k-step
+  constexpr int RPJ = NT / CPR;  // rows covered by one chunk index of the workgroup
+  constexpr int CHUNKS = ROWS * CPR;
+  constexpr int CPT = CHUNKS / NT;
+  constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
+  const int m_tiles = (n_rows + TT - 1) / TT;
+  const int nk_all = g.K / BK;
   const int nt = unit / m_tiles, mt = unit % m_tiles;
   const int m0 = mt * TT, n0 = nt * TP;
   const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, wk = tid >> 8;
@@ -233,11 +260,14 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
     xoff[j] = o + (o & 0x80000000u ? 0u : (uint32_t)(kc * 16));
   }
   u16* const ldsw = lds + r0 * PITCH + kc * 8;
-  // Every workgroup walks its k-steps from its own starting point (wrapping
-  // around): workgroups are dealt round-robin to the 8 XCDs, so the ~nk
-  // workgroups sharing an XCD's L2 read different k-slices of the gathered
-  // rows at any moment instead of all hitting the same lines.
-  const int krot = ((int)blockIdx.x >> 3) % nk;
+  // The 64-feature weight-streaming tiling (short selections) walks each
+  // workgroup's k-steps from its own starting point (wrapping around):
+  // workgroups are dealt round-robin to the 8 XCDs, so the workgroups sharing
+  // an XCD's L2 read different k-slices of the gathered rows (which all of
+  // them re-read, and which fit in L2) instead of all hitting the same lines.
+  // The larger tilings keep one order, so that tiles running together share
+  // each weight and row slice while it is in L2.
+  const int krot = TP == 64 ? ((int)blockIdx.x >> 3) % nk : 0;
   auto gload = [&](int j, int kstep) -> u32x4 {
     int kp = kstep + krot;
     kp -= kp >= nk ? nk : 0;
@@ -388,7 +418,7 @@ __global__ __launch_bounds__(256) void gemm_dual_kernel(GemmArgs g) {
 // split order and storing them; the LM-head epilogue needs whole rows, so one
 // workgroup reduces one tile.
 template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
-__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g, int main_grid) {
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g) {
   constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
   constexpr int NQ = FP * FT * 4;
   __shared__ int s_drow[TT];
@@ -397,7 +427,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g, int
   if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
   const int m_tiles = (n_rows + TT - 1) / TT;
   const int n_tiles = g.N / TP;
-  const GemmSplit sp = gemm_split(m_tiles * n_tiles, main_grid, g.K / BK, PF, SB, ST);
+  const GemmSplit sp = gemm_split(m_tiles * n_tiles, g.K / BK, PF, SB, ST);
   if (sp.ks <= 1) return;
   const int RS = EPI == EPI_LMHEAD ? 1 : min(NQ, (kReduceTarget + sp.units - 1) / sp.units);
   if ((int)blockIdx.x >= sp.units * RS) return;
@@ -527,24 +557,49 @@ size_t gemm_workspace_bytes(int epi, int max_rows, int N, int K) {
 }
 
 template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
-static void launch_reduce(const GemmArgs& g, int main_grid, hipStream_t st) {
+static void launch_reduce(const GemmArgs& g, hipStream_t st) {
   hipLaunchKernelGGL((gemm_splitk_reduce_kernel<TP, TT, WP, WT, BK, PF, EPI, AMODE, GATE, SB, ST>),
-                     dim3(SB + kReduceTarget), dim3(256), 0, st, g, main_grid);
+                     dim3(SB + kReduceTarget), dim3(256), 0, st, g);
+}
+
+// CUs of the current device (queried once per device; 256 on MI355X)
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Grid of a tiling whose work items loop over workgroups: as many workgroups
+// as are resident at once (one per CU for the 256-wide tiles, two otherwise),
+// never more than there are items.
+static int persistent_grid(int items, int TP, int TT) {
+  const int resident = device_cus() * (TP * TT >= 256 * 256 ? 1 : 2);
+  return items < resident ? items : resident;
 }
 
 template <int TP, int TT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST, int WK = 1>
 static void launch_bf16(const GemmArgs& g, hipStream_t st) {
   // one workgroup per possible output tile, and at least enough for the
   // split the device may choose when the real selection turns out short
+  // every output tile (and every split the device may choose when the real
+  // selection turns out short) is a work item; the two-k-half tiling runs one
+  // item per workgroup, the others loop over a resident grid
   const int m_tiles_max = (g.max_rows + TT - 1) / TT;
-  int grid = (g.N / TP) * m_tiles_max;
+  int items = (g.N / TP) * m_tiles_max;
   if (SB > 0) {
     const int cap = ST < kSplitCap ? 2 * ST : kSplitCap;
-    if (grid < cap) grid = cap;
+    if (items < cap) items = cap;
   }
+  const int grid = WK == 1 ? persistent_grid(items, TP, TT) : items;
   hipLaunchKernelGGL((gemm_bf16_kernel<TP, TT, 2, 2, BK, PF, EPI, AMODE, GATE, SB, ST, WK>), dim3(grid),
                      dim3(256 * WK), 0, st, g);
-  if (SB > 0) launch_reduce<TP, TT, 2, 2, BK, PF, EPI, AMODE, GATE, SB, ST>(g, grid, st);
+  if (SB > 0) launch_reduce<TP, TT, 2, 2, BK, PF, EPI, AMODE, GATE, SB, ST>(g, st);
 }
 
 // the weight-streaming tiling alone (GATE 0 or 1).  Measured at n = 102:
@@ -564,13 +619,13 @@ static void launch_skinny(const GemmArgs& g, hipStream_t st) {
 // split-K pass of the large body when it may split
 template <int BK1, int PF1, int TP2, int TT2, int PF2, int SB2, int ST2, int EPI, int AMODE>
 static void launch_dual(const GemmArgs& g, hipStream_t st) {
-  int grid2 = (g.N / TP2) * ((g.max_rows + TT2 - 1) / TT2);
-  if (SB2 > 0 && grid2 < kSplitCap) grid2 = kSplitCap;
-  const int grid1 = g.N / 64;
+  int items2 = (g.N / TP2) * ((g.max_rows + TT2 - 1) / TT2);
+  if (SB2 > 0 && items2 < kSplitCap) items2 = kSplitCap;
+  const int grid1 = persistent_grid(g.N / 64, 64, 128), grid2 = persistent_grid(items2, TP2, TT2);
   const int grid = grid1 > grid2 ? grid1 : grid2;
   hipLaunchKernelGGL((gemm_dual_kernel<64, 128, BK1, PF1, 0, 0, TP2, TT2, 64, PF2, SB2, ST2, EPI, AMODE>),
                      dim3(grid), dim3(256), 0, st, g);
-  if (SB2 > 0) launch_reduce<TP2, TT2, 2, 2, 64, PF2, EPI, AMODE, 2, SB2, ST2>(g, grid, st);
+  if (SB2 > 0) launch_reduce<TP2, TT2, 2, 2, 64, PF2, EPI, AMODE, 2, SB2, ST2>(g, st);
 }
 
 template <int EPI, int AMODE>
