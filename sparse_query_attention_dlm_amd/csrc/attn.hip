@@ -475,19 +475,36 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   for (int k0 = 0; k0 < a.S; k0 += 64) {
     const int key = k0 + lane;
+    // HD = 64: this lane's V column over the whole tile is loaded together with
+    // its K row, so the tile costs one memory round trip (rows past the
+    // sequence re-read its last row, with p = 0)
+    float vt[HD == 64 ? 64 : 1];
+    if constexpr (HD == 64) {
+#pragma unroll
+      for (int j = 0; j < 64; ++j) vt[j] = vb[(size_t)min(k0 + j, a.S - 1) * kstride + lane];
+    }
     float s = -INFINITY;
     if (key < a.S) {
+      // the key row's float4 loads go out in groups of 8 before use; four
+      // partial dot products
       const float4* kr = reinterpret_cast<const float4*>(kb + (size_t)key * kstride);
-      float dot = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < HD / 4; ++d) {
-        const float4 kv = kr[d];
-        dot = fmaf(sq[wave][4 * d], kv.x, dot);
-        dot = fmaf(sq[wave][4 * d + 1], kv.y, dot);
-        dot = fmaf(sq[wave][4 * d + 2], kv.z, dot);
-        dot = fmaf(sq[wave][4 * d + 3], kv.w, dot);
+      float dp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int d0 = 0; d0 < HD / 4; d0 += 8) {
+        float4 kv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kv[u] = kr[d0 + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int d = d0 + u;
+          float& dot = dp[u & 3];
+          dot = fmaf(sq[wave][4 * d], kv[u].x, dot);
+          dot = fmaf(sq[wave][4 * d + 1], kv[u].y, dot);
+          dot = fmaf(sq[wave][4 * d + 2], kv[u].z, dot);
+          dot = fmaf(sq[wave][4 * d + 3], kv[u].w, dot);
+        }
       }
-      s = dot * a.scale;
+      s = ((dp[0] + dp[1]) + (dp[2] + dp[3])) * a.scale;
     }
     const float mn = fmaxf(m, wave_max(s));
     const float alpha = __expf(m - mn);
@@ -495,12 +512,27 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
     l = l * alpha + wave_sum(p);
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] *= alpha;
+    // P.V over the tile's keys, 16 V rows loaded before they are used (rows
+    // past the sequence re-read its last row, with p = 0)
     const int nk = min(64, a.S - k0);
-    for (int j = 0; j < nk; ++j) {
-      const float pj = __shfl(p, j, 64);
-      const float* vr = vb + (size_t)(k0 + j) * kstride;
+    if constexpr (HD == 64) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = fmaf(pj, vr[lane + 64 * e], o[e]);
+      for (int j = 0; j < 64; ++j) o[0] = fmaf(__shfl(p, j, 64), vt[j], o[0]);
+    } else
+    for (int j0 = 0; j0 < nk; j0 += 16) {
+      float vv[16][E];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float* vr = vb + (size_t)min(k0 + j0 + u, a.S - 1) * kstride;
+#pragma unroll
+        for (int e = 0; e < E; ++e) vv[u][e] = vr[lane + 64 * e];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float pj = __shfl(p, j0 + u, 64);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = fmaf(pj, vv[u][e], o[e]);
+      }
     }
     m = mn;
   }
