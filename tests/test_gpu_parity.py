@@ -269,10 +269,12 @@ def run_attention_plan(dlm, B, S, Hq, Hkv, hd, rows_per_b, sample=None, seed=21)
     assert eo <= TOL["bf16"] and el <= TOL["bf16"]
 
 
-def test_attention_many_tiles_gqa_ragged(dlm):
-    """>= 512 tiles of 128 query vectors: no key split (GQA 4:1, ragged last
-    query tile and last 64-key tile); sampled rows against the oracle."""
-    run_attention_plan(dlm, B=2, S=1500, Hq=32, Hkv=8, hd=128, rows_per_b=[1500, 1436], sample=48)
+@pytest.mark.parametrize("hd", [64, 128])
+def test_attention_many_tiles_gqa_ragged(dlm, hd):
+    """>= 512 tiles of 128 query vectors: no key split, 256-vector workgroups
+    (GQA 4:1, ragged last query tile and last 64-key tile); sampled rows
+    against the oracle."""
+    run_attention_plan(dlm, B=2, S=1500, Hq=32, Hkv=8, hd=hd, rows_per_b=[1500, 1436], sample=48)
 
 
 @pytest.mark.parametrize("hd", [64, 128])
@@ -343,6 +345,52 @@ def run_colsum(dlm, zero_q=False, **override):
     torch.cuda.synchronize()
     assert torch.equal(c2, colsum) and torch.equal(ti2, ti)
     return ti_g, c_g
+
+
+def test_colsum_workload_full_size(dlm):
+    """The attention + column-sum workload at its full size, in the launch
+    configuration the benchmark times (B = 4, S = 4096, 32 heads of 128, the
+    3072 masked positions of every sequence as queries): O and LSE of 32 rows
+    sampled over all sequences, and every column sum of sequence 0, against the
+    oracle; sequence 0's top-64 by the selection rule; for every sequence the
+    total sum_j c = Hq * n_q."""
+    inp = W.colsum_inputs(W.COLSUM_TOP64)
+    s = inp.shape
+    B, S, nq = s.B, s.S, s.S - s.prompt
+    scale = 1.0 / math.sqrt(s.hd)
+    say(f"[colsum full size] B={B} S={S} prompt={s.prompt} Hq={s.Hq} Hkv={s.Hkv} k={s.k}")
+    sc = inp.masked_scores()
+    ridx, _, roff = O.compact(sc, 0, S, 0.5)
+    n = int(roff[-1])
+    q_np = inp.q.reshape(n, s.Hq, s.hd)
+    q, kc, vc = dev(q_np, "bf16"), dev(inp.k_cache, "bf16"), dev(inp.v_cache, "bf16")
+    offsets = i32(roff)
+    o = torch.zeros_like(q)
+    lse = torch.zeros(n, s.Hq, dtype=torch.float32, device="cuda")
+    wsa = workspace(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, n, B, S, s.Hq, s.Hkv, s.hd))
+    dlm.dlm_partial_attn(q, i32(ridx), offsets, n, kc, vc, scale, o, lse, workspace=wsa)
+    colsum = torch.zeros(B, S, dtype=torch.float32, device="cuda")
+    ti = torch.zeros(B, s.k, dtype=torch.int32, device="cuda")
+    wsc = workspace(dlm.dlm_attn_colsum_workspace_size(B, S, s.Hkv))
+    dlm.dlm_attn_colsum(q, offsets, n, kc, lse, scale, colsum, key_lo=s.prompt, key_hi=S, k=s.k,
+                        topk_idx=ti, workspace=wsc)
+    torch.cuda.synchronize()
+    # sampled rows over all sequences
+    pick = np.unique(np.linspace(0, n - 1, 32).astype(np.int64))
+    counts = np.array([np.sum((pick >= roff[b]) & (pick < roff[b + 1])) for b in range(B)])
+    poff = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    o_o, lse_o = O.partial_attention(q_np[pick], ridx[pick], poff, inp.k_cache, inp.v_cache, s.Hq, s.Hkv, scale)
+    eo, el = maxabs(host(o)[pick], o_o), maxabs(host(lse)[pick], lse_o)
+    # every column of sequence 0, with the oracle's own LSE of all its queries
+    off0 = np.array([0, nq], dtype=np.int64)
+    _, lse0 = O.partial_attention(q_np[:nq], ridx[:nq], off0, inp.k_cache[:1], inp.v_cache[:1], s.Hq, s.Hkv, scale)
+    c0 = O.column_sums(q_np[:nq], off0, inp.k_cache[:1], lse0, s.Hq, s.Hkv, scale)
+    c_g = host(colsum)
+    ec = maxabs(c_g[:1], c0)
+    say(f"  rows {len(pick)}: o={eo:.2e} lse={el:.2e}; sequence 0 column sums {ec:.2e}")
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"] and ec <= TOL["bf16"]
+    check_topk(ti.cpu().numpy()[:1], c0, s.prompt, S, s.k)
+    assert np.allclose(c_g.sum(axis=1), s.Hq * nq, rtol=1e-4)
 
 
 def test_colsum_topk_reduced(dlm):
