@@ -186,6 +186,57 @@ def test_gqa_lock_loop_reduced(dlm):
             assert v_ <= TOL["bf16"], f"step {t} {k_}: {v_}"
 
 
+def test_gqa_lock_loop_last_step_full_size(dlm):
+    """The last step (t = 63, 103 unlocked rows per sequence) of the 64-step GQA
+    lock loop at its full size (B = 8, S = 2048, D = 4096, 32 query / 8 KV heads
+    of 128) with the loose row bound the loop runs with (the 256-wide GEMM
+    tiling, 256-vector attention workgroups and a split-KV merge).  The caches
+    hold seeded earlier rows; Q, every scattered K/V row and O/LSE of 48 sampled
+    rows against the oracle; all other cache rows byte-identical."""
+    inp = W.lock_loop_inputs(W.GQA_LOCK_LOOP)
+    s = inp.shape
+    B, S, t = s.B, s.S, s.steps - 1
+    scale = 1.0 / math.sqrt(s.hd)
+    say(f"[lock loop full size] B={B} S={S} D={s.D} Hq={s.Hq} Hkv={s.Hkv} t={t}")
+    rng = np.random.default_rng(77)
+    kc0 = W.round_bf16(rng.standard_normal((B, S, s.Hkv, s.hd), dtype=np.float32))
+    vc0 = W.round_bf16(rng.standard_normal((B, S, s.Hkv, s.hd), dtype=np.float32))
+    sc, x = inp.unlocked_scores(t), inp.hidden(t)
+    ridx, _, roff = O.compact(sc, 0, S, 0.5)
+    n = int(roff[-1])
+    q_o, kc_o, vc_o = O.qkv_project_scatter(x, ridx, roff, inp.w_qkv, s.Hq, s.Hkv, s.hd, kc0, vc0)
+    pick = np.unique(np.linspace(0, n - 1, 48).astype(np.int64))
+    counts = np.array([np.sum((pick >= roff[b]) & (pick < roff[b + 1])) for b in range(B)])
+    poff = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    o_o, lse_o = O.partial_attention(q_o[pick], ridx[pick], poff, kc_o, vc_o, s.Hq, s.Hkv, scale)
+
+    max_rows = B * S
+    kc, vc = dev(kc0, "bf16"), dev(vc0, "bf16")
+    kc_before, vc_before = kc.clone(), vc.clone()
+    q = torch.zeros(max_rows, s.Hq, s.hd, dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros_like(q)
+    lse = torch.zeros(max_rows, s.Hq, dtype=torch.float32, device="cuda")
+    idx = torch.zeros(B * S, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    wsa = workspace(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, max_rows, B, S, s.Hq, s.Hkv, s.hd))
+    wsq = workspace(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, max_rows, s.D, s.Hq, s.Hkv, s.hd))
+    dlm.dlm_saliency_select(dlm.DLM_SCORE_GIVEN, dev(sc, "f32"), None, lo=0, hi=S, threshold=0.5,
+                            idx=idx, counts=cnt, offsets=offsets)
+    dlm.dlm_gather_qkv_scatter_kv(dev(x, "bf16"), idx, offsets, max_rows, dev(inp.w_qkv, "bf16"), s.Hq,
+                                  s.Hkv, s.hd, q, kc, vc, workspace=wsq)
+    dlm.dlm_partial_attn(q, idx, offsets, max_rows, kc, vc, scale, o, lse, workspace=wsa)
+    torch.cuda.synchronize()
+    assert np.array_equal(offsets.cpu().numpy(), roff) and np.array_equal(idx.cpu().numpy()[:n], ridx)
+    sel = torch.from_numpy(rows_mask(B, S, ridx, roff)).cuda()
+    assert torch.equal(kc[~sel], kc_before[~sel]) and torch.equal(vc[~sel], vc_before[~sel])
+    errs = dict(q=maxabs(host(q)[:n], q_o), k=maxabs(host(kc), kc_o), v=maxabs(host(vc), vc_o),
+                o=maxabs(host(o)[pick], o_o), lse=maxabs(host(lse)[pick], lse_o))
+    say(f"  n={n} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k_, v_ in errs.items():
+        assert v_ <= TOL["bf16"], f"{k_}: {v_}"
+
+
 def test_loose_row_bound_picks_every_tiling(dlm):
     """The host passes max_rows = B*S > 1024 while the device count is 50, 600
     or 2000: the one GEMM launch must take the weight-streaming tiling, then
