@@ -532,6 +532,49 @@ def test_confidence_and_stable_prefix_loop(dlm):
     assert committed.cpu().numpy().max() > 0
 
 
+def test_confidence_full_size_first_step(dlm):
+    """The first step of the confidence + stable-prefix workload at full size
+    (B = 16, S = 1024, D = 4096, V = 32768, 230 evaluated rows per sequence),
+    in the launch configuration the benchmark times: max-prob and argmax of 48
+    sampled evaluated rows against the oracle (argmax where the top-2 logit gap
+    is outside the band); the selected set is exactly the generated positions
+    whose returned max-prob is below the threshold."""
+    sh = W.LSP_COMMIT
+    inp = W.lsp_inputs(sh)
+    B, S = sh.B, sh.S
+    say(f"[confidence full size] B={B} S={S} D={sh.D} V={sh.V}")
+    rows = inp.active_rows(0)
+    h = inp.hidden(0)
+    ev_idx, ev_off = W.pack_rows(rows)
+    scores = torch.zeros(B, S, dtype=torch.float32, device="cuda")
+    argmax = torch.full((B, S), -1, dtype=torch.int32, device="cuda")
+    idx = torch.zeros(B * S, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(B, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    ws = workspace(dlm.dlm_select_workspace_size(dlm.DLM_SCORE_CONFIDENCE, B, S, sh.V, len(ev_idx)))
+    dlm.dlm_saliency_select(dlm.DLM_SCORE_CONFIDENCE, dev(h, "bf16"), dev(inp.w_lm, "bf16"), lo=sh.prompt,
+                            hi=S, threshold=sh.conf, idx=idx, counts=counts, offsets=offsets, scores=scores,
+                            argmax=argmax, eval_idx=i32(ev_idx), eval_offsets=i32(ev_off),
+                            max_eval=len(ev_idx), workspace=ws)
+    torch.cuda.synchronize()
+    sc_g, am_g = scores.cpu().numpy(), argmax.cpu().numpy()
+    worst, checked = 0.0, 0
+    for b in range(B):
+        pick = np.asarray(rows[b])[[0, len(rows[b]) // 2, len(rows[b]) - 1]]
+        mp, a, gap = O.confidence(h[b, pick], inp.w_lm)
+        clear = gap > BAND
+        assert np.array_equal(am_g[b, pick][clear], a[clear]), f"b {b}: argmax"
+        worst = max(worst, maxabs(sc_g[b, pick], mp))
+        checked += len(pick)
+    say(f"  {checked} sampled rows: max-prob err {worst:.2e}")
+    assert worst <= TOL["bf16"]
+    # compaction of the returned scores over the generated region
+    offs, ix = offsets.cpu().numpy(), idx.cpu().numpy()
+    for b in range(B):
+        want = sh.prompt + np.nonzero(sc_g[b, sh.prompt:] < sh.conf)[0]
+        assert np.array_equal(ix[offs[b]:offs[b + 1]], want), f"b {b}: selected set"
+
+
 def test_stable_prefix_bit_exact_on_given_inputs(dlm):
     """Prefix step alone, fed identical float32 max-probs: the frontiers and the
     ring must match the oracle bit for bit (decisions in the same precision)."""
