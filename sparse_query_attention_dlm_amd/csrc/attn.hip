@@ -6,12 +6,17 @@
 // the cost is O(M N d) for M active rows.  No mask: the model is bidirectional.
 //
 // bf16 kernel (gfx950 matrix cores), flash-style online softmax:
-//   * A workgroup owns 128 query vectors (row, head) that share one KV head of
-//     one sequence (GQA packs the G query heads of a KV head together); each
-//     wave owns 32 of them.
-//   * Per 32-key tile, K and V are staged in LDS and every wave computes the
-//     transposed score tile S^T = K . Q^T (32 keys x 32 queries) with eight
-//     32x32x16 MFMAs; Q^T stays in registers for the whole key loop.
+//   * A workgroup owns 128 or 256 query vectors (row, head) that share one KV
+//     head of one sequence (GQA packs the G query heads of a KV head
+//     together); each wave owns 32 of them.  256-vector workgroups (eight
+//     waves) serve selections with many query tiles: every K/V tile is read
+//     from L2 once per 256 vectors instead of once per 128.
+//   * Per 64-key tile, K and V come in through buffer loads (one tile ahead,
+//     in registers) and are staged in LDS; every wave computes the transposed
+//     score tiles S^T = K . Q^T (32 keys x 32 queries each) with 32x32x16
+//     MFMAs; Q^T stays in registers for the whole key loop.  The key mask is
+//     compiled only into the copy of the tile math that runs the split's
+//     partial last tile.
 //   * In that layout a lane holds 16 keys of one query, so the running max and
 //     sum are in-lane reductions plus one v_permlane32_swap with the lane that
 //     holds the other 16 keys of the same query.
@@ -20,7 +25,8 @@
 //     blocks of V on the way out of LDS.
 //   * Few queries (short selections): the key range is split over workgroups
 //     and a merge pass combines the partial outputs by their LSE.
-// fp32 kernel (small fp32 layers): one wave per (row, head), float32 FMA.
+// fp32 kernel (small fp32 layers): one wave per (row, head), float32 FMA,
+// loads issued in batches ahead of use (the layer is latency-bound).
 #include <type_traits>
 
 #include "common.hpp"

@@ -21,7 +21,10 @@
 // double-buffered LDS with 16-byte row padding, a branch-free register ring
 // of PF k-steps, operands fetched with buffer loads (one VGPR offset per
 // chunk; padding token rows point past the end of the buffer and read zeros
-// without touching memory).
+// without touching memory).  The large tilings run on a resident grid (one
+// workgroup per slot that fits on the GPU at once) that loops over the output
+// tiles, so the tiles in flight on an XCD advance together and share their
+// weight and row slices in its L2.
 #include "common.hpp"
 #include "launch.hpp"
 
