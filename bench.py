@@ -20,6 +20,7 @@ timed on a bounded sample of the same workload as a reported baseline.
 Prints one JSON line.
 """
 import argparse
+import re
 import hashlib
 import json
 import math
@@ -61,10 +62,15 @@ def parse():
 
 
 def source_digest(*names):
+    """Digest of the kernel sources with comments and whitespace removed, so
+    that a comment edit does not orphan the committed counter summary."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "sparse_query_attention_dlm_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sparse_query_attention_dlm_amd", "csrc", n), encoding="utf-8") as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update("".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
