@@ -192,6 +192,9 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
  * If k > 0: topk_idx [B,k] i32 / topk_val [B,k] f32 receive the k keys of
  * [key_lo,key_hi) with the largest sums, ordered by (-colsum, j): equal sums
  * go to the lower position.  k <= key_hi-key_lo <= 8192.
+ * Workspace: dlm_attn_colsum_workspace_size(B, S, Hkv) bytes, the per-key
+ * float partial sums of up to 4 query ranges of every KV head (the split
+ * depends on the shapes and the device's CU count; reruns are bit-identical).
  * ------------------------------------------------------------------------ */
 size_t dlm_attn_colsum_workspace_size(int B, int S, int Hkv);
 int dlm_attn_colsum(int dtype, const void* q_sel, const int32_t* offsets, int max_rows,

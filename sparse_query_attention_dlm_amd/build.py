@@ -22,6 +22,11 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
+# Per-source additions.  The column-sum pass reads every MFMA result back for
+# its exponentials; left to itself the compiler puts those results in AGPRs
+# and copies them out (32 v_accvgpr_read plus hazard NOPs per tile), so that
+# file asks for MFMA results in VGPRs.
+EXTRA_FLAGS = {"colsum.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -45,7 +50,8 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES]
-    cmds = [[hipcc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    cmds = [[hipcc, *FLAGS, *EXTRA_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for cmd, msg in zip(cmds, ex.map(_run, cmds)):
             if verbose and msg:

@@ -4,123 +4,209 @@
 // tokens are decoded in descending order of the column sums of the attention
 // matrix (total attention a key receives), aggregated over all heads.
 //
-// Pass 1 (matrix cores): a workgroup owns 128 keys of one KV head of one
-// sequence (each wave 32 keys, its K rows held in registers as the MFMA
-// A-operand for the whole pass) and streams every selected query vector of
-// that KV head through LDS in tiles of 32.  S^T = K . Q^T puts one query per
-// lane column, so p = exp2(s*scale*log2e - lse*log2e) is accumulated into the
-// lane's own 16 key sums with no cross-lane traffic inside the loop; one
-// 32-lane reduction at the end.  Results go to a [Hkv][B][S] partial array.
-// Pass 2: per sequence, sums the Hkv partials in a fixed order (no float
-// atomics: reruns are bit-identical) and selects the top-k keys of
-// [key_lo,key_hi) with a bitonic sort of (colsum bits, ~key) 64-bit keys in
-// LDS: descending sums, equal sums ordered by the lower position.
+// Pass 1 (matrix cores): a workgroup owns 256 keys of one KV head of one
+// sequence, 64 per wave, held in registers as two 32-row MFMA A-operands for
+// the whole pass, and streams the selected query vectors of that KV head
+// through a double-buffered LDS tile of 32 vectors (one barrier per tile).
+// S^T = K . Q^T puts one query per lane column, so each fragment read from
+// LDS feeds two MFMAs and p = exp2(s*scale*log2e - lse*log2e) is accumulated
+// into the lane's own 32 key sums with no cross-lane traffic inside the
+// loop; one 32-lane reduction at the end.  When there are few such
+// workgroups, or their count leaves the last round of the chip half empty,
+// the query vectors are split into up to 4 ranges, one workgroup each.
+// Results go to a [split][Hkv][B][S] partial array.
+// Pass 2: sums the partials of every key in a fixed order (no float atomics:
+// reruns are bit-identical).
+// Pass 3 (k > 0): per sequence, the top-k keys of [key_lo,key_hi) by a
+// bitonic sort of (colsum bits, ~key) 64-bit keys in LDS: descending sums,
+// equal sums ordered by the lower position.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace dlm {
 
-template <int HD>
-__global__ __launch_bounds__(256, 2) void colsum_bf16_kernel(const u16* __restrict__ q,
-                                                             const int32_t* __restrict__ offsets,
-                                                             const u16* __restrict__ k,
-                                                             const float* __restrict__ lse, int B,
-                                                             int S, int Hq, int Hkv, int max_rows,
-                                                             float scale,
-                                                             float* __restrict__ partial) {
-  constexpr int QTL = 32, PITCH = HD + 8, NS = HD / 16, CPR = HD / 8;
-  __shared__ __attribute__((aligned(16))) u16 sQ[QTL * PITCH];
-  __shared__ float sL[QTL];
-  const int nkb = (S + 127) / 128;
-  const int g = blockIdx.x % Hkv;
-  const int kb = (blockIdx.x / Hkv) % nkb;
-  const int b = blockIdx.x / (Hkv * nkb);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
-  const int G = Hq / Hkv;
-  const int key_a = min(kb * 128 + wave * 32 + lr, S - 1);  // A-operand row (clamped for loads)
-  const float c = scale * kLog2e;
+constexpr int kColsumMaxSplit = 4;
 
-  bf16x8 kf[NS];
-  {
-    const u16* kp = k + (((size_t)b * S + key_a) * Hkv + g) * HD + lg * 8;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 16 * s));
-  }
-  const int row0 = min(offsets[b], max_rows);
-  const int nvec = (min(offsets[b + 1], max_rows) - row0) * G;
-  float acc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-
-  for (int v0 = 0; v0 < nvec; v0 += QTL) {
-    // stage 32 query vectors (2 x 16-byte chunks per thread for HD = 128)
-    u32x4 st[QTL * CPR / 256 > 0 ? QTL * CPR / 256 : 1];
-#pragma unroll
-    for (int j = 0; j < QTL * CPR / 256; ++j) {
-      const int cidx = tid + 256 * j, r = cidx / CPR, ch = cidx % CPR;
-      const int v = min(v0 + r, nvec - 1);
-      const int row = row0 + v / G, h = g * G + v % G;
-      st[j] = *reinterpret_cast<const u32x4*>(q + ((size_t)row * Hq + h) * HD + ch * 8);
-    }
-    float lv = 0.f;
-    if (tid < QTL) {
-      const int v = v0 + tid;
-      if (v < nvec) {
-        const int row = row0 + v / G, h = g * G + v % G;
-        lv = lse[(size_t)row * Hq + h] * kLog2e;
-      } else {
-        lv = INFINITY;  // padding query: contributes exp2(-inf) = 0
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < QTL * CPR / 256; ++j) {
-      const int cidx = tid + 256 * j, r = cidx / CPR, ch = cidx % CPR;
-      *reinterpret_cast<u32x4*>(sQ + r * PITCH + ch * 8) = st[j];
-    }
-    if (tid < QTL) sL[tid] = lv;
-    __syncthreads();
-    f32x16 sacc = f32x16{};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bf16x8 qf = as_bf16x8(*reinterpret_cast<const u32x4*>(sQ + lr * PITCH + 16 * s + 8 * lg));
-      sacc = mfma32x32x16(kf[s], qf, sacc);
-    }
-    const float l2 = sL[lr];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -l2));
-  }
-  // reduce each key's sum over the 32 query columns of its lane half
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) acc[i] += __shfl_xor(acc[i], o, 64);
-  }
-  if (lr == 0) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kb * 128 + wave * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
-      if (key < S) partial[((size_t)g * B + b) * S + key] = acc[i];
-    }
+// Query vector v of a sequence (v = local row * G + head within the group):
+// its row and head offset, with a shift and mask when G is a power of two.
+template <bool P2>
+__device__ __forceinline__ void split_vec(int v, int G, int gsh, int& r, int& h) {
+  if constexpr (P2) {
+    r = v >> gsh;
+    h = v & (G - 1);
+  } else {
+    r = v / G;
+    h = v - r * G;
   }
 }
 
-__global__ __launch_bounds__(1024) void colsum_reduce_topk_kernel(const float* __restrict__ partial,
-                                                                  int Hkv, int B, int S,
-                                                                  float* __restrict__ colsum,
-                                                                  int key_lo, int key_hi, int kk,
-                                                                  int p2, int32_t* topk_idx,
-                                                                  float* topk_val) {
+template <int HD, int WAVES, bool P2>
+__global__ __launch_bounds__(64 * WAVES, HD == 128 ? 3 : 4) void colsum_bf16_kernel(const u16* __restrict__ q,
+                                                                 const int32_t* __restrict__ offsets,
+                                                                 const u16* __restrict__ k,
+                                                                 const float* __restrict__ lse,
+                                                                 int B, int S, int Hq, int Hkv,
+                                                                 int gsh, int max_rows, int nsq,
+                                                                 float scale,
+                                                                 float* __restrict__ partial) {
+  constexpr int NT = 64 * WAVES, KEYS = 64 * WAVES;
+  constexpr int QTL = 32, PITCH = HD + 8, NS = HD / 16, CPR = HD / 8;
+  constexpr int CH = QTL * CPR, CPT = (CH + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) u16 sQ[2][QTL * PITCH];
+  __shared__ float sL[2][QTL];
+  const int nkb = (S + KEYS - 1) / KEYS;
+  // workgroups of one KV head are Hkv apart, so with Hkv a multiple of 8 they
+  // share an XCD (and its L2) and read each query tile from there
+  const int g = blockIdx.x % Hkv;
+  const int sp = (blockIdx.x / Hkv) % nsq;
+  const int kb = (blockIdx.x / (Hkv * nsq)) % nkb;
+  const int b = blockIdx.x / (Hkv * nsq * nkb);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  const int G = Hq / Hkv;
+  const int key0 = kb * KEYS + wave * 64;
+  const float c = scale * kLog2e;
+
+  // the wave's 64 keys as two 32-row MFMA A-operands, held for the whole pass
+  bf16x8 kf[2][NS];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int key_a = min(key0 + 32 * kk + lr, S - 1);
+    const u16* kp = k + (((size_t)b * S + key_a) * Hkv + g) * HD + lg * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[kk][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 16 * s));
+  }
+  const int row0 = min(offsets[b], max_rows);
+  const int nvec = (min(offsets[b + 1], max_rows) - row0) * G;
+  // this workgroup's query tiles: [v_lo, v_hi) in vectors
+  const int tchunk = ((nvec + QTL - 1) / QTL + nsq - 1) / nsq;
+  const int v_lo = min(nvec, sp * tchunk * QTL), v_hi = min(nvec, (sp + 1) * tchunk * QTL);
+  const u16* qb = q + ((size_t)row0 * Hq + g * G) * HD;
+  const float* lb = lse + (size_t)row0 * Hq + g * G;
+
+  // Tile of 32 query vectors starting at v0 into registers, and the LSE of
+  // the lane's query column (every half-wave holds the same 32 values and
+  // writes them, so the store needs no branch).  Rows past the end repeat the
+  // last vector; their LSE is +inf so they add exp2(-inf) = 0.
+  u32x4 st[CPT];
+  float lraw;
+  bool lvalid;
+  auto load_tile = [&](int v0) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int cidx = tid + NT * j;
+      if (CH % NT == 0 || cidx < CH) {
+        int r, h;
+        split_vec<P2>(min(v0 + cidx / CPR, nvec - 1), G, gsh, r, h);
+        st[j] = *reinterpret_cast<const u32x4*>(qb + ((size_t)r * Hq + h) * HD + (cidx % CPR) * 8);
+      }
+    }
+    int r, h;
+    split_vec<P2>(min(v0 + lr, nvec - 1), G, gsh, r, h);
+    lraw = lb[(size_t)r * Hq + h];
+    lvalid = v0 + lr < nvec;
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int cidx = tid + NT * j;
+      if (CH % NT == 0 || cidx < CH)
+        *reinterpret_cast<u32x4*>(sQ[buf] + (cidx / CPR) * PITCH + (cidx % CPR) * 8) = st[j];
+    }
+    sL[buf][lr] = lvalid ? lraw * kLog2e : INFINITY;
+  };
+
+  float acc[2][16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[0][i] = acc[1][i] = 0.f;
+  if (v_lo < v_hi) {
+    load_tile(v_lo);
+    store_tile(0);
+  }
+  // the K fragments are complete from here on; waiting once lets the
+  // loop's waits count only the tile loads
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  // One barrier per tile: tile t is read from buffer t&1 while tile t+1 is
+  // loaded into registers and then written to the other buffer.  The
+  // scheduling fences keep the loads at the top of the iteration and the LDS
+  // writes at its end, so the loads have the whole tile's work to land.
+  for (int v0 = v_lo, t = 0; v0 < v_hi; v0 += QTL, ++t) {
+    load_tile(v0 + QTL);
+    __builtin_amdgcn_sched_barrier(0);
+    const u16* sq = sQ[t & 1] + lr * PITCH + 8 * lg;
+    const float l2 = sL[t & 1][lr];
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 qf = as_bf16x8(*reinterpret_cast<const u32x4*>(sq + 16 * s));
+      s0 = mfma32x32x16(kf[0][s], qf, s0);
+      s1 = mfma32x32x16(kf[1][s], qf, s1);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      acc[0][i] += __builtin_amdgcn_exp2f(fmaf(s0[i], c, -l2));
+      acc[1][i] += __builtin_amdgcn_exp2f(fmaf(s1[i], c, -l2));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+  // each key's sum over the 32 query columns of its lane half
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) acc[kk][i] += __shfl_xor(acc[kk][i], o, 64);
+    }
+  if (lr == 0) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + 32 * kk + 8 * (i >> 2) + 4 * lg + (i & 3);
+        if (key < S) partial[(((size_t)sp * Hkv + g) * B + b) * S + key] = acc[kk][i];
+      }
+  }
+}
+
+// colsum[b][j] = sum over splits and KV heads of the partials, in that fixed
+// order; one thread per key, consecutive threads on consecutive keys.
+__global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* __restrict__ partial,
+                                                            int parts, int BS,
+                                                            float* __restrict__ colsum) {
+  for (int j = blockIdx.x * 256 + threadIdx.x; j < BS; j += gridDim.x * 256) {
+    float cs = 0.f;
+    for (int p = 0; p < parts; ++p) cs += partial[(size_t)p * BS + j];
+    colsum[j] = cs;
+  }
+}
+
+// FUSED: the kernel also sums its sequence's partials (few of them: the
+// separate reduce launch would cost more than it saves).
+template <bool FUSED>
+__global__ __launch_bounds__(1024) void colsum_topk_kernel(const float* __restrict__ partial,
+                                                           int parts, int B, int S,
+                                                           float* __restrict__ colsum, int key_lo,
+                                                           int key_hi, int kk, int p2,
+                                                           int32_t* topk_idx, float* topk_val) {
   extern __shared__ unsigned long long skeys[];
   const int b = blockIdx.x, tid = threadIdx.x;
-  for (int j = tid; j < S; j += 1024) {
-    float cs = 0.f;
-    for (int g = 0; g < Hkv; ++g) cs += partial[((size_t)g * B + b) * S + j];
-    colsum[(size_t)b * S + j] = cs;
-    if (kk > 0 && j >= key_lo && j < key_hi)
-      skeys[j - key_lo] = ((unsigned long long)__float_as_uint(cs) << 32) | (0xFFFFFFFFu - (unsigned)j);
+  if constexpr (FUSED) {
+    const size_t BS = (size_t)B * S;
+    for (int j = tid; j < S; j += 1024) {
+      float cs = 0.f;
+      for (int p = 0; p < parts; ++p) cs += partial[p * BS + (size_t)b * S + j];
+      colsum[(size_t)b * S + j] = cs;
+      if (kk > 0 && j >= key_lo && j < key_hi)
+        skeys[j - key_lo] = ((unsigned long long)__float_as_uint(cs) << 32) | (0xFFFFFFFFu - (unsigned)j);
+    }
+    if (kk <= 0) return;
+  } else {
+    for (int j = key_lo + tid; j < key_hi; j += 1024)
+      skeys[j - key_lo] = ((unsigned long long)__float_as_uint(colsum[(size_t)b * S + j]) << 32) |
+                          (0xFFFFFFFFu - (unsigned)j);
   }
-  if (kk <= 0) return;
   for (int j = (key_hi - key_lo) + tid; j < p2; j += 1024) skeys[j] = 0ull;
   __syncthreads();
   for (int size = 2; size <= p2; size <<= 1) {
@@ -145,28 +231,69 @@ __global__ __launch_bounds__(1024) void colsum_reduce_topk_kernel(const float* _
   }
 }
 
+// Query splits, only to fill the chip: with fewer (sequence, key block, KV
+// head) units than resident workgroup slots, up to 4 workgroups share a
+// unit's query vectors, each keeping at least 4 tiles of the average
+// sequence.  (Splitting further to even out the last round of a full chip
+// was measured slower: every extra workgroup reloads its 64 KB of keys.)
+static int colsum_splits(int units, int occ, int max_rows, int B, int G) {
+  const int slots = device_cus() * occ;
+  const long long tiles = ((long long)max_rows * G / B + 31) / 32;
+  int n = 1;
+  while (n < kColsumMaxSplit && units * (long long)(n + 1) <= slots && tiles >= 4LL * (n + 1)) ++n;
+  return n;
+}
+
+template <int HD, int WAVES>
+static int launch_colsum_pass(const void* q, const int32_t* offsets, int max_rows, const void* k,
+                              const float* lse, int B, int S, int Hq, int Hkv, float scale,
+                              float* partial, hipStream_t st) {
+  const int G = Hq / Hkv;
+  int gsh = 0;
+  while ((1 << gsh) < G) ++gsh;
+  const bool p2 = (1 << gsh) == G;
+  const int units = B * ((S + 64 * WAVES - 1) / (64 * WAVES)) * Hkv;
+  // resident workgroups per CU: one wave per SIMD each, 164 (d = 128) or
+  // 128 (d = 64) registers per lane
+  const int nsq = colsum_splits(units, HD == 128 ? 3 : 4, max_rows, B, G);
+  auto kern = p2 ? colsum_bf16_kernel<HD, WAVES, true> : colsum_bf16_kernel<HD, WAVES, false>;
+  hipLaunchKernelGGL(kern, dim3(units * nsq), dim3(64 * WAVES), 0, st, static_cast<const u16*>(q),
+                     offsets, static_cast<const u16*>(k), lse, B, S, Hq, Hkv, gsh, max_rows, nsq,
+                     scale, partial);
+  return nsq;
+}
+
+size_t colsum_workspace_bytes(int B, int S, int Hkv) {
+  return (size_t)kColsumMaxSplit * Hkv * B * S * sizeof(float);
+}
+
 hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, const void* k,
                          const float* lse, int B, int S, int Hq, int Hkv, int hd, float scale,
                          float* partial, float* colsum, int key_lo, int key_hi, int kk,
                          int32_t* topk_idx, float* topk_val, hipStream_t st) {
-  const int nkb = (S + 127) / 128;
-  const int grid = B * nkb * Hkv;
-  if (hd == 64)
-    hipLaunchKernelGGL(colsum_bf16_kernel<64>, dim3(grid), dim3(256), 0, st,
-                       static_cast<const u16*>(q), offsets, static_cast<const u16*>(k), lse, B, S,
-                       Hq, Hkv, max_rows, scale, partial);
-  else
-    hipLaunchKernelGGL(colsum_bf16_kernel<128>, dim3(grid), dim3(256), 0, st,
-                       static_cast<const u16*>(q), offsets, static_cast<const u16*>(k), lse, B, S,
-                       Hq, Hkv, max_rows, scale, partial);
+  const int nsq = hd == 64 ? launch_colsum_pass<64, 4>(q, offsets, max_rows, k, lse, B, S, Hq, Hkv,
+                                                        scale, partial, st)
+                           : launch_colsum_pass<128, 4>(q, offsets, max_rows, k, lse, B, S, Hq,
+                                                         Hkv, scale, partial, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // when a sequence has few partials, one kernel sums them and picks its top-k
+  const int parts = nsq * Hkv;
+  const bool fused = kk > 0 && (long long)parts * S <= 16384;
+  if (!fused) {
+    const int BS = B * S;
+    hipLaunchKernelGGL(colsum_reduce_kernel, dim3(min((BS + 255) / 256, 1024)), dim3(256), 0, st,
+                       partial, parts, BS, colsum);
+    if (kk <= 0) return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   int p2 = 1;
   while (p2 < key_hi - key_lo) p2 <<= 1;
   if (p2 < 2) p2 = 2;
-  const size_t shmem = kk > 0 ? (size_t)p2 * sizeof(unsigned long long) : 0;
-  hipLaunchKernelGGL(colsum_reduce_topk_kernel, dim3(B), dim3(1024), shmem, st, partial, Hkv, B, S,
-                     colsum, key_lo, key_hi, kk, p2, topk_idx, topk_val);
+  auto topk = fused ? colsum_topk_kernel<true> : colsum_topk_kernel<false>;
+  hipLaunchKernelGGL(topk, dim3(B), dim3(1024), (size_t)p2 * sizeof(unsigned long long), st, partial,
+                     parts, B, S, colsum, key_lo, key_hi, kk, p2, topk_idx, topk_val);
   return hipGetLastError();
 }
 

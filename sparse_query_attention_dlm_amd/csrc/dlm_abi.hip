@@ -317,7 +317,7 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
 // ---------------------------------------------------------------------------
 size_t dlm_attn_colsum_workspace_size(int B, int S, int Hkv) {
   if (B <= 0 || S <= 0 || Hkv <= 0) return 0;
-  return (size_t)Hkv * B * S * sizeof(float);
+  return dlm::colsum_workspace_bytes(B, S, Hkv);
 }
 
 int dlm_attn_colsum(int dtype, const void* q_sel, const int32_t* offsets, int max_rows,

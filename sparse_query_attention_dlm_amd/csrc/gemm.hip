@@ -584,19 +584,6 @@ static void launch_reduce(const GemmArgs& g, hipStream_t st) {
                      dim3(SB + kReduceTarget), dim3(256), 0, st, g);
 }
 
-// CUs of the current device (queried once per device; 256 on MI355X)
-static int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 // Grid of a tiling whose work items loop over workgroups: as many workgroups
 // as are resident at once (one per CU for the 256-wide tiles, two otherwise),
 // never more than there are items.

@@ -7,6 +7,19 @@
 
 namespace dlm {
 
+// CUs of the current device (queried once per device; 256 on MI355X)
+inline int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 // select.hip
 hipError_t launch_cosine_select(int dtype, const void* cur, const void* prev, int B, int S, int D,
                                 int lo, int hi, float thr, float* scores, int32_t* idx,
@@ -68,6 +81,7 @@ hipError_t launch_attn(int dtype, const AttnArgs& a, void* workspace, hipStream_
 hipError_t launch_probe_mfma(int iters, int grid, float* sink, hipStream_t st);
 
 // colsum.hip
+size_t colsum_workspace_bytes(int B, int S, int Hkv);
 hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, const void* k,
                          const float* lse, int B, int S, int Hq, int Hkv, int hd, float scale,
                          float* partial, float* colsum, int key_lo, int key_hi, int kk,

@@ -167,7 +167,8 @@ def test_colsum_rejections(lib):
     assert colsum(lib, S=10000, hi=10000) == INVALID         # top-k window over 8192 keys
     assert colsum(lib, ti=0, tv=0) == INVALID                # k > 0 but nowhere to write
     assert colsum(lib, ws_bytes=4) == WORKSPACE
-    assert lib.dlm_attn_colsum_workspace_size(4, 4096, 32) == 32 * 4 * 4096 * 4
+    # per-key float partials for up to 4 query splits of each KV head
+    assert lib.dlm_attn_colsum_workspace_size(4, 4096, 32) == 4 * 32 * 4 * 4096 * 4
 
 
 def test_probe_rejections(lib):
