@@ -47,8 +47,8 @@ def of_measured(rate, key):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets (cold-cache protocol)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -200,13 +200,16 @@ def main():
     reps, rem = divmod(a.steps, per_replay)
     steps = a.steps
 
-    print(f"[bench] warmup {a.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(max(1, a.warmup // per_replay)):
-        graph.replay()
+    graph.replay()
     torch.cuda.synchronize()
     for r, st in enumerate(sets):   # graph replays reproduce the eager results
         assert int(st.offsets[-1].item()) == n_sel
         assert torch.equal(st.o[:n_sel], ref_o[r]), "graph replay differs from the eager step"
+    # the warm-up runs right before the timed steps, so the chip enters them
+    # at the clock it holds under this load
+    print(f"[bench] warmup {a.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(max(1, a.warmup // per_replay)):
+        graph.replay()
 
     print(f"[bench] timing {steps} steps", file=sys.stderr, flush=True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -224,26 +227,18 @@ def main():
     ms_per_step = wall * 1e3 / steps
     value = n_sel / (ms_per_step / 1e3)
 
-    # stage durations: each stage's call launched kreps times back to back
-    # (rotating the input sets) between two HIP events on the launch stream;
-    # a GPU sleep queued first lets the host enqueue far ahead, so the events
-    # see GPU time only.  The QKV stage is a single kernel launch, so its mean
-    # is the dominant kernel's launch duration.
+    # stage durations: each stage's call captured kreps times back to back
+    # (rotating the input sets) in one HIP graph, replayed for ~30 ms so the
+    # clock settles under that stage, then timed over three replays between
+    # two HIP events (a select call is shorter than the host's launch time,
+    # so per-call launches would time the host).  The QKV stage is a single
+    # kernel launch, so its mean is the dominant kernel's launch duration.
     names = ["select", "qkv", "attn"]
     kreps = min(a.steps, 100)
     stage_ms = []
-    host_enqueue_ms = 0.0
     for k in range(3):
-        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        sleep_gpu(0.05 + kreps * 0.0002)
-        host0 = time.perf_counter()
-        e_a.record()
-        for i in range(kreps):
-            stages(sets[i % a.sets])[k]()
-        e_b.record()
-        host_enqueue_ms += (time.perf_counter() - host0) * 1e3
-        torch.cuda.synchronize()
-        stage_ms.append(e_a.elapsed_time(e_b) / kreps)
+        rot = iter(range(1 << 30))
+        stage_ms.append(_graph_time(lambda: stages(sets[next(rot) % a.sets])[k](), kreps))
     stage_ms = np.array([stage_ms])
 
     # algorithmic work per stage (bytes the method must move / flops it must do)
@@ -278,7 +273,7 @@ def main():
         "stages_ms": {k: float(v) for k, v in zip(names, mean)},
         "measured_ceilings": ceilings,
         "step_gpu_ms": step_ms,
-        "stage_timing": f"{kreps} back-to-back launches per stage between two HIP events, behind a queued GPU sleep (host enqueue {host_enqueue_ms:.1f} ms)",
+        "stage_timing": f"one HIP graph of {kreps} back-to-back calls per stage, replayed for ~30 ms, then 3 replays between two HIP events",
         "roofline": {"kernel": "gemm_dual_kernel, 64x128 weight-streaming body (gathered QKV + K/V scatter)", "bound": "hbm",
                      "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM, "traffic": traffic,
@@ -322,32 +317,72 @@ def _gen(shape, seed, scale=1.0, dtype=None):
     return t.to(dtype or torch.bfloat16)
 
 
-_SLEEP_CYCLES_PER_S = None
-
-
-def sleep_gpu(seconds):
-    """Queue a GPU spin of about `seconds` (calibrated once) so that work the host
-    enqueues next starts back to back on the GPU."""
+def queue_warm(fn, ms=30.0):
+    """Queue about `ms` of GPU time of real calls of fn (never fewer than one)
+    without waiting, so that calls the host enqueues next run back to back on
+    a GPU that is already at the clock it holds under this load.  (A GPU spin
+    kernel would also keep the queue full, but the chip lowers its clock
+    during a spin and the first milliseconds after it run up to 20 % slower.)"""
     import torch
-    global _SLEEP_CYCLES_PER_S
-    if _SLEEP_CYCLES_PER_S is None:
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        torch.cuda._sleep(10_000_000)
-        b.record()
-        torch.cuda.synchronize()
-        _SLEEP_CYCLES_PER_S = 10_000_000 / (a.elapsed_time(b) / 1e3)
-    torch.cuda._sleep(int(seconds * _SLEEP_CYCLES_PER_S))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    fn()
+    b.record()
+    torch.cuda.synchronize()
+    one = max(a.elapsed_time(b), 1e-3)
+    for _ in range(int(min(4000, max(1, math.ceil(ms / one))))):
+        fn()
 
 
-def _time(fn, reps, warmup=2):
+GRAPH_BELOW_MS = 0.15  # calls shorter than this are timed as a captured graph
+
+
+def _graph_time(fn, reps, warm_ms=30.0):
+    """Mean GPU time (ms) per call of `reps` back-to-back calls of fn captured
+    in one HIP graph.  For calls shorter than the host's launch time the host
+    cannot stay ahead of the GPU; one graph launch submits them all.  The
+    graph is replayed for about warm_ms first (the clock settles under this
+    exact load), then three replays are timed between two HIP events."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    for _ in range(int(min(1000, max(1, math.ceil(warm_ms / max(a.elapsed_time(b), 1e-3)))))):
+        g.replay()
+    a.record()
+    for _ in range(3):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (3 * reps)
+
+
+def _time(fn, reps, warmup=2, graph=True):
+    """Mean GPU time (ms) of fn over `reps` back-to-back calls.  Calls of
+    GRAPH_BELOW_MS or more: each between two HIP events on the current
+    stream, behind a queue of warm-up calls.  Shorter calls (graph=True):
+    captured in a HIP graph, see _graph_time."""
     import torch
     for _ in range(warmup):
         fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    a.record()
+    fn()
+    b.record()
+    torch.cuda.synchronize()
+    if graph and a.elapsed_time(b) < GRAPH_BELOW_MS:
+        return _graph_time(fn, reps)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    sleep_gpu(0.05 + 0.002 * reps)
+    queue_warm(fn)
     for a, b in ev:
         a.record()
         fn()
@@ -535,7 +570,7 @@ def extra_tiny(dlm, W):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
-    t = _time(g.replay, 50, warmup=5)
+    t = _time(g.replay, 50, warmup=5, graph=False)
     n = int(offsets[-1].item())
     return {"workload": sh.name, "n_selected": n, "step_us": t * 1e3, "tokens_per_s": n / (t / 1e3)}
 
