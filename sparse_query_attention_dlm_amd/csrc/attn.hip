@@ -295,6 +295,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
         sacc[kb] = mfma32x32x16(kf, qf[s], sacc[kb]);
       }
     }
+    // keep four K-fragment reads in flight: 4 reads, then (MFMA, read)
+    // pairs, then the last 4 MFMAs (left alone the scheduler issues each read
+    // right before its MFMA and waits out the whole LDS latency 16 times)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     if constexpr (decltype(masked)::value) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
