@@ -27,21 +27,8 @@ namespace dlm {
 
 constexpr int kColsumMaxSplit = 4;
 
-// Query vector v of a sequence (v = local row * G + head within the group):
-// its row and head offset, with a shift and mask when G is a power of two.
-template <bool P2>
-__device__ __forceinline__ void split_vec(int v, int G, int gsh, int& r, int& h) {
-  if constexpr (P2) {
-    r = v >> gsh;
-    h = v & (G - 1);
-  } else {
-    r = v / G;
-    h = v - r * G;
-  }
-}
-
-template <int HD, int WAVES, bool P2>
-__global__ __launch_bounds__(64 * WAVES, HD == 128 ? 3 : 4) void colsum_bf16_kernel(const u16* __restrict__ q,
+template <int HD, int WAVES, bool FAST>
+__global__ __launch_bounds__(64 * WAVES, HD == 128 || FAST ? 3 : 4) void colsum_bf16_kernel(const u16* __restrict__ q,
                                                                  const int32_t* __restrict__ offsets,
                                                                  const u16* __restrict__ k,
                                                                  const float* __restrict__ lse,
@@ -86,24 +73,54 @@ __global__ __launch_bounds__(64 * WAVES, HD == 128 ? 3 : 4) void colsum_bf16_ker
   // Tile of 32 query vectors starting at v0 into registers, and the LSE of
   // the lane's query column (every half-wave holds the same 32 values and
   // writes them, so the store needs no branch).  Rows past the end repeat the
-  // last vector; their LSE is +inf so they add exp2(-inf) = 0.
+  // last vector; their LSE is +inf so they add exp2(-inf) = 0.  Tiles are
+  // loaded in order, v_lo first.
+  //
+  // FAST (G a power of two dividing 32, element offsets below 2^31): vector
+  // v sits (v >> gsh) * Hq + (v & (G-1)) vectors after the base, which grows
+  // with v and moves by a fixed step per tile, so each thread keeps its
+  // chunk's offset and clamps it to the last vector's; otherwise the row and
+  // head come from a division.
   u32x4 st[CPT];
   float lraw;
   bool lvalid;
-  auto load_tile = [&](int v0) {
+  uint32_t qo[CPT], qlim = 0, lo = 0, llim = 0;  // NT is a multiple of CPR: one column per thread
+  const uint32_t dq = (uint32_t)(QTL >> gsh) * Hq * HD, dl = (uint32_t)(QTL >> gsh) * Hq;
+  auto vec_off = [&](int v) { return (uint32_t)(v >> gsh) * Hq + (uint32_t)(v & (G - 1)); };
+  if constexpr (FAST) {
+    if (v_lo < v_hi) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int cidx = tid + NT * j;
-      if (CH % NT == 0 || cidx < CH) {
-        int r, h;
-        split_vec<P2>(min(v0 + cidx / CPR, nvec - 1), G, gsh, r, h);
-        st[j] = *reinterpret_cast<const u32x4*>(qb + ((size_t)r * Hq + h) * HD + (cidx % CPR) * 8);
-      }
+      for (int j = 0; j < CPT; ++j) qo[j] = vec_off(v_lo + (tid + NT * j) / CPR) * HD + (tid % CPR) * 8;
+      qlim = vec_off(nvec - 1) * HD + (tid % CPR) * 8;
+      lo = vec_off(v_lo + lr);
+      llim = vec_off(nvec - 1);
     }
-    int r, h;
-    split_vec<P2>(min(v0 + lr, nvec - 1), G, gsh, r, h);
-    lraw = lb[(size_t)r * Hq + h];
-    lvalid = v0 + lr < nvec;
+  }
+  auto load_tile = [&](int v0) {
+    if constexpr (FAST) {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        if (CH % NT == 0 || tid + NT * j < CH) {
+          st[j] = *reinterpret_cast<const u32x4*>(qb + min(qo[j], qlim));
+          qo[j] += dq;
+        }
+      }
+      lraw = lb[min(lo, llim)];
+      lvalid = lo <= llim;  // the offset grows with the vector index
+      lo += dl;
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int cidx = tid + NT * j;
+        if (CH % NT == 0 || cidx < CH) {
+          const int v = min(v0 + cidx / CPR, nvec - 1), r = v / G, h = v - r * G;
+          st[j] = *reinterpret_cast<const u32x4*>(qb + ((size_t)r * Hq + h) * HD + (cidx % CPR) * 8);
+        }
+      }
+      const int v = min(v0 + lr, nvec - 1), r = v / G, h = v - r * G;
+      lraw = lb[(size_t)r * Hq + h];
+      lvalid = v0 + lr < nvec;
+    }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
@@ -251,12 +268,12 @@ static int launch_colsum_pass(const void* q, const int32_t* offsets, int max_row
   const int G = Hq / Hkv;
   int gsh = 0;
   while ((1 << gsh) < G) ++gsh;
-  const bool p2 = (1 << gsh) == G;
+  const bool fast = (1 << gsh) == G && G <= 32 && (long long)max_rows * Hq * HD < (1LL << 31);
   const int units = B * ((S + 64 * WAVES - 1) / (64 * WAVES)) * Hkv;
-  // resident workgroups per CU: one wave per SIMD each, 164 (d = 128) or
-  // 128 (d = 64) registers per lane
-  const int nsq = colsum_splits(units, HD == 128 ? 3 : 4, max_rows, B, G);
-  auto kern = p2 ? colsum_bf16_kernel<HD, WAVES, true> : colsum_bf16_kernel<HD, WAVES, false>;
+  // resident workgroups per CU: one wave per SIMD each, at most 168
+  // registers per lane (128 for the generic d = 64 body)
+  const int nsq = colsum_splits(units, HD == 128 || fast ? 3 : 4, max_rows, B, G);
+  auto kern = fast ? colsum_bf16_kernel<HD, WAVES, true> : colsum_bf16_kernel<HD, WAVES, false>;
   hipLaunchKernelGGL(kern, dim3(units * nsq), dim3(64 * WAVES), 0, st, static_cast<const u16*>(q),
                      offsets, static_cast<const u16*>(k), lse, B, S, Hq, Hkv, gsh, max_rows, nsq,
                      scale, partial);
