@@ -15,11 +15,13 @@
 // workgroups, or their count leaves the last round of the chip half empty,
 // the query vectors are split into up to 4 ranges, one workgroup each.
 // Results go to a [split][Hkv][B][S] partial array.
-// Pass 2: sums the partials of every key in a fixed order (no float atomics:
-// reruns are bit-identical).
-// Pass 3 (k > 0): per sequence, the top-k keys of [key_lo,key_hi) by a
-// bitonic sort of (colsum bits, ~key) 64-bit keys in LDS: descending sums,
-// equal sums ordered by the lower position.
+// Pass 2: sums the partials of every key in a fixed order, four threads per
+// key (no float atomics: reruns are bit-identical).
+// Pass 3 (k > 0): per sequence, the top-k keys of [key_lo,key_hi) ordered by
+// (colsum bits, ~key) 64-bit keys: descending sums, equal sums ordered by the
+// lower position.  k <= 64 over a window of 1024+ keys: radix select of the
+// k-th key, then a sort of the k winners; otherwise a bitonic sort of the
+// whole window in LDS.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -187,64 +189,169 @@ __global__ __launch_bounds__(64 * WAVES, HD == 128 || FAST ? 3 : 4) void colsum_
   }
 }
 
-// colsum[b][j] = sum over splits and KV heads of the partials, in that fixed
-// order; one thread per key, consecutive threads on consecutive keys.
+// colsum[b][j] = sum over splits and KV heads of the partials, in a fixed
+// order: wave w of a workgroup adds parts [w*P/4, (w+1)*P/4) of 64
+// consecutive keys (coalesced), wave 0 then adds the four sums in order.
 __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* __restrict__ partial,
                                                             int parts, int BS,
                                                             float* __restrict__ colsum) {
-  for (int j = blockIdx.x * 256 + threadIdx.x; j < BS; j += gridDim.x * 256) {
+  __shared__ float s_part[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p0 = parts * wave / 4, p1 = parts * (wave + 1) / 4;
+  for (int j0 = blockIdx.x * 64; j0 < BS; j0 += gridDim.x * 64) {
+    const int j = j0 + lane;
     float cs = 0.f;
-    for (int p = 0; p < parts; ++p) cs += partial[(size_t)p * BS + j];
-    colsum[j] = cs;
+    if (j < BS)
+      for (int p = p0; p < p1; ++p) cs += partial[(size_t)p * BS + j];
+    s_part[wave][lane] = cs;
+    __syncthreads();
+    if (wave == 0 && j < BS) colsum[j] = ((s_part[0][lane] + s_part[1][lane]) + s_part[2][lane]) + s_part[3][lane];
+    __syncthreads();
   }
 }
 
-// FUSED: the kernel also sums its sequence's partials (few of them: the
-// separate reduce launch would cost more than it saves).
-template <bool FUSED>
+// Key of window position j: colsum bits (non-negative floats order as
+// unsigned integers) above ~j, so that larger keys are larger sums and, for
+// equal sums, lower positions; all keys of a window are distinct.
+__device__ __forceinline__ unsigned long long topk_key(float cs, int j) {
+  return ((unsigned long long)__float_as_uint(cs) << 32) | (0xFFFFFFFFu - (unsigned)j);
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const unsigned lo = __shfl_xor((unsigned)v, m, 64), hi = __shfl_xor((unsigned)(v >> 32), m, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Top-k of one sequence's key window [key_lo, key_hi) (one workgroup of 1024
+// threads per sequence), written in descending key order.  FUSED: the kernel
+// first sums the sequence's partials itself (few of them: the separate
+// reduce launch would cost more than it saves).
+//   SMALL (k <= 64, window of 1024+ keys): radix select.  Each thread keeps its (at most 8) keys in
+//   registers; 8-bit digits from the top narrow the candidates to the k-th
+//   largest key (a 256-bin LDS histogram per digit, scanned by one wave), and
+//   stop as soon as the threshold bin holds exactly the keys still missing.
+//   The k keys at or above the threshold are then sorted by one wave with a
+//   bitonic network on shuffles.
+//   Otherwise: bitonic sort of the whole window in LDS.
+template <bool FUSED, bool SMALL>
 __global__ __launch_bounds__(1024) void colsum_topk_kernel(const float* __restrict__ partial,
                                                            int parts, int B, int S,
                                                            float* __restrict__ colsum, int key_lo,
                                                            int key_hi, int kk, int p2,
                                                            int32_t* topk_idx, float* topk_val) {
   extern __shared__ unsigned long long skeys[];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = key_hi - key_lo;
+  float* crow = colsum + (size_t)b * S;
   if constexpr (FUSED) {
     const size_t BS = (size_t)B * S;
     for (int j = tid; j < S; j += 1024) {
       float cs = 0.f;
       for (int p = 0; p < parts; ++p) cs += partial[p * BS + (size_t)b * S + j];
-      colsum[(size_t)b * S + j] = cs;
-      if (kk > 0 && j >= key_lo && j < key_hi)
-        skeys[j - key_lo] = ((unsigned long long)__float_as_uint(cs) << 32) | (0xFFFFFFFFu - (unsigned)j);
+      crow[j] = cs;
     }
     if (kk <= 0) return;
-  } else {
-    for (int j = key_lo + tid; j < key_hi; j += 1024)
-      skeys[j - key_lo] = ((unsigned long long)__float_as_uint(colsum[(size_t)b * S + j]) << 32) |
-                          (0xFFFFFFFFu - (unsigned)j);
+    __syncthreads();  // the sums are re-read below by other threads of this workgroup
   }
-  for (int j = (key_hi - key_lo) + tid; j < p2; j += 1024) skeys[j] = 0ull;
-  __syncthreads();
-  for (int size = 2; size <= p2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < (p2 >> 1); t += 1024) {
-        const int i = 2 * t - (t & (stride - 1));
-        const int j = i + stride;
-        const bool desc = (i & size) == 0;
-        const unsigned long long x = skeys[i], y = skeys[j];
-        if ((x < y) == desc) {
-          skeys[i] = y;
-          skeys[j] = x;
+  if constexpr (SMALL) {
+    constexpr int KPT = 8;  // keys per thread (windows of at most 8192 keys)
+    __shared__ unsigned hist[256];
+    __shared__ int s_bin, s_above, s_cntb, s_pos;
+    __shared__ unsigned long long s_out[64];
+    unsigned long long key[KPT];
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+      const int w = tid + 1024 * e;
+      key[e] = w < n ? topk_key(crow[key_lo + w], key_lo + w) : 0ull;
+    }
+    unsigned long long prefix = 0, mask = 0;
+    int rem = kk;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < KPT; ++e)
+        if (tid + 1024 * e < n && (key[e] & mask) == prefix)
+          atomicAdd(&hist[(unsigned)(key[e] >> shift) & 255u], 1u);
+      __syncthreads();
+      if (wave == 0) {
+        // lane l holds bins 255-4l .. 252-4l, highest first
+        unsigned c[4], tot = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[q] = hist[255 - 4 * lane - q];
+          tot += c[q];
+        }
+        unsigned incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const unsigned t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        unsigned cum = incl - tot;  // candidates in the bins above this lane's
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (cum < (unsigned)rem && (unsigned)rem <= cum + c[q]) {
+            s_bin = 255 - 4 * lane - q;
+            s_above = (int)cum;
+            s_cntb = (int)c[q];
+          }
+          cum += c[q];
         }
       }
       __syncthreads();
+      prefix |= (unsigned long long)s_bin << shift;
+      mask |= 0xFFull << shift;
+      rem -= s_above;
+      if (s_cntb == rem) break;  // the whole threshold bin is in the top k
     }
-  }
-  for (int t = tid; t < kk; t += 1024) {
-    const unsigned long long u = skeys[t];
-    if (topk_idx) topk_idx[(size_t)b * kk + t] = (int32_t)(0xFFFFFFFFu - (unsigned)(u & 0xFFFFFFFFull));
-    if (topk_val) topk_val[(size_t)b * kk + t] = __uint_as_float((unsigned)(u >> 32));
+    // exactly k keys satisfy (key & mask) >= prefix
+    if (tid == 0) s_pos = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < KPT; ++e)
+      if (tid + 1024 * e < n && (key[e] & mask) >= prefix) {
+        const int pos = atomicAdd(&s_pos, 1);
+        if (pos < 64) s_out[pos] = key[e];
+      }
+    __syncthreads();
+    if (wave != 0) return;
+    unsigned long long v = lane < kk ? s_out[lane] : 0ull;
+    for (int size = 2; size <= 64; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const unsigned long long o = shfl_xor_u64(v, stride);
+        const bool desc = (lane & size) == 0, lower = (lane & stride) == 0;
+        v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+      }
+    }
+    if (lane < kk) {
+      if (topk_idx) topk_idx[(size_t)b * kk + lane] = (int32_t)(0xFFFFFFFFu - (unsigned)(v & 0xFFFFFFFFull));
+      if (topk_val) topk_val[(size_t)b * kk + lane] = __uint_as_float((unsigned)(v >> 32));
+    }
+  } else {
+    for (int w = tid; w < n; w += 1024) skeys[w] = topk_key(crow[key_lo + w], key_lo + w);
+    for (int w = n + tid; w < p2; w += 1024) skeys[w] = 0ull;
+    __syncthreads();
+    for (int size = 2; size <= p2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int t = tid; t < (p2 >> 1); t += 1024) {
+          const int i = 2 * t - (t & (stride - 1));
+          const int j = i + stride;
+          const bool desc = (i & size) == 0;
+          const unsigned long long x = skeys[i], y = skeys[j];
+          if ((x < y) == desc) {
+            skeys[i] = y;
+            skeys[j] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int t = tid; t < kk; t += 1024) {
+      const unsigned long long u = skeys[t];
+      if (topk_idx) topk_idx[(size_t)b * kk + t] = (int32_t)(0xFFFFFFFFu - (unsigned)(u & 0xFFFFFFFFull));
+      if (topk_val) topk_val[(size_t)b * kk + t] = __uint_as_float((unsigned)(u >> 32));
+    }
   }
 }
 
@@ -299,7 +406,7 @@ hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, co
   const bool fused = kk > 0 && (long long)parts * S <= 16384;
   if (!fused) {
     const int BS = B * S;
-    hipLaunchKernelGGL(colsum_reduce_kernel, dim3(min((BS + 255) / 256, 1024)), dim3(256), 0, st,
+    hipLaunchKernelGGL(colsum_reduce_kernel, dim3(min((BS + 63) / 64, 2048)), dim3(256), 0, st,
                        partial, parts, BS, colsum);
     if (kk <= 0) return hipGetLastError();
     e = hipGetLastError();
@@ -308,9 +415,13 @@ hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, co
   int p2 = 1;
   while (p2 < key_hi - key_lo) p2 <<= 1;
   if (p2 < 2) p2 = 2;
-  auto topk = fused ? colsum_topk_kernel<true> : colsum_topk_kernel<false>;
-  hipLaunchKernelGGL(topk, dim3(B), dim3(1024), (size_t)p2 * sizeof(unsigned long long), st, partial,
-                     parts, B, S, colsum, key_lo, key_hi, kk, p2, topk_idx, topk_val);
+  // radix select for k <= 64 over windows of 1024+ keys (a short window
+  // sorts faster than the select's histogram passes)
+  const bool small = kk <= 64 && key_hi - key_lo >= 1024;
+  auto topk = small ? (fused ? colsum_topk_kernel<true, true> : colsum_topk_kernel<false, true>)
+                    : (fused ? colsum_topk_kernel<true, false> : colsum_topk_kernel<false, false>);
+  hipLaunchKernelGGL(topk, dim3(B), dim3(1024), small ? 0 : (size_t)p2 * sizeof(unsigned long long), st,
+                     partial, parts, B, S, colsum, key_lo, key_hi, kk, p2, topk_idx, topk_val);
   return hipGetLastError();
 }
 

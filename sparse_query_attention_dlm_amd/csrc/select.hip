@@ -9,21 +9,35 @@
 // Layout: one wave64 per scored row, 16-byte vector loads (a lane's whole
 // batch of loads is issued before any arithmetic), float32 accumulation, wave
 // reductions.  The compaction (flag -> prefix sum -> ascending index list,
-// counts, offsets) is a single-workgroup pass launched after the scores.
+// counts, offsets) is a second launch after the scores, one workgroup per
+// batch row.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace dlm {
 
-// Block-wide (256 threads) compaction of [lo,hi) of every batch row.
-__device__ void compact_rows(const float* scores, int B, int S, int lo, int hi, float thr,
-                             int32_t* idx, int32_t* counts, int32_t* offsets) {
-  constexpr int NT = 256, E = 8;
+constexpr int kCompactNT = 256;
+
+// Block-wide sum of one int per thread (256 threads).
+__device__ __forceinline__ int block_sum(int v, int* s_wave) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if (lane == 0) s_wave[wave] = v;
+  __syncthreads();
+  return s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+}
+
+// Block-wide (256 threads) compaction of [lo,hi) of batch rows [b0, b1),
+// whose first index goes to idx[base].
+__device__ void compact_rows(const float* scores, int B, int S, int lo, int hi, float thr, int b0,
+                             int b1, int base, int32_t* idx, int32_t* counts, int32_t* offsets) {
+  constexpr int NT = kCompactNT, E = 8;
   __shared__ int s_wave[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int W = hi - lo;
-  int base = 0;
-  for (int b = 0; b < B; ++b) {
+  for (int b = b0; b < b1; ++b) {
     const float* row = scores + (size_t)b * S + lo;
     int rowcount = 0;
     for (int c0 = 0; c0 < W; c0 += NT * E) {
@@ -65,7 +79,7 @@ __device__ void compact_rows(const float* scores, int B, int S, int lo, int hi, 
     }
     base += rowcount;
   }
-  if (tid == 0) offsets[B] = base;
+  if (tid == 0 && b1 == B) offsets[B] = base;
 }
 
 template <int DT>
@@ -136,7 +150,22 @@ __global__ __launch_bounds__(256) void given_select_kernel(const float* __restri
                                                            int S, int lo, int hi, float thr,
                                                            int32_t* idx, int32_t* counts,
                                                            int32_t* offsets) {
-  compact_rows(scores, B, S, lo, hi, thr, idx, counts, offsets);
+  if (gridDim.x == 1) {
+    compact_rows(scores, B, S, lo, hi, thr, 0, B, 0, idx, counts, offsets);
+    return;
+  }
+  // one workgroup per batch row: the rows before it are counted again here
+  // (a few KB of scores each), which gives this row's first output slot
+  // without any ordering between workgroups
+  __shared__ int s_sum[4];
+  const int b = blockIdx.x, W = hi - lo;
+  int before = 0;
+  for (int bb = 0; bb < b; ++bb) {
+    const float* row = scores + (size_t)bb * S + lo;
+    for (int p = threadIdx.x; p < W; p += kCompactNT) before += row[p] < thr;
+  }
+  const int base = block_sum(before, s_sum);
+  compact_rows(scores, B, S, lo, hi, thr, b, b + 1, base, idx, counts, offsets);
 }
 
 // Merge of per-vocabulary-tile partials (max logit, sum exp(z - max), argmax)
@@ -175,8 +204,11 @@ __global__ __launch_bounds__(256) void lmhead_combine_kernel(
 // ---------------------------------------------------------------------------
 hipError_t launch_given_select(const float* scores, int B, int S, int lo, int hi, float thr,
                                int32_t* idx, int32_t* counts, int32_t* offsets, hipStream_t st) {
-  hipLaunchKernelGGL(given_select_kernel, dim3(1), dim3(256), 0, st, scores, B, S, lo, hi, thr,
-                     idx, counts, offsets);
+  // one workgroup per batch row while the repeated counting of the earlier
+  // rows stays small (B*B*(hi-lo)/2 scores), else one workgroup for all rows
+  const bool wide = B > 1 && (long long)B * B * (hi - lo) <= (32LL << 20);
+  hipLaunchKernelGGL(given_select_kernel, dim3(wide ? B : 1), dim3(kCompactNT), 0, st, scores, B, S,
+                     lo, hi, thr, idx, counts, offsets);
   return hipGetLastError();
 }
 

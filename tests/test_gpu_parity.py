@@ -388,6 +388,11 @@ def run_colsum(dlm, zero_q=False, **override):
     assert np.all(np.diff(tv_g, axis=1) <= 0)
     for b in range(B):
         assert np.array_equal(tv_g[b], c_g[b, ti_g[b]].astype(np.float32))
+        # the selection itself is exact on the kernel's own sums: the first k
+        # window positions ordered by (-colsum, position)
+        win = np.arange(s.prompt, S)
+        order = win[np.lexsort((win, -c_g[b, win].astype(np.float64)))]
+        assert np.array_equal(ti_g[b], order[: s.k]), f"sequence {b}: top-{s.k} differs from its own sums"
     # determinism: a second run is bit-identical
     c2 = torch.zeros_like(colsum)
     ti2 = torch.zeros_like(ti)
@@ -452,9 +457,48 @@ def test_colsum_topk_gqa_ragged(dlm):
     run_colsum(dlm, B=3, S=520, prompt=77, Hq=8, Hkv=2, k=24)
 
 
-def test_colsum_uniform_ties_pick_lowest_positions(dlm):
-    ti, c = run_colsum(dlm, zero_q=True, B=2, S=512, prompt=128, Hq=4, Hkv=4, k=20)
-    assert ti.tolist() == [list(range(128, 148))] * 2
+@pytest.mark.parametrize("B,S", [(5, 1000), (70, 8192)])
+def test_given_select_batch_paths(dlm, B, S):
+    """Compaction of supplied scores over the window [3, S-5): B = 5 takes the
+    one-workgroup-per-row kernel, B = 70 (B*B*window over the limit for
+    recounting) the single-workgroup loop.  Index sets, counts and offsets
+    are bit-exact against the oracle (the scores are exact float32 values and
+    0.5 is exact, so both sides take the same decisions)."""
+    lo, hi = 3, S - 5
+    say(f"[given select] B={B} S={S} window=[{lo},{hi})")
+    rng = np.random.default_rng(7000 + B)
+    sc = rng.random((B, S), dtype=np.float32)
+    sc[0, lo:hi] = 1.0  # an empty row
+    ridx, rcnt, roff = O.compact(sc, lo, hi, 0.5)
+    idx = torch.full((B * S,), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    dlm.dlm_saliency_select(dlm.DLM_SCORE_GIVEN, dev(sc, "f32"), None, lo=lo, hi=hi, threshold=0.5,
+                            idx=idx, counts=cnt, offsets=offsets)
+    torch.cuda.synchronize()
+    n = int(roff[-1])
+    assert np.array_equal(offsets.cpu().numpy(), roff) and np.array_equal(cnt.cpu().numpy(), rcnt)
+    got = idx.cpu().numpy()
+    assert np.array_equal(got[:n], ridx)
+    assert np.all(got[n:] == -7), "compaction wrote past the selected entries"
+
+
+@pytest.mark.parametrize("k,S,prompt", [(1, 1536, 256), (64, 1536, 256), (100, 1536, 256), (16, 1024, 256)])
+def test_colsum_topk_sizes(dlm, k, S, prompt):
+    """k = 1 and k = 64 over a 1280-key window take the radix-select path,
+    k = 100 and the 768-key window the sort of the whole window; all against
+    the oracle's band rule and, exactly, against the order of the kernel's
+    own sums."""
+    run_colsum(dlm, B=2, S=S, prompt=prompt, Hq=4, Hkv=4, k=k)
+
+
+@pytest.mark.parametrize("S,prompt,k", [(512, 128, 20), (2048, 512, 64)])
+def test_colsum_uniform_ties_pick_lowest_positions(dlm, S, prompt, k):
+    """Q = 0: every column sum is equal, so the top-k is the k lowest window
+    positions; the 1536-key window resolves the ties in the radix select's
+    position digits."""
+    ti, c = run_colsum(dlm, zero_q=True, B=2, S=S, prompt=prompt, Hq=4, Hkv=4, k=k)
+    assert ti.tolist() == [list(range(prompt, prompt + k))] * 2
 
 
 # ---------------------------------------------------------------------------
