@@ -408,24 +408,38 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void attn_fwd_bf16_kerne
 // broadcast, and all splits' partial rows are loaded before any accumulation
 // (NS2 = 8 or 16 slots, branch-free; unused slots re-read a valid split with
 // weight 0).
+// One (row, head) pair of the split-KV merge, in two phases so that a wave
+// can issue the loads of several pairs before it waits for any of them.
 template <int HD, int NS2>
-__device__ __forceinline__ void merge_row(const AttnArgs& a, const AttnPlan& plan, int pr, int lane) {
+struct MergeLoads {
+  float ls;            // this lane's split LSE (lanes < nsplit)
+  float v[NS2][HD / 64];  // this lane's output columns of every split slot
+};
+
+template <int HD, int NS2>
+__device__ __forceinline__ void merge_load(const AttnArgs& a, const AttnPlan& plan, int pr, int lane,
+                                           MergeLoads<HD, NS2>& m) {
   constexpr int E = HD / 64;
   const int nsplit = plan.nsplit;
   const size_t split_stride = (size_t)plan.n_rows * a.Hq;
-  const float ls = lane < nsplit ? a.part_lse[lane * split_stride + pr] : -INFINITY;
-  const float M = wave_max(ls);
-  const float wl = lane < nsplit ? __expf(ls - M) : 0.f;
-  const float tot = wave_sum(wl);
-  const float L = M + __logf(tot);
-  float v[NS2][E];
+  m.ls = lane < nsplit ? a.part_lse[lane * split_stride + pr] : -INFINITY;
 #pragma unroll
   for (int s = 0; s < NS2; ++s) {
-    const int sc = min(s, nsplit - 1);
+    const int sc = min(s, nsplit - 1);  // slots past nsplit get weight 0
     const float* po = a.part_o + (sc * split_stride + pr) * HD + lane * E;
 #pragma unroll
-    for (int e = 0; e < E; ++e) v[s][e] = po[e];
+    for (int e = 0; e < E; ++e) m.v[s][e] = po[e];
   }
+}
+
+template <int HD, int NS2>
+__device__ __forceinline__ void merge_finish(const AttnArgs& a, int pr, int lane,
+                                             const MergeLoads<HD, NS2>& m, int nsplit) {
+  constexpr int E = HD / 64;
+  const float M = wave_max(m.ls);
+  const float wl = lane < nsplit ? __expf(m.ls - M) : 0.f;
+  const float tot = wave_sum(wl);
+  const float L = M + __logf(tot);
   float o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
@@ -433,7 +447,7 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, const AttnPlan& pla
   for (int s = 0; s < NS2; ++s) {
     const float w = __shfl(wl, s, 64) / tot;  // zero for slots past nsplit
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = fmaf(w, v[s][e], o[e]);
+    for (int e = 0; e < E; ++e) o[e] = fmaf(w, m.v[s][e], o[e]);
   }
   const int row = pr / a.Hq, h = pr % a.Hq;
   u16* op = static_cast<u16*>(a.o) + (size_t)pr * HD + lane * E;
@@ -451,18 +465,37 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, const AttnPlan& pla
   if (lane == 0 && a.lse) a.lse[pr] = L;
 }
 
+// A wave merges pairs pr and pr + stride together: both pairs' loads are in
+// flight before either is combined.
+template <int HD, int NS2>
+__device__ __forceinline__ void merge_pairs(const AttnArgs& a, const AttnPlan& plan, int first,
+                                            int stride, int pairs, int lane) {
+  for (int pr = first; pr < pairs; pr += 2 * stride) {
+    const int pr2 = pr + stride;
+    MergeLoads<HD, NS2> m0, m1;
+    merge_load<HD, NS2>(a, plan, pr, lane, m0);
+    if (pr2 < pairs) merge_load<HD, NS2>(a, plan, pr2, lane, m1);
+    merge_finish<HD, NS2>(a, pr, lane, m0, plan.nsplit);
+    if (pr2 < pairs) merge_finish<HD, NS2>(a, pr2, lane, m1, plan.nsplit);
+  }
+}
+
 template <int HD, int QT>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const AttnPlan plan = attn_plan(a, QT);
   if (plan.nsplit <= 1) return;  // the attention kernel already wrote the outputs
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int pairs = plan.n_rows * a.Hq;
-  for (int pr = blockIdx.x * 4 + wave; pr < pairs; pr += gridDim.x * 4) {
-    if (plan.nsplit <= 8)
-      merge_row<HD, 8>(a, plan, pr, lane);
-    else
-      merge_row<HD, 16>(a, plan, pr, lane);
-  }
+  const int first = blockIdx.x * 4 + wave, stride = gridDim.x * 4;
+  // slices read per pair: the split count rounded up to a power of two
+  if (plan.nsplit <= 2)
+    merge_pairs<HD, 2>(a, plan, first, stride, pairs, lane);
+  else if (plan.nsplit <= 4)
+    merge_pairs<HD, 4>(a, plan, first, stride, pairs, lane);
+  else if (plan.nsplit <= 8)
+    merge_pairs<HD, 8>(a, plan, first, stride, pairs, lane);
+  else
+    merge_pairs<HD, 16>(a, plan, first, stride, pairs, lane);
 }
 
 template <int HD>
