@@ -162,7 +162,16 @@ __global__ __launch_bounds__(256) void given_select_kernel(const float* __restri
   int before = 0;
   for (int bb = 0; bb < b; ++bb) {
     const float* row = scores + (size_t)bb * S + lo;
-    for (int p = threadIdx.x; p < W; p += kCompactNT) before += row[p] < thr;
+    for (int p0 = threadIdx.x; p0 < W; p0 += 8 * kCompactNT) {
+      float v[8];  // eight loads in flight before any compare
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int p = p0 + u * kCompactNT;
+        v[u] = p < W ? row[p] : thr;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) before += v[u] < thr;
+    }
   }
   const int base = block_sum(before, s_sum);
   compact_rows(scores, B, S, lo, hi, thr, b, b + 1, base, idx, counts, offsets);
