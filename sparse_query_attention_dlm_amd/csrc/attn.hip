@@ -406,8 +406,8 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void attn_fwd_bf16_kerne
 // Combine split-KV partials: O = sum_s exp(lse_s - L) O_s with L = logsumexp_s lse_s.
 // One wave per (row, head): lane s < nsplit reads split s's LSE, the weights are
 // broadcast, and all splits' partial rows are loaded before any accumulation
-// (NS2 = 8 or 16 slots, branch-free; unused slots re-read a valid split with
-// weight 0).
+// (NS2 = the split count rounded up to 2, 4, 8 or 16 slots, branch-free; unused
+// slots re-read a valid split with weight 0).
 // One (row, head) pair of the split-KV merge, in two phases so that a wave
 // can issue the loads of several pairs before it waits for any of them.
 template <int HD, int NS2>
