@@ -11,9 +11,9 @@
 // S^T = K . Q^T puts one query per lane column, so each fragment read from
 // LDS feeds two MFMAs and p = exp2(s*scale*log2e - lse*log2e) is accumulated
 // into the lane's own 32 key sums with no cross-lane traffic inside the
-// loop; one 32-lane reduction at the end.  When there are few such
-// workgroups, or their count leaves the last round of the chip half empty,
-// the query vectors are split into up to 4 ranges, one workgroup each.
+// loop; one 32-lane reduction at the end.  When there are too few such
+// workgroups to fill the chip, the query vectors are split into up to 4
+// ranges, one workgroup each.
 // Results go to a [split][Hkv][B][S] partial array.
 // Pass 2: sums the partials of every key in a fixed order, four threads per
 // key (no float atomics: reruns are bit-identical).
