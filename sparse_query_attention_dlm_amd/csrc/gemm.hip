@@ -53,7 +53,7 @@ __device__ __forceinline__ void epi_store4(const GemmArgs& g, int m, int drow, i
 
 // Epilogues on the accumulated tile.  Register i of acc[a][b] in lane l holds
 // feature n0 + wp*WTP + 32a + 8(i/4) + 4(l/32) + i%4 of token m0 + wt*WTT + 32b + l%32.
-template <int TP, int TT, int WP, int WT, int EPI>
+template <int TP, int TT, int WP, int WT, int EPI, int TPV = TP>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
                                               f32x16 (&acc)[TP / WP / 32][TT / WT / 32], int m0,
                                               int n0, int nt, const int* s_drow) {
@@ -70,9 +70,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
 #pragma unroll
       for (int a = 0; a < FP; ++a)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          epi_store4<EPI>(g, m0 + ml, drow, n0 + wp * WTP + a * 32 + 8 * q4 + 4 * lg, acc[a][b][4 * q4],
-                          acc[a][b][4 * q4 + 1], acc[a][b][4 * q4 + 2], acc[a][b][4 * q4 + 3]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int nl = wp * WTP + a * 32 + 8 * q4 + 4 * lg;  // feature within the tile
+          if (TPV < TP && nl >= TPV) continue;                 // zero-filled padding rows
+          epi_store4<EPI>(g, m0 + ml, drow, n0 + nl, acc[a][b][4 * q4], acc[a][b][4 * q4 + 1],
+                          acc[a][b][4 * q4 + 2], acc[a][b][4 * q4 + 3]);
+        }
     }
   } else {
     __shared__ float s_pm[WP][TT], s_ps[WP][TT];
@@ -185,11 +188,18 @@ __device__ __forceinline__ void gemm_rows(const GemmArgs& g, int n_rows, int m0,
 // WK = 2: eight waves; waves 4..7 repeat the layout of waves 0..3 on the
 // other half of every k-step's 16-wide sub-steps, two waves per SIMD hide each
 // other's LDS and barrier latency, and the halves are added through LDS.
-template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK>
+template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK,
+          int TPV>
 __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u16* lds, uint32_t* s_xoff,
                                                int* s_drow, const GemmSplit sp, int unit, int ksi);
 
-template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK = 1>
+// TPV (<= TP): weight rows a tile really owns.  A tile of TP MFMA rows with
+// TPV = 48 < TP = 64 lets the 12288-feature Q/K/V projection spread over 256
+// tiles (one per CU) instead of 192: the other rows load zeros without memory
+// traffic and the epilogue skips them (the weight-streaming body is bound by
+// the bytes each CU reads, not by its MFMAs).
+template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK = 1,
+          int TPV = TP>
 __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u16* lds,
                                                uint32_t* s_xoff, int* s_drow) {
   constexpr int NT = 256 * WK;   // threads
@@ -209,7 +219,7 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
                 "two k-halves: row epilogues only, partial sums fit the tile's LDS");
 
   const int m_tiles = (n_rows + TT - 1) / TT;
-  const int n_tiles = g.N / TP;
+  const int n_tiles = g.N / TPV;
   const int nk_all = g.K / BK;
   const GemmSplit sp = gemm_split(m_tiles * n_tiles, nk_all, PF, SB, ST);
   const int total = sp.units * sp.ks;
@@ -218,13 +228,15 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
   // workgroup on the same k-step of its current tile and the tiles running
   // together on an XCD share their weight and row slices in its L2.
   for (int work = (int)blockIdx.x; work < total; work += (WK == 1 ? (int)gridDim.x : total)) {
-    gemm_tile_work<TP, TT, WP, WT, BK, PF, EPI, AMODE, SB, ST, WK>(g, n_rows, lds, s_xoff, s_drow, sp,
-                                                                   work % sp.units, work / sp.units);
+    gemm_tile_work<TP, TT, WP, WT, BK, PF, EPI, AMODE, SB, ST, WK, TPV>(g, n_rows, lds, s_xoff, s_drow,
+                                                                        sp, work % sp.units,
+                                                                        work / sp.units);
     if constexpr (WK == 1) __syncthreads();  // the next item rewrites the row table and tiles
   }
 }
 
-template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK>
+template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK,
+          int TPV>
 __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u16* lds, uint32_t* s_xoff,
                                                int* s_drow, const GemmSplit sp, int unit, int ksi) {
   constexpr int NT = 256 * WK;   // threads
@@ -238,7 +250,7 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
   const int m_tiles = (n_rows + TT - 1) / TT;
   const int nk_all = g.K / BK;
   const int nt = unit / m_tiles, mt = unit % m_tiles;
-  const int m0 = mt * TT, n0 = nt * TP;
+  const int m0 = mt * TT, n0 = nt * TPV;
   const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, wk = tid >> 8;
   const int nk = nk_all / sp.ks;        // k-steps of this split
   const int kbase = ksi * nk;           // first k-step of this split
@@ -271,11 +283,15 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
   // The larger tilings keep one order, so that tiles running together share
   // each weight and row slice while it is in L2.
   const int krot = TP == 64 ? ((int)blockIdx.x >> 3) % nk : 0;
+  // weight rows past TPV: an offset past the resource's end reads zeros
+  uint32_t wvoff[CW];
+#pragma unroll
+  for (int j = 0; j < CW; ++j) wvoff[j] = (TPV == TP || r0 + RPJ * j < TPV) ? woff : 0x80000000u;
   auto gload = [&](int j, int kstep) -> u32x4 {
     int kp = kstep + krot;
     kp -= kp >= nk ? nk : 0;
     const uint32_t ko = (uint32_t)(kbase + kp) * (BK * 2);
-    if (j < CW) return buffer_load16(rW, woff, ko + (uint32_t)j * wstride);
+    if (j < CW) return buffer_load16(rW, wvoff[j], ko + (uint32_t)j * wstride);
     return buffer_load16(rX, xoff[j - CW], ko);
   };
 
@@ -379,7 +395,7 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
     }
     return;
   }
-  gemm_epilogue<TP, TT, WP, WT, EPI>(g, acc, m0, n0, nt, s_drow);
+  gemm_epilogue<TP, TT, WP, WT, EPI, TPV>(g, acc, m0, n0, nt, s_drow);
 }
 
 // GATE: 0 = always run; 1 = run only when the device row count is <= kSkinnyRows;
@@ -400,8 +416,9 @@ __global__ __launch_bounds__(256 * WK) void gemm_bf16_kernel(GemmArgs g) {
 // tiling, so no second launch has to start just to exit.  Both bodies share
 // one LDS allocation sized for the larger of the two.
 template <int TP, int TT, int BK, int PF, int SB, int ST, int TP2, int TT2, int BK2, int PF2, int SB2,
-          int ST2, int EPI, int AMODE>
+          int ST2, int EPI, int AMODE, int TPV1>
 __global__ __launch_bounds__(256) void gemm_dual_kernel(GemmArgs g) {
+  // TPV1: weight rows per tile of the weight-streaming body (see gemm_tile_body)
   constexpr int L1 = gemm_lds_u16(TP, TT, BK), L2 = gemm_lds_u16(TP2, TT2, BK2);
   constexpr int TTM = TT > TT2 ? TT : TT2;
   __shared__ __attribute__((aligned(16))) u16 lds[L1 > L2 ? L1 : L2];
@@ -409,7 +426,7 @@ __global__ __launch_bounds__(256) void gemm_dual_kernel(GemmArgs g) {
   __shared__ int s_drow[TTM];
   const int n_rows = min(g.offsets[g.B], g.max_rows);
   if (n_rows <= kSkinnyRows)
-    gemm_tile_body<TP, TT, 2, 2, BK, PF, EPI, AMODE, SB, ST>(g, n_rows, lds, s_xoff, s_drow);
+    gemm_tile_body<TP, TT, 2, 2, BK, PF, EPI, AMODE, SB, ST, 1, TPV1>(g, n_rows, lds, s_xoff, s_drow);
   else
     gemm_tile_body<TP2, TT2, 2, 2, BK2, PF2, EPI, AMODE, SB2, ST2>(g, n_rows, lds, s_xoff, s_drow);
 }
@@ -594,8 +611,6 @@ static int persistent_grid(int items, int TP, int TT) {
 
 template <int TP, int TT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST, int WK = 1>
 static void launch_bf16(const GemmArgs& g, hipStream_t st) {
-  // one workgroup per possible output tile, and at least enough for the
-  // split the device may choose when the real selection turns out short
   // every output tile (and every split the device may choose when the real
   // selection turns out short) is a work item; the two-k-half tiling runs one
   // item per workgroup, the others loop over a resident grid
@@ -630,10 +645,16 @@ template <int BK1, int PF1, int TP2, int TT2, int PF2, int SB2, int ST2, int EPI
 static void launch_dual(const GemmArgs& g, hipStream_t st) {
   int items2 = (g.N / TP2) * ((g.max_rows + TT2 - 1) / TT2);
   if (SB2 > 0 && items2 < kSplitCap) items2 = kSplitCap;
-  const int grid1 = persistent_grid(g.N / 64, 64, 128), grid2 = persistent_grid(items2, TP2, TT2);
+  // 48 weight rows per weight-streaming tile when they divide N (every CU gets a tile)
+  const bool t48 = g.N % 48 == 0;
+  const int grid1 = persistent_grid(g.N / (t48 ? 48 : 64), 64, 128), grid2 = persistent_grid(items2, TP2, TT2);
   const int grid = grid1 > grid2 ? grid1 : grid2;
-  hipLaunchKernelGGL((gemm_dual_kernel<64, 128, BK1, PF1, 0, 0, TP2, TT2, 64, PF2, SB2, ST2, EPI, AMODE>),
-                     dim3(grid), dim3(256), 0, st, g);
+  if (t48)
+    hipLaunchKernelGGL((gemm_dual_kernel<64, 128, BK1, PF1, 0, 0, TP2, TT2, 64, PF2, SB2, ST2, EPI, AMODE, 48>),
+                       dim3(grid), dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_dual_kernel<64, 128, BK1, PF1, 0, 0, TP2, TT2, 64, PF2, SB2, ST2, EPI, AMODE, 64>),
+                       dim3(grid), dim3(256), 0, st, g);
   if (SB2 > 0) launch_reduce<TP2, TT2, 2, 2, 64, PF2, EPI, AMODE, 2, SB2, ST2>(g, st);
 }
 
