@@ -274,7 +274,7 @@ def main():
         "measured_ceilings": ceilings,
         "step_gpu_ms": step_ms,
         "stage_timing": f"one HIP graph of {kreps} back-to-back calls per stage, replayed for ~30 ms, then 3 replays between two HIP events",
-        "roofline": {"kernel": "gemm_dual_kernel, 64x128 weight-streaming body (gathered QKV + K/V scatter)", "bound": "hbm",
+        "roofline": {"kernel": "gemm_dual_kernel, weight-streaming body: 48 weight rows x 128 tokens per tile (gathered QKV + K/V scatter)", "bound": "hbm",
                      "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM, "traffic": traffic,
                      "algorithmic_bytes": qkv_bytes,
