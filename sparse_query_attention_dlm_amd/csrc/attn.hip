@@ -56,7 +56,7 @@ constexpr int kSplitTarget = 512;
 constexpr int kPartRows = 2 * kSplitTarget * 128;
 constexpr int kAttnKT = 64;      // keys per K/V tile
 constexpr int kMinSplitKeys = 256;  // keys per split at least
-constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag
+constexpr float kLaneSumCap = 0x1p64f;  // a lane's tile sum above this: rescale
 constexpr int kMergeGrid = 1024; // workgroups of the merge pass (grid-stride)
 
 struct AttnPlan {
@@ -314,26 +314,42 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
           if (key >= nvalid) sacc[kb][i] = -INFINITY;
         }
     }
-    // tile max: four independent partial maxima (short dependency chains)
-    float mq[4];
+    // Exponentials against the running reference m_run (log2 units), checked
+    // afterwards.  fp32 sums and bf16 P keep the same relative precision at
+    // any magnitude, so the reference only has to keep the numbers finite:
+    // while a lane's tile sum stays <= kLaneSumCap every probability of the
+    // tile is <= 2^64, and O and l stay far from the fp32 range even summed
+    // over the whole sequence.  Otherwise (every split's first tile, where
+    // m_run = -inf and the sums are inf or NaN, or a score far above the
+    // reference) the wave takes the exact tile max, rescales O and l and redoes
+    // the exponentials.  No max is computed on the common path.
+    float p[2][16];
+    auto tile_exp = [&]() {
+      float lq[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums (short dependency chains)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mq[j] = fmaxf(sacc[j >> 1][8 * (j & 1)], sacc[j >> 1][8 * (j & 1) + 1]);
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < 16; ++i) {
+          p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_run));
+          lq[i & 3] += p[kb][i];
+        }
+      return (lq[0] + lq[1]) + (lq[2] + lq[3]);
+    };
+    float lt = tile_exp();
+    if (__any(!(lt <= kLaneSumCap))) {
+      // tile max: four independent partial maxima (short dependency chains),
+      // then the lane pair that holds the other half of the query's keys
+      float mq[4];
 #pragma unroll
-      for (int i = 2; i < 8; ++i) mq[j] = fmaxf(mq[j], sacc[j >> 1][8 * (j & 1) + i]);
-    float mt = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-    mt = pair_max(mt);
-    // Lazy rescaling: the reference max m_run (log2 units) moves only when a
-    // tile's max exceeds it by more than kRescaleSlack.  Until then every
-    // probability exp2(s*c - m_run) stays <= 2^kRescaleSlack, which fp32 sums
-    // and bf16 P carry with the same relative precision, and the normalised
-    // output and the LSE are unchanged; the rescale of O (64 multiplies) is
-    // then skipped by the whole wave.  The first tile of a split always holds
-    // a valid key, so m_run leaves -inf there (alpha = 0 on the empty sums).
-    const bool move = mt * c > m_run + kRescaleSlack;
-    if (__any(move)) {
-      const float m_new = move ? mt * c : m_run;
+      for (int j = 0; j < 4; ++j) mq[j] = fmaxf(sacc[j >> 1][8 * (j & 1)], sacc[j >> 1][8 * (j & 1) + 1]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 2; i < 8; ++i) mq[j] = fmaxf(mq[j], sacc[j >> 1][8 * (j & 1) + i]);
+      const float mt = pair_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
+      // the first tile of a split always holds a valid key, so m_run leaves
+      // -inf there (alpha = 0 on the empty sums)
+      const float m_new = fmaxf(m_run, mt * c);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -341,17 +357,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[d][i] *= alpha;
       m_run = m_new;
+      lt = tile_exp();
     }
-    float p[2][16];
-    float lq[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums (short dependency chains)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_run));
-        lq[i & 3] += p[kb][i];
-      }
-    l_run += (lq[0] + lq[1]) + (lq[2] + lq[3]);
+    l_run += lt;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) attn_pv_block<HD>(sV, 32 * kb, p[kb], acc, lane);
   };

@@ -286,20 +286,29 @@ def test_loose_row_bound_picks_every_tiling(dlm):
             assert v_ <= TOL["bf16"], f"n={n} {k_}: {v_}"
 
 
-def run_attention_plan(dlm, B, S, Hq, Hkv, hd, rows_per_b, sample=None, seed=21):
+def run_attention_plan(dlm, B, S, Hq, Hkv, hd, rows_per_b, sample=None, seed=21, late_keys=None):
     """Partial attention on given q/k/v (bf16) against the oracle; with
     `sample`, only that many selected rows (spread over the batch rows) are
-    recomputed by the oracle, over all S keys."""
+    recomputed by the oracle, over all S keys.  `late_keys` (positions): those
+    keys are set to 200 times a unit direction u and every query gets +3 u,
+    so their scaled scores exceed the early keys' by ~75 in log2 units."""
     rng = np.random.default_rng(seed)
     scale = 1.0 / math.sqrt(hd)
-    kc = W.round_bf16(rng.standard_normal((B, S, Hkv, hd)))
+    kc = rng.standard_normal((B, S, Hkv, hd))
+    u = np.ones(hd) / math.sqrt(hd)
+    if late_keys is not None:
+        kc[:, late_keys] = 200.0 * u
+    kc = W.round_bf16(kc)
     vc = W.round_bf16(rng.standard_normal((B, S, Hkv, hd)))
     sc = np.ones((B, S))
     for b in range(B):
         sc[b, rng.choice(S, rows_per_b[b], replace=False)] = 0.0
     ridx, _, roff = O.compact(sc, 0, S, 0.5)
     n = int(roff[-1])
-    q = W.round_bf16(rng.standard_normal((n, Hq, hd)))
+    q = rng.standard_normal((n, Hq, hd))
+    if late_keys is not None:
+        q = q + 3.0 * u
+    q = W.round_bf16(q)
     say(f"[attention plan] B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} n={n} sample={sample}")
     o = torch.zeros(n, Hq, hd, dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros(n, Hq, dtype=torch.float32, device="cuda")
@@ -334,6 +343,17 @@ def test_attention_few_tiles_split_keys(dlm, hd):
     (more than 8, the merge's second register layout) and the LSE merge pass;
     every row against the oracle."""
     run_attention_plan(dlm, B=2, S=4200, Hq=4, Hkv=2, hd=hd, rows_per_b=[37, 5])
+
+
+@pytest.mark.parametrize("rows_per_b", [[40, 17], [2048, 1900]])
+def test_attention_rescale_on_late_large_scores(dlm, rows_per_b):
+    """Keys far above every earlier score appear after the first tiles (and in
+    a later split): the running reference must move mid-sequence (a lane's
+    tile sum of probabilities against the old reference would pass 2^64).
+    Short selections take the split-KV path, long ones the unsplit wide
+    tiles; outputs and LSE against the oracle."""
+    run_attention_plan(dlm, B=2, S=2048, Hq=8, Hkv=4, hd=128, rows_per_b=rows_per_b, sample=64,
+                       late_keys=[700, 701, 1500, 2040])
 
 
 def test_attention_short_sequence(dlm):
