@@ -179,25 +179,16 @@ __device__ __forceinline__ void attn_store_lse(const AttnArgs& a, const AttnPlan
 
 // Multiply P^T into O^T for one 32-key block whose first LDS row is kb0:
 // O^T[d] += V^T(32 d x 16 keys) . P^T(16 keys x 32 queries), two 16-key chunks.
-// P^T register i of the block is key 8(i/4) + 4*lg + i%4; the V^T operand is
-// read with ds_read_b64_tr_b16 in the matching key-slot order: k-slots
-// 8*ga+0..3 <-> keys 16cc+4ga+0..3, slots 8*ga+4..7 <-> keys 16cc+8+4ga+0..3.
+// pw[cc] holds the block's probabilities as bf16 pairs, word j of chunk cc =
+// registers 8cc + 2j and 8cc + 2j + 1; register i of the block is key
+// 8(i/4) + 4*lg + i%4.  The V^T operand is read with ds_read_b64_tr_b16 in the
+// matching key-slot order: k-slots 8*ga+0..3 <-> keys 16cc+4ga+0..3, slots
+// 8*ga+4..7 <-> keys 16cc+8+4ga+0..3.
 template <int HD>
-__device__ __forceinline__ void attn_pv_block(const u16* sV, int kb0, const float (&p)[16],
+__device__ __forceinline__ void attn_pv_block(const u16* sV, int kb0, const u32x4 (&pw)[2],
                                               f32x16 (&acc)[HD / 32], int lane) {
   constexpr int PITCH = AttnLds<HD>::VPITCH, NDB = HD / 32;
   const int g16 = lane >> 4, j16 = lane & 15, ga = g16 >> 1;
-  bf16x8 pb[2];
-  {
-    u32x4 w0, w1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w0[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
-      w1[j] = pack_bf16x2(p[8 + 2 * j], p[8 + 2 * j + 1]);
-    }
-    pb[0] = as_bf16x8(w0);
-    pb[1] = as_bf16x8(w1);
-  }
 #pragma unroll
   for (int d = 0; d < NDB; ++d) {
     const int m0 = 32 * d + 16 * (g16 & 1);
@@ -207,7 +198,7 @@ __device__ __forceinline__ void attn_pv_block(const u16* sV, int kb0, const floa
       const i16x4 va = lds_read_tr16(pa);
       const i16x4 vb = lds_read_tr16(pa + 8 * PITCH);
       const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[d] = mfma32x32x16(av, pb[cc], acc[d]);
+      acc[d] = mfma32x32x16(av, as_bf16x8(pw[cc]), acc[d]);
     }
   }
 }
@@ -323,15 +314,23 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
     // m_run = -inf and the sums are inf or NaN, or a score far above the
     // reference) the wave takes the exact tile max, rescales O and l and redoes
     // the exponentials.  No max is computed on the common path.
-    float p[2][16];
+    // The probabilities are rounded to bf16 pairs as they are produced (the
+    // P.V operand), and the lane sum adds those pairs with v_dot2_f32_bf16
+    // against (1, 1): 16 instructions for 32 values instead of 32 adds, and
+    // the sum holds exactly the weights that P.V applies.
+    u32x4 pw[2][2];
     auto tile_exp = [&]() {
+      const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
       float lq[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums (short dependency chains)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -m_run));
-          lq[i & 3] += p[kb][i];
+        for (int j = 0; j < 8; ++j) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][2 * j], c, -m_run));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][2 * j + 1], c, -m_run));
+          const uint32_t w = pack_bf16x2(e0, e1);
+          pw[kb][j >> 2][j & 3] = w;
+          lq[j & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, lq[j & 3], false);
         }
       return (lq[0] + lq[1]) + (lq[2] + lq[3]);
     };
@@ -361,7 +360,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
     }
     l_run += lt;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) attn_pv_block<HD>(sV, 32 * kb, p[kb], acc, lane);
+    for (int kb = 0; kb < 2; ++kb) attn_pv_block<HD>(sV, 32 * kb, pw[kb], acc, lane);
   };
 
   if (kbeg < kend) load_tile(kbeg);
