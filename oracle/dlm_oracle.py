@@ -191,6 +191,68 @@ def output_scatter(o_sel, idx, offsets, out_cache, w_o=None):
     return out
 
 
+def gather_rows(src, idx, offsets):
+    """Rows src[b, idx[r]] of every selected r, packed (row r of batch row b):
+    how a caller keeps the salient rows' K/V from before this step's scatter."""
+    s = np.asarray(src)
+    out = np.zeros((int(offsets[-1]),) + s.shape[2:], dtype=s.dtype)
+    for b in range(s.shape[0]):
+        out[offsets[b]:offsets[b + 1]] = s[b, rows_of(idx, offsets, b)]
+    return out
+
+
+def scatter_rows(rows, idx, offsets, dst):
+    """dst with dst[b, idx[r]] = rows[r] for every selected r; other rows kept."""
+    out = np.array(dst, copy=True)
+    for b in range(out.shape[0]):
+        out[b, rows_of(idx, offsets, b)] = np.asarray(rows)[offsets[b]:offsets[b + 1]]
+    return out
+
+
+def nonsalient_dv_update(q_cache, lse_cache, idx, offsets, k_old, v_old, v_cache, o_cache, Hq,
+                         Hkv, scale):
+    """[DyLLM] Methodologie 2, non-salient path: for a stable token the
+    attention weights are taken as unchanged (their change is neglected), and
+    its output moves only by the change of the salient tokens' values, weighted
+    by its existing attention weights:
+
+        o_i <- o_i + sum_{j in A} P_ij (v_j^new - v_j^old)
+
+    Reading (the page names no formula for the weights): P_ij is token i's
+    softmax weight on key j as of its last computation, exp(scale q_i . k_j^old
+    - lse_i), from its cached query q_i, its cached natural-log LSE lse_i and
+    key j's K row from before this step's scatter.
+
+    q_cache [B,S,Hq,hd] and lse_cache [B,S,Hq]: each position's query and LSE
+    as last computed; idx/offsets: the salient set A; k_old, v_old [n,Hkv,hd]:
+    the salient rows' K/V before this step's scatter (row r = idx[r]);
+    v_cache [B,S,Hkv,hd] after it; o_cache [B,S,Hq,hd] the per-head context
+    cache.  Returns the updated context cache: salient rows are left as given
+    (their outputs come from the salient path), every other row gets the
+    update.  Query head h reads KV head h // (Hq // Hkv)."""
+    q = np.asarray(q_cache, dtype=f64)
+    lse = np.asarray(lse_cache, dtype=f64)
+    ko = np.asarray(k_old, dtype=f64)
+    vo = np.asarray(v_old, dtype=f64)
+    vc = np.asarray(v_cache, dtype=f64)
+    out = np.array(o_cache, dtype=f64, copy=True)
+    B, S = q.shape[0], q.shape[1]
+    G = Hq // Hkv
+    for b in range(B):
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        if r1 == r0:
+            continue
+        sal = rows_of(idx, offsets, b)
+        stable = np.setdiff1d(np.arange(S), sal)
+        for h in range(Hq):
+            g = h // G
+            s = scale * (q[b, stable, h, :] @ ko[r0:r1, g, :].T)     # [N - n_b, n_b]
+            p = np.exp(s - lse[b, stable, h][:, None])
+            dv = vc[b, sal, g, :] - vo[r0:r1, g, :]                  # [n_b, hd]
+            out[b, stable, h, :] += p @ dv
+    return out
+
+
 # --------------------------------------------------------------------------
 # (4') attention column sums and the top-k decode order
 # --------------------------------------------------------------------------

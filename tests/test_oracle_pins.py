@@ -305,6 +305,107 @@ def _attn_inputs(B, S, nq, Hq, Hkv, hd, seed):
     return q, kc, vc, idx, offsets
 
 
+def _dv_case(seed, B=2, S=7, Hq=4, Hkv=2, hd=3, sal=((1, 4), (0, 2, 6))):
+    """Previous step: every position computed exactly (pure-Python softmax over
+    the old K/V).  This step: the salient rows A get new K and new V."""
+    rng = np.random.default_rng(seed)
+    k_old_c, v_old_c = rng.standard_normal((2, B, S, Hkv, hd))
+    q = rng.standard_normal((B, S, Hq, hd))
+    scale = 0.7
+    G = Hq // Hkv
+    o = np.zeros((B, S, Hq, hd))
+    lse = np.zeros((B, S, Hq))
+    for b in range(B):
+        for i in range(S):
+            for h in range(Hq):
+                ob, lb = bf_attention_row(to_list(q[b, i, h]), to_list(k_old_c[b, :, h // G]),
+                                          to_list(v_old_c[b, :, h // G]), scale)
+                o[b, i, h], lse[b, i, h] = ob, lb
+    idx = np.concatenate([np.array(a, np.int32) for a in sal])
+    offsets = np.concatenate([[0], np.cumsum([len(a) for a in sal])]).astype(np.int32)
+    k_new_c, v_new_c = k_old_c.copy(), v_old_c.copy()
+    for b in range(B):
+        for i in sal[b]:
+            k_new_c[b, i] = rng.standard_normal((Hkv, hd))
+            v_new_c[b, i] = rng.standard_normal((Hkv, hd))
+    k_old = O.gather_rows(k_old_c, idx, offsets)
+    v_old = O.gather_rows(v_old_c, idx, offsets)
+    return dict(q=q, lse=lse, o=o, idx=idx, offsets=offsets, k_old=k_old, v_old=v_old, k_old_c=k_old_c,
+                v_new_c=v_new_c, k_new_c=k_new_c, scale=scale, Hq=Hq, Hkv=Hkv, sal=sal)
+
+
+def _dv(c, v_cache=None, idx=None, offsets=None, k_old=None, v_old=None):
+    return O.nonsalient_dv_update(c["q"], c["lse"], c["idx"] if idx is None else idx,
+                                  c["offsets"] if offsets is None else offsets,
+                                  c["k_old"] if k_old is None else k_old,
+                                  c["v_old"] if v_old is None else v_old,
+                                  c["v_new_c"] if v_cache is None else v_cache, c["o"], c["Hq"], c["Hkv"],
+                                  c["scale"])
+
+
+def test_dv_update_equals_old_weights_on_new_values():
+    """With its existing weights (the old keys' softmax) held fixed, a stable
+    row's exact output on the new values is sum_j P_old(j) v_new(j) over all
+    keys; the update reaches exactly that, although the salient rows' K changed
+    too (pure-Python softmax per row).  Salient rows are left as given."""
+    c = _dv_case(12)
+    out = _dv(c)
+    G = c["Hq"] // c["Hkv"]
+    for b, sal in enumerate(c["sal"]):
+        for i in range(out.shape[1]):
+            for h in range(c["Hq"]):
+                if i in sal:
+                    assert np.array_equal(out[b, i, h], c["o"][b, i, h])
+                    continue
+                ref, _ = bf_attention_row(to_list(c["q"][b, i, h]), to_list(c["k_old_c"][b, :, h // G]),
+                                          to_list(c["v_new_c"][b, :, h // G]), c["scale"])
+                assert np.allclose(out[b, i, h], ref, atol=1e-12)
+    # the new keys are not what the weights use: with them the result differs
+    k_new = O.gather_rows(c["k_new_c"], c["idx"], c["offsets"])
+    assert not np.allclose(_dv(c, k_old=k_new), out, atol=1e-6)
+
+
+def test_dv_update_invariants():
+    c = _dv_case(13)
+    # unchanged values: nothing moves, whatever the keys did
+    v_same = O.scatter_rows(c["v_old"], c["idx"], c["offsets"], c["v_new_c"])
+    assert np.allclose(_dv(c, v_cache=v_same), c["o"], atol=1e-15)
+    # empty salient set: nothing moves
+    e = np.zeros(0, np.int32)
+    assert np.array_equal(_dv(c, idx=e, offsets=np.zeros(3, np.int32), k_old=np.zeros((0, 2, 3)),
+                              v_old=np.zeros((0, 2, 3))), c["o"])
+    # linear in the value change: two halves of the change add up
+    v_half = O.scatter_rows(0.5 * (O.gather_rows(c["v_new_c"], c["idx"], c["offsets"]) + c["v_old"]),
+                            c["idx"], c["offsets"], c["v_new_c"])
+    d_full = _dv(c) - c["o"]
+    d_half = _dv(c, v_cache=v_half) - c["o"]
+    assert np.allclose(d_full, 2 * d_half, atol=1e-12)
+    # GQA head map: a change on KV head 1 only moves query heads 2 and 3
+    v1 = v_same.copy()
+    for b, sal in enumerate(c["sal"]):
+        v1[b, list(sal), 1] += 1.0
+    d = _dv(c, v_cache=v1) - c["o"]
+    assert np.array_equal(d[:, :, :2], np.zeros_like(d[:, :, :2])) and np.abs(d[:, :, 2:]).max() > 1e-3
+
+
+def test_gather_scatter_rows_brute_force():
+    rng = np.random.default_rng(14)
+    B, S, W = 3, 6, 5
+    src = rng.standard_normal((B, S, W))
+    idx = np.array([5, 0, 2, 3], np.int32)
+    offsets = np.array([0, 1, 1, 4], np.int32)
+    g = O.gather_rows(src, idx, offsets)
+    assert g.shape == (4, W)
+    for r, (b, i) in enumerate([(0, 5), (2, 0), (2, 2), (2, 3)]):
+        assert to_list(g[r]) == to_list(src[b, i])
+    dst = rng.standard_normal((B, S, W))
+    out = O.scatter_rows(g, idx, offsets, dst)
+    for b in range(B):
+        for i in range(S):
+            want = src[b, i] if (b, i) in [(0, 5), (2, 0), (2, 2), (2, 3)] else dst[b, i]
+            assert to_list(out[b, i]) == to_list(want)
+
+
 def test_colsum_sum_invariant_and_library_softmax():
     B, S, nq, Hq, Hkv, hd = 2, 11, 6, 4, 2, 3
     q, kc, vc, idx, offsets = _attn_inputs(B, S, nq, Hq, Hkv, hd, 13)
