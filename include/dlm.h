@@ -13,6 +13,8 @@
  *                                                       -> dlm_partial_attn
  *      optional: per-key attention column sums + top-k  -> dlm_attn_colsum
  *      optional: longest-stable-prefix commit           -> dlm_stable_prefix
+ *      optional: value-change update of the stable rows -> dlm_nonsalient_dv_update
+ *                (caches kept with dlm_gather_rows / dlm_scatter_rows)
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
@@ -225,6 +227,64 @@ int dlm_attn_colsum(int dtype, const void* q_sel, const int32_t* offsets, int ma
 int dlm_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
                       int gen_lo, int gen_hi, int32_t* ring, int W, int step,
                       float conf_threshold, int min_commit, int32_t* committed, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dlm_nonsalient_dv_update
+ *
+ * Value-change update of the stable rows' cached attention outputs.  Follows:
+ * "DyLLM: Efficient Diffusion LLM Inference via Saliency-based Token
+ * Selection and Partial Attention", Methodologie 2, non-salient path (the
+ * stable tokens' attention weights are taken as unchanged; their outputs move
+ * by the salient tokens' value change times those weights, cost O(N |A|)).
+ *
+ * For every b, every position i not in the salient set A_b (idx/offsets) and
+ * every query head h, with g = h / (Hq/Hkv):
+ *   o_cache[b,i,h] += sum_{r in A_b} exp(scale * q_cache[b,i,h] . k_old[r,g]
+ *                                        - lse_cache[b,i,h])
+ *                                    * (v_cache[b,idx[r],g] - v_old[r,g])
+ * The weights are token i's softmax weights of its last computation: its
+ * cached query, its cached natural-log LSE and the salient rows' K from
+ * before this step's scatter.  Rows in A_b are not touched (dlm_partial_attn
+ * writes them).
+ *   q_cache   [B,S,Hq,hd]   dtype   queries as last computed per position
+ *   lse_cache [B,S,Hq]      f32     their LSE (dlm_partial_attn's lse,
+ *                                   scattered with dlm_scatter_rows)
+ *   k_old, v_old [max_rows,Hkv,hd] dtype  salient rows' K/V before this
+ *                                   step's dlm_gather_qkv_scatter_kv
+ *                                   (dlm_gather_rows of the caches)
+ *   v_cache   [B,S,Hkv,hd]  dtype   V cache after that scatter
+ *   o_cache   [B,S,Hq,hd]   dtype   per-head context cache, updated in place
+ *                                   (the out_cache of dlm_partial_attn
+ *                                   without W_o); bf16 adds in float32 and
+ *                                   rounds once.
+ * hd in {64,128}; Hq/Hkv must divide 128.  bf16 rounds the weights and the
+ * value change to bf16 for the matrix cores (float32 accumulation).
+ * ------------------------------------------------------------------------ */
+int dlm_nonsalient_dv_update(int dtype, const void* q_cache, const float* lse_cache,
+                             const int32_t* idx, const int32_t* offsets, int max_rows,
+                             const void* k_old, const void* v_old, const void* v_cache,
+                             int B, int S, int Hq, int Hkv, int hd, float scale,
+                             void* o_cache, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dlm_gather_rows / dlm_scatter_rows
+ *
+ * Row copies between a per-position cache [B,S,row_bytes] and the packed
+ * rows of a selection [max_rows,row_bytes] (row r <-> cache row (b, idx[r])).
+ * They keep the caches of the non-salient update: the salient rows' K/V
+ * before the step's scatter (gather), and the recomputed rows' queries and
+ * LSE (scatter).  Follows: "DyLLM ...", Methodologie 1 (recomputed tokens
+ * replace their cached activations; all others keep theirs).
+ *   gather:  rows[r] = cache[b, idx[r]]     scatter: cache[b, idx[r]] = rows[r]
+ * row_bytes a positive multiple of 4 (both pointers 4-byte aligned, 16-byte
+ * aligned when row_bytes is a multiple of 16).  Other cache rows are not
+ * touched.
+ * ------------------------------------------------------------------------ */
+int dlm_gather_rows(const void* cache, int B, int S, int row_bytes,
+                    const int32_t* idx, const int32_t* offsets, int max_rows,
+                    void* rows, void* stream);
+int dlm_scatter_rows(const void* rows, const int32_t* idx, const int32_t* offsets,
+                     int max_rows, int B, int S, int row_bytes, void* cache, void* stream);
 
 /* ------------------------------------------------------------------------
  * dlm_probe_mfma_bf16  (measurement aid, not a step of the method)

@@ -65,6 +65,13 @@ lib.dlm_stable_prefix.restype = _I
 lib.dlm_stable_prefix.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _I, _F, _I, _P, _P]
 lib.dlm_probe_mfma_bf16.restype = _I
 lib.dlm_probe_mfma_bf16.argtypes = [_I, _I, _P, _P]
+lib.dlm_nonsalient_dv_update.restype = _I
+lib.dlm_nonsalient_dv_update.argtypes = [_I, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P,
+                                         _P]
+lib.dlm_gather_rows.restype = _I
+lib.dlm_gather_rows.argtypes = [_P, _I, _I, _I, _P, _P, _I, _P, _P]
+lib.dlm_scatter_rows.restype = _I
+lib.dlm_scatter_rows.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P]
 
 
 def version() -> str:
@@ -205,6 +212,39 @@ def dlm_stable_prefix(argmax, maxprob, gen_lo, gen_hi, ring, step, conf_threshol
         int(gen_lo), int(gen_hi), _ptr(ring, "ring", torch.int32), W, int(step),
         float(conf_threshold), int(min_commit), _ptr(committed, "committed", torch.int32),
         _stream(stream))
+    _check(rc)
+
+
+def dlm_nonsalient_dv_update(q_cache, lse_cache, idx, offsets, max_rows, k_old, v_old, v_cache, scale,
+                             o_cache, stream=None):
+    B, S, Hq, hd = q_cache.shape
+    Hkv = v_cache.shape[2]
+    dt = q_cache.dtype
+    rc = lib.dlm_nonsalient_dv_update(
+        _dt(q_cache), _ptr(q_cache, "q_cache"), _ptr(lse_cache, "lse_cache", torch.float32),
+        _ptr(idx, "idx", torch.int32, False), _ptr(offsets, "offsets", torch.int32, False), int(max_rows),
+        _ptr(k_old, "k_old", dt, False), _ptr(v_old, "v_old", dt, False), _ptr(v_cache, "v_cache", dt),
+        B, S, Hq, Hkv, hd, float(scale), _ptr(o_cache, "o_cache", dt), _stream(stream))
+    _check(rc)
+
+
+def dlm_gather_rows(cache, idx, offsets, max_rows, rows, stream=None):
+    """rows[r] = cache[b, idx[r]] for cache [B, S, ...] and rows [max_rows, ...]."""
+    B, S = cache.shape[0], cache.shape[1]
+    row_bytes = cache[0, 0].numel() * cache.element_size()
+    rc = lib.dlm_gather_rows(_ptr(cache, "cache"), B, S, row_bytes, _ptr(idx, "idx", torch.int32, False),
+                             _ptr(offsets, "offsets", torch.int32, False), int(max_rows),
+                             _ptr(rows, "rows", cache.dtype, False), _stream(stream))
+    _check(rc)
+
+
+def dlm_scatter_rows(rows, idx, offsets, max_rows, cache, stream=None):
+    """cache[b, idx[r]] = rows[r] for cache [B, S, ...] and rows [max_rows, ...]."""
+    B, S = cache.shape[0], cache.shape[1]
+    row_bytes = cache[0, 0].numel() * cache.element_size()
+    rc = lib.dlm_scatter_rows(_ptr(rows, "rows", cache.dtype, False), _ptr(idx, "idx", torch.int32, False),
+                              _ptr(offsets, "offsets", torch.int32, False), int(max_rows), B, S, row_bytes,
+                              _ptr(cache, "cache"), _stream(stream))
     _check(rc)
 
 

@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libdlm.so")
-SOURCES = ["select.hip", "gemm.hip", "attn.hip", "colsum.hip", "prefix.hip", "probe.hip", "dlm_abi.hip"]
+SOURCES = ["select.hip", "gemm.hip", "attn.hip", "colsum.hip", "dv.hip", "prefix.hip", "probe.hip",
+           "dlm_abi.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -375,6 +375,88 @@ int dlm_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
 }
 
 // ---------------------------------------------------------------------------
+static int row_copy(const void* src, void* dst, const int32_t* idx, const int32_t* offsets,
+                    int max_rows, int B, int S, int row_bytes, int scatter, void* stream) {
+  REQUIRE(B > 0 && S > 0, "B and S must be positive");
+  REQUIRE(row_bytes > 0 && row_bytes % 4 == 0, "row_bytes=%d must be a positive multiple of 4",
+          row_bytes);
+  REQUIRE(max_rows >= 0 && (long long)max_rows <= (long long)B * S, "max_rows=%d out of range",
+          max_rows);
+  if (max_rows == 0) return DLM_OK;
+  REQUIRE_PTR(src);
+  REQUIRE_PTR(dst);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(offsets);
+  REQUIRE(((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 3u) == 0,
+          "src and dst must be 4-byte aligned");
+  if (row_bytes % 16 == 0) {
+    REQUIRE_ALIGNED(src);
+    REQUIRE_ALIGNED(dst);
+  }
+  return hip_status(dlm::launch_row_copy(src, dst, idx, offsets, max_rows, B, S, row_bytes, scatter,
+                                         static_cast<hipStream_t>(stream)),
+                    scatter ? "row scatter" : "row gather");
+}
+
+int dlm_gather_rows(const void* cache, int B, int S, int row_bytes, const int32_t* idx,
+                    const int32_t* offsets, int max_rows, void* rows, void* stream) {
+  return row_copy(cache, rows, idx, offsets, max_rows, B, S, row_bytes, 0, stream);
+}
+
+int dlm_scatter_rows(const void* rows, const int32_t* idx, const int32_t* offsets, int max_rows,
+                     int B, int S, int row_bytes, void* cache, void* stream) {
+  return row_copy(rows, cache, idx, offsets, max_rows, B, S, row_bytes, 1, stream);
+}
+
+int dlm_nonsalient_dv_update(int dtype, const void* q_cache, const float* lse_cache,
+                             const int32_t* idx, const int32_t* offsets, int max_rows,
+                             const void* k_old, const void* v_old, const void* v_cache, int B,
+                             int S, int Hq, int Hkv, int hd, float scale, void* o_cache,
+                             void* stream) {
+  REQUIRE(dtype == DLM_F32 || dtype == DLM_BF16, "unknown dtype %d", dtype);
+  REQUIRE(B > 0 && S > 0, "B and S must be positive");
+  REQUIRE(Hq > 0 && Hkv > 0 && Hq % Hkv == 0, "Hq=%d must be a positive multiple of Hkv=%d", Hq,
+          Hkv);
+  REQUIRE(128 % (Hq / Hkv) == 0, "query heads per KV head (%d) must divide 128", Hq / Hkv);
+  REQUIRE(hd == 64 || hd == 128, "head dim %d not supported (64 or 128)", hd);
+  REQUIRE(max_rows >= 0 && (long long)max_rows <= (long long)B * S, "max_rows=%d out of range",
+          max_rows);
+  REQUIRE(scale > 0.f, "scale must be positive");
+  if (max_rows == 0) return DLM_OK;  // no salient rows: nothing changes
+  REQUIRE_PTR(q_cache);
+  REQUIRE_PTR(lse_cache);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(k_old);
+  REQUIRE_PTR(v_old);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(o_cache);
+  REQUIRE_ALIGNED(q_cache);
+  REQUIRE_ALIGNED(k_old);
+  REQUIRE_ALIGNED(v_old);
+  REQUIRE_ALIGNED(v_cache);
+  REQUIRE_ALIGNED(o_cache);
+  dlm::DvArgs a{};
+  a.q = q_cache;
+  a.lse = lse_cache;
+  a.idx = idx;
+  a.offsets = offsets;
+  a.max_rows = max_rows;
+  a.k_old = k_old;
+  a.v_old = v_old;
+  a.v = v_cache;
+  a.B = B;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.hd = hd;
+  a.scale = scale;
+  a.o = o_cache;
+  return hip_status(dlm::launch_dv_update(dtype, a, static_cast<hipStream_t>(stream)),
+                    "non-salient update");
+}
+
+// ---------------------------------------------------------------------------
 int dlm_probe_mfma_bf16(int iters, int grid, float* sink, void* stream) {
   REQUIRE(iters > 0 && grid > 0, "iters=%d and grid=%d must be positive", iters, grid);
   REQUIRE_PTR(sink);

@@ -1,0 +1,300 @@
+// Non-salient rows: the value-change update of their cached attention outputs,
+// and the row gather/scatter that keeps the caches it reads.
+//
+// DyLLM, Methodologie 2 (non-salient path): for a stable token the attention
+// weights are taken as unchanged, and its output moves only by the salient
+// tokens' value change times its existing weights, at cost O(N |A|):
+//   o[b,i,h] += sum_{j in A_b} exp(scale q[b,i,h] . k_old[j,g] - lse[b,i,h])
+//                              (v[b,idx[j],g] - v_old[j,g]),   g = h / (Hq/Hkv)
+// for every position i not in A_b; salient rows are not touched (the salient
+// path recomputes them).  The weights are token i's softmax weights of its last
+// computation: its cached query and natural-log LSE and the salient rows' K
+// from before this step's scatter.
+//
+// bf16 kernel (gfx950 matrix cores), a skinny attention without a running max
+// (the cached LSE bounds every weight by about 1):
+//   * A workgroup of four waves owns 128 query vectors: consecutive positions
+//     of one sequence times the G query heads of one KV head (vector v =
+//     position * G + head-in-group); each wave owns 32.
+//   * Per 64-row tile of the salient set, K_old rows and the value change
+//     dV = v_new - v_old (rounded to bf16) are staged in LDS; S^T = K . Q^T and
+//     dO^T = dV^T . P^T run on 32x32x16 MFMAs in the layouts of the attention
+//     kernel (P^T is the B operand, dV^T comes from transposed LDS reads).
+//   * The salient positions that fall in the workgroup's own range are flagged
+//     in LDS while their rows are staged; the epilogue adds dO to the cached
+//     output of every other position.
+// fp32 kernel (small fp32 layers): one wave per (position, head), float32 FMA.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dlm {
+
+typedef __attribute__((address_space(3))) i16x4 dv_lds_i16x4;
+
+__device__ __forceinline__ i16x4 dv_read_tr16(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((dv_lds_i16x4*)(p));
+}
+
+constexpr int kDvQT = 128;  // query vectors per workgroup
+constexpr int kDvKT = 64;   // salient rows per tile
+
+// Row pitches (u16) for conflict-free LDS reads, as in the attention kernel:
+// K rows are 16-byte A-fragments read by 16 lanes on 16 consecutive rows
+// (pitch HD + 8); dV rows are read transposed by 32 lanes on 4 consecutive
+// rows (pitch HD + 32 puts consecutive rows 16 banks apart).
+template <int HD>
+struct DvLds {
+  static constexpr int KPITCH = HD + 8;
+  static constexpr int VPITCH = HD + 32;
+  static constexpr int WORDS = kDvKT * (KPITCH + VPITCH);
+};
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void dv_update_bf16_kernel(DvArgs a) {
+  constexpr int NS = HD / 16, NDB = HD / 32, CPR = HD / 8;
+  constexpr int PITCH = DvLds<HD>::KPITCH, VPITCH = DvLds<HD>::VPITCH;
+  constexpr int RPJ = 256 / CPR;        // tile rows between a thread's chunks
+  constexpr int JT = kDvKT * CPR / 256; // chunks per tensor per thread
+  __shared__ __attribute__((aligned(16))) u16 smem[DvLds<HD>::WORDS];
+  __shared__ int sflag[kDvQT];
+  u16* sK = smem;
+  u16* sV = smem + kDvKT * PITCH;
+
+  const int G = a.Hq / a.Hkv;
+  const int tiles = (a.S * G + kDvQT - 1) / kDvQT;
+  const int t = blockIdx.x % tiles;
+  const int g = (blockIdx.x / tiles) % a.Hkv;
+  const int b = blockIdx.x / (tiles * a.Hkv);
+  const int r0 = min(a.offsets[b], a.max_rows), r1 = min(a.offsets[b + 1], a.max_rows);
+  const int nb = r1 - r0;
+  if (nb <= 0) return;  // no salient rows: every output stays
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  // positions [p_lo, p_lo + kDvQT / G) belong to this workgroup
+  const int p_lo = t * kDvQT / G;
+  const int vq = t * kDvQT + wave * 32 + lr;
+  const bool qvalid = vq < a.S * G;
+  const int vqc = qvalid ? vq : a.S * G - 1;
+  const int pos = vqc / G, h = g * G + vqc % G;
+  if (tid < kDvQT) sflag[tid] = 0;
+
+  const size_t qrow = ((size_t)b * a.S + pos) * a.Hq + h;
+  bf16x8 qf[NS];
+  {
+    const u16* qp = static_cast<const u16*>(a.q) + qrow * HD + lg * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s));
+  }
+  const float c = a.scale * kLog2e;
+  const float l2 = a.lse[qrow] * kLog2e;
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) acc[d] = f32x16{};
+
+  const u16* kold = static_cast<const u16*>(a.k_old);
+  const u16* vold = static_cast<const u16*>(a.v_old);
+  const u16* vcache = static_cast<const u16*>(a.v);
+  const int ch = tid % CPR;
+  for (int k0 = 0; k0 < nb; k0 += kDvKT) {
+    // staging loads: chunk ch of tile rows tid / CPR + RPJ j (rows past the
+    // salient set give zeros)
+    u32x4 kr[JT], vn[JT], vo[JT];
+    int rpos[JT];
+#pragma unroll
+    for (int j = 0; j < JT; ++j) {
+      const int rr = k0 + tid / CPR + RPJ * j;
+      if (rr < nb) {
+        const size_t r = (size_t)(r0 + rr);
+        rpos[j] = a.idx[r0 + rr];
+        kr[j] = *reinterpret_cast<const u32x4*>(kold + (r * a.Hkv + g) * HD + ch * 8);
+        vo[j] = *reinterpret_cast<const u32x4*>(vold + (r * a.Hkv + g) * HD + ch * 8);
+        vn[j] = *reinterpret_cast<const u32x4*>(vcache + (((size_t)b * a.S + rpos[j]) * a.Hkv + g) * HD + ch * 8);
+      } else {
+        rpos[j] = -1;
+        kr[j] = vo[j] = vn[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int j = 0; j < JT; ++j) {
+      const int rl = tid / CPR + RPJ * j;
+      float fn[8], fo[8];
+      unpack8(vn[j], fn);
+      unpack8(vo[j], fo);
+      u32x4 dv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dv[e] = pack_bf16x2(fn[2 * e] - fo[2 * e], fn[2 * e + 1] - fo[2 * e + 1]);
+      *reinterpret_cast<u32x4*>(sK + rl * PITCH + ch * 8) = kr[j];
+      *reinterpret_cast<u32x4*>(sV + rl * VPITCH + ch * 8) = dv;
+      // one chunk column flags the salient positions inside this workgroup's range
+      if (ch == 0 && rpos[j] >= p_lo && rpos[j] - p_lo < kDvQT / G) sflag[rpos[j] - p_lo] = 1;
+    }
+    __syncthreads();
+
+    // S^T = K_old . Q^T for the tile's two 32-row blocks
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(sK + (32 * kb + lr) * PITCH + 16 * s + 8 * lg));
+        sacc[kb] = mfma32x32x16(kf, qf[s], sacc[kb]);
+      }
+    // weights against the cached LSE; register i of block kb is tile row
+    // 32 kb + 8 (i / 4) + 4 lg + i % 4; rows past the salient set weigh 0
+    const int nvalid = nb - k0;
+    u32x4 pw[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float e[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 2 * j + u;
+          const int key = 32 * kb + 8 * (i >> 2) + 4 * lg + (i & 3);
+          e[u] = key < nvalid ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -l2)) : 0.f;
+        }
+        pw[kb][j >> 2][j & 3] = pack_bf16x2(e[0], e[1]);
+      }
+    // dO^T += dV^T . P^T (the V^T operand read as in the attention kernel)
+    const int g16 = lane >> 4, j16 = lane & 15, ga = g16 >> 1;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        const int m0 = 32 * d + 16 * (g16 & 1);
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const u16* pa = sV + (32 * kb + 16 * cc + 4 * ga + (j16 >> 2)) * VPITCH + m0 + 4 * (j16 & 3);
+          const i16x4 va = dv_read_tr16(pa);
+          const i16x4 vb = dv_read_tr16(pa + 8 * VPITCH);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[d] = mfma32x32x16(av, as_bf16x8(pw[kb][cc]), acc[d]);
+        }
+      }
+  }
+  __syncthreads();  // the flags of every tile are in
+  if (!qvalid || sflag[pos - p_lo]) return;
+  // o += dO: register i of block d holds dimension 32 d + 8 (i / 4) + 4 lg + i % 4
+  u16* op = static_cast<u16*>(a.o) + qrow * HD;
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * d + 8 * q4 + 4 * lg;
+      u32x2 w = *reinterpret_cast<const u32x2*>(op + d0);
+      const float o0 = __uint_as_float(w[0] << 16) + acc[d][4 * q4];
+      const float o1 = __uint_as_float(w[0] & 0xFFFF0000u) + acc[d][4 * q4 + 1];
+      const float o2 = __uint_as_float(w[1] << 16) + acc[d][4 * q4 + 2];
+      const float o3 = __uint_as_float(w[1] & 0xFFFF0000u) + acc[d][4 * q4 + 3];
+      w[0] = pack_bf16x2(o0, o1);
+      w[1] = pack_bf16x2(o2, o3);
+      *reinterpret_cast<u32x2*>(op + d0) = w;
+    }
+}
+
+// fp32: one wave per (position, head); lane e-slices of the head dimension.
+template <int HD>
+__global__ __launch_bounds__(256) void dv_update_f32_kernel(DvArgs a) {
+  constexpr int E = HD / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long pr = (long long)blockIdx.x * 4 + wave;  // (b, pos, h) flattened
+  if (pr >= (long long)a.B * a.S * a.Hq) return;
+  const int h = (int)(pr % a.Hq);
+  const int pos = (int)((pr / a.Hq) % a.S);
+  const int b = (int)(pr / ((long long)a.Hq * a.S));
+  const int r0 = min(a.offsets[b], a.max_rows), r1 = min(a.offsets[b + 1], a.max_rows);
+  if (r1 <= r0) return;
+  // salient positions are left alone (idx ascending per batch row)
+  int lo = r0, hi = r1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a.idx[mid] < pos) lo = mid + 1; else hi = mid;
+  }
+  if (lo < r1 && a.idx[lo] == pos) return;
+  const int g = h / (a.Hq / a.Hkv);
+  const float* q = static_cast<const float*>(a.q) + (((size_t)b * a.S + pos) * a.Hq + h) * HD;
+  float qv[E], o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    qv[e] = q[lane + 64 * e];
+    o[e] = 0.f;
+  }
+  const float lse = a.lse[((size_t)b * a.S + pos) * a.Hq + h];
+  const float* ko = static_cast<const float*>(a.k_old);
+  const float* vo = static_cast<const float*>(a.v_old);
+  const float* vc = static_cast<const float*>(a.v);
+  for (int r = r0; r < r1; ++r) {
+    const float* kr = ko + ((size_t)r * a.Hkv + g) * HD;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) s = fmaf(qv[e], kr[lane + 64 * e], s);
+    const float p = __expf(wave_sum(s) * a.scale - lse);
+    const float* vn = vc + (((size_t)b * a.S + a.idx[r]) * a.Hkv + g) * HD;
+    const float* vr = vo + ((size_t)r * a.Hkv + g) * HD;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = fmaf(p, vn[lane + 64 * e] - vr[lane + 64 * e], o[e]);
+  }
+  float* op = static_cast<float*>(a.o) + (((size_t)b * a.S + pos) * a.Hq + h) * HD;
+#pragma unroll
+  for (int e = 0; e < E; ++e) op[lane + 64 * e] += o[e];
+}
+
+// Row gather (rows[r] = cache[b, idx[r]]) or scatter (cache[b, idx[r]] =
+// rows[r]) of row_bytes per row, one workgroup per selected row (grid-stride);
+// T is the copy unit (16 or 4 bytes).
+template <typename T>
+__global__ __launch_bounds__(256) void row_copy_kernel(const char* src, char* dst, const int32_t* idx,
+                                                       const int32_t* offsets, int max_rows, int B,
+                                                       int S, int row_bytes, int scatter) {
+  const int n = min(offsets[B], max_rows);
+  const int units = row_bytes / (int)sizeof(T);
+  for (int r = blockIdx.x; r < n; r += gridDim.x) {
+    const int b = batch_of(offsets, B, r);
+    const size_t cache_row = (size_t)b * S + idx[r];
+    const T* s = reinterpret_cast<const T*>(src + (scatter ? (size_t)r : cache_row) * row_bytes);
+    T* d = reinterpret_cast<T*>(dst + (scatter ? cache_row : (size_t)r) * row_bytes);
+    for (int u = threadIdx.x; u < units; u += 256) d[u] = s[u];
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_dv_update(int dtype, const DvArgs& a, hipStream_t st) {
+  if (a.max_rows <= 0) return hipSuccess;
+  if (dtype == 0) {
+    const long long pairs = (long long)a.B * a.S * a.Hq;
+    const int grid = (int)((pairs + 3) / 4);
+    if (a.hd == 64)
+      hipLaunchKernelGGL(dv_update_f32_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(dv_update_f32_kernel<128>, dim3(grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  const int G = a.Hq / a.Hkv;
+  const long long tiles = ((long long)a.S * G + kDvQT - 1) / kDvQT;
+  const int grid = (int)(tiles * a.Hkv * a.B);
+  if (a.hd == 64)
+    hipLaunchKernelGGL(dv_update_bf16_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(dv_update_bf16_kernel<128>, dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_copy(const void* src, void* dst, const int32_t* idx, const int32_t* offsets,
+                           int max_rows, int B, int S, int row_bytes, int scatter, hipStream_t st) {
+  if (max_rows <= 0) return hipSuccess;
+  const int grid = max_rows < 4096 ? max_rows : 4096;
+  const char* s = static_cast<const char*>(src);
+  char* d = static_cast<char*>(dst);
+  if (row_bytes % 16 == 0)
+    hipLaunchKernelGGL(row_copy_kernel<u32x4>, dim3(grid), dim3(256), 0, st, s, d, idx, offsets, max_rows,
+                       B, S, row_bytes, scatter);
+  else
+    hipLaunchKernelGGL(row_copy_kernel<uint32_t>, dim3(grid), dim3(256), 0, st, s, d, idx, offsets,
+                       max_rows, B, S, row_bytes, scatter);
+  return hipGetLastError();
+}
+
+}  // namespace dlm

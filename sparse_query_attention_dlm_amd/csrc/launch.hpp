@@ -87,6 +87,24 @@ hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, co
                          float* partial, float* colsum, int key_lo, int key_hi, int kk,
                          int32_t* topk_idx, float* topk_val, hipStream_t st);
 
+// dv.hip
+struct DvArgs {
+  const void* q;            // [B][S][Hq][hd] cached queries
+  const float* lse;         // [B][S][Hq] cached natural-log LSE
+  const int32_t* idx;       // salient positions
+  const int32_t* offsets;
+  int max_rows;
+  const void* k_old;        // [n][Hkv][hd] salient K rows before the scatter
+  const void* v_old;        // [n][Hkv][hd]
+  const void* v;            // [B][S][Hkv][hd] V cache after the scatter
+  int B, S, Hq, Hkv, hd;
+  float scale;
+  void* o;                  // [B][S][Hq][hd] context cache, updated in place
+};
+hipError_t launch_dv_update(int dtype, const DvArgs& a, hipStream_t st);
+hipError_t launch_row_copy(const void* src, void* dst, const int32_t* idx, const int32_t* offsets,
+                           int max_rows, int B, int S, int row_bytes, int scatter, hipStream_t st);
+
 // prefix.hip
 hipError_t launch_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
                                 int gen_lo, int gen_hi, int32_t* ring, int W, int step, float thr,

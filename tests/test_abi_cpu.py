@@ -186,3 +186,37 @@ def test_stable_prefix_rejections(lib):
     assert sp(hi=33) == INVALID
     assert sp(W=0) == INVALID
     assert sp(step=-1) == INVALID
+
+
+def test_dv_update_rejections(lib):
+    def dv(dtype=BF16, q=FAKE, lse=FAKE, idx=FAKE, off=FAKE, max_rows=4, ko=FAKE, vo=FAKE, v=FAKE, B=1,
+           S=64, Hq=4, Hkv=2, hd=128, scale=0.1, o=FAKE):
+        return lib.dlm_nonsalient_dv_update(dtype, p(q), p(lse), p(idx), p(off), max_rows, p(ko), p(vo), p(v),
+                                            B, S, Hq, Hkv, hd, f(scale), p(o), p(0))
+    assert dv(dtype=7) == INVALID
+    assert dv(q=0) == INVALID
+    assert dv(lse=0) == INVALID
+    assert dv(ko=0) == INVALID
+    assert dv(o=MISALIGNED) == INVALID
+    assert dv(hd=96) == INVALID
+    assert dv(Hq=6, Hkv=4) == INVALID                        # Hq not a multiple of Hkv
+    assert dv(Hq=3, Hkv=1) == INVALID                        # G = 3 must divide 128
+    assert dv(max_rows=65) == INVALID                        # more rows than B*S
+    assert dv(scale=0.0) == INVALID
+    # no salient rows: nothing to do, and the row arrays may be NULL
+    assert dv(max_rows=0, idx=0, off=0, ko=0, vo=0) == OK
+
+
+def test_row_copy_rejections(lib):
+    def g(cache=FAKE, B=2, S=8, rb=64, idx=FAKE, off=FAKE, max_rows=3, rows=FAKE):
+        return lib.dlm_gather_rows(p(cache), B, S, rb, p(idx), p(off), max_rows, p(rows), p(0))
+
+    def s(rows=FAKE, idx=FAKE, off=FAKE, max_rows=3, B=2, S=8, rb=64, cache=FAKE):
+        return lib.dlm_scatter_rows(p(rows), p(idx), p(off), max_rows, B, S, rb, p(cache), p(0))
+    for fn in (g, s):
+        assert fn(rb=6) == INVALID                           # not a multiple of 4 bytes
+        assert fn(rb=0) == INVALID
+        assert fn(idx=0) == INVALID
+        assert fn(max_rows=17) == INVALID                    # more rows than B*S
+        assert fn(max_rows=0, idx=0, off=0) == OK
+    assert g(rows=MISALIGNED) == INVALID                     # 16-byte rows need 16-byte alignment

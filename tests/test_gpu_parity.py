@@ -698,3 +698,104 @@ def test_mfma_probe_matches_closed_form(dlm):
     err = float(np.max(np.abs(got - exp[None, :]) / np.abs(exp[None, :])))
     say(f"  max relative error {err:.2e}")
     assert err <= 1e-4
+
+
+# ---------------------------------------------------------------------------
+# non-salient value-change update, and the row copies that keep its caches
+# ---------------------------------------------------------------------------
+def run_dv_update(dlm, B, S, Hq, Hkv, hd, n_per_b, dtype="bf16", seed=31):
+    """Previous step: each position's query and LSE over the old K (its last
+    computation) and a cached output.  This step: the salient rows get new V.
+    On the device the old K/V rows are gathered from the caches before the new
+    values are scattered in (both bit-exact), then the update runs; every row
+    is compared with the oracle, and salient rows must be left untouched."""
+    rng = np.random.default_rng(seed)
+    rnd = W.round_bf16 if dtype == "bf16" else (lambda a: np.asarray(a, np.float32).astype(np.float64))
+    scale = 1.0 / math.sqrt(hd)
+    G = Hq // Hkv
+    k_old_c = rnd(rng.standard_normal((B, S, Hkv, hd)))
+    v_old_c = rnd(rng.standard_normal((B, S, Hkv, hd)))
+    q = rnd(rng.standard_normal((B, S, Hq, hd)))
+    lse = np.zeros((B, S, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            s = scale * (q[b, :, h] @ k_old_c[b, :, h // G].T)
+            m = s.max(axis=1, keepdims=True)
+            lse[b, :, h] = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+    lse = lse.astype(np.float32).astype(np.float64)
+    o = rnd(0.5 * rng.standard_normal((B, S, Hq, hd)))
+    sal = [np.sort(rng.choice(S, n, replace=False)).astype(np.int32) for n in n_per_b]
+    idx = np.concatenate(sal).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(n_per_b)]).astype(np.int32)
+    v_new_c = v_old_c.copy()
+    for b in range(B):
+        v_new_c[b, sal[b]] = rnd(rng.standard_normal((len(sal[b]), Hkv, hd)))
+    n = int(offsets[-1])
+    say(f"[dv update] {dtype} B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} salient per row {list(n_per_b)}")
+    kd, vd = dev(k_old_c, dtype), dev(v_old_c, dtype)
+    k_rows = torch.zeros(max(n, 1), Hkv, hd, dtype=kd.dtype, device="cuda")
+    v_rows = torch.zeros_like(k_rows)
+    it, ot = i32(idx), i32(offsets)
+    dlm.dlm_gather_rows(kd, it, ot, n, k_rows)
+    dlm.dlm_gather_rows(vd, it, ot, n, v_rows)
+    dlm.dlm_scatter_rows(dev(O.gather_rows(v_new_c, idx, offsets), dtype), it, ot, n, vd)
+    od = dev(o, dtype)
+    dlm.dlm_nonsalient_dv_update(dev(q, dtype), dev(lse, "f32"), it, ot, n, k_rows, v_rows, vd, scale, od)
+    torch.cuda.synchronize()
+    k_old, v_old = O.gather_rows(k_old_c, idx, offsets), O.gather_rows(v_old_c, idx, offsets)
+    assert np.array_equal(host(k_rows)[:n], k_old) and np.array_equal(host(v_rows)[:n], v_old)
+    assert np.array_equal(host(vd), v_new_c)
+    ref = O.nonsalient_dv_update(q, lse, idx, offsets, k_old, v_old, v_new_c, o, Hq, Hkv, scale)
+    got = host(od)
+    for b in range(B):
+        assert np.array_equal(got[b, sal[b]], o[b, sal[b]])
+    err, moved = maxabs(got, ref), maxabs(ref, o)
+    say(f"  max |o - oracle| = {err:.2e}; largest update {moved:.2e}")
+    assert err <= TOL[dtype]
+    assert moved > 0.05
+
+
+def test_dv_update_mha_ragged_with_empty_row(dlm):
+    """MHA, d = 128; 300 positions (ragged last position tile); salient sets of
+    70 (a full and a ragged 64-row tile), none, and 13."""
+    run_dv_update(dlm, B=3, S=300, Hq=4, Hkv=4, hd=128, n_per_b=[70, 0, 13])
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 4), (8, 2)])
+def test_dv_update_gqa(dlm, Hq, Hkv):
+    """GQA 2:1 and 4:1 (two or four query heads per KV head in a position
+    tile); one salient set of exactly two tiles, one ragged."""
+    run_dv_update(dlm, B=2, S=257, Hq=Hq, Hkv=Hkv, hd=128, n_per_b=[128, 65], seed=32)
+
+
+def test_dv_update_head_dim_64(dlm):
+    run_dv_update(dlm, B=1, S=200, Hq=4, Hkv=2, hd=64, n_per_b=[37], seed=33)
+
+
+def test_dv_update_one_layer_full_size(dlm):
+    """One bf16 layer of 1024 positions, 32 heads x 128, 102 salient rows: all
+    922 stable rows of every head against the oracle."""
+    run_dv_update(dlm, B=1, S=1024, Hq=32, Hkv=32, hd=128, n_per_b=[102], seed=34)
+
+
+def test_dv_update_fp32_tiny_layer(dlm):
+    """The tiny fp32 layer: 128 positions, 4 heads x 64, 16 salient rows."""
+    run_dv_update(dlm, B=1, S=128, Hq=4, Hkv=4, hd=64, n_per_b=[16], dtype="f32", seed=35)
+
+
+def test_row_copies_four_byte_rows(dlm):
+    """Rows of 12 bytes (an LSE row of 3 heads): the 4-byte copy path; gather
+    and scatter bit-exact, other rows untouched."""
+    rng = np.random.default_rng(36)
+    B, S, H = 2, 50, 3
+    cache = rng.standard_normal((B, S, H)).astype(np.float32)
+    idx = np.array([3, 49, 0, 7, 8], np.int32)
+    offsets = np.array([0, 2, 5], np.int32)
+    cd = torch.from_numpy(cache).cuda()
+    rows = torch.zeros(5, H, dtype=torch.float32, device="cuda")
+    dlm.dlm_gather_rows(cd, i32(idx), i32(offsets), 5, rows)
+    new = rng.standard_normal((5, H)).astype(np.float32)
+    dlm.dlm_scatter_rows(torch.from_numpy(new).cuda(), i32(idx), i32(offsets), 5, cd)
+    torch.cuda.synchronize()
+    assert np.array_equal(rows.cpu().numpy(), O.gather_rows(cache, idx, offsets))
+    assert np.array_equal(cd.cpu().numpy(), O.scatter_rows(new, idx, offsets, cache))
