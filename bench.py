@@ -636,8 +636,51 @@ def extra_select_b8(dlm, W):
             "frac_of_measured_ceiling": of_measured(nbytes / (t / 1e3), "hbm_copy")}
 
 
+def extra_dv_update(dlm, W):
+    """The non-salient value-change update (DyLLM's non-salient path) on two
+    shapes: the bf16 one-layer step (1024 positions, 32 x 128 heads, 102
+    salient) and a mid-loop step of the GQA lock loop (B = 8, S = 2048, 32 / 8
+    heads, half the positions unlocked).  Rotating input sets larger than the
+    Infinity Cache.  Algorithmic bytes: the stable rows' query, LSE and output
+    (read and written) plus the salient rows' K_old, V_old and new V."""
+    import torch
+    out = {}
+    for name, B, S, Hq, Hkv, hd, n_b, nsets in (("bf16_s1024_32x128_102_salient", 1, 1024, 32, 32, 128, 102, 12),
+                                                ("gqa_b8_s2048_32q8kv_half_unlocked", 8, 2048, 32, 8, 128, 1024, 2)):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(700)
+        rows = [torch.sort(torch.randperm(S, device="cuda", generator=g)[:n_b]).values for _ in range(B)]
+        idx, offsets = _packed_rows(rows)
+        n = B * n_b
+        sets = []
+        for r in range(nsets):
+            q = _gen((B, S, Hq, hd), 710 + 5 * r, dtype=torch.bfloat16)
+            lse = torch.full((B, S, Hq), 7.0, dtype=torch.float32, device="cuda")
+            o = _gen((B, S, Hq, hd), 711 + 5 * r, dtype=torch.bfloat16)
+            ko = _gen((n, Hkv, hd), 712 + 5 * r, dtype=torch.bfloat16)
+            vo = _gen((n, Hkv, hd), 713 + 5 * r, dtype=torch.bfloat16)
+            v = _gen((B, S, Hkv, hd), 714 + 5 * r, dtype=torch.bfloat16)
+            sets.append((q, lse, ko, vo, v, o))
+        calls = [lambda st=st: dlm.dlm_nonsalient_dv_update(st[0], st[1], idx, offsets, n, st[2], st[3], st[4],
+                                                            1.0 / math.sqrt(hd), st[5]) for st in sets]
+        state = {"i": 0}
+
+        def call():
+            calls[state["i"] % nsets]()
+            state["i"] += 1
+        t = _time(call, 24)
+        stable = B * S - n
+        nbytes = stable * Hq * (3 * hd * 2 + 4) + 3 * n * Hkv * hd * 2
+        flops = 4.0 * (S - n_b) * n_b * hd * Hq * B
+        out[name] = {"ms": t, "GB/s": nbytes / (t / 1e3) / 1e9, "frac": nbytes / (t / 1e3) / PEAK_HBM,
+                     "frac_of_measured_ceiling": of_measured(nbytes / (t / 1e3), "hbm_copy"),
+                     "TFLOP/s": flops / t / 1e9, "algorithmic_bytes": nbytes}
+    return out
+
+
 EXTRAS = (("tiny_fp32", extra_tiny), ("colsum_top64", extra_colsum), ("lsp_commit", extra_lsp),
-          ("gqa_lock_loop", extra_lock_loop), ("select_b8_asymptote", extra_select_b8))
+          ("gqa_lock_loop", extra_lock_loop), ("select_b8_asymptote", extra_select_b8),
+          ("nonsalient_dv_update", extra_dv_update))
 
 
 def cpu_baseline(W, sh, seconds):

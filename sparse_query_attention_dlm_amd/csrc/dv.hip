@@ -13,9 +13,9 @@
 //
 // bf16 kernel (gfx950 matrix cores), a skinny attention without a running max
 // (the cached LSE bounds every weight by about 1):
-//   * A workgroup of four waves owns 128 query vectors: consecutive positions
-//     of one sequence times the G query heads of one KV head (vector v =
-//     position * G + head-in-group); each wave owns 32.
+//   * A workgroup of four (eight) waves owns 128 (256) query vectors:
+//     consecutive positions of one sequence times the G query heads of one KV
+//     head (vector v = position * G + head-in-group); each wave owns 32.
 //   * Per 64-row tile of the salient set, K_old rows and the value change
 //     dV = v_new - v_old (rounded to bf16) are staged in LDS; S^T = K . Q^T and
 //     dO^T = dV^T . P^T run on 32x32x16 MFMAs in the layouts of the attention
@@ -35,7 +35,6 @@ __device__ __forceinline__ i16x4 dv_read_tr16(const u16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((dv_lds_i16x4*)(p));
 }
 
-constexpr int kDvQT = 128;  // query vectors per workgroup
 constexpr int kDvKT = 64;   // salient rows per tile
 
 // Row pitches (u16) for conflict-free LDS reads, as in the attention kernel:
@@ -49,19 +48,23 @@ struct DvLds {
   static constexpr int WORDS = kDvKT * (KPITCH + VPITCH);
 };
 
-template <int HD>
-__global__ __launch_bounds__(256, 2) void dv_update_bf16_kernel(DvArgs a) {
+// WQ = 1: 128 query vectors in four waves, two workgroups per CU; WQ = 2: 256
+// vectors in eight waves, one per CU, for selections with many position tiles
+// (every salient tile is read from L2 once per 256 vectors instead of 128).
+template <int HD, int WQ>
+__global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kernel(DvArgs a) {
+  constexpr int QT = 128 * WQ, NT = 256 * WQ;
   constexpr int NS = HD / 16, NDB = HD / 32, CPR = HD / 8;
   constexpr int PITCH = DvLds<HD>::KPITCH, VPITCH = DvLds<HD>::VPITCH;
-  constexpr int RPJ = 256 / CPR;        // tile rows between a thread's chunks
-  constexpr int JT = kDvKT * CPR / 256; // chunks per tensor per thread
+  constexpr int RPJ = NT / CPR;        // tile rows between a thread's chunks
+  constexpr int JT = kDvKT * CPR / NT; // chunks per tensor per thread
   __shared__ __attribute__((aligned(16))) u16 smem[DvLds<HD>::WORDS];
-  __shared__ int sflag[kDvQT];
+  __shared__ int sflag[QT];
   u16* sK = smem;
   u16* sV = smem + kDvKT * PITCH;
 
   const int G = a.Hq / a.Hkv;
-  const int tiles = (a.S * G + kDvQT - 1) / kDvQT;
+  const int tiles = (a.S * G + QT - 1) / QT;
   const int t = blockIdx.x % tiles;
   const int g = (blockIdx.x / tiles) % a.Hkv;
   const int b = blockIdx.x / (tiles * a.Hkv);
@@ -70,13 +73,13 @@ __global__ __launch_bounds__(256, 2) void dv_update_bf16_kernel(DvArgs a) {
   if (nb <= 0) return;  // no salient rows: every output stays
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
-  // positions [p_lo, p_lo + kDvQT / G) belong to this workgroup
-  const int p_lo = t * kDvQT / G;
-  const int vq = t * kDvQT + wave * 32 + lr;
+  // positions [p_lo, p_lo + QT / G) belong to this workgroup
+  const int p_lo = t * QT / G;
+  const int vq = t * QT + wave * 32 + lr;
   const bool qvalid = vq < a.S * G;
   const int vqc = qvalid ? vq : a.S * G - 1;
   const int pos = vqc / G, h = g * G + vqc % G;
-  if (tid < kDvQT) sflag[tid] = 0;
+  if (tid < QT) sflag[tid] = 0;
 
   const size_t qrow = ((size_t)b * a.S + pos) * a.Hq + h;
   bf16x8 qf[NS];
@@ -96,25 +99,44 @@ __global__ __launch_bounds__(256, 2) void dv_update_bf16_kernel(DvArgs a) {
   const u16* vold = static_cast<const u16*>(a.v_old);
   const u16* vcache = static_cast<const u16*>(a.v);
   const int ch = tid % CPR;
-  for (int k0 = 0; k0 < nb; k0 += kDvKT) {
-    // staging loads: chunk ch of tile rows tid / CPR + RPJ j (rows past the
-    // salient set give zeros)
-    u32x4 kr[JT], vn[JT], vo[JT];
-    int rpos[JT];
+  // staging registers of one tile: chunk ch of tile rows tid / CPR + RPJ j
+  // (rows past the salient set give zeros and position -1).  A row's new V
+  // sits at its position idx[r]: the positions are loaded one tile ahead of
+  // the rows, so no tile waits for two memory round trips in a row.
+  u32x4 kr[JT], vn[JT], vo[JT];
+  int rpos[JT], pnext[JT];
+  // branch-free: a row past the salient set reads the set's first row and is
+  // then zeroed
+  auto row_of = [&](int k0, int j) {
+    const int rr = k0 + tid / CPR + RPJ * j;
+    return r0 + (rr < nb ? rr : 0);
+  };
+  auto load_pos = [&](int k0, int (&ps)[JT]) {
+#pragma unroll
+    for (int j = 0; j < JT; ++j) ps[j] = a.idx[row_of(k0, j)];
+  };
+  auto load_tile = [&](int k0, const int (&ps)[JT]) {
 #pragma unroll
     for (int j = 0; j < JT; ++j) {
-      const int rr = k0 + tid / CPR + RPJ * j;
-      if (rr < nb) {
-        const size_t r = (size_t)(r0 + rr);
-        rpos[j] = a.idx[r0 + rr];
-        kr[j] = *reinterpret_cast<const u32x4*>(kold + (r * a.Hkv + g) * HD + ch * 8);
-        vo[j] = *reinterpret_cast<const u32x4*>(vold + (r * a.Hkv + g) * HD + ch * 8);
-        vn[j] = *reinterpret_cast<const u32x4*>(vcache + (((size_t)b * a.S + rpos[j]) * a.Hkv + g) * HD + ch * 8);
-      } else {
-        rpos[j] = -1;
-        kr[j] = vo[j] = vn[j] = u32x4{0, 0, 0, 0};
-      }
+      const bool ok = k0 + tid / CPR + RPJ * j < nb;
+      const size_t r = (size_t)row_of(k0, j);
+      const u32x4 k = *reinterpret_cast<const u32x4*>(kold + (r * a.Hkv + g) * HD + ch * 8);
+      const u32x4 o = *reinterpret_cast<const u32x4*>(vold + (r * a.Hkv + g) * HD + ch * 8);
+      const u32x4 n = *reinterpret_cast<const u32x4*>(vcache + (((size_t)b * a.S + ps[j]) * a.Hkv + g) * HD + ch * 8);
+      const u32x4 z = u32x4{0, 0, 0, 0};
+      rpos[j] = ok ? ps[j] : -1;
+      kr[j] = ok ? k : z;
+      vo[j] = ok ? o : z;
+      vn[j] = ok ? n : z;
     }
+  };
+  {
+    int p0[JT];
+    load_pos(0, p0);
+    load_tile(0, p0);
+  }
+  if (kDvKT < nb) load_pos(kDvKT, pnext);
+  for (int k0 = 0; k0 < nb; k0 += kDvKT) {
     __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
     for (int j = 0; j < JT; ++j) {
@@ -128,9 +150,13 @@ __global__ __launch_bounds__(256, 2) void dv_update_bf16_kernel(DvArgs a) {
       *reinterpret_cast<u32x4*>(sK + rl * PITCH + ch * 8) = kr[j];
       *reinterpret_cast<u32x4*>(sV + rl * VPITCH + ch * 8) = dv;
       // one chunk column flags the salient positions inside this workgroup's range
-      if (ch == 0 && rpos[j] >= p_lo && rpos[j] - p_lo < kDvQT / G) sflag[rpos[j] - p_lo] = 1;
+      if (ch == 0 && rpos[j] >= p_lo && rpos[j] - p_lo < QT / G) sflag[rpos[j] - p_lo] = 1;
     }
     __syncthreads();
+    // the next tile streams in during this tile's math, and the positions of
+    // the one after it
+    if (k0 + kDvKT < nb) load_tile(k0 + kDvKT, pnext);
+    if (k0 + 2 * kDvKT < nb) load_pos(k0 + 2 * kDvKT, pnext);
 
     // S^T = K_old . Q^T for the tile's two 32-row blocks
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -141,6 +167,16 @@ __global__ __launch_bounds__(256, 2) void dv_update_bf16_kernel(DvArgs a) {
         const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(sK + (32 * kb + lr) * PITCH + 16 * s + 8 * lg));
         sacc[kb] = mfma32x32x16(kf, qf[s], sacc[kb]);
       }
+    // four K-fragment reads kept in flight: 4 reads, then (MFMA, read) pairs,
+    // then the last 4 MFMAs (left alone, the scheduler issues each read right
+    // before its MFMA and waits out the LDS latency every time)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // weights against the cached LSE; register i of block kb is tile row
     // 32 kb + 8 (i / 4) + 4 lg + i % 4; rows past the salient set weigh 0
     const int nvalid = nb - k0;
@@ -179,12 +215,17 @@ __global__ __launch_bounds__(256, 2) void dv_update_bf16_kernel(DvArgs a) {
   if (!qvalid || sflag[pos - p_lo]) return;
   // o += dO: register i of block d holds dimension 32 d + 8 (i / 4) + 4 lg + i % 4
   u16* op = static_cast<u16*>(a.o) + qrow * HD;
+  u32x2 oin[NDB][4];  // all of the lane's cached output words in flight at once
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) oin[d][q4] = *reinterpret_cast<const u32x2*>(op + 32 * d + 8 * q4 + 4 * lg);
 #pragma unroll
   for (int d = 0; d < NDB; ++d)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d0 = 32 * d + 8 * q4 + 4 * lg;
-      u32x2 w = *reinterpret_cast<const u32x2*>(op + d0);
+      u32x2 w = oin[d][q4];
       const float o0 = __uint_as_float(w[0] << 16) + acc[d][4 * q4];
       const float o1 = __uint_as_float(w[0] & 0xFFFF0000u) + acc[d][4 * q4 + 1];
       const float o2 = __uint_as_float(w[1] << 16) + acc[d][4 * q4 + 2];
@@ -272,13 +313,24 @@ hipError_t launch_dv_update(int dtype, const DvArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(dv_update_f32_kernel<128>, dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
+  // 256-vector workgroups once they still give two workgroups per CU
   const int G = a.Hq / a.Hkv;
-  const long long tiles = ((long long)a.S * G + kDvQT - 1) / kDvQT;
-  const int grid = (int)(tiles * a.Hkv * a.B);
-  if (a.hd == 64)
-    hipLaunchKernelGGL(dv_update_bf16_kernel<64>, dim3(grid), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(dv_update_bf16_kernel<128>, dim3(grid), dim3(256), 0, st, a);
+  const long long wide_grid = ((long long)a.S * G + 255) / 256 * a.Hkv * a.B;
+  const bool wide = wide_grid >= 2LL * device_cus();
+  const int QT = wide ? 256 : 128;
+  const int grid = (int)(((long long)a.S * G + QT - 1) / QT * a.Hkv * a.B);
+  const dim3 block(wide ? 512 : 256);
+  if (a.hd == 64) {
+    if (wide)
+      hipLaunchKernelGGL((dv_update_bf16_kernel<64, 2>), dim3(grid), block, 0, st, a);
+    else
+      hipLaunchKernelGGL((dv_update_bf16_kernel<64, 1>), dim3(grid), block, 0, st, a);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((dv_update_bf16_kernel<128, 2>), dim3(grid), block, 0, st, a);
+    else
+      hipLaunchKernelGGL((dv_update_bf16_kernel<128, 1>), dim3(grid), block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

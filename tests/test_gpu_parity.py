@@ -768,6 +768,13 @@ def test_dv_update_gqa(dlm, Hq, Hkv):
     run_dv_update(dlm, B=2, S=257, Hq=Hq, Hkv=Hkv, hd=128, n_per_b=[128, 65], seed=32)
 
 
+@pytest.mark.parametrize("hd", [64, 128])
+def test_dv_update_wide_workgroups(dlm, hd):
+    """Enough position tiles (B = 2, S = 2048, GQA 32/8) for the 256-vector
+    workgroups; salient sets of 300 and 777 rows (ragged last tiles)."""
+    run_dv_update(dlm, B=2, S=2048, Hq=32, Hkv=8, hd=hd, n_per_b=[300, 777], seed=37)
+
+
 def test_dv_update_head_dim_64(dlm):
     run_dv_update(dlm, B=1, S=200, Hq=4, Hkv=2, hd=64, n_per_b=[37], seed=33)
 
