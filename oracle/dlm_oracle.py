@@ -11,8 +11,9 @@ Pages followed (title, section):
   [DyLLM]   "DyLLM: Efficient Diffusion LLM Inference via Saliency-based Token
             Selection and Partial Attention" - Methodologie 1 (temporal cosine
             similarity per token; low similarity = salient, recomputed; stable
-            tokens reuse cached activations), Methodologie 2 (salient path: full
-            recomputation of the attention rows).
+            tokens reuse cached activations, the FFN included), Methodologie 2
+            (salient path: full recomputation of the attention rows;
+            non-salient path: existing weights times the value change).
   [SlowFast] "Accelerating Diffusion Large Language Models with SlowFast
             Sampling" - Metodologia, certainty and convergence principles
             (max predicted confidence as the stability signal).
@@ -189,6 +190,24 @@ def output_scatter(o_sel, idx, offsets, out_cache, w_o=None):
         rows = rows_of(idx, offsets, b)
         out[b, rows] = y[offsets[b]:offsets[b + 1]]
     return out
+
+
+def salient_ffn(x, idx, offsets, w_gu, w_down, out_cache):
+    """[DyLLM] Methodologie 1: the FFN is computed for the salient tokens only;
+    every other token keeps its cached FFN output.
+
+    Reading (the pages name no FFN form): a SwiGLU MLP, y = (silu(x W_g^T) *
+    (x W_u^T)) W_d^T with silu(z) = z / (1 + e^-z), on the selected rows of x
+    [B,S,D].  w_gu [2F, D] holds gate and up rows interleaved (row 2f = gate
+    feature f, row 2f+1 = up feature f); w_down [D, F].  Returns (h [n,F], the
+    output cache [B,S,D] with the selected rows replaced by y)."""
+    xs = gather_rows(np.asarray(x, dtype=f64), idx, offsets)
+    wgu = np.asarray(w_gu, dtype=f64)
+    g = xs @ wgu[0::2].T
+    u = xs @ wgu[1::2].T
+    h = g / (1.0 + np.exp(-g)) * u
+    y = h @ np.asarray(w_down, dtype=f64).T
+    return h, scatter_rows(y, idx, offsets, np.asarray(out_cache, dtype=f64))
 
 
 def gather_rows(src, idx, offsets):

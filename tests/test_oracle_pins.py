@@ -406,6 +406,70 @@ def test_gather_scatter_rows_brute_force():
             assert to_list(out[b, i]) == to_list(want)
 
 
+def test_salient_ffn_brute_force_and_library():
+    """Pure-Python brute force on a tiny case, and torch's CPU silu/matmul in
+    float64 with all rows selected; unselected rows keep the cache."""
+    rng = np.random.default_rng(15)
+    B, S, D, F = 2, 5, 4, 3
+    x = rng.standard_normal((B, S, D))
+    wgu = rng.standard_normal((2 * F, D))
+    wd = rng.standard_normal((D, F))
+    cache = rng.standard_normal((B, S, D))
+    idx = np.array([4, 1, 3], np.int32)
+    offsets = np.array([0, 1, 3], np.int32)
+    h, out = O.salient_ffn(x, idx, offsets, wgu, wd, cache)
+    sel = [(0, 4), (1, 1), (1, 3)]
+    for r, (b, i) in enumerate(sel):
+        xr = to_list(x[b, i])
+        hh = []
+        for f in range(F):
+            gte = sum(a * w for a, w in zip(xr, to_list(wgu[2 * f])))
+            up = sum(a * w for a, w in zip(xr, to_list(wgu[2 * f + 1])))
+            hh.append(gte / (1 + math.exp(-gte)) * up)
+        assert np.allclose(h[r], hh, atol=1e-13)
+        y = [sum(hh[f] * wd[d, f] for f in range(F)) for d in range(D)]
+        assert np.allclose(out[b, i], y, atol=1e-12)
+    for b in range(B):
+        for i in range(S):
+            if (b, i) not in sel:
+                assert np.array_equal(out[b, i], cache[b, i])
+    # every row selected: torch's silu and matmul on the whole batch
+    idx_all = np.tile(np.arange(S, dtype=np.int32), B)
+    off_all = np.arange(B + 1, dtype=np.int32) * S
+    _, out_all = O.salient_ffn(x, idx_all, off_all, wgu, wd, cache)
+    xt = torch.tensor(x)
+    ref = (torch.nn.functional.silu(xt @ torch.tensor(wgu[0::2]).T) * (xt @ torch.tensor(wgu[1::2]).T)) @ torch.tensor(wd).T
+    assert np.allclose(out_all, ref.numpy(), atol=1e-12)
+
+
+def test_salient_ffn_closed_forms():
+    """silu(0) = 0 (a zero gate zeroes the row); a unit up row and identity-like
+    down weights make y_d = silu(g_d); an empty selection returns the cache."""
+    rng = np.random.default_rng(16)
+    B, S, D = 1, 3, 2
+    x = rng.standard_normal((B, S, D))
+    cache = rng.standard_normal((B, S, D))
+    wgu = np.zeros((4, D))
+    wgu[1] = rng.standard_normal(D)
+    wgu[3] = rng.standard_normal(D)
+    h, _ = O.salient_ffn(x, [0, 1, 2], [0, 3], wgu, np.eye(D), cache)
+    assert np.array_equal(h, np.zeros_like(h))
+    # gate f = x_f, up = 1 (a constant input column), down = identity
+    x1 = np.concatenate([x, np.ones((B, S, 1))], axis=2)
+    wgu = np.zeros((2 * D, D + 1))
+    for f in range(D):
+        wgu[2 * f, f] = 1.0
+        wgu[2 * f + 1, D] = 1.0
+    wd = np.zeros((D + 1, D))
+    wd[:D, :D] = np.eye(D)
+    _, out = O.salient_ffn(x1, [0, 2], [0, 2], wgu, wd, np.zeros((B, S, D + 1)))
+    for i in (0, 2):
+        assert np.allclose(out[0, i, :D], x[0, i] / (1 + np.exp(-x[0, i])), atol=1e-15)
+    assert np.array_equal(out[0, 1], np.zeros(D + 1))
+    _, out = O.salient_ffn(x, np.zeros(0, np.int32), [0, 0], np.ones((4, D)), np.ones((D, 2)), cache)
+    assert np.array_equal(out, cache)
+
+
 def test_colsum_sum_invariant_and_library_softmax():
     B, S, nq, Hq, Hkv, hd = 2, 11, 6, 4, 2, 3
     q, kc, vc, idx, offsets = _attn_inputs(B, S, nq, Hq, Hkv, hd, 13)
