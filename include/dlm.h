@@ -13,6 +13,7 @@
  *                                                       -> dlm_partial_attn
  *      optional: per-key attention column sums + top-k  -> dlm_attn_colsum
  *      optional: longest-stable-prefix commit           -> dlm_stable_prefix
+ *      optional: FFN of the salient rows                -> dlm_salient_ffn
  *      optional: value-change update of the stable rows -> dlm_nonsalient_dv_update
  *                (caches kept with dlm_gather_rows / dlm_scatter_rows)
  *
@@ -265,6 +266,31 @@ int dlm_nonsalient_dv_update(int dtype, const void* q_cache, const float* lse_ca
                              const void* k_old, const void* v_old, const void* v_cache,
                              int B, int S, int Hq, int Hkv, int hd, float scale,
                              void* o_cache, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dlm_salient_ffn
+ *
+ * The FFN of the salient rows only.  Follows: "DyLLM: Efficient Diffusion
+ * LLM Inference via Saliency-based Token Selection and Partial Attention",
+ * Methodologie 1 (the FFN is skipped for non-salient tokens, which reuse
+ * their cached activations).  The pages name no FFN form; this is a SwiGLU
+ * MLP (bf16 only, float32 accumulation):
+ *   h[r, f]            = silu(x[b,idx[r]] . w_gu[2f]) * (x[b,idx[r]] . w_gu[2f+1])
+ *   out_cache[b,idx[r]] = h[r] . w_down^T,   silu(z) = z / (1 + e^-z)
+ *   x        [B,S,D]  bf16  FFN input per position (under 2 GiB)
+ *   w_gu     [2F,D]   bf16  gate and up rows interleaved: row 2f = gate
+ *                           feature f, row 2f+1 = up feature f
+ *   w_down   [D,F]    bf16  output-major
+ *   out_cache [B,S,D] bf16  selected rows replaced; others not touched
+ * D and F multiples of 64.  h (rounded to bf16) lives in the workspace of
+ * dlm_salient_ffn_workspace_size(dtype, max_rows, D, F) bytes, followed by
+ * split-K tiles for long selections.  dtype DLM_F32 -> DLM_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------ */
+size_t dlm_salient_ffn_workspace_size(int dtype, int max_rows, int D, int F);
+int dlm_salient_ffn(int dtype, const void* x, int B, int S, int D,
+                    const int32_t* idx, const int32_t* offsets, int max_rows,
+                    const void* w_gu, int F, const void* w_down, void* out_cache,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * dlm_gather_rows / dlm_scatter_rows

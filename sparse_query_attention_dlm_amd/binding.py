@@ -68,6 +68,10 @@ lib.dlm_probe_mfma_bf16.argtypes = [_I, _I, _P, _P]
 lib.dlm_nonsalient_dv_update.restype = _I
 lib.dlm_nonsalient_dv_update.argtypes = [_I, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P,
                                          _P]
+lib.dlm_salient_ffn_workspace_size.restype = _Z
+lib.dlm_salient_ffn_workspace_size.argtypes = [_I] * 4
+lib.dlm_salient_ffn.restype = _I
+lib.dlm_salient_ffn.argtypes = [_I, _P, _I, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _Z, _P]
 lib.dlm_gather_rows.restype = _I
 lib.dlm_gather_rows.argtypes = [_P, _I, _I, _I, _P, _P, _I, _P, _P]
 lib.dlm_scatter_rows.restype = _I
@@ -225,6 +229,21 @@ def dlm_nonsalient_dv_update(q_cache, lse_cache, idx, offsets, max_rows, k_old, 
         _ptr(idx, "idx", torch.int32, False), _ptr(offsets, "offsets", torch.int32, False), int(max_rows),
         _ptr(k_old, "k_old", dt, False), _ptr(v_old, "v_old", dt, False), _ptr(v_cache, "v_cache", dt),
         B, S, Hq, Hkv, hd, float(scale), _ptr(o_cache, "o_cache", dt), _stream(stream))
+    _check(rc)
+
+
+def dlm_salient_ffn_workspace_size(dtype, max_rows, D, F) -> int:
+    return int(lib.dlm_salient_ffn_workspace_size(int(dtype), int(max_rows), int(D), int(F)))
+
+
+def dlm_salient_ffn(x, idx, offsets, max_rows, w_gu, w_down, out_cache, workspace=None, stream=None):
+    B, S, D = x.shape
+    F = w_down.shape[1]
+    wp, wn = _ws(workspace)
+    rc = lib.dlm_salient_ffn(
+        _dt(x), _ptr(x, "x"), B, S, D, _ptr(idx, "idx", torch.int32, False),
+        _ptr(offsets, "offsets", torch.int32, False), int(max_rows), _ptr(w_gu, "w_gu", x.dtype), F,
+        _ptr(w_down, "w_down", x.dtype), _ptr(out_cache, "out_cache", x.dtype), wp, wn, _stream(stream))
     _check(rc)
 
 

@@ -375,6 +375,83 @@ int dlm_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
 }
 
 // ---------------------------------------------------------------------------
+size_t dlm_salient_ffn_workspace_size(int dtype, int max_rows, int D, int F) {
+  if (dtype != DLM_BF16 || max_rows <= 0 || D <= 0 || F <= 0) return 0;
+  const size_t h = round_up((size_t)max_rows * F * 2, 256);
+  const size_t g1 = dlm::gemm_workspace_bytes(dlm::EPI_SWIGLU, max_rows, 2 * F, D);
+  const size_t g2 = dlm::gemm_workspace_bytes(dlm::EPI_ROWS, max_rows, D, F);
+  return h + (g1 > g2 ? g1 : g2);
+}
+
+int dlm_salient_ffn(int dtype, const void* x, int B, int S, int D, const int32_t* idx,
+                    const int32_t* offsets, int max_rows, const void* w_gu, int F,
+                    const void* w_down, void* out_cache, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  REQUIRE(dtype == DLM_F32 || dtype == DLM_BF16, "unknown dtype %d", dtype);
+  if (dtype != DLM_BF16) return fail(DLM_ERR_UNSUPPORTED, "the salient-row FFN is bf16 only");
+  REQUIRE(B > 0 && S > 0 && D > 0 && F > 0, "B, S, D, F must be positive");
+  REQUIRE(D % 64 == 0 && F % 64 == 0, "D=%d and F=%d must be multiples of 64", D, F);
+  REQUIRE(max_rows >= 0 && (long long)max_rows <= (long long)B * S, "max_rows=%d out of range",
+          max_rows);
+  REQUIRE((long long)B * S * D * 2 < (1ll << 31), "x of 2 GiB or more is not supported");
+  REQUIRE((long long)2 * F * D * 2 < (1ll << 32), "w_gu of 4 GiB or more");
+  REQUIRE((long long)max_rows * F * 2 < (1ll << 31), "the FFN rows of 2 GiB or more");
+  if (max_rows == 0) return DLM_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(offsets);
+  REQUIRE_PTR(w_gu);
+  REQUIRE_PTR(w_down);
+  REQUIRE_PTR(out_cache);
+  REQUIRE_ALIGNED(x);
+  REQUIRE_ALIGNED(w_gu);
+  REQUIRE_ALIGNED(w_down);
+  REQUIRE_ALIGNED(out_cache);
+  const size_t need = dlm_salient_ffn_workspace_size(dtype, max_rows, D, F);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  REQUIRE_ALIGNED(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* h = workspace;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         round_up((size_t)max_rows * F * 2, 256));
+  // gate and up of the gathered rows, SwiGLU in the epilogue -> h [max_rows, F]
+  dlm::GemmArgs g{};
+  g.w = w_gu;
+  g.x = x;
+  g.x_bytes = (uint32_t)((size_t)B * S * D * 2);
+  g.K = D;
+  g.N = 2 * F;
+  g.B = B;
+  g.S = S;
+  g.idx = idx;
+  g.offsets = offsets;
+  g.max_rows = max_rows;
+  g.out = h;
+  g.ld_out = F;
+  g.part = part;
+  int rc = hip_status(dlm::launch_gemm(dtype, dlm::EPI_SWIGLU, dlm::A_GATHER, g, st), "FFN gate/up");
+  if (rc != DLM_OK) return rc;
+  // down projection of h, rows scattered into the output cache
+  dlm::GemmArgs d{};
+  d.w = w_down;
+  d.x = h;
+  d.x_bytes = (uint32_t)((size_t)max_rows * F * 2);
+  d.K = F;
+  d.N = D;
+  d.B = B;
+  d.S = S;
+  d.idx = idx;
+  d.offsets = offsets;
+  d.max_rows = max_rows;
+  d.out = out_cache;
+  d.ld_out = D;
+  d.part = part;
+  return hip_status(dlm::launch_gemm(dtype, dlm::EPI_ROWS, dlm::A_COMPACT, d, st), "FFN down");
+}
+
+// ---------------------------------------------------------------------------
 static int row_copy(const void* src, void* dst, const int32_t* idx, const int32_t* offsets,
                     int max_rows, int B, int S, int row_bytes, int scatter, void* stream) {
   REQUIRE(B > 0 && S > 0, "B and S must be positive");

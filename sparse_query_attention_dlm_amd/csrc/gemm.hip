@@ -34,6 +34,14 @@ namespace dlm {
 template <int EPI>
 __device__ __forceinline__ void epi_store4(const GemmArgs& g, int m, int drow, int n, float v0, float v1,
                                            float v2, float v3) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    // n..n+3 = (gate, up) of features n/2 and n/2 + 1 (n is a multiple of 4):
+    // h = silu(gate) * up, silu(z) = z / (1 + e^-z), two bf16 to the compact row
+    const float h0 = v0 / (1.f + __expf(-v0)) * v1;
+    const float h1 = v2 / (1.f + __expf(-v2)) * v3;
+    *reinterpret_cast<uint32_t*>(static_cast<u16*>(g.out) + (size_t)m * g.ld_out + (n >> 1)) = pack_bf16x2(h0, h1);
+    return;
+  }
   u32x2 pk;
   pk[0] = pack_bf16x2(v0, v1);
   pk[1] = pack_bf16x2(v2, v3);
@@ -61,7 +69,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wp = wave / WT, wt = wave % WT;
   const int lr = lane & 31, lg = lane >> 5;
-  if constexpr (EPI == EPI_QKV || EPI == EPI_ROWS) {
+  if constexpr (EPI == EPI_QKV || EPI == EPI_ROWS || EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int b = 0; b < FT; ++b) {
       const int ml = wt * WTT + b * 32 + lr;
@@ -683,14 +691,20 @@ hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStre
   }
   if (epi == EPI_LMHEAD) {
     launch_bf16<kLmTP, 256, 64, 1, EPI_LMHEAD, A_GATHER, 0, 256, 768>(g, st);
-  } else if ((g.K / 64) % 4 != 0 && g.max_rows > kSkinnyRows) {
+  } else if ((g.K / 64) % 4 != 0 && g.max_rows > kSkinnyRows && g.N % 128 == 0) {
     // short K: the 4-deep skinny ring does not divide it; one large tiling
+    // (its 128-feature tiles must divide N; otherwise the 64-feature tiling
+    // below, whose ring depth divides any K)
     if (epi == EPI_QKV)
       launch_bf16<128, 128, 64, 1, EPI_QKV, A_GATHER, 0, 0, 0>(g, st);
+    else if (epi == EPI_SWIGLU)
+      launch_bf16<128, 128, 64, 1, EPI_SWIGLU, A_GATHER, 0, 0, 0>(g, st);
     else
       launch_bf16<128, 128, 64, 1, EPI_ROWS, A_COMPACT, 0, 0, 0>(g, st);
   } else if (epi == EPI_QKV) {
     launch_by_rows<EPI_QKV, A_GATHER>(g, st);
+  } else if (epi == EPI_SWIGLU) {
+    launch_by_rows<EPI_SWIGLU, A_GATHER>(g, st);
   } else {
     launch_by_rows<EPI_ROWS, A_COMPACT>(g, st);
   }

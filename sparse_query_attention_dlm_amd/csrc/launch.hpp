@@ -32,7 +32,7 @@ hipError_t launch_lmhead_combine(const float4* part, int ntile, const int32_t* e
                                  int32_t* counts, int32_t* offsets, hipStream_t st);
 
 // gemm.hip -- D^T[n][m] = sum_k W[n][k] * A[row(m)][k]; W output-major [N][K].
-enum GemmEpilogue { EPI_QKV = 0, EPI_ROWS = 1, EPI_LMHEAD = 2 };
+enum GemmEpilogue { EPI_QKV = 0, EPI_ROWS = 1, EPI_LMHEAD = 2, EPI_SWIGLU = 3 };
 enum GemmAMode { A_GATHER = 0, A_COMPACT = 1 };
 struct GemmArgs {
   const void* w;            // [N][K]
@@ -48,6 +48,8 @@ struct GemmArgs {
   void* v_cache;
   int nq, nk;
   // EPI_ROWS: out[(b*S + idx[m])*ld_out + n]
+  // EPI_SWIGLU: features (2f, 2f+1) = (gate, up) of f; out[m*ld_out + f] =
+  //             silu(gate) * up
   void* out;
   int ld_out;
   // EPI_LMHEAD: lm_part[m*ntile + tile] = {max, sum exp(z-max), argmax bits, 0}

@@ -220,3 +220,25 @@ def test_row_copy_rejections(lib):
         assert fn(max_rows=17) == INVALID                    # more rows than B*S
         assert fn(max_rows=0, idx=0, off=0) == OK
     assert g(rows=MISALIGNED) == INVALID                     # 16-byte rows need 16-byte alignment
+
+
+def test_salient_ffn_rejections(lib):
+    lib.dlm_salient_ffn_workspace_size.restype = ctypes.c_size_t
+
+    def ffn(dtype=BF16, x=FAKE, B=1, S=64, D=128, idx=FAKE, off=FAKE, max_rows=8, wgu=FAKE, F=256, wd=FAKE,
+            out=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return lib.dlm_salient_ffn(dtype, p(x), B, S, D, p(idx), p(off), max_rows, p(wgu), F, p(wd), p(out), p(ws),
+                                   ctypes.c_size_t(ws_bytes), p(0))
+    assert ffn(dtype=F32) == UNSUPPORTED
+    assert ffn(x=0) == INVALID
+    assert ffn(wgu=0) == INVALID
+    assert ffn(out=MISALIGNED) == INVALID
+    assert ffn(D=100) == INVALID                             # D and F multiples of 64
+    assert ffn(F=100) == INVALID
+    assert ffn(max_rows=65) == INVALID
+    assert ffn(ws_bytes=16) == WORKSPACE
+    assert ffn(ws=0) == WORKSPACE
+    assert ffn(max_rows=0, idx=0, off=0, ws=0) == OK
+    # h [max_rows, F] bf16 first, 256-byte aligned
+    assert lib.dlm_salient_ffn_workspace_size(BF16, 8, 128, 256) == 8 * 256 * 2
+    assert lib.dlm_salient_ffn_workspace_size(F32, 8, 128, 256) == 0

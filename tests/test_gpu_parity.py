@@ -806,3 +806,56 @@ def test_row_copies_four_byte_rows(dlm):
     torch.cuda.synchronize()
     assert np.array_equal(rows.cpu().numpy(), O.gather_rows(cache, idx, offsets))
     assert np.array_equal(cd.cpu().numpy(), O.scatter_rows(new, idx, offsets, cache))
+
+
+# ---------------------------------------------------------------------------
+# FFN of the salient rows (SwiGLU; gate and up interleaved by row)
+# ---------------------------------------------------------------------------
+def run_salient_ffn(dlm, B, S, D, F, n_per_b, seed=41, loose_bound=None):
+    rng = np.random.default_rng(seed)
+    x = W.round_bf16(rng.standard_normal((B, S, D)))
+    w_gu = W.round_bf16(rng.standard_normal((2 * F, D)) / math.sqrt(D))
+    w_down = W.round_bf16(rng.standard_normal((D, F)) / math.sqrt(F))
+    cache = W.round_bf16(rng.standard_normal((B, S, D)))
+    sal = [np.sort(rng.choice(S, n, replace=False)).astype(np.int32) for n in n_per_b]
+    idx = np.concatenate(sal).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(n_per_b)]).astype(np.int32)
+    n = int(offsets[-1])
+    max_rows = n if loose_bound is None else loose_bound
+    say(f"[salient ffn] B={B} S={S} D={D} F={F} rows {list(n_per_b)} bound {max_rows}")
+    out = dev(cache, "bf16")
+    ws = workspace(dlm.dlm_salient_ffn_workspace_size(dlm.DLM_BF16, max_rows, D, F))
+    dlm.dlm_salient_ffn(dev(x, "bf16"), i32(idx), i32(offsets), max_rows, dev(w_gu, "bf16"), dev(w_down, "bf16"),
+                        out, workspace=ws)
+    torch.cuda.synchronize()
+    h_ref, ref = O.salient_ffn(x, idx, offsets, w_gu, w_down, cache)
+    got = host(out)
+    mask = rows_mask(B, S, idx, offsets)
+    assert np.array_equal(got[~mask], cache[~mask])
+    err = maxabs(got[mask], ref[mask])
+    # h, the bf16 intermediate in the workspace (not an output), reaches |h| ~ 16
+    # at 4 sigma: checked relative to its size (half a bf16 ulp is 2^-9 of it)
+    h = host(ws[:n * F * 2].view(torch.bfloat16).reshape(n, F))
+    eh = float(np.max(np.abs(h - h_ref) - 2.0 ** -7 * np.abs(h_ref)))
+    say(f"  max |y - oracle| = {err:.2e}; max of |h - oracle| - 2^-7 |h| = {eh:.2e}")
+    assert err <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_salient_ffn_short_selection(dlm):
+    """100 rows: the weight-streaming tilings (two batch rows, one empty)."""
+    run_salient_ffn(dlm, B=2, S=512, D=1024, F=1024, n_per_b=[100, 0])
+
+
+def test_salient_ffn_long_selection_split_k(dlm):
+    """1300 rows: the resident 256x256 tiling with split-K partials (workspace)."""
+    run_salient_ffn(dlm, B=2, S=1024, D=512, F=1536, n_per_b=[700, 600], seed=42)
+
+
+def test_salient_ffn_short_k_and_loose_bound(dlm):
+    """K / 64 not a multiple of 4 (D = 320, F = 640) with a loose row bound."""
+    run_salient_ffn(dlm, B=1, S=1024, D=320, F=640, n_per_b=[300], seed=43, loose_bound=1024)
+
+
+def test_salient_ffn_one_layer_full_size(dlm):
+    """One layer of 1024 positions, D = 4096, F = 12288, 102 salient rows."""
+    run_salient_ffn(dlm, B=1, S=1024, D=4096, F=12288, n_per_b=[102], seed=44)
