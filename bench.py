@@ -678,9 +678,43 @@ def extra_dv_update(dlm, W):
     return out
 
 
+def extra_salient_ffn(dlm, W):
+    """The salient-row SwiGLU FFN (D = 4096, F = 12288) on the one-layer step's
+    102 selected rows (weight-stream bound: 2F.D + D.F bf16 weights per call,
+    two rotating weight sets larger than the Infinity Cache) and on 2048
+    selected rows (matrix-core bound)."""
+    import torch
+    D, F = 4096, 12288
+    out = {}
+    for name, B, S, n_b, nsets in (("bf16_s1024_102_rows", 1, 1024, 102, 2), ("bf16_b2_s1024_2048_rows", 2, 1024, 1024, 1)):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(800)
+        rows = [torch.sort(torch.randperm(S, device="cuda", generator=g)[:n_b]).values for _ in range(B)]
+        idx, offsets = _packed_rows(rows)
+        n = B * n_b
+        x = _gen((B, S, D), 801, dtype=torch.bfloat16)
+        cache = _gen((B, S, D), 802, dtype=torch.bfloat16)
+        wsets = [(_gen((2 * F, D), 803 + 2 * r, 1 / 64, torch.bfloat16), _gen((D, F), 804 + 2 * r, 1 / 110, torch.bfloat16))
+                 for r in range(nsets)]
+        ws = torch.zeros(dlm.dlm_salient_ffn_workspace_size(dlm.DLM_BF16, n, D, F), dtype=torch.uint8, device="cuda")
+        calls = [lambda w=w: dlm.dlm_salient_ffn(x, idx, offsets, n, w[0], w[1], cache, workspace=ws) for w in wsets]
+        state = {"i": 0}
+
+        def call():
+            calls[state["i"] % nsets]()
+            state["i"] += 1
+        t = _time(call, 10)
+        flops = 2.0 * n * D * 3 * F
+        nbytes = 3 * F * D * 2 + n * D * 2 * 2 + n * F * 2 * 2
+        out[name] = {"ms": t, "TFLOP/s": flops / t / 1e9, "frac_mfma": flops / (t / 1e3) / PEAK_BF16,
+                     "GB/s": nbytes / (t / 1e3) / 1e9, "frac_hbm": nbytes / (t / 1e3) / PEAK_HBM,
+                     "algorithmic_bytes": nbytes}
+    return out
+
+
 EXTRAS = (("tiny_fp32", extra_tiny), ("colsum_top64", extra_colsum), ("lsp_commit", extra_lsp),
           ("gqa_lock_loop", extra_lock_loop), ("select_b8_asymptote", extra_select_b8),
-          ("nonsalient_dv_update", extra_dv_update))
+          ("nonsalient_dv_update", extra_dv_update), ("salient_ffn", extra_salient_ffn))
 
 
 def cpu_baseline(W, sh, seconds):
