@@ -27,12 +27,16 @@ Pages followed (title, section):
   [LSP]     "Beyond Scattered Acceptance: Fast and Coherent Inference for DLMs
             via Longest Stable Prefixes" - Methodologie (commit the longest
             contiguous stable block at the start of the active region in one
-            step; commit at least one token as a fallback).
+            step; commit at least one token as a fallback; logit margin
+            as the stability score, adaptive threshold within a fraction range
+            of the active length).
 
 Pinning status: every function here is pinned by tests/test_oracle_pins.py to
 closed forms, brute force on tiny inputs or invariants (see that file).
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -356,6 +360,50 @@ def stable_prefix_step(argmax, maxprob, ring, step, gen_lo, gen_hi, conf_thresho
             run = 1
         new[b] = L + run
     return ring, new
+
+
+def logit_margin(rows, w_lm):
+    """[LSP] Methodologie, stability diagnosis: a position's logit margin, the
+    top-1 minus the top-2 logit (0 when the maximum is attained twice), and the
+    argmax (lowest index on ties).  rows [n, D], w_lm [V, D]."""
+    z = np.asarray(rows, dtype=f64) @ np.asarray(w_lm, dtype=f64).T
+    a = np.argmax(z, axis=1)
+    srt = np.sort(z, axis=1)
+    return srt[:, -1] - srt[:, -2], a.astype(np.int64)
+
+
+def lsp_adaptive_commit(margin, gen_lo, gen_hi, committed, frac_lo=0.25, frac_hi=0.5):
+    """[LSP] Methodologie, adaptive sizing: the threshold tau is searched so
+    that the stable block at the start of the active suffix covers a fraction
+    of the active length within [frac_lo, frac_hi]; at least one token is
+    committed.
+
+    Reading: with A the active length, lo = max(1, ceil(frac_lo A)) and
+    hi = max(lo, floor(frac_hi A)), tau is the largest threshold under which
+    the first lo active positions are all stable (their minimum margin), and
+    the block is the run of leading positions with margin >= tau, cut at hi.
+    margin [B,S] (float32 values compared exactly); committed [B] = committed
+    generated positions so far.  Returns (new committed [B], tau [B]; tau is
+    nan where nothing is active)."""
+    m = np.asarray(margin)
+    B = m.shape[0]
+    out = np.array(committed, dtype=np.int64, copy=True)
+    tau = np.full(B, np.nan)
+    G = gen_hi - gen_lo
+    for b in range(B):
+        A = G - int(out[b])
+        if A <= 0:
+            continue
+        act = m[b, gen_lo + out[b]:gen_hi]
+        lo = max(1, math.ceil(frac_lo * A))
+        hi = max(lo, math.floor(frac_hi * A))
+        t = act[:lo].min()
+        L = 0
+        while L < A and act[L] >= t:
+            L += 1
+        out[b] += min(L, hi)
+        tau[b] = t
+    return out, tau
 
 
 def admissible_frontiers(prev_set, stable_state, S_gen, min_commit):

@@ -470,6 +470,78 @@ def test_salient_ffn_closed_forms():
     assert np.array_equal(out, cache)
 
 
+def test_logit_margin_brute_force_and_ties():
+    rng = np.random.default_rng(17)
+    rows = rng.standard_normal((5, 6))
+    w = rng.standard_normal((9, 6))
+    m, a = O.logit_margin(rows, w)
+    for r in range(5):
+        z = [sum(x * y for x, y in zip(to_list(rows[r]), to_list(w[v]))) for v in range(9)]
+        zs = sorted(z, reverse=True)
+        assert m[r] == pytest.approx(zs[0] - zs[1], abs=1e-13) and a[r] == z.index(zs[0])
+    # a maximum attained twice: margin 0, argmax the lower index
+    w2 = np.zeros((4, 2))
+    w2[1] = w2[3] = [1.0, 0.0]
+    m, a = O.logit_margin(np.array([[2.0, 1.0]]), w2)
+    assert m[0] == 0.0 and a[0] == 1
+
+
+def bf_lsp(margins, committed, G, frac_lo, frac_hi):
+    """Brute force: try every candidate threshold (each margin value) and keep
+    the largest one whose leading stable run reaches lo."""
+    A = G - committed
+    if A <= 0:
+        return committed, None
+    act = margins[committed:]
+    lo = max(1, math.ceil(frac_lo * A))
+    hi = max(lo, math.floor(frac_hi * A))
+    best = None
+    for t in sorted(set(act), reverse=True):
+        run = 0
+        while run < A and act[run] >= t:
+            run += 1
+        if run >= lo:
+            best = (t, run)
+            break
+    return committed + min(best[1], hi), best[0]
+
+
+def test_lsp_adaptive_commit_brute_force():
+    rng = np.random.default_rng(18)
+    B, S, lo_g = 6, 40, 8
+    G = S - lo_g
+    for trial in range(20):
+        m = np.round(rng.standard_normal((B, S)) * 3, 1).astype(np.float32)   # ties on purpose
+        com = rng.integers(0, G + 1, B)
+        fl, fh = [(0.25, 0.5), (0.1, 0.3), (0.5, 0.5)][trial % 3]
+        out, tau = O.lsp_adaptive_commit(m, lo_g, S, com, fl, fh)
+        for b in range(B):
+            want, t = bf_lsp([float(x) for x in m[b, lo_g:]], int(com[b]), G, fl, fh)
+            assert out[b] == want
+            assert (t is None and np.isnan(tau[b])) or tau[b] == t
+
+
+def test_lsp_adaptive_commit_closed_forms():
+    # strictly decreasing margins over A = 8 active: tau = 2nd margin, block = lo = 2
+    m = np.array([[9.0, 8, 7, 6, 5, 4, 3, 2]], np.float32)
+    out, tau = O.lsp_adaptive_commit(m, 0, 8, [0])
+    assert out[0] == 2 and tau[0] == 8.0
+    # all equal: every position is stable under tau, the block is cut at hi = 4
+    out, _ = O.lsp_adaptive_commit(np.ones((1, 8), np.float32), 0, 8, [0])
+    assert out[0] == 4
+    # one active position: it is committed (the fallback); none active: unchanged
+    out, tau = O.lsp_adaptive_commit(np.zeros((1, 8), np.float32), 0, 8, [7])
+    assert out[0] == 8
+    out, tau = O.lsp_adaptive_commit(np.zeros((1, 8), np.float32), 0, 8, [8])
+    assert out[0] == 8 and np.isnan(tau[0])
+    # the geometric shrink: repeated commits on equal margins take half each time
+    c, seen = 0, []
+    while c < 64:
+        c = int(O.lsp_adaptive_commit(np.ones((1, 64), np.float32), 0, 64, [c])[0][0])
+        seen.append(c)
+    assert seen[:4] == [32, 48, 56, 60]
+
+
 def test_colsum_sum_invariant_and_library_softmax():
     B, S, nq, Hq, Hkv, hd = 2, 11, 6, 4, 2, 3
     q, kc, vc, idx, offsets = _attn_inputs(B, S, nq, Hq, Hkv, hd, 13)
