@@ -13,6 +13,7 @@
  *                                                       -> dlm_partial_attn
  *      optional: per-key attention column sums + top-k  -> dlm_attn_colsum
  *      optional: longest-stable-prefix commit           -> dlm_stable_prefix
+ *                (adaptive threshold on the logit margin -> dlm_lsp_adaptive_commit)
  *      optional: FFN of the salient rows                -> dlm_salient_ffn
  *      optional: value-change update of the stable rows -> dlm_nonsalient_dv_update
  *                (caches kept with dlm_gather_rows / dlm_scatter_rows)
@@ -68,6 +69,7 @@ extern "C" {
 #define DLM_SCORE_COSINE 0
 #define DLM_SCORE_CONFIDENCE 1
 #define DLM_SCORE_GIVEN 2
+#define DLM_SCORE_MARGIN 3
 
 const char* dlm_status_string(int status);
 const char* dlm_last_error(void);
@@ -98,6 +100,11 @@ const char* dlm_version(void);
  *     argmax[b,i] = lowest v attaining max z.  `scores` [B,S] f32 and
  *     `argmax` [B,S] i32 are required and act as caches: entries of rows
  *     not evaluated keep their values.  D % 64 == 0, V % 256 == 0.
+ * mode DLM_SCORE_MARGIN:  as DLM_SCORE_CONFIDENCE, with scores[b,i] = the
+ *     logit margin, max z minus the second-largest logit (0 when the maximum
+ *     is attained twice).  Follows "Beyond Scattered Acceptance: Fast and
+ *     Coherent Inference for DLMs via Longest Stable Prefixes", Methodologie
+ *     (stability diagnosis by the logit margin).
  * mode DLM_SCORE_GIVEN:  a = scores f32 [B,S] supplied by the caller
  *     (e.g. 1 = locked, 0 = unlocked); b, scores, argmax unused.
  *
@@ -311,6 +318,32 @@ int dlm_gather_rows(const void* cache, int B, int S, int row_bytes,
                     void* rows, void* stream);
 int dlm_scatter_rows(const void* rows, const int32_t* idx, const int32_t* offsets,
                      int max_rows, int B, int S, int row_bytes, void* cache, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dlm_lsp_adaptive_commit
+ *
+ * Commit with an adaptive threshold on the logit margin.  Follows: "Beyond
+ * Scattered Acceptance: Fast and Coherent Inference for DLMs via Longest
+ * Stable Prefixes", Methodologie (stability by the logit margin; the
+ * threshold tau is searched so that the committed stable block covers a
+ * fraction range of the active length, e.g. 25 % to 50 %; at least one
+ * token is committed; structural snapping is not done).
+ *
+ * margin [B,S] f32 (DLM_SCORE_MARGIN scores); committed [B] i32 = generated
+ * positions committed so far, updated in place.  For each b with A =
+ * (gen_hi - gen_lo) - committed[b] > 0 active positions starting at
+ * gen_lo + committed[b]:
+ *   lo = max(1, ceil(frac_lo * A)), hi = max(lo, floor(frac_hi * A))
+ *        (computed in double from the float32 fractions)
+ *   tau = min of the first lo active margins (the largest threshold under
+ *         which they are all stable)
+ *   committed[b] += min(run of leading active margins >= tau, hi)
+ * tau [B] f32 (may be NULL) receives tau, or NaN where nothing is active.
+ * 0 < frac_lo <= frac_hi <= 1, else DLM_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------ */
+int dlm_lsp_adaptive_commit(const float* margin, int B, int S, int gen_lo, int gen_hi,
+                            float frac_lo, float frac_hi, int32_t* committed, float* tau,
+                            void* stream);
 
 /* ------------------------------------------------------------------------
  * dlm_probe_mfma_bf16  (measurement aid, not a step of the method)

@@ -17,7 +17,7 @@ from .build import LIB_PATH
 
 DLM_OK, DLM_ERR_INVALID_ARG, DLM_ERR_UNSUPPORTED, DLM_ERR_WORKSPACE, DLM_ERR_HIP = range(5)
 DLM_F32, DLM_BF16 = 0, 1
-DLM_SCORE_COSINE, DLM_SCORE_CONFIDENCE, DLM_SCORE_GIVEN = 0, 1, 2
+DLM_SCORE_COSINE, DLM_SCORE_CONFIDENCE, DLM_SCORE_GIVEN, DLM_SCORE_MARGIN = 0, 1, 2, 3
 
 
 class DlmError(RuntimeError):
@@ -72,6 +72,8 @@ lib.dlm_salient_ffn_workspace_size.restype = _Z
 lib.dlm_salient_ffn_workspace_size.argtypes = [_I] * 4
 lib.dlm_salient_ffn.restype = _I
 lib.dlm_salient_ffn.argtypes = [_I, _P, _I, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _Z, _P]
+lib.dlm_lsp_adaptive_commit.restype = _I
+lib.dlm_lsp_adaptive_commit.argtypes = [_P, _I, _I, _I, _I, _F, _F, _P, _P, _P]
 lib.dlm_gather_rows.restype = _I
 lib.dlm_gather_rows.argtypes = [_P, _I, _I, _I, _P, _P, _I, _P, _P]
 lib.dlm_scatter_rows.restype = _I
@@ -142,8 +144,8 @@ def dlm_attn_colsum_workspace_size(B, S, Hkv) -> int:
 def dlm_saliency_select(mode, a, b, *, lo, hi, threshold, idx, counts, offsets, workspace=None,
                         scores=None, argmax=None, eval_idx=None, eval_offsets=None, max_eval=0,
                         stream=None):
-    """a, b: COSINE cur/prev [B,S,D]; CONFIDENCE hidden [B,S,D] / W_lm [V,D];
-    GIVEN scores f32 [B,S] (b None)."""
+    """a, b: COSINE cur/prev [B,S,D]; CONFIDENCE and MARGIN hidden [B,S,D] /
+    W_lm [V,D]; GIVEN scores f32 [B,S] (b None)."""
     if mode == DLM_SCORE_GIVEN:
         B, S = a.shape
         D = V = 0
@@ -152,7 +154,7 @@ def dlm_saliency_select(mode, a, b, *, lo, hi, threshold, idx, counts, offsets, 
     else:
         B, S, D = a.shape
         dtype = _dt(a)
-        V = b.shape[0] if mode == DLM_SCORE_CONFIDENCE else 0
+        V = b.shape[0] if mode in (DLM_SCORE_CONFIDENCE, DLM_SCORE_MARGIN) else 0
     wp, wn = _ws(workspace)
     rc = lib.dlm_saliency_select(
         mode, dtype, _ptr(a, "a"), _ptr(b, "b", required=False), B, S, D, V,
@@ -244,6 +246,15 @@ def dlm_salient_ffn(x, idx, offsets, max_rows, w_gu, w_down, out_cache, workspac
         _dt(x), _ptr(x, "x"), B, S, D, _ptr(idx, "idx", torch.int32, False),
         _ptr(offsets, "offsets", torch.int32, False), int(max_rows), _ptr(w_gu, "w_gu", x.dtype), F,
         _ptr(w_down, "w_down", x.dtype), _ptr(out_cache, "out_cache", x.dtype), wp, wn, _stream(stream))
+    _check(rc)
+
+
+def dlm_lsp_adaptive_commit(margin, gen_lo, gen_hi, committed, frac_lo=0.25, frac_hi=0.5, tau=None,
+                            stream=None):
+    B, S = margin.shape
+    rc = lib.dlm_lsp_adaptive_commit(
+        _ptr(margin, "margin", torch.float32), B, S, int(gen_lo), int(gen_hi), float(frac_lo), float(frac_hi),
+        _ptr(committed, "committed", torch.int32), _ptr(tau, "tau", torch.float32, False), _stream(stream))
     _check(rc)
 
 

@@ -101,6 +101,14 @@ __device__ __forceinline__ int batch_of(const int32_t* offsets, int B, int r) {
 // Merge two softmax partials (max m, sum of exp(z - m), argmax a) of disjoint
 // logit sets.  Ties in the max keep the lower index.  s*exp(m-M) + s2*exp(m2-M)
 // is commutative, so merge(x, y) and merge(y, x) give identical bits.
+// Second-largest value of the union of two sets given each set's largest (m,
+// c1) and second-largest (t2, c2) values: the smaller of the two maxima or
+// either set's second value, whichever is larger.  Call before the maxima are
+// merged.
+__device__ __forceinline__ float merge_second(float m, float t2, float c1, float c2) {
+  return fmaxf(fminf(m, c1), fmaxf(t2, c2));
+}
+
 __device__ __forceinline__ void merge_part(float& m, float& s, int& a, float m2, float s2, int a2) {
   if (m2 == -INFINITY) return;  // empty partner (lane without tiles)
   if (m == -INFINITY) {

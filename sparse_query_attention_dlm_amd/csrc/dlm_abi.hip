@@ -62,7 +62,7 @@ const char* dlm_version(void) { return "libdlm 0.1 (gfx950)"; }
 size_t dlm_select_workspace_size(int mode, int B, int S, int V, int max_eval) {
   size_t n = kSelectTicketBytes;
   if (B > 0 && S > 0) n += round_up((size_t)B * S * sizeof(float), 256);
-  if (mode == DLM_SCORE_CONFIDENCE && V > 0 && max_eval > 0) {
+  if ((mode == DLM_SCORE_CONFIDENCE || mode == DLM_SCORE_MARGIN) && V > 0 && max_eval > 0) {
     n += round_up((size_t)max_eval * dlm::gemm_lmhead_ntile(V) * sizeof(float4), 256);
     n += dlm::gemm_workspace_bytes(dlm::EPI_LMHEAD, max_eval, V, 0);
   }
@@ -74,7 +74,8 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b, int B
                         int lo, int hi, float threshold, float* scores, int32_t* argmax,
                         int32_t* idx, int32_t* counts, int32_t* offsets, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  REQUIRE(mode == DLM_SCORE_COSINE || mode == DLM_SCORE_CONFIDENCE || mode == DLM_SCORE_GIVEN,
+  REQUIRE(mode == DLM_SCORE_COSINE || mode == DLM_SCORE_CONFIDENCE || mode == DLM_SCORE_GIVEN ||
+              mode == DLM_SCORE_MARGIN,
           "unknown scoring mode %d", mode);
   REQUIRE(dtype == DLM_F32 || dtype == DLM_BF16, "unknown dtype %d", dtype);
   REQUIRE(B > 0 && S > 0, "B and S must be positive (B=%d S=%d)", B, S);
@@ -146,8 +147,8 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b, int B
     if (rc != DLM_OK) return rc;
   }
   return hip_status(dlm::launch_lmhead_combine(part, ntile, eval_idx, eval_offsets, max_eval, B, S,
-                                               lo, hi, threshold, scores, argmax, idx, counts,
-                                               offsets, st),
+                                               lo, hi, threshold, mode == DLM_SCORE_MARGIN,
+                                               scores, argmax, idx, counts, offsets, st),
                     "LM-head combine");
 }
 
@@ -531,6 +532,22 @@ int dlm_nonsalient_dv_update(int dtype, const void* q_cache, const float* lse_ca
   a.o = o_cache;
   return hip_status(dlm::launch_dv_update(dtype, a, static_cast<hipStream_t>(stream)),
                     "non-salient update");
+}
+
+// ---------------------------------------------------------------------------
+int dlm_lsp_adaptive_commit(const float* margin, int B, int S, int gen_lo, int gen_hi,
+                            float frac_lo, float frac_hi, int32_t* committed, float* tau,
+                            void* stream) {
+  REQUIRE_PTR(margin);
+  REQUIRE_PTR(committed);
+  REQUIRE(B > 0 && S > 0, "B and S must be positive");
+  REQUIRE(0 <= gen_lo && gen_lo < gen_hi && gen_hi <= S, "generated region [%d,%d) invalid",
+          gen_lo, gen_hi);
+  REQUIRE(frac_lo > 0.f && frac_lo <= frac_hi && frac_hi <= 1.f,
+          "fractions must satisfy 0 < frac_lo <= frac_hi <= 1 (got %g, %g)", frac_lo, frac_hi);
+  return hip_status(dlm::launch_lsp_adaptive(margin, B, S, gen_lo, gen_hi, frac_lo, frac_hi,
+                                             committed, tau, static_cast<hipStream_t>(stream)),
+                    "adaptive commit");
 }
 
 // ---------------------------------------------------------------------------

@@ -86,50 +86,60 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
         }
     }
   } else {
-    __shared__ float s_pm[WP][TT], s_ps[WP][TT];
+    __shared__ float s_pm[WP][TT], s_ps[WP][TT], s_p2[WP][TT];
     __shared__ int s_pa[WP][TT];
 #pragma unroll
     for (int b = 0; b < FT; ++b) {
       const int ml = wt * WTT + b * 32 + lr;
-      // running (max, sum exp(z - max), argmax) merged 16 logits at a time
-      float m = -INFINITY, s = 0.f;
+      // running (max, sum exp(z - max), argmax) merged 16 logits at a time,
+      // and the second-largest logit (the max itself when attained twice)
+      float m = -INFINITY, s = 0.f, t2 = -INFINITY;
       int am = 0x7fffffff;
 #pragma unroll
       for (int a = 0; a < FP; ++a) {
-        float cm = acc[a][b][0];
+        float cm = acc[a][b][0], c2 = -INFINITY;
         int ca = n0 + wp * WTP + a * 32 + 4 * lg;
 #pragma unroll
         for (int i = 1; i < 16; ++i) {
           const int n = n0 + wp * WTP + a * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
           const float v = acc[a][b][i];
           if (v > cm) {  // rows grow with i, so ties keep the lower index
+            c2 = cm;
             cm = v;
             ca = n;
+          } else {
+            c2 = fmaxf(c2, v);
           }
         }
         const float cm2 = cm * kLog2e;
         float cs = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) cs += __builtin_amdgcn_exp2f(fmaf(acc[a][b][i], kLog2e, -cm2));
+        t2 = merge_second(m, t2, cm, c2);
         merge_part(m, s, am, cm, cs, ca);
       }
-      const float m2 = __shfl_xor(m, 32, 64), s2 = __shfl_xor(s, 32, 64);
+      const float m2 = __shfl_xor(m, 32, 64), s2 = __shfl_xor(s, 32, 64), q2 = __shfl_xor(t2, 32, 64);
       const int a2 = __shfl_xor(am, 32, 64);
+      t2 = merge_second(m, t2, m2, q2);
       merge_part(m, s, am, m2, s2, a2);
       if (lg == 0) {
         s_pm[wp][ml] = m;
         s_ps[wp][ml] = s;
         s_pa[wp][ml] = am;
+        s_p2[wp][ml] = t2;
       }
     }
     __syncthreads();
     for (int t = tid; t < TT; t += 256) {
       if (s_drow[t] < 0) continue;
-      float m = s_pm[0][t], s = s_ps[0][t];
+      float m = s_pm[0][t], s = s_ps[0][t], t2 = s_p2[0][t];
       int am = s_pa[0][t];
 #pragma unroll
-      for (int w = 1; w < WP; ++w) merge_part(m, s, am, s_pm[w][t], s_ps[w][t], s_pa[w][t]);
-      g.lm_part[(size_t)(m0 + t) * g.ntile + nt] = make_float4(m, s, __int_as_float(am), 0.f);
+      for (int w = 1; w < WP; ++w) {
+        t2 = merge_second(m, t2, s_pm[w][t], s_p2[w][t]);
+        merge_part(m, s, am, s_pm[w][t], s_ps[w][t], s_pa[w][t]);
+      }
+      g.lm_part[(size_t)(m0 + t) * g.ntile + nt] = make_float4(m, s, __int_as_float(am), t2);
     }
   }
 }

@@ -28,8 +28,8 @@ hipError_t launch_given_select(const float* scores, int B, int S, int lo, int hi
                                int32_t* idx, int32_t* counts, int32_t* offsets, hipStream_t st);
 hipError_t launch_lmhead_combine(const float4* part, int ntile, const int32_t* eval_idx,
                                  const int32_t* eval_offsets, int max_eval, int B, int S, int lo,
-                                 int hi, float thr, float* scores, int32_t* argmax, int32_t* idx,
-                                 int32_t* counts, int32_t* offsets, hipStream_t st);
+                                 int hi, float thr, int margin, float* scores, int32_t* argmax,
+                                 int32_t* idx, int32_t* counts, int32_t* offsets, hipStream_t st);
 
 // gemm.hip -- D^T[n][m] = sum_k W[n][k] * A[row(m)][k]; W output-major [N][K].
 enum GemmEpilogue { EPI_QKV = 0, EPI_ROWS = 1, EPI_LMHEAD = 2, EPI_SWIGLU = 3 };
@@ -108,6 +108,9 @@ hipError_t launch_row_copy(const void* src, void* dst, const int32_t* idx, const
                            int max_rows, int B, int S, int row_bytes, int scatter, hipStream_t st);
 
 // prefix.hip
+hipError_t launch_lsp_adaptive(const float* margin, int B, int S, int gen_lo, int gen_hi,
+                               float frac_lo, float frac_hi, int32_t* committed, float* tau,
+                               hipStream_t st);
 hipError_t launch_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
                                 int gen_lo, int gen_hi, int32_t* ring, int W, int step, float thr,
                                 int min_commit, int32_t* committed, hipStream_t st);

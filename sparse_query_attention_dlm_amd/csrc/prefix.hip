@@ -48,6 +48,57 @@ __global__ __launch_bounds__(256) void stable_prefix_kernel(const int32_t* __res
   }
 }
 
+// Adaptive-threshold commit (Longest Stable Prefixes, Methodologie: stability
+// by the logit margin; the threshold is searched so that the stable block
+// covers a fraction range of the active length; at least one token).  With A
+// active positions, lo = max(1, ceil(frac_lo A)) and hi = max(lo, floor(frac_hi
+// A)): tau is the largest threshold under which the first lo active positions
+// are stable (their minimum margin), and the block is the run of leading
+// positions with margin >= tau, cut at hi.  One workgroup per sequence: a
+// block min for tau, then an LDS atomicMin for the first position below it.
+__global__ __launch_bounds__(256) void lsp_adaptive_kernel(const float* __restrict__ margin, int S,
+                                                           int gen_lo, int gen_hi, float frac_lo,
+                                                           float frac_hi,
+                                                           int32_t* __restrict__ committed,
+                                                           float* __restrict__ tau) {
+  __shared__ float s_min[4];
+  __shared__ int s_first;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = committed[b];
+  const int A = (gen_hi - gen_lo) - c;
+  if (A <= 0) {
+    if (tid == 0 && tau) tau[b] = __builtin_nanf("");
+    return;
+  }
+  // integer bounds in double, from the float32 fractions given
+  const int lo = max(1, (int)ceil((double)frac_lo * A));
+  const int hi = max(lo, (int)floor((double)frac_hi * A));
+  const float* act = margin + (size_t)b * S + gen_lo + c;
+  float m = INFINITY;
+  for (int i = tid; i < lo; i += 256) m = fminf(m, act[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fminf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) s_min[wave] = m;
+  if (tid == 0) s_first = A;
+  __syncthreads();
+  const float t = fminf(fminf(s_min[0], s_min[1]), fminf(s_min[2], s_min[3]));
+  for (int i = tid; i < A; i += 256)
+    if (act[i] < t) atomicMin(&s_first, i);
+  __syncthreads();
+  if (tid == 0) {
+    committed[b] = c + min(s_first, hi);
+    if (tau) tau[b] = t;
+  }
+}
+
+hipError_t launch_lsp_adaptive(const float* margin, int B, int S, int gen_lo, int gen_hi,
+                               float frac_lo, float frac_hi, int32_t* committed, float* tau,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(lsp_adaptive_kernel, dim3(B), dim3(256), 0, st, margin, S, gen_lo, gen_hi,
+                     frac_lo, frac_hi, committed, tau);
+  return hipGetLastError();
+}
+
 hipError_t launch_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
                                 int gen_lo, int gen_hi, int32_t* ring, int W, int step, float thr,
                                 int min_commit, int32_t* committed, hipStream_t st) {

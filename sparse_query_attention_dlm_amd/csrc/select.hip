@@ -177,32 +177,37 @@ __global__ __launch_bounds__(256) void given_select_kernel(const float* __restri
   compact_rows(scores, B, S, lo, hi, thr, b, b + 1, base, idx, counts, offsets);
 }
 
-// Merge of per-vocabulary-tile partials (max logit, sum exp(z - max), argmax)
-// into max-prob and argmax per evaluated row, then the compaction.
+// Merge of per-vocabulary-tile partials (max logit, sum exp(z - max), argmax,
+// second-largest logit) into the score and argmax per evaluated row, then the
+// compaction.  The score is the max-prob (SlowFast, Metodologia, certainty
+// principle) or the logit margin, top-1 minus top-2 (LSP, Methodologie,
+// stability diagnosis).
 __global__ __launch_bounds__(256) void lmhead_combine_kernel(
     const float4* __restrict__ part, int ntile, const int32_t* __restrict__ eval_idx,
-    const int32_t* __restrict__ eval_offsets, int max_eval, int B, int S, float* scores,
+    const int32_t* __restrict__ eval_offsets, int max_eval, int B, int S, int margin, float* scores,
     int32_t* argmax) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + wave;
   const int n_eval = min(eval_offsets[B], max_eval);
   if (r < n_eval) {
-    float m = -INFINITY, s = 0.f;
+    float m = -INFINITY, s = 0.f, t2 = -INFINITY;
     int a = 0x7fffffff;
     for (int t = lane; t < ntile; t += 64) {
       const float4 p = part[(size_t)r * ntile + t];
+      t2 = merge_second(m, t2, p.x, p.w);
       merge_part(m, s, a, p.x, p.y, __float_as_int(p.z));
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+      const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64), q2 = __shfl_xor(t2, o, 64);
       const int a2 = __shfl_xor(a, o, 64);
+      t2 = merge_second(m, t2, m2, q2);
       merge_part(m, s, a, m2, s2, a2);
     }
     if (lane == 0) {
       const int b = batch_of(eval_offsets, B, r);
       const size_t pos = (size_t)b * S + eval_idx[r];
-      scores[pos] = 1.0f / s;
+      scores[pos] = margin ? m - t2 : 1.0f / s;
       argmax[pos] = a;
     }
   }
@@ -244,12 +249,12 @@ hipError_t launch_cosine_select(int dtype, const void* cur, const void* prev, in
 
 hipError_t launch_lmhead_combine(const float4* part, int ntile, const int32_t* eval_idx,
                                  const int32_t* eval_offsets, int max_eval, int B, int S, int lo,
-                                 int hi, float thr, float* scores, int32_t* argmax, int32_t* idx,
-                                 int32_t* counts, int32_t* offsets, hipStream_t st) {
+                                 int hi, float thr, int margin, float* scores, int32_t* argmax,
+                                 int32_t* idx, int32_t* counts, int32_t* offsets, hipStream_t st) {
   if (max_eval > 0) {
     const int grid = (max_eval + 3) / 4;
     hipLaunchKernelGGL(lmhead_combine_kernel, dim3(grid), dim3(256), 0, st, part, ntile, eval_idx,
-                       eval_offsets, max_eval, B, S, scores, argmax);
+                       eval_offsets, max_eval, B, S, margin, scores, argmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

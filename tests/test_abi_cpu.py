@@ -242,3 +242,22 @@ def test_salient_ffn_rejections(lib):
     # h [max_rows, F] bf16 first, 256-byte aligned
     assert lib.dlm_salient_ffn_workspace_size(BF16, 8, 128, 256) == 8 * 256 * 2
     assert lib.dlm_salient_ffn_workspace_size(F32, 8, 128, 256) == 0
+
+
+def test_margin_mode_and_adaptive_commit_rejections(lib):
+    MARGIN = 3
+    assert select(lib, mode=MARGIN, dtype=F32, V=256, ev=FAKE, evo=FAKE, scores=FAKE, argmax=FAKE) == INVALID
+    assert select(lib, mode=MARGIN, V=128, ev=FAKE, evo=FAKE, scores=FAKE, argmax=FAKE, max_eval=4) == INVALID
+    assert select(lib, mode=MARGIN, V=256, ev=FAKE, evo=FAKE, scores=0, argmax=FAKE) == INVALID
+    # the margin mode needs the same LM-head partials as the confidence mode
+    assert lib.dlm_select_workspace_size(MARGIN, 2, 64, 32768, 16) == lib.dlm_select_workspace_size(CONFIDENCE, 2, 64, 32768, 16)
+
+    def lsp(m=FAKE, B=2, S=32, lo=8, hi=32, fl=0.25, fh=0.5, com=FAKE, tau=0):
+        return lib.dlm_lsp_adaptive_commit(p(m), B, S, lo, hi, f(fl), f(fh), p(com), p(tau), p(0))
+    assert lsp(m=0) == INVALID
+    assert lsp(com=0) == INVALID
+    assert lsp(lo=8, hi=8) == INVALID
+    assert lsp(hi=33) == INVALID
+    assert lsp(fl=0.0) == INVALID
+    assert lsp(fl=0.6, fh=0.5) == INVALID
+    assert lsp(fh=1.5) == INVALID

@@ -859,3 +859,116 @@ def test_salient_ffn_short_k_and_loose_bound(dlm):
 def test_salient_ffn_one_layer_full_size(dlm):
     """One layer of 1024 positions, D = 4096, F = 12288, 102 salient rows."""
     run_salient_ffn(dlm, B=1, S=1024, D=4096, F=12288, n_per_b=[102], seed=44)
+
+
+# ---------------------------------------------------------------------------
+# LSP: logit margin scores and the adaptive-threshold commit
+# ---------------------------------------------------------------------------
+def margin_select(dlm, h, w_lm, rows, lo, S):
+    """Margin scores (and argmax) of the listed rows through the select call."""
+    B = h.shape[0]
+    ev_idx, ev_off = W.pack_rows(rows)
+    scores = torch.zeros(B, S, dtype=torch.float32, device="cuda")
+    argmax = torch.full((B, S), -1, dtype=torch.int32, device="cuda")
+    idx = torch.zeros(B * S, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(B, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    ws = workspace(dlm.dlm_select_workspace_size(dlm.DLM_SCORE_MARGIN, B, S, w_lm.shape[0], len(ev_idx)))
+    dlm.dlm_saliency_select(dlm.DLM_SCORE_MARGIN, dev(h, "bf16"), dev(w_lm, "bf16"), lo=lo, hi=S, threshold=0.5,
+                            idx=idx, counts=counts, offsets=offsets, scores=scores, argmax=argmax,
+                            eval_idx=i32(ev_idx), eval_offsets=i32(ev_off), max_eval=len(ev_idx), workspace=ws)
+    torch.cuda.synchronize()
+    return scores, argmax
+
+
+def check_margins(h, w_lm, rows, scores, argmax, sample=None):
+    sc, am = scores.cpu().numpy(), argmax.cpu().numpy()
+    worst, n = 0.0, 0
+    for b, r in enumerate(rows):
+        pick = np.asarray(r) if sample is None else np.asarray(r)[np.linspace(0, len(r) - 1, sample).astype(int)]
+        m, a = O.logit_margin(h[b, pick], w_lm)
+        clear = m > BAND
+        assert np.array_equal(am[b, pick][clear], a[clear]), f"b {b}: argmax"
+        worst = max(worst, maxabs(sc[b, pick], m))
+        n += len(pick)
+    say(f"  {n} rows: margin err {worst:.2e}")
+    assert worst <= TOL["bf16"]
+
+
+def test_margin_scores_small(dlm):
+    """A few evaluated rows (split-K LM-head tiles and their reduce pass):
+    margins and argmax against the oracle; rows not evaluated keep -1."""
+    rng = np.random.default_rng(51)
+    B, S, D, V = 2, 96, 512, 2048
+    h = W.round_bf16(rng.standard_normal((B, S, D)))
+    w = W.round_bf16(rng.standard_normal((V, D)) * 0.05)
+    rows = [np.arange(40, 70), np.arange(10, 19)]
+    say(f"[margin small] B={B} S={S} D={D} V={V}")
+    scores, argmax = margin_select(dlm, h, w, rows, 0, S)
+    check_margins(h, w, rows, scores, argmax)
+    assert argmax[0, 0].item() == -1 and argmax[1, 95].item() == -1
+
+
+def test_margin_scores_lsp_workload_full_size(dlm):
+    """The LSP workload's first step at full size (B = 16, S = 1024, D = 4096,
+    V = 32768, the active rows): 48 sampled rows against the oracle."""
+    sh = W.LSP_COMMIT
+    inp = W.lsp_inputs(sh)
+    rows = inp.active_rows(0)
+    h = inp.hidden(0)
+    say(f"[margin full size] B={sh.B} S={sh.S} D={sh.D} V={sh.V}")
+    scores, argmax = margin_select(dlm, h, inp.w_lm, rows, sh.prompt, sh.S)
+    check_margins(h, inp.w_lm, rows, scores, argmax, sample=3)
+
+
+def test_lsp_adaptive_commit_bit_exact(dlm):
+    """On given float32 margins (ties on purpose, every frontier including the
+    done and one-left cases, three fraction ranges): committed and tau
+    identical to the oracle."""
+    rng = np.random.default_rng(52)
+    B, S, gen_lo = 16, 700, 100
+    G = S - gen_lo
+    for fl, fh in [(0.25, 0.5), (0.1, 0.3), (0.5, 0.5)]:
+        m = np.round(rng.standard_normal((B, S)) * 2, 1).astype(np.float32)
+        com = rng.integers(0, G + 1, B).astype(np.int32)
+        com[0], com[1], com[2] = G, G - 1, 0
+        ct = i32(com)
+        tau = torch.zeros(B, dtype=torch.float32, device="cuda")
+        dlm.dlm_lsp_adaptive_commit(torch.from_numpy(m).cuda(), gen_lo, S, ct, fl, fh, tau=tau)
+        torch.cuda.synchronize()
+        want, wt = O.lsp_adaptive_commit(m, gen_lo, S, com, float(np.float32(fl)), float(np.float32(fh)))
+        assert np.array_equal(ct.cpu().numpy(), want)
+        got_t = tau.cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isnan(got_t), np.isnan(wt))
+        assert np.array_equal(got_t[~np.isnan(wt)], wt[~np.isnan(wt)])
+
+
+def test_lsp_margin_commit_loop(dlm):
+    """A decoding loop on the library alone: margins of the active rows, then the
+    adaptive commit, until every generated position is committed; each commit
+    equals the oracle's on the same margins, and each step commits between
+    the fraction bounds."""
+    rng = np.random.default_rng(53)
+    B, S, D, V, gen_lo = 3, 192, 256, 1024, 64
+    G = S - gen_lo
+    w = W.round_bf16(rng.standard_normal((V, D)) * 0.05)
+    com = torch.zeros(B, dtype=torch.int32, device="cuda")
+    steps = 0
+    say(f"[margin loop] B={B} S={S} D={D} V={V}")
+    while int(com.min().item()) < G:
+        h = W.round_bf16(rng.standard_normal((B, S, D)))
+        c = com.cpu().numpy()
+        rows = [np.arange(gen_lo + int(c[b]), S) if c[b] < G else np.arange(gen_lo, gen_lo + 1) for b in range(B)]
+        scores, _ = margin_select(dlm, h, w, rows, gen_lo, S)
+        dlm.dlm_lsp_adaptive_commit(scores, gen_lo, S, com)
+        torch.cuda.synchronize()
+        want, _ = O.lsp_adaptive_commit(scores.cpu().numpy(), gen_lo, S, c)
+        got = com.cpu().numpy()
+        assert np.array_equal(got, want)
+        for b in range(B):
+            A = G - int(c[b])
+            if A > 0:
+                assert max(1, math.ceil(0.25 * A)) <= got[b] - c[b] <= max(1, math.ceil(0.25 * A), math.floor(0.5 * A))
+        steps += 1
+        assert steps < 40
+    say(f"  done in {steps} steps")
