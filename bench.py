@@ -464,14 +464,30 @@ def extra_lsp(dlm, W):
     def prefix():
         dlm.dlm_stable_prefix(argmax, scores, sh.prompt, S, ring, step[0], sh.conf, com)
         step[0] += 1
+    # the margin variant: the same LM-head pass scoring top-1 minus top-2, then
+    # the adaptive-threshold commit from a fresh frontier (restored each call)
+    margin = torch.zeros(B, S, dtype=torch.float32, device="cuda")
+    mar = lambda: dlm.dlm_saliency_select(dlm.DLM_SCORE_MARGIN, h, w, lo=sh.prompt, hi=S, threshold=0.0, idx=idx,
+                                          counts=counts, offsets=offsets, scores=margin, argmax=argmax,
+                                          eval_idx=eidx, eval_offsets=eoff, max_eval=n, workspace=ws)
+    com2 = torch.zeros(B, dtype=torch.int32, device="cuda")
+    tau = torch.empty(B, dtype=torch.float32, device="cuda")
+
+    def adaptive():
+        com2.zero_()
+        dlm.dlm_lsp_adaptive_commit(margin, sh.prompt, S, com2, 0.25, 0.5, tau=tau)
     t_conf = _time(conf, 10)
     t_pre = _time(prefix, 10)
+    t_mar = _time(mar, 10)
+    t_ad = _time(adaptive, 10)
     f = 2.0 * n * D * V
     return {"workload": sh.name, "n_selected": n,
             "confidence_lm_head": {"ms": t_conf, "TFLOP/s": f / t_conf / 1e9, "frac": f / (t_conf / 1e3) / PEAK_BF16,
                                    "frac_of_measured_ceiling": of_measured(f / (t_conf / 1e3), "mfma_bf16")},
             "stable_prefix": {"ms": t_pre},
-            "tokens_per_s": n / ((t_conf + t_pre) / 1e3)}
+            "tokens_per_s": n / ((t_conf + t_pre) / 1e3),
+            "margin_lm_head": {"ms": t_mar, "TFLOP/s": f / t_mar / 1e9, "frac": f / (t_mar / 1e3) / PEAK_BF16},
+            "adaptive_commit": {"ms": t_ad, "note": "includes a 64-byte frontier reset"}}
 
 
 def extra_lock_loop(dlm, W):
