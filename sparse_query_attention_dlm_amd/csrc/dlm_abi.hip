@@ -142,7 +142,8 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b, int B
     g.lm_part = part;
     g.ntile = ntile;
     g.part = reinterpret_cast<float*>(gws);
-    int rc = hip_status(dlm::launch_gemm(DLM_BF16, dlm::EPI_LMHEAD, dlm::A_GATHER, g, st),
+    const int epi = mode == DLM_SCORE_MARGIN ? dlm::EPI_LMMARGIN : dlm::EPI_LMHEAD;
+    int rc = hip_status(dlm::launch_gemm(DLM_BF16, epi, dlm::A_GATHER, g, st),
                         "LM-head GEMM");
     if (rc != DLM_OK) return rc;
   }

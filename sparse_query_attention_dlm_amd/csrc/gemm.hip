@@ -17,6 +17,7 @@
 //   EPI_ROWS   - rows scattered into an output cache (W_o projection)
 //   EPI_LMHEAD - per (token, 256-column vocabulary tile): max logit, sum of
 //                exp(z - max) and the lowest argmax; logits never stored.
+//   EPI_LMMARGIN - the same plus the second-largest logit (the logit margin)
 // Tiles: TP (features) x TT (tokens) x 64 (k), 4 waves, 32x32x16 bf16 MFMA,
 // double-buffered LDS with 16-byte row padding, a branch-free register ring
 // of PF k-steps, operands fetched with buffer loads (one VGPR offset per
@@ -86,13 +87,16 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
         }
     }
   } else {
-    __shared__ float s_pm[WP][TT], s_ps[WP][TT], s_p2[WP][TT];
+    __shared__ float s_pm[WP][TT], s_ps[WP][TT], s_p2[EPI == EPI_LMMARGIN ? WP : 1][TT];
     __shared__ int s_pa[WP][TT];
 #pragma unroll
     for (int b = 0; b < FT; ++b) {
       const int ml = wt * WTT + b * 32 + lr;
       // running (max, sum exp(z - max), argmax) merged 16 logits at a time,
-      // and the second-largest logit (the max itself when attained twice)
+      // and for the margin the second-largest logit (the max itself when
+      // attained twice); the confidence epilogue leaves it out, as it costs
+      // registers in a kernel that already spills a little
+      constexpr bool TOP2 = EPI == EPI_LMMARGIN;
       float m = -INFINITY, s = 0.f, t2 = -INFINITY;
       int am = 0x7fffffff;
 #pragma unroll
@@ -104,10 +108,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
           const int n = n0 + wp * WTP + a * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
           const float v = acc[a][b][i];
           if (v > cm) {  // rows grow with i, so ties keep the lower index
-            c2 = cm;
+            if constexpr (TOP2) c2 = cm;
             cm = v;
             ca = n;
-          } else {
+          } else if constexpr (TOP2) {
             c2 = fmaxf(c2, v);
           }
         }
@@ -115,28 +119,29 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
         float cs = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) cs += __builtin_amdgcn_exp2f(fmaf(acc[a][b][i], kLog2e, -cm2));
-        t2 = merge_second(m, t2, cm, c2);
+        if constexpr (TOP2) t2 = merge_second(m, t2, cm, c2);
         merge_part(m, s, am, cm, cs, ca);
       }
-      const float m2 = __shfl_xor(m, 32, 64), s2 = __shfl_xor(s, 32, 64), q2 = __shfl_xor(t2, 32, 64);
+      const float m2 = __shfl_xor(m, 32, 64), s2 = __shfl_xor(s, 32, 64);
       const int a2 = __shfl_xor(am, 32, 64);
-      t2 = merge_second(m, t2, m2, q2);
+      if constexpr (TOP2) t2 = merge_second(m, t2, m2, __shfl_xor(t2, 32, 64));
       merge_part(m, s, am, m2, s2, a2);
       if (lg == 0) {
         s_pm[wp][ml] = m;
         s_ps[wp][ml] = s;
         s_pa[wp][ml] = am;
-        s_p2[wp][ml] = t2;
+        if constexpr (TOP2) s_p2[wp][ml] = t2;
       }
     }
     __syncthreads();
     for (int t = tid; t < TT; t += 256) {
       if (s_drow[t] < 0) continue;
-      float m = s_pm[0][t], s = s_ps[0][t], t2 = s_p2[0][t];
+      constexpr bool TOP2 = EPI == EPI_LMMARGIN;
+      float m = s_pm[0][t], s = s_ps[0][t], t2 = TOP2 ? s_p2[0][t] : 0.f;
       int am = s_pa[0][t];
 #pragma unroll
       for (int w = 1; w < WP; ++w) {
-        t2 = merge_second(m, t2, s_pm[w][t], s_p2[w][t]);
+        if constexpr (TOP2) t2 = merge_second(m, t2, s_pm[w][t], s_p2[w][t]);
         merge_part(m, s, am, s_pm[w][t], s_ps[w][t], s_pa[w][t]);
       }
       g.lm_part[(size_t)(m0 + t) * g.ntile + nt] = make_float4(m, s, __int_as_float(am), t2);
@@ -232,7 +237,7 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
   static_assert(WP * WT == 4 && FP >= 1 && FT >= 1, "wave layout");
   static_assert(PF >= 1, "prefetch depth");
   static_assert(2 * ROWS * PITCH == gemm_lds_u16(TP, TT, BK), "LDS size");
-  static_assert(WK == 1 || (WK == 2 && EPI != EPI_LMHEAD && (BK / 16) % 2 == 0 &&
+  static_assert(WK == 1 || (WK == 2 && !epi_lm(EPI) && (BK / 16) % 2 == 0 &&
                             FP * FT * 16 * 256 * 4 <= 2 * ROWS * PITCH * 2),
                 "two k-halves: row epilogues only, partial sums fit the tile's LDS");
 
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g) {
   const int n_tiles = g.N / TP;
   const GemmSplit sp = gemm_split(m_tiles * n_tiles, g.K / BK, PF, SB, ST);
   if (sp.ks <= 1) return;
-  const int RS = EPI == EPI_LMHEAD ? 1 : min(NQ, (kReduceTarget + sp.units - 1) / sp.units);
+  const int RS = epi_lm(EPI) ? 1 : min(NQ, (kReduceTarget + sp.units - 1) / sp.units);
   if ((int)blockIdx.x >= sp.units * RS) return;
   const int unit = (int)blockIdx.x / RS, slice = (int)blockIdx.x % RS;
   const int nt = unit / m_tiles, mt = unit % m_tiles;
@@ -494,7 +499,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g) {
       }
     return sum;
   };
-  if constexpr (EPI == EPI_LMHEAD) {
+  if constexpr (epi_lm(EPI)) {
     f32x16 acc[FP][FT];
 #pragma unroll
     for (int a = 0; a < FP; ++a)
@@ -608,7 +613,7 @@ static int pf_for(int nk, int pfmax) {
 
 size_t gemm_workspace_bytes(int epi, int max_rows, int N, int K) {
   if (max_rows <= 0) return 0;
-  if (epi == EPI_LMHEAD) return (size_t)kSplitCap * kLmTP * 256 * sizeof(float);
+  if (epi_lm(epi)) return (size_t)kSplitCap * kLmTP * 256 * sizeof(float);
   if (max_rows > 1024 && N % 256 == 0) return (size_t)kSplitCap * 256 * 256 * sizeof(float);
   return 0;
 }
@@ -701,6 +706,8 @@ hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStre
   }
   if (epi == EPI_LMHEAD) {
     launch_bf16<kLmTP, 256, 64, 1, EPI_LMHEAD, A_GATHER, 0, 256, 768>(g, st);
+  } else if (epi == EPI_LMMARGIN) {
+    launch_bf16<kLmTP, 256, 64, 1, EPI_LMMARGIN, A_GATHER, 0, 256, 768>(g, st);
   } else if ((g.K / 64) % 4 != 0 && g.max_rows > kSkinnyRows && g.N % 128 == 0) {
     // short K: the 4-deep skinny ring does not divide it; one large tiling
     // (its 128-feature tiles must divide N; otherwise the 64-feature tiling

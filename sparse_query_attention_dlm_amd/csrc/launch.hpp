@@ -32,7 +32,9 @@ hipError_t launch_lmhead_combine(const float4* part, int ntile, const int32_t* e
                                  int32_t* idx, int32_t* counts, int32_t* offsets, hipStream_t st);
 
 // gemm.hip -- D^T[n][m] = sum_k W[n][k] * A[row(m)][k]; W output-major [N][K].
-enum GemmEpilogue { EPI_QKV = 0, EPI_ROWS = 1, EPI_LMHEAD = 2, EPI_SWIGLU = 3 };
+enum GemmEpilogue { EPI_QKV = 0, EPI_ROWS = 1, EPI_LMHEAD = 2, EPI_SWIGLU = 3, EPI_LMMARGIN = 4 };
+// the two LM-head epilogues (the margin one also keeps the second-largest logit)
+constexpr bool epi_lm(int epi) { return epi == EPI_LMHEAD || epi == EPI_LMMARGIN; }
 enum GemmAMode { A_GATHER = 0, A_COMPACT = 1 };
 struct GemmArgs {
   const void* w;            // [N][K]
@@ -52,7 +54,8 @@ struct GemmArgs {
   //             silu(gate) * up
   void* out;
   int ld_out;
-  // EPI_LMHEAD: lm_part[m*ntile + tile] = {max, sum exp(z-max), argmax bits, 0}
+  // EPI_LMHEAD: lm_part[m*ntile + tile] = {max, sum exp(z-max), argmax bits, 0};
+  // EPI_LMMARGIN: the same with the second-largest logit in the last slot
   float4* lm_part;
   int ntile;
   // split-K scratch (workspace): partial tiles
