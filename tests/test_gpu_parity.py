@@ -703,7 +703,7 @@ def test_mfma_probe_matches_closed_form(dlm):
 # ---------------------------------------------------------------------------
 # non-salient value-change update, and the row copies that keep its caches
 # ---------------------------------------------------------------------------
-def run_dv_update(dlm, B, S, Hq, Hkv, hd, n_per_b, dtype="bf16", seed=31):
+def run_dv_update(dlm, B, S, Hq, Hkv, hd, n_per_b, dtype="bf16", seed=31, loose_bound=None):
     """Previous step: each position's query and LSE over the old K (its last
     computation) and a cached output.  This step: the salient rows get new V.
     On the device the old K/V rows are gathered from the caches before the new
@@ -731,16 +731,19 @@ def run_dv_update(dlm, B, S, Hq, Hkv, hd, n_per_b, dtype="bf16", seed=31):
     for b in range(B):
         v_new_c[b, sal[b]] = rnd(rng.standard_normal((len(sal[b]), Hkv, hd)))
     n = int(offsets[-1])
-    say(f"[dv update] {dtype} B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} salient per row {list(n_per_b)}")
+    bound = n if loose_bound is None else loose_bound   # host-side row bound (>= the device count)
+    say(f"[dv update] {dtype} B={B} S={S} Hq={Hq} Hkv={Hkv} hd={hd} salient per row {list(n_per_b)} bound {bound}")
     kd, vd = dev(k_old_c, dtype), dev(v_old_c, dtype)
-    k_rows = torch.zeros(max(n, 1), Hkv, hd, dtype=kd.dtype, device="cuda")
+    k_rows = torch.zeros(max(bound, 1), Hkv, hd, dtype=kd.dtype, device="cuda")
     v_rows = torch.zeros_like(k_rows)
     it, ot = i32(idx), i32(offsets)
-    dlm.dlm_gather_rows(kd, it, ot, n, k_rows)
-    dlm.dlm_gather_rows(vd, it, ot, n, v_rows)
-    dlm.dlm_scatter_rows(dev(O.gather_rows(v_new_c, idx, offsets), dtype), it, ot, n, vd)
+    dlm.dlm_gather_rows(kd, it, ot, bound, k_rows)
+    dlm.dlm_gather_rows(vd, it, ot, bound, v_rows)
+    new_rows = torch.zeros_like(k_rows)
+    new_rows[:n] = dev(O.gather_rows(v_new_c, idx, offsets), dtype)
+    dlm.dlm_scatter_rows(new_rows, it, ot, bound, vd)
     od = dev(o, dtype)
-    dlm.dlm_nonsalient_dv_update(dev(q, dtype), dev(lse, "f32"), it, ot, n, k_rows, v_rows, vd, scale, od)
+    dlm.dlm_nonsalient_dv_update(dev(q, dtype), dev(lse, "f32"), it, ot, bound, k_rows, v_rows, vd, scale, od)
     torch.cuda.synchronize()
     k_old, v_old = O.gather_rows(k_old_c, idx, offsets), O.gather_rows(v_old_c, idx, offsets)
     assert np.array_equal(host(k_rows)[:n], k_old) and np.array_equal(host(v_rows)[:n], v_old)
@@ -773,6 +776,13 @@ def test_dv_update_wide_workgroups(dlm, hd):
     """Enough position tiles (B = 2, S = 2048, GQA 32/8) for the 256-vector
     workgroups; salient sets of 300 and 777 rows (ragged last tiles)."""
     run_dv_update(dlm, B=2, S=2048, Hq=32, Hkv=8, hd=hd, n_per_b=[300, 777], seed=37)
+
+
+def test_dv_update_loose_row_bound(dlm):
+    """A host-side row bound far above the device count (as a caller without the
+    selection count passes it): every call, the row copies included, stops at
+    the device's offsets."""
+    run_dv_update(dlm, B=2, S=300, Hq=8, Hkv=2, hd=128, n_per_b=[45, 70], seed=38, loose_bound=600)
 
 
 def test_dv_update_head_dim_64(dlm):
