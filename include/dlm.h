@@ -214,6 +214,19 @@ int dlm_attn_colsum(int dtype, const void* q_sel, const int32_t* offsets, int ma
                     int32_t* topk_idx, float* topk_val,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* dlm_attn_colsum_window: the same call with the work cut to the key window,
+ * for block-wise use ("Attention-Based Sampler for Diffusion Language
+ * Models", Methodologie 2: the scores are computed per sub-block rather than
+ * over the whole sequence).  colsum[b,j] is computed for the 256-key blocks
+ * that cover [key_lo, key_hi) only (so for every j in the window); entries of
+ * other blocks are not touched.  Same arguments, limits and workspace. */
+int dlm_attn_colsum_window(int dtype, const void* q_sel, const int32_t* offsets, int max_rows,
+                           const void* k_cache, const float* lse,
+                           int B, int S, int Hq, int Hkv, int hd, float scale,
+                           float* colsum, int key_lo, int key_hi, int k,
+                           int32_t* topk_idx, float* topk_val,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * dlm_stable_prefix
  *

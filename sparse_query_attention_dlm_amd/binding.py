@@ -61,6 +61,8 @@ lib.dlm_attn_colsum_workspace_size.argtypes = [_I, _I, _I]
 lib.dlm_attn_colsum.restype = _I
 lib.dlm_attn_colsum.argtypes = [_I, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _I, _I,
                                 _P, _P, _P, _Z, _P]
+lib.dlm_attn_colsum_window.restype = _I
+lib.dlm_attn_colsum_window.argtypes = lib.dlm_attn_colsum.argtypes
 lib.dlm_stable_prefix.restype = _I
 lib.dlm_stable_prefix.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _I, _F, _I, _P, _P]
 lib.dlm_probe_mfma_bf16.restype = _I
@@ -195,12 +197,14 @@ def dlm_partial_attn(q_sel, idx, offsets, max_rows, k_cache, v_cache, scale, o_s
 
 
 def dlm_attn_colsum(q_sel, offsets, max_rows, k_cache, lse, scale, colsum, key_lo=0, key_hi=None,
-                    k=0, topk_idx=None, topk_val=None, workspace=None, stream=None):
+                    k=0, topk_idx=None, topk_val=None, workspace=None, stream=None, window_only=False):
+    """window_only: dlm_attn_colsum_window (sums of the window's key blocks only)."""
     B, S, Hkv, hd = k_cache.shape
     Hq = q_sel.shape[1]
     key_hi = S if key_hi is None else key_hi
     wp, wn = _ws(workspace)
-    rc = lib.dlm_attn_colsum(
+    fn = lib.dlm_attn_colsum_window if window_only else lib.dlm_attn_colsum
+    rc = fn(
         _dt(q_sel), _ptr(q_sel, "q_sel"), _ptr(offsets, "offsets", torch.int32), int(max_rows),
         _ptr(k_cache, "k_cache", q_sel.dtype), _ptr(lse, "lse", torch.float32), B, S, Hq, Hkv, hd,
         float(scale), _ptr(colsum, "colsum", torch.float32), int(key_lo), int(key_hi), int(k),

@@ -36,14 +36,15 @@ __global__ __launch_bounds__(64 * WAVES, HD == 128 || FAST ? 3 : 4) void colsum_
                                                                  const float* __restrict__ lse,
                                                                  int B, int S, int Hq, int Hkv,
                                                                  int gsh, int max_rows, int nsq,
-                                                                 float scale,
+                                                                 int kb0, int nkb, float scale,
                                                                  float* __restrict__ partial) {
   constexpr int NT = 64 * WAVES, KEYS = 64 * WAVES;
   constexpr int QTL = 32, PITCH = HD + 8, NS = HD / 16, CPR = HD / 8;
   constexpr int CH = QTL * CPR, CPT = (CH + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) u16 sQ[2][QTL * PITCH];
   __shared__ float sL[2][QTL];
-  const int nkb = (S + KEYS - 1) / KEYS;
+  // key blocks kb0 .. kb0 + nkb - 1 of KEYS keys (all of them, or the
+  // blocks that cover a key window)
   // workgroups of one KV head are Hkv apart, so with Hkv a multiple of 8 they
   // share an XCD (and its L2) and read each query tile from there
   const int g = blockIdx.x % Hkv;
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(64 * WAVES, HD == 128 || FAST ? 3 : 4) void colsum_
   const int b = blockIdx.x / (Hkv * nsq * nkb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
   const int G = Hq / Hkv;
-  const int key0 = kb * KEYS + wave * 64;
+  const int key0 = (kb0 + kb) * KEYS + wave * 64;
   const float c = scale * kLog2e;
 
   // the wave's 64 keys as two 32-row MFMA A-operands, held for the whole pass
@@ -192,20 +193,24 @@ __global__ __launch_bounds__(64 * WAVES, HD == 128 || FAST ? 3 : 4) void colsum_
 // colsum[b][j] = sum over splits and KV heads of the partials, in a fixed
 // order: wave w of a workgroup adds parts [w*P/4, (w+1)*P/4) of 64
 // consecutive keys (coalesced), wave 0 then adds the four sums in order.
+// Keys w0 .. w0 + W - 1 of every sequence (all S keys: w0 = 0, W = S).
 __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* __restrict__ partial,
-                                                            int parts, int BS,
+                                                            int parts, int B, int S, int w0, int W,
                                                             float* __restrict__ colsum) {
   __shared__ float s_part[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p0 = parts * wave / 4, p1 = parts * (wave + 1) / 4;
-  for (int j0 = blockIdx.x * 64; j0 < BS; j0 += gridDim.x * 64) {
+  const size_t BS = (size_t)B * S;
+  const int n = B * W;
+  for (int j0 = blockIdx.x * 64; j0 < n; j0 += gridDim.x * 64) {
     const int j = j0 + lane;
+    const size_t at = (size_t)(j / W) * S + w0 + j % W;
     float cs = 0.f;
-    if (j < BS)
-      for (int p = p0; p < p1; ++p) cs += partial[(size_t)p * BS + j];
+    if (j < n)
+      for (int p = p0; p < p1; ++p) cs += partial[(size_t)p * BS + at];
     s_part[wave][lane] = cs;
     __syncthreads();
-    if (wave == 0 && j < BS) colsum[j] = ((s_part[0][lane] + s_part[1][lane]) + s_part[2][lane]) + s_part[3][lane];
+    if (wave == 0 && j < n) colsum[at] = ((s_part[0][lane] + s_part[1][lane]) + s_part[2][lane]) + s_part[3][lane];
     __syncthreads();
   }
 }
@@ -237,15 +242,16 @@ template <bool FUSED, bool SMALL>
 __global__ __launch_bounds__(1024) void colsum_topk_kernel(const float* __restrict__ partial,
                                                            int parts, int B, int S,
                                                            float* __restrict__ colsum, int key_lo,
-                                                           int key_hi, int kk, int p2,
+                                                           int key_hi, int kk, int p2, int w0, int W,
                                                            int32_t* topk_idx, float* topk_val) {
   extern __shared__ unsigned long long skeys[];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = key_hi - key_lo;
   float* crow = colsum + (size_t)b * S;
   if constexpr (FUSED) {
+    // the sums of keys w0 .. w0 + W - 1 (all S keys, or the window's blocks)
     const size_t BS = (size_t)B * S;
-    for (int j = tid; j < S; j += 1024) {
+    for (int j = w0 + tid; j < w0 + W; j += 1024) {
       float cs = 0.f;
       for (int p = 0; p < parts; ++p) cs += partial[p * BS + (size_t)b * S + j];
       crow[j] = cs;
@@ -371,19 +377,19 @@ static int colsum_splits(int units, int occ, int max_rows, int B, int G) {
 template <int HD, int WAVES>
 static int launch_colsum_pass(const void* q, const int32_t* offsets, int max_rows, const void* k,
                               const float* lse, int B, int S, int Hq, int Hkv, float scale,
-                              float* partial, hipStream_t st) {
+                              int kb0, int nkb, float* partial, hipStream_t st) {
   const int G = Hq / Hkv;
   int gsh = 0;
   while ((1 << gsh) < G) ++gsh;
   const bool fast = (1 << gsh) == G && G <= 32 && (long long)max_rows * Hq * HD < (1LL << 31);
-  const int units = B * ((S + 64 * WAVES - 1) / (64 * WAVES)) * Hkv;
+  const int units = B * nkb * Hkv;
   // resident workgroups per CU: one wave per SIMD each, at most 168
   // registers per lane (128 for the generic d = 64 body)
   const int nsq = colsum_splits(units, HD == 128 || fast ? 3 : 4, max_rows, B, G);
   auto kern = fast ? colsum_bf16_kernel<HD, WAVES, true> : colsum_bf16_kernel<HD, WAVES, false>;
   hipLaunchKernelGGL(kern, dim3(units * nsq), dim3(64 * WAVES), 0, st, static_cast<const u16*>(q),
                      offsets, static_cast<const u16*>(k), lse, B, S, Hq, Hkv, gsh, max_rows, nsq,
-                     scale, partial);
+                     kb0, nkb, scale, partial);
   return nsq;
 }
 
@@ -394,20 +400,26 @@ size_t colsum_workspace_bytes(int B, int S, int Hkv) {
 hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, const void* k,
                          const float* lse, int B, int S, int Hq, int Hkv, int hd, float scale,
                          float* partial, float* colsum, int key_lo, int key_hi, int kk,
-                         int32_t* topk_idx, float* topk_val, hipStream_t st) {
+                         int32_t* topk_idx, float* topk_val, int window, hipStream_t st) {
+  // all key blocks, or (window) only the 256-key blocks that cover [key_lo, key_hi)
+  constexpr int KEYS = 256;
+  const int kb0 = window ? key_lo / KEYS : 0;
+  const int kb1 = window ? (key_hi + KEYS - 1) / KEYS : (S + KEYS - 1) / KEYS;
+  if (kb1 <= kb0) return hipSuccess;  // empty window
+  const int w0 = kb0 * KEYS, W = min(S, kb1 * KEYS) - w0;
   const int nsq = hd == 64 ? launch_colsum_pass<64, 4>(q, offsets, max_rows, k, lse, B, S, Hq, Hkv,
-                                                        scale, partial, st)
+                                                        scale, kb0, kb1 - kb0, partial, st)
                            : launch_colsum_pass<128, 4>(q, offsets, max_rows, k, lse, B, S, Hq,
-                                                         Hkv, scale, partial, st);
+                                                         Hkv, scale, kb0, kb1 - kb0, partial, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // when a sequence has few partials, one kernel sums them and picks its top-k
   const int parts = nsq * Hkv;
   const bool fused = kk > 0 && (long long)parts * S <= 16384;
   if (!fused) {
-    const int BS = B * S;
-    hipLaunchKernelGGL(colsum_reduce_kernel, dim3(min((BS + 63) / 64, 2048)), dim3(256), 0, st,
-                       partial, parts, BS, colsum);
+    const int n = B * W;
+    hipLaunchKernelGGL(colsum_reduce_kernel, dim3(min((n + 63) / 64, 2048)), dim3(256), 0, st,
+                       partial, parts, B, S, w0, W, colsum);
     if (kk <= 0) return hipGetLastError();
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -421,7 +433,7 @@ hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, co
   auto topk = small ? (fused ? colsum_topk_kernel<true, true> : colsum_topk_kernel<false, true>)
                     : (fused ? colsum_topk_kernel<true, false> : colsum_topk_kernel<false, false>);
   hipLaunchKernelGGL(topk, dim3(B), dim3(1024), small ? 0 : (size_t)p2 * sizeof(unsigned long long), st,
-                     partial, parts, B, S, colsum, key_lo, key_hi, kk, p2, topk_idx, topk_val);
+                     partial, parts, B, S, colsum, key_lo, key_hi, kk, p2, w0, W, topk_idx, topk_val);
   return hipGetLastError();
 }
 

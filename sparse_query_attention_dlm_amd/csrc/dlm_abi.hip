@@ -322,10 +322,11 @@ size_t dlm_attn_colsum_workspace_size(int B, int S, int Hkv) {
   return dlm::colsum_workspace_bytes(B, S, Hkv);
 }
 
-int dlm_attn_colsum(int dtype, const void* q_sel, const int32_t* offsets, int max_rows,
-                    const void* k_cache, const float* lse, int B, int S, int Hq, int Hkv, int hd,
-                    float scale, float* colsum, int key_lo, int key_hi, int k, int32_t* topk_idx,
-                    float* topk_val, void* workspace, size_t workspace_bytes, void* stream) {
+static int attn_colsum(int dtype, const void* q_sel, const int32_t* offsets, int max_rows,
+                       const void* k_cache, const float* lse, int B, int S, int Hq, int Hkv,
+                       int hd, float scale, float* colsum, int key_lo, int key_hi, int k,
+                       int32_t* topk_idx, float* topk_val, void* workspace,
+                       size_t workspace_bytes, int window, void* stream) {
   if (dtype != DLM_BF16)
     return fail(DLM_ERR_UNSUPPORTED, "attention column sums are implemented for bf16 only");
   REQUIRE_PTR(q_sel);
@@ -352,9 +353,28 @@ int dlm_attn_colsum(int dtype, const void* q_sel, const int32_t* offsets, int ma
                 workspace ? workspace_bytes : (size_t)0);
   return hip_status(dlm::launch_colsum(q_sel, offsets, max_rows, k_cache, lse, B, S, Hq, Hkv, hd,
                                        scale, static_cast<float*>(workspace), colsum, key_lo,
-                                       key_hi, k, topk_idx, topk_val,
+                                       key_hi, k, topk_idx, topk_val, window,
                                        static_cast<hipStream_t>(stream)),
                     "attention column sums");
+}
+
+int dlm_attn_colsum(int dtype, const void* q_sel, const int32_t* offsets, int max_rows,
+                    const void* k_cache, const float* lse, int B, int S, int Hq, int Hkv, int hd,
+                    float scale, float* colsum, int key_lo, int key_hi, int k, int32_t* topk_idx,
+                    float* topk_val, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_colsum(dtype, q_sel, offsets, max_rows, k_cache, lse, B, S, Hq, Hkv, hd, scale,
+                     colsum, key_lo, key_hi, k, topk_idx, topk_val, workspace, workspace_bytes, 0,
+                     stream);
+}
+
+int dlm_attn_colsum_window(int dtype, const void* q_sel, const int32_t* offsets, int max_rows,
+                           const void* k_cache, const float* lse, int B, int S, int Hq, int Hkv,
+                           int hd, float scale, float* colsum, int key_lo, int key_hi, int k,
+                           int32_t* topk_idx, float* topk_val, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return attn_colsum(dtype, q_sel, offsets, max_rows, k_cache, lse, B, S, Hq, Hkv, hd, scale,
+                     colsum, key_lo, key_hi, k, topk_idx, topk_val, workspace, workspace_bytes, 1,
+                     stream);
 }
 
 // ---------------------------------------------------------------------------

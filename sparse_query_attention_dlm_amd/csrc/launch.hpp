@@ -90,7 +90,7 @@ size_t colsum_workspace_bytes(int B, int S, int Hkv);
 hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, const void* k,
                          const float* lse, int B, int S, int Hq, int Hkv, int hd, float scale,
                          float* partial, float* colsum, int key_lo, int key_hi, int kk,
-                         int32_t* topk_idx, float* topk_val, hipStream_t st);
+                         int32_t* topk_idx, float* topk_val, int window, hipStream_t st);
 
 // dv.hip
 struct DvArgs {

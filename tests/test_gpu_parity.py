@@ -982,3 +982,41 @@ def test_lsp_margin_commit_loop(dlm):
         steps += 1
         assert steps < 40
     say(f"  done in {steps} steps")
+
+
+def test_colsum_key_window_only(dlm):
+    """Attn-Sampler's block-wise column sums: the window call computes the key
+    blocks covering [key_lo, key_hi) only. Inside the window its sums match the
+    full call's and the oracle's; outside the covering blocks nothing is
+    written; its top-k is exact on its own sums."""
+    rng = np.random.default_rng(61)
+    B, S, Hq, Hkv, hd = 2, 1500, 8, 4, 128
+    scale = 1.0 / math.sqrt(hd)
+    kc = W.round_bf16(rng.standard_normal((B, S, Hkv, hd)))
+    vc = W.round_bf16(rng.standard_normal((B, S, Hkv, hd)))
+    rows = [np.sort(rng.choice(S, 64, replace=False)), np.sort(rng.choice(S, 40, replace=False))]
+    idx = np.concatenate(rows).astype(np.int32)
+    offsets = np.array([0, 64, 104], np.int32)
+    q = W.round_bf16(rng.standard_normal((104, Hq, hd)))
+    _, lse = O.partial_attention(q, idx, offsets, kc, vc, Hq, Hkv, scale)
+    c_o = O.column_sums(q, offsets, kc, lse, Hq, Hkv, scale)
+    lo, hi, kk = 600, 1100, 16
+    say(f"[colsum window] B={B} S={S} window [{lo},{hi}) k={kk}")
+    qd, kd, ld, od = dev(q, "bf16"), dev(kc, "bf16"), dev(lse, "f32"), i32(offsets)
+    ws = workspace(dlm.dlm_attn_colsum_workspace_size(B, S, Hkv))
+    full = torch.zeros(B, S, dtype=torch.float32, device="cuda")
+    dlm.dlm_attn_colsum(qd, od, 104, kd, ld, scale, full, workspace=ws)
+    win = torch.full((B, S), -1.0, dtype=torch.float32, device="cuda")
+    ti = torch.zeros(B, kk, dtype=torch.int32, device="cuda")
+    tv = torch.zeros(B, kk, dtype=torch.float32, device="cuda")
+    dlm.dlm_attn_colsum(qd, od, 104, kd, ld, scale, win, key_lo=lo, key_hi=hi, k=kk, topk_idx=ti, topk_val=tv,
+                        workspace=ws, window_only=True)
+    torch.cuda.synchronize()
+    f, w = full.cpu().numpy(), win.cpu().numpy()
+    assert np.allclose(w[:, lo:hi], f[:, lo:hi], rtol=1e-5, atol=1e-6)
+    assert maxabs(w[:, lo:hi], c_o[:, lo:hi]) <= TOL["bf16"]
+    assert np.all(w[:, :512] == -1.0) and np.all(w[:, 1280:] == -1.0)   # blocks [512, 1280) cover the window
+    for b in range(B):
+        order = np.lexsort((np.arange(lo, hi), -w[b, lo:hi].astype(np.float64)))[:kk] + lo
+        assert np.array_equal(ti[b].cpu().numpy(), order)
+        assert np.array_equal(tv[b].cpu().numpy(), w[b, order])
