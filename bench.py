@@ -421,8 +421,12 @@ def extra_colsum(dlm, W):
     attn = lambda: dlm.dlm_partial_attn(q, idx, offsets, n, k, v, scale, o, lse, workspace=wsa)
     col = lambda: dlm.dlm_attn_colsum(q, offsets, n, k, lse, scale, colsum, sh.prompt, S, sh.k,
                                       topk_idx=ti, topk_val=tv, workspace=wsc)
+    # block-wise variant: sums and top-64 over a 1024-key sub-block of the masked region
+    colw = lambda: dlm.dlm_attn_colsum(q, offsets, n, k, lse, scale, colsum, sh.prompt, sh.prompt + 1024, sh.k,
+                                       topk_idx=ti, topk_val=tv, workspace=wsc, window_only=True)
     t_attn = _time(attn, 10)
     t_col = _time(col, 10)
+    t_colw = _time(colw, 10)
     f_attn = 4.0 * n * S * hd * Hq
     f_col = 2.0 * n * S * hd * Hq
     return {"workload": sh.name, "n_selected": n,
@@ -430,7 +434,8 @@ def extra_colsum(dlm, W):
                              "frac_of_measured_ceiling": of_measured(f_attn / (t_attn / 1e3), "mfma_bf16")},
             "colsum_topk": {"ms": t_col, "TFLOP/s": f_col / t_col / 1e9, "frac": f_col / (t_col / 1e3) / PEAK_BF16,
                             "frac_of_measured_ceiling": of_measured(f_col / (t_col / 1e3), "mfma_bf16")},
-            "tokens_per_s": n / ((t_attn + t_col) / 1e3)}
+            "tokens_per_s": n / ((t_attn + t_col) / 1e3),
+            "colsum_topk_window_1024_keys": {"ms": t_colw, "TFLOP/s": f_col / 4 / t_colw / 1e9}}
 
 
 def extra_lsp(dlm, W):
