@@ -403,6 +403,7 @@ hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, co
                          int32_t* topk_idx, float* topk_val, int window, hipStream_t st) {
   // all key blocks, or (window) only the 256-key blocks that cover [key_lo, key_hi)
   constexpr int KEYS = 256;
+  if (window && key_hi <= key_lo) return hipSuccess;  // an empty window: nothing to compute
   const int kb0 = window ? key_lo / KEYS : 0;
   const int kb1 = window ? (key_hi + KEYS - 1) / KEYS : (S + KEYS - 1) / KEYS;
   if (kb1 <= kb0) return hipSuccess;  // empty window
@@ -413,9 +414,12 @@ hipError_t launch_colsum(const void* q, const int32_t* offsets, int max_rows, co
                                                          Hkv, scale, kb0, kb1 - kb0, partial, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // when a sequence has few partials, one kernel sums them and picks its top-k
+  // when a sequence has few partials over the keys summed (all S, or the
+  // window's covering blocks), one kernel sums them and picks its top-k: at
+  // most 16 partial loads per thread of its 1024, where a separate reduce
+  // launch would cost more than it saves
   const int parts = nsq * Hkv;
-  const bool fused = kk > 0 && (long long)parts * S <= 16384;
+  const bool fused = kk > 0 && (long long)parts * W <= 16384;
   if (!fused) {
     const int n = B * W;
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3(min((n + 63) / 64, 2048)), dim3(256), 0, st,

@@ -154,19 +154,22 @@ def test_partial_attn_rejections(lib):
 
 
 def colsum(lib, dtype=BF16, q=FAKE, off=FAKE, max_rows=4, k=FAKE, lse=FAKE, B=1, S=64, Hq=2, Hkv=1,
-           hd=128, cs=FAKE, lo=0, hi=64, kk=4, ti=FAKE, tv=0, ws=FAKE, ws_bytes=1 << 20):
-    return lib.dlm_attn_colsum(dtype, p(q), p(off), max_rows, p(k), p(lse), B, S, Hq, Hkv, hd, f(0.1),
-                               p(cs), lo, hi, kk, p(ti), p(tv), p(ws), ctypes.c_size_t(ws_bytes), p(0))
+           hd=128, cs=FAKE, lo=0, hi=64, kk=4, ti=FAKE, tv=0, ws=FAKE, ws_bytes=1 << 20, window=False):
+    fn = lib.dlm_attn_colsum_window if window else lib.dlm_attn_colsum
+    return fn(dtype, p(q), p(off), max_rows, p(k), p(lse), B, S, Hq, Hkv, hd, f(0.1),
+              p(cs), lo, hi, kk, p(ti), p(tv), p(ws), ctypes.c_size_t(ws_bytes), p(0))
 
 
-def test_colsum_rejections(lib):
-    assert colsum(lib, dtype=F32) == UNSUPPORTED
-    assert colsum(lib, lse=0) == INVALID
-    assert colsum(lib, lo=10, hi=5) == INVALID
-    assert colsum(lib, kk=65) == INVALID                     # k larger than the key window
-    assert colsum(lib, S=10000, hi=10000) == INVALID         # top-k window over 8192 keys
-    assert colsum(lib, ti=0, tv=0) == INVALID                # k > 0 but nowhere to write
-    assert colsum(lib, ws_bytes=4) == WORKSPACE
+@pytest.mark.parametrize("window", [False, True])
+def test_colsum_rejections(lib, window):
+    assert colsum(lib, dtype=F32, window=window) == UNSUPPORTED
+    assert colsum(lib, lse=0, window=window) == INVALID
+    assert colsum(lib, lo=10, hi=5, window=window) == INVALID
+    assert colsum(lib, kk=65, window=window) == INVALID                     # k larger than the key window
+    assert colsum(lib, S=10000, hi=10000, window=window) == INVALID         # top-k window over 8192 keys
+    assert colsum(lib, ti=0, tv=0, window=window) == INVALID                # k > 0 but nowhere to write
+    assert colsum(lib, ws_bytes=4, window=window) == WORKSPACE
+    assert colsum(lib, ws=0, window=window) == WORKSPACE
     # per-key float partials for up to 4 query splits of each KV head
     assert lib.dlm_attn_colsum_workspace_size(4, 4096, 32) == 4 * 32 * 4 * 4096 * 4
 
