@@ -3,6 +3,7 @@
 // a rejected request enqueues nothing and works without a GPU present.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "../../include/dlm.h"
@@ -39,6 +40,38 @@ size_t elt(int dtype) { return dtype == DLM_BF16 ? 2 : 4; }
 #define REQUIRE_ALIGNED(p) REQUIRE(aligned16(p), "%s must be 16-byte aligned", #p)
 
 constexpr size_t kSelectTicketBytes = 256;
+
+// DLM_VALIDATE=1 in the environment (read at every call): the calls that take
+// a selection check its index arrays on the device before any other launch
+// (and wait for the verdict).  Off by default: the arrays are trusted.
+bool validate_on() {
+  const char* v = std::getenv("DLM_VALIDATE");
+  return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
+
+int check_rows(const int32_t* idx, const int32_t* offsets, int B, int S, int max_rows, bool check_idx,
+               void* stream, const char* what) {
+  if (max_rows <= 0 || !validate_on()) return DLM_OK;
+  int verdict = 0;
+  if (hipError_t e = dlm::validate_rows(idx, offsets, B, S, max_rows, check_idx ? 1 : 0,
+                                        static_cast<hipStream_t>(stream), &verdict);
+      e != hipSuccess)
+    return fail(DLM_ERR_HIP, "%s: selection check: %s", what, hipGetErrorString(e));
+  if (verdict == 0) return DLM_OK;
+  std::string why;
+  if (verdict & dlm::kBadFirstOffset) why += " offsets[0] != 0;";
+  if (verdict & dlm::kOffsetsDecrease) why += " offsets decrease;";
+  if (verdict & dlm::kOffsetsPastBound) why += " offsets[B] exceeds max_rows;";
+  if (verdict & dlm::kIndexOutside) why += " a position outside [0, S);";
+  if (verdict & dlm::kIndexOrder) why += " positions of a batch row not strictly increasing;";
+  return fail(DLM_ERR_INVALID_ARG, "%s: invalid selection (DLM_VALIDATE):%s", what, why.c_str());
+}
+
+#define CHECK_ROWS(idx, offsets, B, S, max_rows, check_idx, stream, what)                    \
+  do {                                                                                     \
+    if (int rc_ = check_rows(idx, offsets, B, S, max_rows, check_idx, stream, what); rc_) \
+      return rc_;                                                                          \
+  } while (0)
 
 }  // namespace
 
@@ -123,6 +156,7 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b, int B
                                                 counts, offsets, st),
                       "cosine select");
   }
+  CHECK_ROWS(eval_idx, eval_offsets, B, S, max_eval, true, stream, "confidence select");
   const int ntile = dlm::gemm_lmhead_ntile(V);
   char* wsb = static_cast<char*>(workspace) + kSelectTicketBytes + round_up((size_t)B * S * sizeof(float), 256);
   float4* part = reinterpret_cast<float4*>(wsb);
@@ -197,6 +231,7 @@ int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D, con
                 workspace ? workspace_bytes : (size_t)0);
   if (need > 0) REQUIRE_ALIGNED(workspace);
   REQUIRE((long long)B * S * D < (1ll << 31), "x larger than 2^31 elements is not supported");
+  CHECK_ROWS(idx, offsets, B, S, max_rows, true, stream, "gathered QKV");
   dlm::GemmArgs g{};
   g.w = w_qkv;
   g.part = static_cast<float*>(workspace);
@@ -275,6 +310,7 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
                 workspace ? workspace_bytes : (size_t)0);
   if (need > 0) REQUIRE_ALIGNED(workspace);
   if (max_rows == 0) return DLM_OK;
+  CHECK_ROWS(idx, offsets, B, S, max_rows, true, stream, "partial attention");
   hipStream_t st = static_cast<hipStream_t>(stream);
   dlm::AttnArgs a{};
   a.q = q_sel;
@@ -351,6 +387,7 @@ static int attn_colsum(int dtype, const void* q_sel, const int32_t* offsets, int
   if (workspace == nullptr || workspace_bytes < need)
     return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
+  CHECK_ROWS(nullptr, offsets, B, S, max_rows, false, stream, "column sums");
   return hip_status(dlm::launch_colsum(q_sel, offsets, max_rows, k_cache, lse, B, S, Hq, Hkv, hd,
                                        scale, static_cast<float*>(workspace), colsum, key_lo,
                                        key_hi, k, topk_idx, topk_val, window,
@@ -434,6 +471,7 @@ int dlm_salient_ffn(int dtype, const void* x, int B, int S, int D, const int32_t
     return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   REQUIRE_ALIGNED(workspace);
+  CHECK_ROWS(idx, offsets, B, S, max_rows, true, stream, "salient FFN");
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* h = workspace;
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
@@ -492,6 +530,7 @@ static int row_copy(const void* src, void* dst, const int32_t* idx, const int32_
     REQUIRE_ALIGNED(src);
     REQUIRE_ALIGNED(dst);
   }
+  CHECK_ROWS(idx, offsets, B, S, max_rows, true, stream, scatter ? "row scatter" : "row gather");
   return hip_status(dlm::launch_row_copy(src, dst, idx, offsets, max_rows, B, S, row_bytes, scatter,
                                          static_cast<hipStream_t>(stream)),
                     scatter ? "row scatter" : "row gather");
@@ -535,6 +574,7 @@ int dlm_nonsalient_dv_update(int dtype, const void* q_cache, const float* lse_ca
   REQUIRE_ALIGNED(v_old);
   REQUIRE_ALIGNED(v_cache);
   REQUIRE_ALIGNED(o_cache);
+  CHECK_ROWS(idx, offsets, B, S, max_rows, true, stream, "non-salient update");
   dlm::DvArgs a{};
   a.q = q_cache;
   a.lse = lse_cache;

@@ -110,6 +110,19 @@ hipError_t launch_dv_update(int dtype, const DvArgs& a, hipStream_t st);
 hipError_t launch_row_copy(const void* src, void* dst, const int32_t* idx, const int32_t* offsets,
                            int max_rows, int B, int S, int row_bytes, int scatter, hipStream_t st);
 
+// validate.hip: the opt-in check of a selection's index arrays.  Runs one
+// check kernel on `st`, waits for it and returns its verdict (0 = valid, else
+// a mask of the flags below).
+enum ValidateFlags {
+  kBadFirstOffset = 1,    // offsets[0] != 0
+  kOffsetsDecrease = 2,   // offsets[b+1] < offsets[b]
+  kOffsetsPastBound = 4,  // offsets[B] > max_rows
+  kIndexOutside = 8,      // a position outside [0, S)
+  kIndexOrder = 16,       // positions of a batch row not strictly increasing
+};
+hipError_t validate_rows(const int32_t* idx, const int32_t* offsets, int B, int S, int max_rows,
+                         int check_idx, hipStream_t st, int* verdict);
+
 // prefix.hip
 hipError_t launch_lsp_adaptive(const float* margin, int B, int S, int gen_lo, int gen_hi,
                                float frac_lo, float frac_hi, int32_t* committed, float* tau,
