@@ -13,7 +13,9 @@ Pages followed (title, section):
             similarity per token; low similarity = salient, recomputed; stable
             tokens reuse cached activations, the FFN included), Methodologie 2
             (salient path: full recomputation of the attention rows;
-            non-salient path: existing weights times the value change).
+            non-salient path: existing weights times the value change),
+            Methodologie 3 (adaptive input: response tokens only on most
+            steps, the whole sequence every few steps).
   [SlowFast] "Accelerating Diffusion Large Language Models with SlowFast
             Sampling" - Metodologia, certainty and convergence principles
             (max predicted confidence as the stability signal).
@@ -447,6 +449,18 @@ def full_recompute_caches(x, w_qkv, Hq, Hkv, hd, scale, w_o=None):
     d_out = Hq * hd if w_o is None else np.asarray(w_o).shape[0]
     out = output_scatter(o, idx, offsets, np.zeros((B, S, d_out)), w_o)
     return kc, vc, out
+
+
+def adaptive_input_window(t, prompt, S, refresh=4):
+    """[DyLLM] Methodologie 3 (adaptive input): on most steps only the response
+    tokens are input, so only they can be scored and selected; every
+    `refresh` steps the whole sequence (prompt + response) is input to refresh
+    the context, and even then only salient tokens are recomputed.
+
+    Reading: the full sequence is input at the steps t with t % refresh == 0
+    (the first step included), the response [prompt, S) at every other step.
+    Returns the scoring window (lo, hi)."""
+    return (0, S) if t % refresh == 0 else (prompt, S)
 
 
 def cosine_step(cur, prev, w_qkv, Hq, Hkv, hd, tau, k_cache, v_cache, out_cache, w_o=None,

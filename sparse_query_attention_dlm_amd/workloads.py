@@ -21,6 +21,9 @@ or trained weight is available here):
 * ``lsp_commit``     - B=16, S=1024, LM head 4096 x 32768, confidence + longest
                         stable prefix (Longest Stable Prefixes, Methodologie 2;
                         SlowFast Sampling, Metodologia principles 1-2).
+* ``dyllm_loop``     - the bf16 S=1024 layer over 8 steps with a 512-token prompt
+                        and a 512-token response (DyLLM, Methodologie 3:
+                        response-only input on most steps).
 
 Every generator takes explicit sizes so tests can run reduced versions that
 still span several kernel tiles and a ragged tail.
@@ -337,6 +340,77 @@ def lsp_inputs(shape: LspShape = LSP_COMMIT, **override) -> LspInputs:
     wd = w.astype(np.float64)
     unit = (wd / np.linalg.norm(wd, axis=1, keepdims=True)).astype(np.float32)
     return LspInputs(s, w, frontier.astype(np.int64), targets.astype(np.int64), flip, base, unit)
+
+
+# --------------------------------------------------------------------------
+# DyLLM's adaptive input: a multi-step loop with a prompt and a response
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class DyllmLoopShape:
+    name: str
+    B: int
+    S: int
+    prompt: int             # positions [0, prompt) are the prompt, the rest the response
+    D: int
+    Hq: int
+    Hkv: int
+    hd: int
+    steps: int
+    refresh: int            # the whole sequence is scored every `refresh` steps
+    response_redrawn: int   # response rows redrawn fresh per step (per batch row)
+    prompt_redrawn: int     # prompt rows redrawn fresh per step (per batch row)
+    noise_std: float        # per-step drift of every other row
+    w_std: float
+    tau: float
+    seed: int
+
+
+DYLLM_LOOP = DyllmLoopShape(
+    name="bf16_dyllm_b1_s1024_p512_8steps", B=1, S=1024, prompt=512, D=4096, Hq=32, Hkv=32, hd=128,
+    steps=8, refresh=4, response_redrawn=51, prompt_redrawn=4, noise_std=1e-3, w_std=1.0 / 64.0, tau=0.95,
+    seed=6)
+
+
+@dataclass
+class DyllmLoopInputs:
+    shape: DyllmLoopShape
+    w_qkv: np.ndarray                       # [(Hq+2Hkv)*hd, D] bf16-exact
+    _states: list = field(repr=False, default=None)
+    _redrawn: list = field(repr=False, default=None)
+
+    def hidden(self, t: int) -> np.ndarray:
+        """Hidden states h_t [B,S,D] (bf16-exact) for t = -1 .. steps-1: h_{-1}
+        ~ N(0,1); each later step adds N(0, noise_std) drift to every row and
+        redraws `response_redrawn` response rows and `prompt_redrawn` prompt
+        rows fresh (the salient tokens of that step)."""
+        return self._states[t + 1]
+
+    def redrawn(self, t: int) -> list:
+        """Per batch row, the sorted positions redrawn at step t (t >= 0)."""
+        return self._redrawn[t]
+
+
+def dyllm_loop_inputs(shape: DyllmLoopShape = DYLLM_LOOP, **override) -> DyllmLoopInputs:
+    if override:
+        shape = DyllmLoopShape(**{**shape.__dict__, **override})
+    s = shape
+    rng = np.random.default_rng(s.seed)
+    n_qkv = (s.Hq + 2 * s.Hkv) * s.hd
+    w = round_bf16(np.float32(s.w_std) * rng.standard_normal((n_qkv, s.D), dtype=np.float32))
+    h = rng.standard_normal((s.B, s.S, s.D), dtype=np.float32)
+    states, redrawn = [round_bf16(h)], []
+    for _ in range(s.steps):
+        h = h + np.float32(s.noise_std) * rng.standard_normal((s.B, s.S, s.D), dtype=np.float32)
+        per_b = []
+        for b in range(s.B):
+            pos = np.concatenate([rng.choice(s.prompt, s.prompt_redrawn, replace=False),
+                                  s.prompt + rng.choice(s.S - s.prompt, s.response_redrawn, replace=False)])
+            pos = np.sort(pos)
+            h[b, pos] = rng.standard_normal((pos.size, s.D), dtype=np.float32)
+            per_b.append(pos.astype(np.int64))
+        states.append(round_bf16(h))
+        redrawn.append(per_b)
+    return DyllmLoopInputs(s, w, states, redrawn)
 
 
 def pack_rows(rows_per_batch) -> tuple:

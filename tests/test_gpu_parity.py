@@ -172,6 +172,72 @@ def test_none_selected_returns_cache(dlm):
     assert n == 0
 
 
+def test_dyllm_adaptive_input_loop(dlm):
+    """DyLLM's adaptive input over 8 steps of the one-layer bf16 workload (1024
+    positions: a 512-token prompt and a 512-token response; every row drifts,
+    51 response rows and 4 prompt rows are redrawn per step): steps with
+    t % 4 == 0 score the whole sequence, the others the response [512, 1024)
+    only; each step selects by cosine < 0.95 inside its window and recomputes
+    the selected rows' Q/K/V (K/V scatter) and attention over all 1024 keys
+    (context scatter), with the loose row bound the benchmark passes.  Each
+    step against the oracle, which carries its own caches: the scores in the
+    window (none written outside), the index set, Q, K/V and output rows, O,
+    LSE; every row not selected keeps the step's input cache bytes."""
+    inp = W.dyllm_loop_inputs(W.DYLLM_LOOP)
+    s = inp.shape
+    B, S = s.B, s.S
+    scale = 1.0 / math.sqrt(s.hd)
+    say(f"[dyllm loop] B={B} S={S} prompt={s.prompt} D={s.D} steps={s.steps} refresh={s.refresh}")
+    kc_o, vc_o, out_o = (W.round_bf16(a) for a in
+                         O.full_recompute_caches(inp.hidden(-1), inp.w_qkv, s.Hq, s.Hkv, s.hd, scale))
+    kc, vc, out = dev(kc_o, "bf16"), dev(vc_o, "bf16"), dev(out_o, "bf16")
+    w = dev(inp.w_qkv, "bf16")
+    max_rows = B * S
+    q = torch.zeros(max_rows, s.Hq, s.hd, dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros_like(q)
+    lse = torch.zeros(max_rows, s.Hq, dtype=torch.float32, device="cuda")
+    idx = torch.zeros(B * S, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(B, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    scores = torch.zeros(B, S, dtype=torch.float32, device="cuda")
+    ws = workspace(dlm.dlm_select_workspace_size(dlm.DLM_SCORE_COSINE, B, S))
+    wsq = workspace(dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, max_rows, s.D, s.Hq, s.Hkv, s.hd))
+    wsa = workspace(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, max_rows, B, S, s.Hq, s.Hkv, s.hd))
+    for t in range(s.steps):
+        lo, hi = O.adaptive_input_window(t, s.prompt, S, s.refresh)
+        cur, prev = inp.hidden(t), inp.hidden(t - 1)
+        ref = O.cosine_step(cur, prev, inp.w_qkv, s.Hq, s.Hkv, s.hd, s.tau, kc_o, vc_o, out_o, lo=lo, hi=hi)
+        before = [x.clone() for x in (kc, vc, out)]
+        scores.fill_(-7.0)
+        curd = dev(cur, "bf16")
+        dlm.dlm_saliency_select(dlm.DLM_SCORE_COSINE, curd, dev(prev, "bf16"), lo=lo, hi=hi, threshold=s.tau,
+                                idx=idx, counts=counts, offsets=offsets, scores=scores, workspace=ws)
+        torch.cuda.synchronize()
+        sc_g = host(scores)
+        assert maxabs(sc_g[:, lo:hi], ref["scores"][:, lo:hi]) <= 1e-5
+        assert np.all(sc_g[:, :lo] == -7.0)
+        check_selection(idx.cpu().numpy(), counts.cpu().numpy(), offsets.cpu().numpy(), ref["scores"], lo, hi,
+                        s.tau)
+        n = int(ref["offsets"][-1])
+        idx_o, off_o = i32(ref["idx"]), i32(ref["offsets"])
+        dlm.dlm_gather_qkv_scatter_kv(curd, idx_o, off_o, max_rows, w, s.Hq, s.Hkv, s.hd, q, kc, vc, workspace=wsq)
+        dlm.dlm_partial_attn(q, idx_o, off_o, max_rows, kc, vc, scale, o, lse, out_cache=out, workspace=wsa)
+        torch.cuda.synchronize()
+        sel = rows_mask(B, S, ref["idx"], ref["offsets"])
+        errs = dict(q=maxabs(host(q)[:n], ref["q"]), k=maxabs(host(kc)[sel], ref["k_cache"][sel]),
+                    v=maxabs(host(vc)[sel], ref["v_cache"][sel]), o=maxabs(host(o)[:n], ref["o"]),
+                    lse=maxabs(host(lse)[:n], ref["lse"]), out=maxabs(host(out)[sel], ref["out_cache"][sel]))
+        say(f"  step {t} window [{lo},{hi}) n={n} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        for k_, v_ in errs.items():
+            assert v_ <= TOL["bf16"], f"step {t} {k_}: {v_}"
+        keep = torch.from_numpy(~sel).cuda()
+        for x, x0 in zip((kc, vc, out), before):
+            assert torch.equal(x[keep], x0[keep]), f"step {t}: an unselected row changed"
+        if lo > 0:
+            assert ref["idx"].min() >= lo
+        kc_o, vc_o, out_o = ref["k_cache"], ref["v_cache"], ref["out_cache"]
+
+
 # ---------------------------------------------------------------------------
 # lock loop (GQA, given scores, several steps carrying the caches)
 # ---------------------------------------------------------------------------

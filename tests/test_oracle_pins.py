@@ -89,6 +89,50 @@ def test_planted_bf16_selects_exactly_the_redrawn_rows():
     assert idx.tolist() == inp.redrawn[0].tolist()
 
 
+def test_adaptive_input_window_closed_forms():
+    """DyLLM, Methodologie 3: the whole sequence every `refresh` steps (from the
+    first), the response alone otherwise."""
+    got = [O.adaptive_input_window(t, 512, 1024) for t in range(9)]
+    full, resp = (0, 1024), (512, 1024)
+    assert got == [full, resp, resp, resp, full, resp, resp, resp, full]
+    assert all(O.adaptive_input_window(t, 7, 20, refresh=1) == (0, 20) for t in range(5))
+    assert [O.adaptive_input_window(t, 7, 20, refresh=2) for t in range(4)] == [(0, 20), (7, 20)] * 2
+
+
+def test_dyllm_loop_selects_the_planted_rows_in_the_window():
+    """Each step of the planted loop (every row drifts, a few prompt and
+    response rows are redrawn): the oracle selects exactly the rows redrawn at
+    that step that lie in the step's window - the response rows only on
+    response-only steps, prompt and response rows on refresh steps."""
+    sh = W.DYLLM_LOOP
+    inp = W.dyllm_loop_inputs(sh, B=2, S=256, prompt=128, D=512, response_redrawn=13, prompt_redrawn=3)
+    s = inp.shape
+    for t in range(s.steps):
+        lo, hi = O.adaptive_input_window(t, s.prompt, s.S, s.refresh)
+        sc = O.cosine_scores(inp.hidden(t), inp.hidden(t - 1))
+        idx, counts, off = O.compact(sc, lo, hi, s.tau)
+        for b in range(s.B):
+            want = [i for i in inp.redrawn(t)[b].tolist() if lo <= i < hi]
+            assert O.rows_of(idx, off, b).tolist() == want, f"step {t} row {b}"
+        assert counts.sum() == s.B * (s.response_redrawn + (s.prompt_redrawn if lo == 0 else 0))
+
+
+def test_response_only_step_leaves_prompt_rows():
+    """A step scored on [prompt, S) recomputes no prompt row: the prompt's K/V
+    and output cache rows are exactly the cached ones, even where the prompt's
+    hidden states changed."""
+    inp = W.dyllm_loop_inputs(W.DYLLM_LOOP, B=1, S=96, prompt=40, D=128, Hq=2, Hkv=2, hd=64,
+                              response_redrawn=9, prompt_redrawn=5)
+    s = inp.shape
+    rng = np.random.default_rng(3)
+    kc, vc = rng.standard_normal((1, 96, 2, 64)), rng.standard_normal((1, 96, 2, 64))
+    out = rng.standard_normal((1, 96, 128))
+    r = O.cosine_step(inp.hidden(1), inp.hidden(0), inp.w_qkv, 2, 2, 64, s.tau, kc, vc, out, lo=40, hi=96)
+    assert r["idx"].min() >= 40 and len(r["idx"]) == 9
+    assert np.array_equal(r["k_cache"][:, :40], kc[:, :40]) and np.array_equal(r["v_cache"][:, :40], vc[:, :40])
+    assert np.array_equal(r["out_cache"][:, :40], out[:, :40])
+
+
 # --------------------------------------------------------------------------
 # compaction
 # --------------------------------------------------------------------------
