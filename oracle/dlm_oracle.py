@@ -25,7 +25,9 @@ Pages followed (title, section):
   [SureLock] "Stopping Computation for Converged Tokens in Masked Diffusion-LM
             Decoding" - Methodik, Kernprinzipien (locked positions skip the
             query projection; their K/V stay cached and are still attended to;
-            cost O(M N d)).
+            cost O(M N d)); Kriterium zum Sperren (lock when the local KL
+            divergence between consecutive posteriors falls below eps,
+            optionally gated by a percentile of the uncertainty 1 - max p).
   [LSP]     "Beyond Scattered Acceptance: Fast and Coherent Inference for DLMs
             via Longest Stable Prefixes" - Methodologie (commit the longest
             contiguous stable block at the start of the active region in one
@@ -406,6 +408,73 @@ def lsp_adaptive_commit(margin, gen_lo, gen_hi, committed, frac_lo=0.25, frac_hi
         out[b] += min(L, hi)
         tau[b] = t
     return out, tau
+
+
+def kl_divergence(rows_cur, rows_prev, w_lm):
+    """[SureLock] 2. Methodik, Kriterium zum Sperren (criterion 1): the local
+    KL divergence D_t = KL(p_t || p_{t-1}) between a position's posterior over
+    the vocabulary at this step and at the previous step, with p = softmax of
+    the LM-head logits of the position's hidden state at that step.
+
+    rows_cur, rows_prev [n, D] (the same positions at steps t and t-1), w_lm
+    [V, D].  Written from the definition KL(p||q) = sum_v p_v (log p_v - log
+    q_v), with log-probabilities z - logsumexp(z).  Also returns this step's
+    max probability and argmax (lowest index on ties), which the confidence
+    gate uses, and the top-1 minus top-2 logit gap (to flag argmaxes that
+    rounding could decide either way).  Returns (kl [n], maxprob [n],
+    argmax [n] int64, gap [n])."""
+    w = np.asarray(w_lm, dtype=f64)
+    zt = np.asarray(rows_cur, dtype=f64) @ w.T
+    zp = np.asarray(rows_prev, dtype=f64) @ w.T
+
+    def log_softmax(z):
+        m = z.max(axis=1, keepdims=True)
+        return z - (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))
+    lt, lp = log_softmax(zt), log_softmax(zp)
+    pt = np.exp(lt)
+    kl = (pt * (lt - lp)).sum(axis=1)
+    a = np.argmax(zt, axis=1)
+    maxprob = pt[np.arange(pt.shape[0]), a]
+    srt = np.sort(zt, axis=1)
+    gap = srt[:, -1] - srt[:, -2] if zt.shape[1] > 1 else np.full(zt.shape[0], np.inf)
+    return kl, maxprob, a.astype(np.int64), gap
+
+
+def surelock_lock(kl, maxprob, eval_idx, eval_offsets, locked, eps, gate_q=0.0):
+    """[SureLock] 2. Methodik, Kriterium zum Sperren: an evaluated position is
+    locked when its local KL divergence falls below eps (criterion 1, strict)
+    and, when the optional confidence gate is on (gate_q > 0), its uncertainty
+    1 - max p lies at or below the gate_q percentile of the uncertainties of
+    the positions evaluated in its sequence at this step (criterion 2).  Locks
+    are permanent: locked positions stay locked.
+
+    Reading of the percentile: the nearest-rank order statistic - with n
+    evaluated positions and k = ceil(gate_q * n) (at least 1), the k-th
+    smallest uncertainty.  As 1 - p falls when p rises, a position passes iff
+    its max p is at least the k-th largest max p of its sequence's evaluated
+    positions (compared on the max-probabilities themselves, so that no
+    rounding of 1 - p decides).  k is computed in double from the float32
+    gate_q, as the library does.
+
+    kl, maxprob [B,S] (read at the evaluated positions; the comparisons are
+    exact on the values given); locked [B,S] (1 = locked, 0 = active).
+    Returns the new lock array."""
+    kl = np.asarray(kl)
+    mp = np.asarray(maxprob)
+    out = np.array(locked, copy=True)
+    B = out.shape[0]
+    for b in range(B):
+        rows = rows_of(eval_idx, eval_offsets, b)
+        if rows.size == 0:
+            continue
+        thr = None
+        if gate_q > 0:
+            k = max(1, math.ceil(float(gate_q) * rows.size))
+            thr = sorted(mp[b, rows].tolist(), reverse=True)[min(k, rows.size) - 1]
+        for i in rows:
+            if kl[b, i] < eps and (thr is None or mp[b, i] >= thr):
+                out[b, i] = 1
+    return out
 
 
 def admissible_frontiers(prev_set, stable_state, S_gen, min_commit):

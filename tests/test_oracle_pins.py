@@ -744,3 +744,117 @@ def test_golden_hand_fixtures():
         _, lse = O.partial_attention(q, list(range(nq)), [0, nq], k, v, 1, 1, c["scale"])
         col = O.column_sums(q, [0, nq], k, lse, 1, 1, c["scale"])
         assert np.allclose(col[0], c["c"], atol=1e-12), c["name"]
+
+
+# --------------------------------------------------------------------------
+# SureLock: local KL divergence and the lock decision
+# --------------------------------------------------------------------------
+def _kl_brute(zt, zp):
+    """Pure-Python KL(p_t || p_p) of one position's logit lists."""
+    mt, mp_ = max(zt), max(zp)
+    st = sum(math.exp(z - mt) for z in zt)
+    sp = sum(math.exp(z - mp_) for z in zp)
+    out = 0.0
+    for a, b in zip(zt, zp):
+        lpa = a - mt - math.log(st)
+        lpb = b - mp_ - math.log(sp)
+        out += math.exp(lpa) * (lpa - lpb)
+    return out
+
+
+def test_kl_brute_force_and_library():
+    """Against a pure-Python sum over the vocabulary and scipy's relative
+    entropy of the two softmax distributions (argument order matters)."""
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    rng = np.random.default_rng(81)
+    n, D, V = 6, 16, 40
+    xt, xp = rng.standard_normal((n, D)), rng.standard_normal((n, D))
+    xp[0] = xt[0] + 0.05 * rng.standard_normal(D)
+    w = rng.standard_normal((V, D)) * 0.5
+    kl, mp, a, gap = O.kl_divergence(xt, xp, w)
+    zt, zp = xt @ w.T, xp @ w.T
+    for r in range(n):
+        assert abs(kl[r] - _kl_brute(zt[r].tolist(), zp[r].tolist())) < 1e-12
+        assert abs(kl[r] - entropy(softmax(zt[r]), softmax(zp[r]))) < 1e-12
+        assert a[r] == int(np.argmax(zt[r])) and abs(mp[r] - softmax(zt[r]).max()) < 1e-15
+    rev, _, _, _ = O.kl_divergence(xp, xt, w)
+    assert np.all(kl >= 0) and np.max(np.abs(kl - rev)) > 1e-3   # asymmetric: the order is pinned
+    assert kl[0] < kl[1:].min()
+
+
+def test_kl_closed_forms():
+    """Equal posteriors give 0 (also when every logit moves by one constant);
+    two tokens with logits (a, 0) against (0, 0): KL = p log 2p + (1-p) log 2(1-p)
+    with p = sigmoid(a)."""
+    rng = np.random.default_rng(82)
+    D, V = 8, 30
+    w = rng.standard_normal((V, D))
+    w[:, 0] = 1.0                                    # a constant column: x + c e0 shifts every logit by c
+    x = rng.standard_normal((3, D))
+    xs = x.copy()
+    xs[:, 0] += np.array([0.0, 2.5, -7.0])
+    kl, _, _, _ = O.kl_divergence(x, x, w)
+    assert np.all(kl == 0.0)
+    kl, _, _, _ = O.kl_divergence(x, xs, w)
+    assert np.max(np.abs(kl)) < 1e-12
+    for a in (0.3, 2.0, -4.0):
+        w2 = np.array([[1.0], [0.0]])
+        kl, mp, am, _ = O.kl_divergence(np.array([[a]]), np.array([[0.0]]), w2)
+        p = 1.0 / (1.0 + math.exp(-a))
+        assert abs(kl[0] - (p * math.log(2 * p) + (1 - p) * math.log(2 * (1 - p)))) < 1e-14
+        assert abs(mp[0] - max(p, 1 - p)) < 1e-15 and am[0] == (0 if a > 0 else 1)
+
+
+def _lock_brute(kl, mp, rows_per_b, locked, eps, q):
+    """The lock rule with the uncertainties 1 - p in exact rational arithmetic
+    and the nearest-rank percentile taken on them."""
+    from fractions import Fraction
+    out = np.array(locked, copy=True)
+    for b, rows in enumerate(rows_per_b):
+        if len(rows) == 0:
+            continue
+        u = {i: 1 - Fraction(float(mp[b, i])) for i in rows}
+        if q > 0:
+            k = max(1, math.ceil(float(q) * len(rows)))
+            pq = sorted(u.values())[min(k, len(rows)) - 1]
+        for i in rows:
+            if kl[b, i] < eps and (q <= 0 or u[i] <= pq):
+                out[b, i] = 1
+    return out
+
+
+def test_surelock_lock_brute_force():
+    rng = np.random.default_rng(83)
+    B, S = 4, 60
+    for q in (0.0, 0.3, 0.5, 1.0, np.float32(0.7)):
+        kl = rng.choice(np.array([0.0, 0.01, 0.02, 0.05, 0.3], np.float32), size=(B, S))
+        mp = rng.choice(np.array([0.2, 0.5, 0.9, 0.95, 0.999], np.float32), size=(B, S))
+        rows = [np.sort(rng.choice(S, m, replace=False)) for m in (20, 0, 33, 7)]
+        idx, off = W.pack_rows(rows)
+        locked = (rng.random((B, S)) < 0.2).astype(np.float32)
+        got = O.surelock_lock(kl, mp, idx, off, locked, np.float32(0.02), q)
+        want = _lock_brute(kl, mp, rows, locked, np.float32(0.02), q)
+        assert np.array_equal(got, want), f"q={q}"
+        assert np.all(got >= locked)                                  # locks are permanent
+        mask = np.zeros((B, S), bool)
+        for b, r in enumerate(rows):
+            mask[b, r] = True
+        assert np.array_equal(got[~mask], locked[~mask])              # only evaluated positions move
+
+
+def test_surelock_lock_closed_forms():
+    """Strict KL threshold; no gate: lock iff kl < eps; q = 1: the gate passes
+    everything; a small q: only the most confident position(s) pass (ties at
+    the percentile value all pass)."""
+    kl = np.array([[0.0, 0.01, 0.02, 0.03, 0.0, 0.0]], np.float32)
+    mp = np.array([[0.9, 0.99, 0.5, 0.99, 0.99, 0.7]], np.float32)
+    idx, off = W.pack_rows([np.arange(6)])
+    z = np.zeros((1, 6), np.float32)
+    eps = np.float32(0.02)
+    assert O.surelock_lock(kl, mp, idx, off, z, eps, 0.0).tolist() == [[1, 1, 0, 0, 1, 1]]
+    assert O.surelock_lock(kl, mp, idx, off, z, eps, 1.0).tolist() == [[1, 1, 0, 0, 1, 1]]
+    # k = ceil(0.1 * 6) = 1: the largest max p is 0.99 (three positions tie)
+    assert O.surelock_lock(kl, mp, idx, off, z, eps, 0.1).tolist() == [[0, 1, 0, 0, 1, 0]]
+    # k = 4: the 4th largest is 0.9
+    assert O.surelock_lock(kl, mp, idx, off, z, eps, 0.6).tolist() == [[1, 1, 0, 0, 1, 0]]
