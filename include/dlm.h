@@ -14,6 +14,7 @@
  *      optional: per-key attention column sums + top-k  -> dlm_attn_colsum
  *      optional: longest-stable-prefix commit           -> dlm_stable_prefix
  *                (adaptive threshold on the logit margin -> dlm_lsp_adaptive_commit)
+ *      optional: KL-divergence lock of converged tokens -> dlm_kl_lock
  *      optional: FFN of the salient rows                -> dlm_salient_ffn
  *      optional: value-change update of the stable rows -> dlm_nonsalient_dv_update
  *                (caches kept with dlm_gather_rows / dlm_scatter_rows)
@@ -286,6 +287,39 @@ int dlm_nonsalient_dv_update(int dtype, const void* q_cache, const float* lse_ca
                              const void* k_old, const void* v_old, const void* v_cache,
                              int B, int S, int Hq, int Hkv, int hd, float scale,
                              void* o_cache, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dlm_kl_lock
+ *
+ * The locking criterion of "Stopping Computation for Converged Tokens in
+ * Masked Diffusion-LM Decoding", 2. Methodik, Kriterium zum Sperren: a
+ * position is locked (its projections and FFN are skipped from then on, its
+ * K/V stay cached) when the local KL divergence between its posteriors at
+ * this and the previous step, KL(p_t || p_{t-1}), falls below eps, and -
+ * the optional confidence gate - its uncertainty 1 - max p_t lies at or
+ * below the gate_q percentile of the uncertainties of its sequence's
+ * evaluated positions.
+ *
+ * For the positions listed by (eval_idx, eval_offsets) (at most max_eval),
+ * p_t and p_{t-1} are the softmax of the LM-head logits h . W_lm^T of the
+ * position's hidden state in h_cur and in h_prev [B,S,D] bf16 (W_lm [V,D]
+ * bf16), formed on the matrix cores in one pass over W_lm and reduced on the
+ * fly (logits are never stored).  Writes, at the evaluated positions of the
+ * [B,S] arrays: kl (f32; rounding can leave a value a few ulps below 0),
+ * maxprob = max p_t (f32) and argmax of p_t (i32, lowest index on ties);
+ * then sets locked[b,i] = 1.0f (f32 [B,S], 1 = locked, other values kept;
+ * usable as the given scores of DLM_SCORE_GIVEN with threshold 0.5) where
+ * kl < eps (strict) and, if 0 < gate_q <= 1, maxprob >= the k-th largest
+ * maxprob of the sequence's evaluated positions, k = max(1, ceil(gate_q *
+ * n_b)) computed in double (the nearest-rank percentile; equal values all
+ * pass).  gate_q <= 0: no gate.  Other entries are not written.
+ * D % 64 == 0, V % 256 == 0; workspace from dlm_kl_lock_workspace_size.
+ * ------------------------------------------------------------------------ */
+size_t dlm_kl_lock_workspace_size(int B, int S, int V, int max_eval);
+int dlm_kl_lock(const void* h_cur, const void* h_prev, const void* w_lm, int B, int S, int D, int V,
+                const int32_t* eval_idx, const int32_t* eval_offsets, int max_eval,
+                float eps, float gate_q, float* kl, float* maxprob, int32_t* argmax,
+                float* locked, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * dlm_salient_ffn

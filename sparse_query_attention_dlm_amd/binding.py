@@ -76,6 +76,10 @@ lib.dlm_salient_ffn.restype = _I
 lib.dlm_salient_ffn.argtypes = [_I, _P, _I, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _Z, _P]
 lib.dlm_lsp_adaptive_commit.restype = _I
 lib.dlm_lsp_adaptive_commit.argtypes = [_P, _I, _I, _I, _I, _F, _F, _P, _P, _P]
+lib.dlm_kl_lock_workspace_size.restype = _Z
+lib.dlm_kl_lock_workspace_size.argtypes = [_I] * 4
+lib.dlm_kl_lock.restype = _I
+lib.dlm_kl_lock.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _P, _P, _Z, _P]
 lib.dlm_gather_rows.restype = _I
 lib.dlm_gather_rows.argtypes = [_P, _I, _I, _I, _P, _P, _I, _P, _P]
 lib.dlm_scatter_rows.restype = _I
@@ -259,6 +263,24 @@ def dlm_lsp_adaptive_commit(margin, gen_lo, gen_hi, committed, frac_lo=0.25, fra
     rc = lib.dlm_lsp_adaptive_commit(
         _ptr(margin, "margin", torch.float32), B, S, int(gen_lo), int(gen_hi), float(frac_lo), float(frac_hi),
         _ptr(committed, "committed", torch.int32), _ptr(tau, "tau", torch.float32, False), _stream(stream))
+    _check(rc)
+
+
+def dlm_kl_lock_workspace_size(B, S, V, max_eval) -> int:
+    return int(lib.dlm_kl_lock_workspace_size(int(B), int(S), int(V), int(max_eval)))
+
+
+def dlm_kl_lock(h_cur, h_prev, w_lm, eval_idx, eval_offsets, max_eval, eps, kl, maxprob, argmax, locked,
+                gate_q=0.0, workspace=None, stream=None):
+    """h_cur, h_prev [B,S,D] bf16; w_lm [V,D] bf16; kl, maxprob, locked f32 [B,S]; argmax i32 [B,S]."""
+    B, S, D = h_cur.shape
+    V = w_lm.shape[0]
+    wp, wn = _ws(workspace)
+    rc = lib.dlm_kl_lock(
+        _ptr(h_cur, "h_cur", torch.bfloat16), _ptr(h_prev, "h_prev", torch.bfloat16), _ptr(w_lm, "w_lm", torch.bfloat16),
+        B, S, D, V, _ptr(eval_idx, "eval_idx", torch.int32, False), _ptr(eval_offsets, "eval_offsets", torch.int32, False),
+        int(max_eval), float(eps), float(gate_q), _ptr(kl, "kl", torch.float32), _ptr(maxprob, "maxprob", torch.float32),
+        _ptr(argmax, "argmax", torch.int32), _ptr(locked, "locked", torch.float32), wp, wn, _stream(stream))
     _check(rc)
 
 

@@ -122,5 +122,22 @@ __device__ __forceinline__ void merge_part(float& m, float& s, int& a, float m2,
   a = A;
 }
 
+// merge_part for partials that also carry a sum w of exp(z - m) times a
+// per-logit weight (rescaled like s)
+__device__ __forceinline__ void merge_part_w(float& m, float& s, float& w, int& a, float m2, float s2,
+                                             float w2, int a2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2; s = s2; w = w2; a = a2;
+    return;
+  }
+  const float M = fmaxf(m, m2);
+  const int A = (m > m2) ? a : ((m2 > m) ? a2 : min(a, a2));
+  const float f1 = exp2f((m - M) * kLog2e), f2 = exp2f((m2 - M) * kLog2e);
+  s = s * f1 + s2 * f2;
+  w = w * f1 + w2 * f2;
+  m = M;
+  a = A;
+}
 
 }  // namespace dlm

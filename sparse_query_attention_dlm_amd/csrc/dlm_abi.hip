@@ -188,6 +188,70 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b, int B
 }
 
 // ---------------------------------------------------------------------------
+size_t dlm_kl_lock_workspace_size(int B, int S, int V, int max_eval) {
+  if (B <= 0 || S <= 0 || V <= 0 || max_eval <= 0) return 0;
+  return round_up((size_t)max_eval * dlm::gemm_lmhead_ntile(V) * 2 * sizeof(float4), 256) +
+         dlm::gemm_workspace_bytes(dlm::EPI_LMKL, max_eval, V, 0);
+}
+
+int dlm_kl_lock(const void* h_cur, const void* h_prev, const void* w_lm, int B, int S, int D, int V,
+                const int32_t* eval_idx, const int32_t* eval_offsets, int max_eval, float eps,
+                float gate_q, float* kl, float* maxprob, int32_t* argmax, float* locked,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(B > 0 && S > 0 && D > 0, "B, S, D must be positive (B=%d S=%d D=%d)", B, S, D);
+  REQUIRE(D % 64 == 0, "D=%d must be a multiple of 64", D);
+  REQUIRE(V > 0 && V % 256 == 0, "V=%d must be a positive multiple of 256", V);
+  REQUIRE(max_eval >= 0 && (long long)max_eval <= (long long)B * S, "max_eval=%d out of range", max_eval);
+  REQUIRE(gate_q <= 1.f, "gate_q=%g must be at most 1 (<= 0: no confidence gate)", gate_q);
+  REQUIRE(eps == eps, "eps must not be NaN");
+  REQUIRE((long long)B * S * D * 2 < (1ll << 31), "hidden states of 2 GiB or more");
+  REQUIRE((long long)V * D * 2 < (1ll << 32), "W_lm of 4 GiB or more");
+  if (max_eval == 0) return DLM_OK;
+  REQUIRE_PTR(h_cur);
+  REQUIRE_PTR(h_prev);
+  REQUIRE_PTR(w_lm);
+  REQUIRE_PTR(eval_idx);
+  REQUIRE_PTR(eval_offsets);
+  REQUIRE_PTR(kl);
+  REQUIRE_PTR(maxprob);
+  REQUIRE_PTR(argmax);
+  REQUIRE_PTR(locked);
+  REQUIRE_ALIGNED(h_cur);
+  REQUIRE_ALIGNED(h_prev);
+  REQUIRE_ALIGNED(w_lm);
+  const size_t need = dlm_kl_lock_workspace_size(B, S, V, max_eval);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  REQUIRE_ALIGNED(workspace);
+  CHECK_ROWS(eval_idx, eval_offsets, B, S, max_eval, true, stream, "KL lock");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ntile = dlm::gemm_lmhead_ntile(V);
+  float4* part = static_cast<float4*>(workspace);
+  dlm::GemmArgs g{};
+  g.w = w_lm;
+  g.x = h_cur;
+  g.x2 = h_prev;
+  g.x_bytes = (uint32_t)((size_t)B * S * D * 2);
+  g.K = D;
+  g.N = V;
+  g.B = B;
+  g.S = S;
+  g.idx = eval_idx;
+  g.offsets = eval_offsets;
+  g.max_rows = max_eval;
+  g.lm_part = part;
+  g.ntile = ntile;
+  g.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    round_up((size_t)max_eval * ntile * 2 * sizeof(float4), 256));
+  int rc = hip_status(dlm::launch_gemm(DLM_BF16, dlm::EPI_LMKL, dlm::A_GATHER, g, st), "two-step LM head");
+  if (rc != DLM_OK) return rc;
+  return hip_status(dlm::launch_kl_lock(part, ntile, eval_idx, eval_offsets, max_eval, B, S, eps, gate_q,
+                                        kl, maxprob, argmax, locked, st),
+                    "KL lock decision");
+}
+
+// ---------------------------------------------------------------------------
 size_t dlm_gather_qkv_workspace_size(int dtype, int max_rows, int D, int Hq, int Hkv, int hd) {
   if (dtype != DLM_BF16 || max_rows <= 0 || D <= 0 || Hq <= 0 || Hkv <= 0 || hd <= 0) return 0;
   return dlm::gemm_workspace_bytes(dlm::EPI_QKV, max_rows, (Hq + 2 * Hkv) * hd, D);

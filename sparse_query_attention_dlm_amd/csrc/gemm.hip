@@ -86,6 +86,69 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
                           acc[a][b][4 * q4 + 2], acc[a][b][4 * q4 + 3]);
         }
     }
+  } else if constexpr (EPI == EPI_LMKL) {
+    // Token columns c and c + 16 of a 32-column block hold one position's
+    // logits at this step and at the previous step (same features, same
+    // registers), so a lane reads its partner's 16 logits with one swizzle.
+    // Per lane: this step's (max, sum e, sum e (z - z_prev), argmax) or the
+    // previous step's (max, sum e) over its features (the lanes of the
+    // previous step compute the cross sum too; it is not used).
+    __shared__ float s_km[WP][TT], s_ks[WP][TT], s_kw[WP][TT];
+    __shared__ int s_ka[WP][TT];
+#pragma unroll
+    for (int b = 0; b < FT; ++b) {
+      const int ml = wt * WTT + b * 32 + lr;
+      float m = -INFINITY, s = 0.f, w = 0.f;
+      int am = 0x7fffffff;
+#pragma unroll
+      for (int a = 0; a < FP; ++a) {
+        float cm = acc[a][b][0];
+        int ca = n0 + wp * WTP + a * 32 + 4 * lg;
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+          const int n = n0 + wp * WTP + a * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
+          if (acc[a][b][i] > cm) {  // rows grow with i, so ties keep the lower index
+            cm = acc[a][b][i];
+            ca = n;
+          }
+        }
+        const float cm2 = cm * kLog2e;
+        float cs = 0.f, cw = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float v = acc[a][b][i];
+          const float e = __builtin_amdgcn_exp2f(fmaf(v, kLog2e, -cm2));
+          cs += e;
+          cw = fmaf(e, v - __shfl_xor(v, 16, 64), cw);
+        }
+        merge_part_w(m, s, w, am, cm, cs, cw, ca);
+      }
+      merge_part_w(m, s, w, am, __shfl_xor(m, 32, 64), __shfl_xor(s, 32, 64), __shfl_xor(w, 32, 64),
+                   __shfl_xor(am, 32, 64));
+      if (lg == 0) {
+        s_km[wp][ml] = m;
+        s_ks[wp][ml] = s;
+        s_kw[wp][ml] = w;
+        s_ka[wp][ml] = am;
+      }
+    }
+    __syncthreads();
+    for (int pp = tid; pp < TT / 2; pp += 256) {
+      const int cc = (pp >> 4) * 32 + (pp & 15);  // the position's column at this step; cc + 16 the previous
+      if (s_drow[cc] < 0) continue;
+      float m = s_km[0][cc], s = s_ks[0][cc], w = s_kw[0][cc];
+      int am = s_ka[0][cc];
+      float mq = s_km[0][cc + 16], sq = s_ks[0][cc + 16], wq = 0.f;
+      int aq = 0;
+#pragma unroll
+      for (int v = 1; v < WP; ++v) {
+        merge_part_w(m, s, w, am, s_km[v][cc], s_ks[v][cc], s_kw[v][cc], s_ka[v][cc]);
+        merge_part_w(mq, sq, wq, aq, s_km[v][cc + 16], s_ks[v][cc + 16], 0.f, 0);
+      }
+      float4* dst = g.lm_part + 2 * ((size_t)(m0 / 2 + pp) * g.ntile + nt);
+      dst[0] = make_float4(m, s, __int_as_float(am), w);
+      dst[1] = make_float4(mq, sq, 0.f, 0.f);
+    }
   } else {
     __shared__ float s_pm[WP][TT], s_ps[WP][TT], s_p2[EPI == EPI_LMMARGIN ? WP : 1][TT];
     __shared__ int s_pa[WP][TT];
@@ -189,17 +252,20 @@ constexpr int gemm_lds_u16(int TP, int TT, int BK) { return 2 * (TP + TT) * (BK 
 // Resolve the tile's token rows: cache row (b*S + idx[m], -1 for padding) and
 // the byte offset of the operand row (past the end of the buffer for padding,
 // so that its loads return zeros).
-template <int TT, int AMODE>
+// PAIRS (EPI_LMKL): token row m is position (m/32)*16 + m%16, loaded from x
+// (m%32 < 16) or x2; n_rows counts positions.
+template <int TT, int AMODE, bool PAIRS = false>
 __device__ __forceinline__ void gemm_rows(const GemmArgs& g, int n_rows, int m0, uint32_t* s_xoff,
                                           int* s_drow) {
   for (int t = threadIdx.x; t < TT; t += 256) {
     const int m = m0 + t;
+    const int p = PAIRS ? (m >> 5) * 16 + (m & 15) : m;
     uint32_t xo = 0x80000000u;
     int drow = -1;
-    if (m < n_rows) {
-      const int b = batch_of(g.offsets, g.B, m);
-      drow = b * g.S + g.idx[m];
-      xo = (uint32_t)((AMODE == A_GATHER ? (size_t)drow : (size_t)m) * g.K * 2);
+    if (p < n_rows) {
+      const int b = batch_of(g.offsets, g.B, p);
+      drow = b * g.S + g.idx[p];
+      xo = (uint32_t)((AMODE == A_GATHER ? (size_t)drow : (size_t)p) * g.K * 2);
     }
     s_xoff[t] = xo;
     s_drow[t] = drow;
@@ -241,7 +307,7 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
                             FP * FT * 16 * 256 * 4 <= 2 * ROWS * PITCH * 2),
                 "two k-halves: row epilogues only, partial sums fit the tile's LDS");
 
-  const int m_tiles = (n_rows + TT - 1) / TT;
+  const int m_tiles = (gemm_token_rows(EPI, n_rows) + TT - 1) / TT;
   const int n_tiles = g.N / TPV;
   const int nk_all = g.K / BK;
   const GemmSplit sp = gemm_split(m_tiles * n_tiles, nk_all, PF, SB, ST);
@@ -270,7 +336,7 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
   constexpr int CHUNKS = ROWS * CPR;
   constexpr int CPT = CHUNKS / NT;
   constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
-  const int m_tiles = (n_rows + TT - 1) / TT;
+  const int m_tiles = (gemm_token_rows(EPI, n_rows) + TT - 1) / TT;
   const int nk_all = g.K / BK;
   const int nt = unit / m_tiles, mt = unit % m_tiles;
   const int m0 = mt * TT, n0 = nt * TPV;
@@ -278,7 +344,7 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
   const int nk = nk_all / sp.ks;        // k-steps of this split
   const int kbase = ksi * nk;           // first k-step of this split
 
-  gemm_rows<TT, AMODE>(g, n_rows, m0, s_xoff, s_drow);
+  gemm_rows<TT, AMODE, EPI == EPI_LMKL>(g, n_rows, m0, s_xoff, s_drow);
   __syncthreads();
 
   // Chunk j of this thread covers LDS row (tid/CPR + RPJ j), 16-byte column
@@ -288,7 +354,15 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
   constexpr int CX = CPT - CW;  // chunks of token rows per thread
   const int r0 = tid / CPR, kc = tid % CPR;
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.w, (uint32_t)((size_t)g.N * g.K * 2));
-  const __amdgpu_buffer_rsrc_t rX = make_rsrc(g.x, g.x_bytes);
+  const void* xsrc = g.x;
+  if constexpr (EPI == EPI_LMKL) {
+    // a thread's token rows are all (tid/CPR) % 32 within their 32-row
+    // groups: waves 0-1 load this step's rows (x), waves 2-3 the previous
+    // step's (x2); the choice is uniform per wave, so the resource stays scalar
+    static_assert(NT == 256 && RPJ == 32 && TP % 32 == 0, "paired token rows need 32 rows per chunk index");
+    if (__builtin_amdgcn_readfirstlane((int)threadIdx.x >> 7)) xsrc = g.x2;
+  }
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(xsrc, g.x_bytes);
   const uint32_t woff = (uint32_t)(((size_t)(n0 + r0) * g.K + kc * 8) * 2);
   const uint32_t wstride = (uint32_t)(RPJ * g.K * 2);
   uint32_t xoff[CX];
@@ -468,7 +542,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g) {
   __shared__ uint32_t s_xoff[TT];
   const int n_rows = min(g.offsets[g.B], g.max_rows);
   if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
-  const int m_tiles = (n_rows + TT - 1) / TT;
+  const int m_tiles = (gemm_token_rows(EPI, n_rows) + TT - 1) / TT;
   const int n_tiles = g.N / TP;
   const GemmSplit sp = gemm_split(m_tiles * n_tiles, g.K / BK, PF, SB, ST);
   if (sp.ks <= 1) return;
@@ -479,7 +553,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g) {
   const int m0 = mt * TT, n0 = nt * TP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
   const int wp = wave / WT, wt = wave % WT;
-  gemm_rows<TT, AMODE>(g, n_rows, m0, s_xoff, s_drow);
+  gemm_rows<TT, AMODE, EPI == EPI_LMKL>(g, n_rows, m0, s_xoff, s_drow);
   __syncthreads();
   const float4* all = reinterpret_cast<const float4*>(g.part) + (size_t)unit * sp.ks * (NQ * 256);
   auto sum_splits = [&](int gi) {
@@ -613,6 +687,7 @@ static int pf_for(int nk, int pfmax) {
 
 size_t gemm_workspace_bytes(int epi, int max_rows, int N, int K) {
   if (max_rows <= 0) return 0;
+  max_rows = gemm_token_rows(epi, max_rows);
   if (epi_lm(epi)) return (size_t)kSplitCap * kLmTP * 256 * sizeof(float);
   if (max_rows > 1024 && N % 256 == 0) return (size_t)kSplitCap * 256 * 256 * sizeof(float);
   return 0;
@@ -637,7 +712,7 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
   // every output tile (and every split the device may choose when the real
   // selection turns out short) is a work item; the two-k-half tiling runs one
   // item per workgroup, the others loop over a resident grid
-  const int m_tiles_max = (g.max_rows + TT - 1) / TT;
+  const int m_tiles_max = (gemm_token_rows(EPI, g.max_rows) + TT - 1) / TT;
   int items = (g.N / TP) * m_tiles_max;
   if (SB > 0) {
     const int cap = ST < kSplitCap ? 2 * ST : kSplitCap;
@@ -708,6 +783,8 @@ hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStre
     launch_bf16<kLmTP, 256, 64, 1, EPI_LMHEAD, A_GATHER, 0, 256, 768>(g, st);
   } else if (epi == EPI_LMMARGIN) {
     launch_bf16<kLmTP, 256, 64, 1, EPI_LMMARGIN, A_GATHER, 0, 256, 768>(g, st);
+  } else if (epi == EPI_LMKL) {
+    launch_bf16<kLmTP, 256, 64, 1, EPI_LMKL, A_GATHER, 0, 256, 768>(g, st);
   } else if ((g.K / 64) % 4 != 0 && g.max_rows > kSkinnyRows && g.N % 128 == 0) {
     // short K: the 4-deep skinny ring does not divide it; one large tiling
     // (its 128-feature tiles must divide N; otherwise the 64-feature tiling

@@ -31,15 +31,29 @@ hipError_t launch_lmhead_combine(const float4* part, int ntile, const int32_t* e
                                  int hi, float thr, int margin, float* scores, int32_t* argmax,
                                  int32_t* idx, int32_t* counts, int32_t* offsets, hipStream_t st);
 
+// KL lock (select.hip): merge the EPI_LMKL tile partials into KL, max-prob and
+// argmax of every evaluated position, then the per-sequence lock decision
+hipError_t launch_kl_lock(const float4* part, int ntile, const int32_t* eval_idx,
+                          const int32_t* eval_offsets, int max_eval, int B, int S, float eps,
+                          float gate_q, float* kl, float* maxprob, int32_t* argmax, float* locked,
+                          hipStream_t st);
+
 // gemm.hip -- D^T[n][m] = sum_k W[n][k] * A[row(m)][k]; W output-major [N][K].
-enum GemmEpilogue { EPI_QKV = 0, EPI_ROWS = 1, EPI_LMHEAD = 2, EPI_SWIGLU = 3, EPI_LMMARGIN = 4 };
-// the two LM-head epilogues (the margin one also keeps the second-largest logit)
-constexpr bool epi_lm(int epi) { return epi == EPI_LMHEAD || epi == EPI_LMMARGIN; }
+enum GemmEpilogue { EPI_QKV = 0, EPI_ROWS = 1, EPI_LMHEAD = 2, EPI_SWIGLU = 3, EPI_LMMARGIN = 4, EPI_LMKL = 5 };
+// the LM-head epilogues (the margin one also keeps the second-largest logit;
+// the KL one reduces the logits of two steps of each position, see below)
+constexpr bool epi_lm(int epi) { return epi == EPI_LMHEAD || epi == EPI_LMMARGIN || epi == EPI_LMKL; }
+// EPI_LMKL: every selected position contributes two token rows, its hidden
+// state at this step (from x) and at the previous step (from x2), interleaved
+// by 16: token row m is position (m/32)*16 + m%16, of this step when m%32 < 16.
+// GEMM token rows for n selected positions:
+constexpr int gemm_token_rows(int epi, int n) { return epi == EPI_LMKL ? ((n + 15) / 16) * 32 : n; }
 enum GemmAMode { A_GATHER = 0, A_COMPACT = 1 };
 struct GemmArgs {
   const void* w;            // [N][K]
   const void* x;            // A_GATHER: x[B][S][K], row (b, idx[m]); A_COMPACT: x[m][K]
-  uint32_t x_bytes;         // size of x (operand loads are range-checked against it)
+  const void* x2;           // EPI_LMKL: the previous step's hidden states, laid out as x
+  uint32_t x_bytes;         // size of x (and x2) (operand loads are range-checked against it)
   int K, N, B, S;
   const int32_t* idx;       // selected positions (packed)
   const int32_t* offsets;   // [B+1]
@@ -55,7 +69,10 @@ struct GemmArgs {
   void* out;
   int ld_out;
   // EPI_LMHEAD: lm_part[m*ntile + tile] = {max, sum exp(z-max), argmax bits, 0};
-  // EPI_LMMARGIN: the same with the second-largest logit in the last slot
+  // EPI_LMMARGIN: the same with the second-largest logit in the last slot;
+  // EPI_LMKL: two per (position p, tile): lm_part[2(p*ntile + tile)] = {max,
+  //   sum e, argmax bits, sum e * (z - z_prev)} of this step's logits z,
+  //   lm_part[... + 1] = {max, sum exp(z_prev - max), 0, 0} of the previous step's
   float4* lm_part;
   int ntile;
   // split-K scratch (workspace): partial tiles

@@ -213,6 +213,116 @@ __global__ __launch_bounds__(256) void lmhead_combine_kernel(
   }
 }
 
+// SureLock (Stopping Computation for Converged Tokens), Methodik, Kriterium
+// zum Sperren: the local KL divergence KL(p_t || p_{t-1}) of each evaluated
+// position, from the LM head's per-tile partials of both steps (never the
+// logits): with lse = m + log s per step and w / s = sum_v p_t(v) (z_t(v) -
+// z_{t-1}(v)), KL = w / s_t - lse_t + lse_{t-1}.  Also the max probability
+// 1 / s_t and the argmax of this step.  One wave per evaluated position.
+__global__ __launch_bounds__(256) void kl_combine_kernel(
+    const float4* __restrict__ part, int ntile, const int32_t* __restrict__ eval_idx,
+    const int32_t* __restrict__ eval_offsets, int max_eval, int B, int S, float* kl, float* maxprob,
+    int32_t* argmax) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  const int n_eval = min(eval_offsets[B], max_eval);
+  if (r >= n_eval) return;
+  float m = -INFINITY, s = 0.f, w = 0.f, mq = -INFINITY, sq = 0.f, wq = 0.f;
+  int a = 0x7fffffff, aq = 0;
+  for (int t = lane; t < ntile; t += 64) {
+    const float4 p = part[2 * ((size_t)r * ntile + t)], q = part[2 * ((size_t)r * ntile + t) + 1];
+    merge_part_w(m, s, w, a, p.x, p.y, p.w, __float_as_int(p.z));
+    merge_part_w(mq, sq, wq, aq, q.x, q.y, 0.f, 0);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    merge_part_w(m, s, w, a, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64), __shfl_xor(w, o, 64),
+                 __shfl_xor(a, o, 64));
+    merge_part_w(mq, sq, wq, aq, __shfl_xor(mq, o, 64), __shfl_xor(sq, o, 64), 0.f, 0);
+  }
+  if (lane == 0) {
+    const int b = batch_of(eval_offsets, B, r);
+    const size_t pos = (size_t)b * S + eval_idx[r];
+    kl[pos] = w / s - (m + __logf(s)) + (mq + __logf(sq));
+    maxprob[pos] = 1.0f / s;
+    argmax[pos] = a;
+  }
+}
+
+// The lock decision per sequence (one workgroup of 1024 threads): an
+// evaluated position locks when KL < eps and, with the confidence gate on,
+// its max probability is at least the k-th largest of its sequence's
+// evaluated positions, k = max(1, ceil(gate_q * n)) (the nearest-rank
+// percentile of the uncertainty 1 - max p, compared on max p itself).  The
+// k-th largest is found by a radix select over the float bits (positive
+// floats order as unsigned integers), 8 bits at a time from the top.
+// Locked entries are set to 1; nothing else is written.
+__global__ __launch_bounds__(1024) void kl_lock_kernel(const float* __restrict__ kl,
+                                                       const float* __restrict__ maxprob,
+                                                       const int32_t* __restrict__ eval_idx,
+                                                       const int32_t* __restrict__ eval_offsets,
+                                                       int max_eval, int S, float eps, float gate_q,
+                                                       float* locked) {
+  __shared__ unsigned hist[256];
+  __shared__ unsigned s_bin, s_above;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = min(eval_offsets[b], max_eval), r1 = min(eval_offsets[b + 1], max_eval);
+  const int n = r1 - r0;
+  if (n <= 0) return;
+  const float* klb = kl + (size_t)b * S;
+  const float* mpb = maxprob + (size_t)b * S;
+  unsigned thr = 0u;  // bits of the gate's max-prob threshold (0: no gate)
+  if (gate_q > 0.f) {
+    int k = (int)ceil((double)gate_q * (double)n);
+    k = max(1, min(k, n));
+    unsigned prefix = 0u, mask = 0u;
+    unsigned rem = (unsigned)k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0u;
+      __syncthreads();
+      for (int r = r0 + tid; r < r1; r += 1024) {
+        const unsigned u = __float_as_uint(mpb[eval_idx[r]]);
+        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane l holds bins 255-4l .. 252-4l, highest first
+        unsigned c[4], tot = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[q] = hist[255 - 4 * lane - q];
+          tot += c[q];
+        }
+        unsigned incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const unsigned t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        unsigned cum = incl - tot;  // candidates in the bins above this lane's
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (cum < rem && rem <= cum + c[q]) {
+            s_bin = 255u - 4u * lane - q;
+            s_above = cum;
+          }
+          cum += c[q];
+        }
+      }
+      __syncthreads();
+      prefix |= s_bin << shift;
+      mask |= 0xFFu << shift;
+      rem -= s_above;
+      __syncthreads();  // s_bin / s_above are rewritten by the next digit
+    }
+    thr = prefix;  // the exact bits of the k-th largest max-prob
+  }
+  for (int r = r0 + tid; r < r1; r += 1024) {
+    const int i = eval_idx[r];
+    if (klb[i] < eps && __float_as_uint(mpb[i]) >= thr) locked[(size_t)b * S + i] = 1.0f;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -259,6 +369,24 @@ hipError_t launch_lmhead_combine(const float4* part, int ntile, const int32_t* e
     if (e != hipSuccess) return e;
   }
   return launch_given_select(scores, B, S, lo, hi, thr, idx, counts, offsets, st);
+}
+
+}  // namespace dlm
+
+namespace dlm {
+
+hipError_t launch_kl_lock(const float4* part, int ntile, const int32_t* eval_idx,
+                          const int32_t* eval_offsets, int max_eval, int B, int S, float eps,
+                          float gate_q, float* kl, float* maxprob, int32_t* argmax, float* locked,
+                          hipStream_t st) {
+  if (max_eval <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kl_combine_kernel, dim3((max_eval + 3) / 4), dim3(256), 0, st, part, ntile, eval_idx,
+                     eval_offsets, max_eval, B, S, kl, maxprob, argmax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kl_lock_kernel, dim3(B), dim3(1024), 0, st, kl, maxprob, eval_idx, eval_offsets,
+                     max_eval, S, eps, gate_q, locked);
+  return hipGetLastError();
 }
 
 }  // namespace dlm
