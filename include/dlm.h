@@ -188,6 +188,26 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
                      const void* w_o, int D_out, void* out_cache,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* dlm_partial_attn_noalloc: dlm_partial_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument.  The split-KV
+ * partials go to a fixed scratch array inside the library, one per GPU, of
+ * dlm_partial_attn_noalloc_scratch_bytes() bytes (64.5 MiB, the largest
+ * workspace dlm_partial_attn ever asks for), held until the process ends; the
+ * call itself allocates nothing.  Same kernels and work plan as
+ * dlm_partial_attn, so the outputs are bit-identical to it.  Limit: a bf16
+ * W_o projection is accepted only for max_rows <= 1024 (larger bounds need
+ * split-K partials), else DLM_ERR_WORKSPACE before any launch.  Calls that
+ * overlap in time on one GPU share the scratch and race: order them on one
+ * stream.  The first call on a device looks up the scratch's address there
+ * (DLM_ERR_HIP if that fails). */
+int dlm_partial_attn_noalloc(int dtype, const void* q_sel, const int32_t* idx,
+                             const int32_t* offsets, int max_rows, const void* k_cache,
+                             const void* v_cache, int B, int S, int Hq, int Hkv, int hd,
+                             float scale, void* o_sel, float* lse, const void* w_o, int D_out,
+                             void* out_cache, void* stream);
+size_t dlm_partial_attn_noalloc_scratch_bytes(void);
+
 /* ------------------------------------------------------------------------
  * dlm_attn_colsum
  *
@@ -251,6 +271,39 @@ int dlm_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
                       float conf_threshold, int min_commit, int32_t* committed, void* stream);
 
 /* ------------------------------------------------------------------------
+ * dlm_kl_lock
+ *
+ * The locking criterion of "Stopping Computation for Converged Tokens in
+ * Masked Diffusion-LM Decoding", 2. Methodik, Kriterium zum Sperren: a
+ * position is locked (its projections and FFN are skipped from then on, its
+ * K/V stay cached) when the local KL divergence between its posteriors at
+ * this and the previous step, KL(p_t || p_{t-1}), falls below eps, and -
+ * the optional confidence gate - its uncertainty 1 - max p_t lies at or
+ * below the gate_q percentile of the uncertainties of its sequence's
+ * evaluated positions.
+ *
+ * For the positions listed by (eval_idx, eval_offsets) (at most max_eval),
+ * p_t and p_{t-1} are the softmax of the LM-head logits h . W_lm^T of the
+ * position's hidden state in h_cur and in h_prev [B,S,D] bf16 (W_lm [V,D]
+ * bf16), formed on the matrix cores in one pass over W_lm and reduced on the
+ * fly (logits are never stored).  Writes, at the evaluated positions of the
+ * [B,S] arrays: kl (f32; rounding can leave a value a few ulps below 0),
+ * maxprob = max p_t (f32) and argmax of p_t (i32, lowest index on ties);
+ * then sets locked[b,i] = 1.0f (f32 [B,S], 1 = locked, other values kept;
+ * usable as the given scores of DLM_SCORE_GIVEN with threshold 0.5) where
+ * kl < eps (strict) and, if 0 < gate_q <= 1, maxprob >= the k-th largest
+ * maxprob of the sequence's evaluated positions, k = max(1, ceil(gate_q *
+ * n_b)) computed in double (the nearest-rank percentile; equal values all
+ * pass).  gate_q <= 0: no gate.  Other entries are not written.
+ * D % 64 == 0, V % 256 == 0; workspace from dlm_kl_lock_workspace_size.
+ * ------------------------------------------------------------------------ */
+size_t dlm_kl_lock_workspace_size(int B, int S, int V, int max_eval);
+int dlm_kl_lock(const void* h_cur, const void* h_prev, const void* w_lm, int B, int S, int D, int V,
+                const int32_t* eval_idx, const int32_t* eval_offsets, int max_eval,
+                float eps, float gate_q, float* kl, float* maxprob, int32_t* argmax,
+                float* locked, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * dlm_nonsalient_dv_update
  *
  * Value-change update of the stable rows' cached attention outputs.  Follows:
@@ -287,39 +340,6 @@ int dlm_nonsalient_dv_update(int dtype, const void* q_cache, const float* lse_ca
                              const void* k_old, const void* v_old, const void* v_cache,
                              int B, int S, int Hq, int Hkv, int hd, float scale,
                              void* o_cache, void* stream);
-
-/* ------------------------------------------------------------------------
- * dlm_kl_lock
- *
- * The locking criterion of "Stopping Computation for Converged Tokens in
- * Masked Diffusion-LM Decoding", 2. Methodik, Kriterium zum Sperren: a
- * position is locked (its projections and FFN are skipped from then on, its
- * K/V stay cached) when the local KL divergence between its posteriors at
- * this and the previous step, KL(p_t || p_{t-1}), falls below eps, and -
- * the optional confidence gate - its uncertainty 1 - max p_t lies at or
- * below the gate_q percentile of the uncertainties of its sequence's
- * evaluated positions.
- *
- * For the positions listed by (eval_idx, eval_offsets) (at most max_eval),
- * p_t and p_{t-1} are the softmax of the LM-head logits h . W_lm^T of the
- * position's hidden state in h_cur and in h_prev [B,S,D] bf16 (W_lm [V,D]
- * bf16), formed on the matrix cores in one pass over W_lm and reduced on the
- * fly (logits are never stored).  Writes, at the evaluated positions of the
- * [B,S] arrays: kl (f32; rounding can leave a value a few ulps below 0),
- * maxprob = max p_t (f32) and argmax of p_t (i32, lowest index on ties);
- * then sets locked[b,i] = 1.0f (f32 [B,S], 1 = locked, other values kept;
- * usable as the given scores of DLM_SCORE_GIVEN with threshold 0.5) where
- * kl < eps (strict) and, if 0 < gate_q <= 1, maxprob >= the k-th largest
- * maxprob of the sequence's evaluated positions, k = max(1, ceil(gate_q *
- * n_b)) computed in double (the nearest-rank percentile; equal values all
- * pass).  gate_q <= 0: no gate.  Other entries are not written.
- * D % 64 == 0, V % 256 == 0; workspace from dlm_kl_lock_workspace_size.
- * ------------------------------------------------------------------------ */
-size_t dlm_kl_lock_workspace_size(int B, int S, int V, int max_eval);
-int dlm_kl_lock(const void* h_cur, const void* h_prev, const void* w_lm, int B, int S, int D, int V,
-                const int32_t* eval_idx, const int32_t* eval_offsets, int max_eval,
-                float eps, float gate_q, float* kl, float* maxprob, int32_t* argmax,
-                float* locked, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * dlm_salient_ffn

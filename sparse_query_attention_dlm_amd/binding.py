@@ -56,6 +56,11 @@ lib.dlm_partial_attn_workspace_size.argtypes = [_I] * 8
 lib.dlm_partial_attn.restype = _I
 lib.dlm_partial_attn.argtypes = [_I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P,
                                  _P, _I, _P, _P, _Z, _P]
+lib.dlm_partial_attn_noalloc.restype = _I
+lib.dlm_partial_attn_noalloc.argtypes = [_I, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P,
+                                         _P, _I, _P, _P]
+lib.dlm_partial_attn_noalloc_scratch_bytes.restype = _Z
+lib.dlm_partial_attn_noalloc_scratch_bytes.argtypes = []
 lib.dlm_attn_colsum_workspace_size.restype = _Z
 lib.dlm_attn_colsum_workspace_size.argtypes = [_I, _I, _I]
 lib.dlm_attn_colsum.restype = _I
@@ -198,6 +203,27 @@ def dlm_partial_attn(q_sel, idx, offsets, max_rows, k_cache, v_cache, scale, o_s
         _ptr(w_o, "w_o", q_sel.dtype, False), D_out, _ptr(out_cache, "out_cache", q_sel.dtype, False),
         wp, wn, _stream(stream))
     _check(rc)
+
+
+def dlm_partial_attn_noalloc(q_sel, idx, offsets, max_rows, k_cache, v_cache, scale, o_sel, lse=None,
+                             w_o=None, out_cache=None, stream=None):
+    """dlm_partial_attn without a workspace: split-KV partials in the library's
+    fixed per-GPU scratch (calls overlapping on one GPU race)."""
+    B, S, Hkv, hd = k_cache.shape
+    Hq = q_sel.shape[1]
+    D_out = out_cache.shape[-1] if out_cache is not None else 0
+    rc = lib.dlm_partial_attn_noalloc(
+        _dt(q_sel), _ptr(q_sel, "q_sel"), _ptr(idx, "idx", torch.int32),
+        _ptr(offsets, "offsets", torch.int32), int(max_rows), _ptr(k_cache, "k_cache", q_sel.dtype),
+        _ptr(v_cache, "v_cache", q_sel.dtype), B, S, Hq, Hkv, hd, float(scale),
+        _ptr(o_sel, "o_sel", q_sel.dtype), _ptr(lse, "lse", torch.float32, False),
+        _ptr(w_o, "w_o", q_sel.dtype, False), D_out, _ptr(out_cache, "out_cache", q_sel.dtype, False),
+        _stream(stream))
+    _check(rc)
+
+
+def dlm_partial_attn_noalloc_scratch_bytes() -> int:
+    return int(lib.dlm_partial_attn_noalloc_scratch_bytes())
 
 
 def dlm_attn_colsum(q_sel, offsets, max_rows, k_cache, lse, scale, colsum, key_lo=0, key_hi=None,

@@ -27,6 +27,7 @@
 //     and a merge pass combines the partial outputs by their LSE.
 // fp32 kernel (small fp32 layers): one wave per (row, head), float32 FMA,
 // loads issued in batches ahead of use (the layer is latency-bound).
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -611,6 +612,38 @@ static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 size_t attn_workspace_bytes(int dtype, int max_rows, int B, int S, int Hq, int Hkv, int hd) {
   if (dtype != 1 || S < 2 * kMinSplitKeys) return 0;  // such sequences are never split
   return (size_t)kPartRows * (hd + 1) * sizeof(float);
+}
+
+// Split-KV partials of the allocation-free entry point: a file-scope device
+// array of the largest workspace the attention ever asks for (head dim 128),
+// one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in, not a device
+// address); it looks up each device's address once with hipGetSymbolAddress
+// and passes that.  The partials need no clearing: the merge pass reads only
+// slots the attention kernel of the same call wrote.  Calls that overlap in
+// time on one GPU share the array and race.
+constexpr size_t kAttnScratchBytes = (size_t)kPartRows * (128 + 1) * sizeof(float);
+static __device__ __align__(256) float scratch[kAttnScratchBytes / sizeof(float)];
+
+size_t attn_scratch_bytes() { return kAttnScratchBytes; }
+
+hipError_t attn_scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attn(int dtype, const AttnArgs& a0, void* workspace, hipStream_t st) {

@@ -328,11 +328,13 @@ size_t dlm_partial_attn_workspace_size(int dtype, int max_rows, int B, int S, in
   return n;
 }
 
-int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int32_t* offsets,
-                     int max_rows, const void* k_cache, const void* v_cache, int B, int S, int Hq,
-                     int Hkv, int hd, float scale, void* o_sel, float* lse, const void* w_o,
-                     int D_out, void* out_cache, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+// noalloc: the split-KV partials go to the library's fixed device scratch
+// instead of a caller workspace (dlm_partial_attn_noalloc)
+static int partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int32_t* offsets,
+                        int max_rows, const void* k_cache, const void* v_cache, int B, int S, int Hq,
+                        int Hkv, int hd, float scale, void* o_sel, float* lse, const void* w_o,
+                        int D_out, void* out_cache, void* workspace, size_t workspace_bytes,
+                        bool noalloc, void* stream) {
   REQUIRE(dtype == DLM_F32 || dtype == DLM_BF16, "unknown dtype %d", dtype);
   REQUIRE_PTR(k_cache);
   REQUIRE_PTR(v_cache);
@@ -368,14 +370,30 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
     REQUIRE(D_out == Hq * hd, "without W_o, D_out (%d) must equal Hq*hd (%d)", D_out, Hq * hd);
   }
   if (out_cache) REQUIRE_ALIGNED(out_cache);
-  const size_t need = dlm_partial_attn_workspace_size(dtype, max_rows, B, S, Hq, Hkv, hd, w_o ? D_out : 0);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (need > 0) REQUIRE_ALIGNED(workspace);
+  if (noalloc) {
+    // the W_o GEMM's split-K partials (loose bounds above 1024 rows) have no
+    // fixed scratch; the attention's split-KV partials always fit
+    if (dtype == DLM_BF16 && w_o && dlm::gemm_workspace_bytes(dlm::EPI_ROWS, max_rows, D_out, Hq * hd) > 0)
+      return fail(DLM_ERR_WORKSPACE,
+                  "the allocation-free call projects through W_o only for row bounds up to 1024 "
+                  "(max_rows=%d); use dlm_partial_attn with a workspace", max_rows);
+    if (dlm::attn_workspace_bytes(dtype, max_rows, B, S, Hq, Hkv, hd) > dlm::attn_scratch_bytes())
+      return fail(DLM_ERR_WORKSPACE, "split-KV partials exceed the fixed scratch of %zu bytes",
+                  dlm::attn_scratch_bytes());
+  } else {
+    const size_t need = dlm_partial_attn_workspace_size(dtype, max_rows, B, S, Hq, Hkv, hd, w_o ? D_out : 0);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+      return fail(DLM_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (need > 0) REQUIRE_ALIGNED(workspace);
+  }
   if (max_rows == 0) return DLM_OK;
   CHECK_ROWS(idx, offsets, B, S, max_rows, true, stream, "partial attention");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (noalloc && dlm::attn_workspace_bytes(dtype, max_rows, B, S, Hq, Hkv, hd) > 0) {
+    int rc = hip_status(dlm::attn_scratch_ptr(&workspace), "scratch address");
+    if (rc != DLM_OK) return rc;
+  }
   dlm::AttnArgs a{};
   a.q = q_sel;
   a.idx = idx;
@@ -407,7 +425,7 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
   g.max_rows = max_rows;
   g.out = out_cache;
   g.ld_out = D_out;
-  if (dtype == DLM_BF16) {
+  if (dtype == DLM_BF16 && !noalloc) {  // (the allocation-free call needs no GEMM partials)
     char* gws = static_cast<char*>(workspace) +
                 round_up(dlm::attn_workspace_bytes(dtype, max_rows, B, S, Hq, Hkv, hd), 256);
     g.part = reinterpret_cast<float*>(gws);
@@ -415,6 +433,27 @@ int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int
   return hip_status(dlm::launch_gemm(dtype, dlm::EPI_ROWS, dlm::A_COMPACT, g, st),
                     "output projection");
 }
+
+int dlm_partial_attn(int dtype, const void* q_sel, const int32_t* idx, const int32_t* offsets,
+                     int max_rows, const void* k_cache, const void* v_cache, int B, int S, int Hq,
+                     int Hkv, int hd, float scale, void* o_sel, float* lse, const void* w_o,
+                     int D_out, void* out_cache, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return partial_attn(dtype, q_sel, idx, offsets, max_rows, k_cache, v_cache, B, S, Hq, Hkv, hd,
+                      scale, o_sel, lse, w_o, D_out, out_cache, workspace, workspace_bytes, false,
+                      stream);
+}
+
+int dlm_partial_attn_noalloc(int dtype, const void* q_sel, const int32_t* idx,
+                             const int32_t* offsets, int max_rows, const void* k_cache,
+                             const void* v_cache, int B, int S, int Hq, int Hkv, int hd,
+                             float scale, void* o_sel, float* lse, const void* w_o, int D_out,
+                             void* out_cache, void* stream) {
+  return partial_attn(dtype, q_sel, idx, offsets, max_rows, k_cache, v_cache, B, S, Hq, Hkv, hd,
+                      scale, o_sel, lse, w_o, D_out, out_cache, nullptr, 0, true, stream);
+}
+
+size_t dlm_partial_attn_noalloc_scratch_bytes(void) { return dlm::attn_scratch_bytes(); }
 
 // ---------------------------------------------------------------------------
 size_t dlm_attn_colsum_workspace_size(int B, int S, int Hkv) {

@@ -100,6 +100,10 @@ struct AttnArgs {
 };
 size_t attn_workspace_bytes(int dtype, int max_rows, int B, int S, int Hq, int Hkv, int hd);
 hipError_t launch_attn(int dtype, const AttnArgs& a, void* workspace, hipStream_t st);
+// the allocation-free variant's split-KV scratch: its size (every head dim)
+// and this device's address of it (looked up once per device)
+size_t attn_scratch_bytes();
+hipError_t attn_scratch_ptr(void** out);
 hipError_t launch_probe_mfma(int iters, int grid, float* sink, hipStream_t st);
 
 // colsum.hip

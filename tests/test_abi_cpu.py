@@ -174,6 +174,33 @@ def test_colsum_rejections(lib, window):
     assert lib.dlm_attn_colsum_workspace_size(4, 4096, 32) == 4 * 32 * 4 * 4096 * 4
 
 
+def test_colsum_window_empty_enqueues_nothing(lib):
+    """An empty key window with k = 0 returns DLM_OK at once: no launch is made
+    (without a GPU any launch would fail with DLM_ERR_HIP)."""
+    for at in (0, 37, 256):
+        assert colsum(lib, S=512, lo=at, hi=at, kk=0, window=True) == OK, lib.dlm_last_error()
+
+
+def test_partial_attn_noalloc_rejections(lib):
+    """The allocation-free attention validates like dlm_partial_attn and
+    refuses, before any launch, a bf16 W_o projection whose loose row bound
+    (above 1024) would need split-K partials it has no scratch for."""
+    L = lib
+    L.dlm_partial_attn_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    assert L.dlm_partial_attn_noalloc_scratch_bytes() == 2 * 512 * 128 * 129 * 4
+
+    def call(dtype=BF16, q=FAKE, max_rows=4, B=1, S=64, Hq=2, Hkv=1, hd=128, o=FAKE, wo=0, D_out=0, out=0):
+        return L.dlm_partial_attn_noalloc(dtype, p(q), p(FAKE), p(FAKE), max_rows, p(FAKE), p(FAKE), B, S, Hq,
+                                          Hkv, hd, f(0.1), p(o), p(0), p(wo), D_out, p(out), p(0))
+    assert call(hd=96) == INVALID
+    assert call(q=0) == INVALID
+    assert call(q=MISALIGNED) == INVALID
+    assert call(Hq=3, Hkv=2) == INVALID
+    assert call(max_rows=0) == OK                       # nothing to do, nothing launched
+    assert call(max_rows=2048, B=1, S=4096, wo=FAKE, D_out=256, out=FAKE) == WORKSPACE
+    assert b"1024" in L.dlm_last_error()
+
+
 def test_probe_rejections(lib):
     assert lib.dlm_probe_mfma_bf16(0, 1, p(FAKE), p(0)) == INVALID
     assert lib.dlm_probe_mfma_bf16(1, 0, p(FAKE), p(0)) == INVALID
