@@ -417,6 +417,78 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
 
   const int wp = wave / WT, wt = wave % WT;
   const int lr = lane & 31, lg = lane >> 5;
+  constexpr bool kBig = TP == 256 && TT == 256 && PF == 1 && WK == 1 && BK == 64;
+  if constexpr (kBig) {
+    // 256 x 256 tiles run one wave per SIMD, each wave a 128 x 128 block (16
+    // accumulators), so the matrix pipe idles whenever an MFMA has to wait for
+    // its fragments.  The fragment registers are double-buffered across the
+    // k-step's four 16-wide substeps: the 16 MFMAs of substep kh issue
+    // one-for-one with the 8 LDS reads of substep kh + 1; half of the last
+    // substep's MFMAs carry the staging writes of the next k-step (into the
+    // other LDS buffer, free since the last barrier) and the global loads of
+    // the one after; its other half issues after the barrier, alongside the
+    // reads of the next k-step's first fragments.
+    static_assert(FP == 4 && FT == 4 && CPT == 16 && BK / 16 == 4, "the 256 x 256 schedule");
+    bf16x8 fa[2][FP], fb[2][FT];
+    auto rd = [&](int buf, int kk, int set) {
+      const u16* sW = lds + buf * ROWS * PITCH;
+      const u16* sX = sW + TP * PITCH;
+#pragma unroll
+      for (int a = 0; a < FP; ++a)
+        fa[set][a] = as_bf16x8(*reinterpret_cast<const u32x4*>(sW + (wp * WTP + a * 32 + lr) * PITCH +
+                                                                kk * 16 + lg * 8));
+#pragma unroll
+      for (int b = 0; b < FT; ++b)
+        fb[set][b] = as_bf16x8(*reinterpret_cast<const u32x4*>(sX + (wt * WTT + b * 32 + lr) * PITCH +
+                                                                kk * 16 + lg * 8));
+    };
+    auto mma = [&](int set, int a0, int a1) {
+#pragma unroll
+      for (int a = a0; a < a1; ++a)
+#pragma unroll
+        for (int b = 0; b < FT; ++b) acc[a][b] = mfma32x32x16(fa[set][a], fb[set][b], acc[a][b]);
+    };
+    rd(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+#pragma unroll
+      for (int kh = 0; kh < 3; ++kh) {
+        rd(buf, kh + 1, (kh + 1) & 1);
+        mma(kh & 1, 0, FP);
+      }
+      {
+        u16* dst = ldsw + (buf ^ 1) * ROWS * PITCH;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(dst + RPJ * j * PITCH) = stg[0][j];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) stg[0][j] = gload(j, min(kt + 2, nk - 1));
+        mma(1, 0, FP / 2);
+      }
+#pragma unroll
+      for (int kh = 0; kh < 3; ++kh) {
+#pragma unroll
+        for (int i = 0; i < FP + FT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FP * FT - (FP + FT), 0);
+      }
+#pragma unroll
+      for (int i = 0; i < FP * FT / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // DS write
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read
+      }
+      __syncthreads();
+      rd(buf ^ 1, 0, 0);
+      mma(1, FP / 2, FP);
+#pragma unroll
+      for (int i = 0; i < FP + FT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      }
+    }
+  } else
   for (int kt0 = 0; kt0 < nk; kt0 += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
