@@ -212,11 +212,17 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
   }
 }
 
-// Split-K plan, computed on the device from the real row count.  When there
-// are fewer than SB output tiles, K is split over spare workgroups of the
-// grid: ks is a power of two (<= 8) that divides the k-steps into whole
-// prefetch rings (at least two rings per split), doubled while units * ks
-// stays below ST and within kSplitCap (the workspace) and the grid.
+// Split-K plan, computed on the device from the real row count (and, for
+// the reduce pass, recomputed from the same inputs).
+//   Fewer than SB output tiles: K is split over spare workgroups of the grid:
+//     ks is a power of two (<= 8) that divides the k-steps into whole
+//     prefetch rings (at least two rings per split), doubled while units * ks
+//     stays below ST and within kSplitCap (the workspace).
+//   SB tiles or more: whole rounds of the G-workgroup resident grid run
+//     unsplit; only the rem = units % G tiles of the last, partial round are
+//     split, ks ways with rem * ks <= G, so that the last round fills the
+//     grid instead of leaving G - rem workgroups idle for a whole tile.
+// Tiles [0, whole) run unsplit, tiles [whole, units) are split ks ways.
 constexpr int kSplitCap = 1024;
 
 // The weight-streaming case (<= kSkinnyRows rows): 64-feature tiles, no
@@ -231,17 +237,32 @@ constexpr int kSkinnyRows = 128;
 constexpr int kReduceTarget = 256;
 
 struct GemmSplit {
-  int units;
-  int ks;
+  int units;  // output tiles
+  int ks;     // K splits of each split tile
+  int whole;  // tiles [0, whole) unsplit
+  __host__ __device__ int items() const { return whole + (units - whole) * ks; }
+  __host__ __device__ int splits_of(int unit) const { return unit >= whole ? ks : 1; }
 };
-__host__ __device__ inline GemmSplit gemm_split(int units, int nk, int pf, int SB, int ST) {
-  GemmSplit s{units, 1};
-  if (units <= 0 || units >= SB) return s;
-  while (true) {
-    const int k2 = s.ks * 2;
-    if (units * k2 > kSplitCap || units * s.ks >= ST) break;
-    if (k2 > 8 || nk % k2 != 0 || (nk / k2) % pf != 0 || nk / k2 < 2 * pf) break;
-    s.ks = k2;
+__host__ __device__ inline GemmSplit gemm_split(int units, int nk, int pf, int SB, int ST, int G) {
+  GemmSplit s{units, 1, units};
+  if (units <= 0 || SB <= 0) return s;
+  auto can_split = [&](int k2) { return k2 <= 8 && nk % k2 == 0 && (nk / k2) % pf == 0 && nk / k2 >= 2 * pf; };
+  if (units < SB) {
+    s.whole = 0;
+    while (true) {
+      const int k2 = s.ks * 2;
+      if (units * k2 > kSplitCap || units * s.ks >= ST || !can_split(k2)) break;
+      s.ks = k2;
+    }
+    return s;
+  }
+  const int rem = G > 0 ? units % G : 0;
+  if (rem == 0) return s;
+  int ks = 1;
+  while (rem * ks * 2 <= G && can_split(ks * 2)) ks *= 2;
+  if (ks > 1) {
+    s.ks = ks;
+    s.whole = units - rem;
   }
   return s;
 }
@@ -310,16 +331,22 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
   const int m_tiles = (gemm_token_rows(EPI, n_rows) + TT - 1) / TT;
   const int n_tiles = g.N / TPV;
   const int nk_all = g.K / BK;
-  const GemmSplit sp = gemm_split(m_tiles * n_tiles, nk_all, PF, SB, ST);
-  const int total = sp.units * sp.ks;
+  const GemmSplit sp = gemm_split(m_tiles * n_tiles, nk_all, PF, SB, ST, g.tile_grid);
+  const int total = sp.items();
   // Work items (tile, k-split) go to workgroups round-robin: item w runs on
   // workgroup w % gridDim.x, so a grid of one workgroup per CU keeps every
   // workgroup on the same k-step of its current tile and the tiles running
-  // together on an XCD share their weight and row slices in its L2.
+  // together on an XCD share their weight and row slices in its L2.  The
+  // split tiles' items come last (the last round).
   for (int work = (int)blockIdx.x; work < total; work += (WK == 1 ? (int)gridDim.x : total)) {
+    int unit = work, ksi = 0;
+    if (work >= sp.whole) {
+      const int j = work - sp.whole, ns = sp.units - sp.whole;
+      unit = sp.whole + j % ns;
+      ksi = j / ns;
+    }
     gemm_tile_work<TP, TT, WP, WT, BK, PF, EPI, AMODE, SB, ST, WK, TPV>(g, n_rows, lds, s_xoff, s_drow,
-                                                                        sp, work % sp.units,
-                                                                        work / sp.units);
+                                                                        sp, unit, ksi);
     if constexpr (WK == 1) __syncthreads();  // the next item rewrites the row table and tiles
   }
 }
@@ -341,7 +368,8 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
   const int nt = unit / m_tiles, mt = unit % m_tiles;
   const int m0 = mt * TT, n0 = nt * TPV;
   const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, wk = tid >> 8;
-  const int nk = nk_all / sp.ks;        // k-steps of this split
+  const int ks = sp.splits_of(unit);
+  const int nk = nk_all / ks;           // k-steps of this split
   const int kbase = ksi * nk;           // first k-step of this split
 
   gemm_rows<TT, AMODE, EPI == EPI_LMKL>(g, n_rows, m0, s_xoff, s_drow);
@@ -545,13 +573,13 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
         for (int i = 0; i < 16; ++i) acc[a][b][i] += red[(((a * FT + b) * 16 + i) * 4 + wave) * 64 + lane];
   }
 
-  if (sp.ks > 1) {
+  if (ks > 1) {
     // split-K: store the partial tile in register order (16-byte vectors,
     // consecutive threads adjacent; padding tokens are skipped, the reduction
     // skips them too); gemm_splitk_reduce_kernel sums the splits in a fixed
     // order after this kernel has finished
     constexpr int NQ = FP * FT * 4;
-    float4* mine = reinterpret_cast<float4*>(g.part) + ((size_t)unit * sp.ks + ksi) * (NQ * 256);
+    float4* mine = reinterpret_cast<float4*>(g.part) + ((size_t)(unit - sp.whole) * ks + ksi) * (NQ * 256);
 #pragma unroll
     for (int b = 0; b < FT; ++b) {
       if (s_drow[wt * WTT + b * 32 + lr] < 0) continue;
@@ -616,18 +644,19 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g) {
   if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
   const int m_tiles = (gemm_token_rows(EPI, n_rows) + TT - 1) / TT;
   const int n_tiles = g.N / TP;
-  const GemmSplit sp = gemm_split(m_tiles * n_tiles, g.K / BK, PF, SB, ST);
-  if (sp.ks <= 1) return;
-  const int RS = epi_lm(EPI) ? 1 : min(NQ, (kReduceTarget + sp.units - 1) / sp.units);
-  if ((int)blockIdx.x >= sp.units * RS) return;
-  const int unit = (int)blockIdx.x / RS, slice = (int)blockIdx.x % RS;
+  const GemmSplit sp = gemm_split(m_tiles * n_tiles, g.K / BK, PF, SB, ST, g.tile_grid);
+  const int n_split = sp.units - sp.whole;  // tiles whose K was split
+  if (sp.ks <= 1 || n_split <= 0) return;
+  const int RS = epi_lm(EPI) ? 1 : min(NQ, (kReduceTarget + n_split - 1) / n_split);
+  if ((int)blockIdx.x >= n_split * RS) return;
+  const int unit = sp.whole + (int)blockIdx.x / RS, slice = (int)blockIdx.x % RS;
   const int nt = unit / m_tiles, mt = unit % m_tiles;
   const int m0 = mt * TT, n0 = nt * TP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
   const int wp = wave / WT, wt = wave % WT;
   gemm_rows<TT, AMODE, EPI == EPI_LMKL>(g, n_rows, m0, s_xoff, s_drow);
   __syncthreads();
-  const float4* all = reinterpret_cast<const float4*>(g.part) + (size_t)unit * sp.ks * (NQ * 256);
+  const float4* all = reinterpret_cast<const float4*>(g.part) + (size_t)(unit - sp.whole) * sp.ks * (NQ * 256);
   auto sum_splits = [&](int gi) {
     const int o = gi * 256 + tid;
     float4 v[8];
@@ -791,9 +820,11 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
     if (items < cap) items = cap;
   }
   const int grid = WK == 1 ? persistent_grid(items, TP, TT) : items;
+  GemmArgs ga = g;
+  ga.tile_grid = grid;  // the split plan fills the last round of this grid
   hipLaunchKernelGGL((gemm_bf16_kernel<TP, TT, 2, 2, BK, PF, EPI, AMODE, GATE, SB, ST, WK>), dim3(grid),
-                     dim3(256 * WK), 0, st, g);
-  if (SB > 0) launch_reduce<TP, TT, 2, 2, BK, PF, EPI, AMODE, GATE, SB, ST>(g, st);
+                     dim3(256 * WK), 0, st, ga);
+  if (SB > 0) launch_reduce<TP, TT, 2, 2, BK, PF, EPI, AMODE, GATE, SB, ST>(ga, st);
 }
 
 // the weight-streaming tiling alone (GATE 0 or 1).  Measured at n = 102:
@@ -819,13 +850,15 @@ static void launch_dual(const GemmArgs& g, hipStream_t st) {
   const bool t48 = g.N % 48 == 0;
   const int grid1 = persistent_grid(g.N / (t48 ? 48 : 64), 64, 128), grid2 = persistent_grid(items2, TP2, TT2);
   const int grid = grid1 > grid2 ? grid1 : grid2;
+  GemmArgs ga = g;
+  ga.tile_grid = grid;  // the split plan fills the last round of this grid
   if (t48)
     hipLaunchKernelGGL((gemm_dual_kernel<64, 128, BK1, PF1, 0, 0, TP2, TT2, 64, PF2, SB2, ST2, EPI, AMODE, 48>),
-                       dim3(grid), dim3(256), 0, st, g);
+                       dim3(grid), dim3(256), 0, st, ga);
   else
     hipLaunchKernelGGL((gemm_dual_kernel<64, 128, BK1, PF1, 0, 0, TP2, TT2, 64, PF2, SB2, ST2, EPI, AMODE, 64>),
-                       dim3(grid), dim3(256), 0, st, g);
-  if (SB2 > 0) launch_reduce<TP2, TT2, 2, 2, 64, PF2, EPI, AMODE, 2, SB2, ST2>(g, st);
+                       dim3(grid), dim3(256), 0, st, ga);
+  if (SB2 > 0) launch_reduce<TP2, TT2, 2, 2, 64, PF2, EPI, AMODE, 2, SB2, ST2>(ga, st);
 }
 
 template <int EPI, int AMODE>

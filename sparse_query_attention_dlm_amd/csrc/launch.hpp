@@ -77,6 +77,9 @@ struct GemmArgs {
   int ntile;
   // split-K scratch (workspace): partial tiles
   float* part;
+  // set by the launcher: workgroups of the persistent grid (the split plan
+  // fills its last round)
+  int tile_grid;
 };
 size_t gemm_workspace_bytes(int epi, int max_rows, int N, int K);
 hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStream_t st);
