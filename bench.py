@@ -768,8 +768,39 @@ def extra_salient_ffn(dlm, W, a=None):
     return out
 
 
+def extra_kl_lock(dlm, W, a=None):
+    """SureLock's lock criterion at the confidence workload's size (B = 16,
+    S = 1024, D = 4096, V = 32768, 230 evaluated positions per sequence): the
+    two-step LM head (both steps' logits of every evaluated position in one
+    pass over W_lm, 2 x 2 n D V flop), the KL merge and the per-sequence lock
+    decision with the 50th-percentile gate."""
+    import torch
+    sh = W.LSP_COMMIT
+    B, S, D, V = sh.B, sh.S, sh.D, sh.V
+    S_gen = S - sh.prompt
+    na = int(math.floor(sh.active_frac * S_gen))
+    hc, hp = _gen((B, S, D), 511), _gen((B, S, D), 512)
+    w = _gen((V, D), 513, scale=sh.w_std)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(514)
+    rows = [torch.sort(torch.randperm(S_gen, generator=g, device="cuda")[:na])[0] + sh.prompt for _ in range(B)]
+    eidx, eoff = _packed_rows(rows)
+    n = int(eidx.numel())
+    kl = torch.zeros(B, S, dtype=torch.float32, device="cuda")
+    mp = torch.zeros_like(kl)
+    am = torch.zeros(B, S, dtype=torch.int32, device="cuda")
+    lk = torch.zeros_like(kl)
+    ws = torch.zeros(dlm.dlm_kl_lock_workspace_size(B, S, V, n), dtype=torch.uint8, device="cuda")
+    call = lambda: dlm.dlm_kl_lock(hc, hp, w, eidx, eoff, n, 0.05, kl, mp, am, lk, gate_q=0.5, workspace=ws)
+    t = _time(call, 10)
+    f = 2.0 * 2.0 * n * D * V
+    return {"workload": sh.name + " two-step KL lock", "n_evaluated": n, "ms": t, "TFLOP/s": f / t / 1e9,
+            "frac": f / (t / 1e3) / PEAK_BF16, "tokens_per_s": n / (t / 1e3)}
+
+
 EXTRAS = (("one_layer_step_bf16_s1024", extra_one_layer_step), ("tiny_fp32", extra_tiny),
-          ("colsum_top64", extra_colsum), ("lsp_commit", extra_lsp), ("select_b8_asymptote", extra_select_b8),
+          ("colsum_top64", extra_colsum), ("lsp_commit", extra_lsp), ("kl_lock", extra_kl_lock),
+          ("select_b8_asymptote", extra_select_b8),
           ("nonsalient_dv_update", extra_dv_update), ("salient_ffn", extra_salient_ffn))
 
 

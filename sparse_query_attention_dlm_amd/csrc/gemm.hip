@@ -220,8 +220,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
 //     stays below ST and within kSplitCap (the workspace).
 //   SB tiles or more: whole rounds of the G-workgroup resident grid run
 //     unsplit; only the rem = units % G tiles of the last, partial round are
-//     split, ks ways with rem * ks <= G, so that the last round fills the
-//     grid instead of leaving G - rem workgroups idle for a whole tile.
+//     split, ks >= 4 ways with rem * ks <= G, so that the last round nearly
+//     fills the grid instead of leaving G - rem workgroups idle for a whole
+//     tile.
 // Tiles [0, whole) run unsplit, tiles [whole, units) are split ks ways.
 constexpr int kSplitCap = 1024;
 
@@ -260,7 +261,10 @@ __host__ __device__ inline GemmSplit gemm_split(int units, int nk, int pf, int S
   if (rem == 0) return s;
   int ks = 1;
   while (rem * ks * 2 <= G && can_split(ks * 2)) ks *= 2;
-  if (ks > 1) {
+  // the reduce pass over the split tiles' partials costs about what a 2-way
+  // split saves (measured: the LM head with 128 of 1920 tiles left over ran
+  // 1.04 ms either way), so only splits of 4 or more are taken
+  if (ks >= 4) {
     s.ks = ks;
     s.whole = units - rem;
   }
