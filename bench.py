@@ -798,9 +798,40 @@ def extra_kl_lock(dlm, W, a=None):
             "frac": f / (t / 1e3) / PEAK_BF16, "tokens_per_s": n / (t / 1e3)}
 
 
+def extra_scatter_rows(dlm, W, a=None):
+    """The output-row scatter at the GQA loop's middle step (t = 32: 8480 of
+    16384 rows of B = 8, S = 2048, rows of 32 x 128 bf16 = 8 KB): the packed
+    rows are read and written into the [B, S, 4096] cache with dlm_scatter_rows.
+    Two rotating sets (row blocks, caches and positions; 2 x 412 MB, more than
+    the Infinity Cache).  Algorithmic bytes: 2 x n x 8 KB."""
+    import torch
+    sh = W.GQA_LOCK_LOOP
+    B, S, Hq, hd = sh.B, sh.S, sh.Hq, sh.hd
+    m = W.unlocked_count(S, 32, sh.steps, sh.lock_max)
+    sets = []
+    for r in range(2):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(900 + r)
+        rows = [torch.sort(torch.randperm(S, generator=g, device="cuda")[:m])[0] for _ in range(B)]
+        idx, off = _packed_rows(rows)
+        n = int(idx.numel())
+        sets.append((idx, off, n, _gen((n, Hq * hd), 910 + r), _gen((B, S, Hq * hd), 920 + r)))
+    calls = [lambda st=st: dlm.dlm_scatter_rows(st[3], st[0], st[1], st[2], st[4]) for st in sets]
+    state = {"i": 0}
+
+    def call():
+        calls[state["i"] % 2]()
+        state["i"] += 1
+    t = _time(call, 20)
+    n = sets[0][2]
+    nbytes = 2 * n * Hq * hd * 2
+    return {"workload": sh.name + " output rows of step t = 32", "rows": n, "row_bytes": Hq * hd * 2, "ms": t,
+            "GB/s": nbytes / (t / 1e3) / 1e9, "frac": nbytes / (t / 1e3) / PEAK_HBM, "algorithmic_bytes": nbytes}
+
+
 EXTRAS = (("one_layer_step_bf16_s1024", extra_one_layer_step), ("tiny_fp32", extra_tiny),
           ("colsum_top64", extra_colsum), ("lsp_commit", extra_lsp), ("kl_lock", extra_kl_lock),
-          ("select_b8_asymptote", extra_select_b8),
+          ("select_b8_asymptote", extra_select_b8), ("scatter_rows", extra_scatter_rows),
           ("nonsalient_dv_update", extra_dv_update), ("salient_ffn", extra_salient_ffn))
 
 

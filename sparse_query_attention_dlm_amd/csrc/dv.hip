@@ -295,9 +295,19 @@ __global__ __launch_bounds__(256) void row_copy_kernel(const char* src, char* ds
   for (int r = blockIdx.x; r < n; r += gridDim.x) {
     const int b = batch_of(offsets, B, r);
     const size_t cache_row = (size_t)b * S + idx[r];
-    const T* s = reinterpret_cast<const T*>(src + (scatter ? (size_t)r : cache_row) * row_bytes);
-    T* d = reinterpret_cast<T*>(dst + (scatter ? cache_row : (size_t)r) * row_bytes);
-    for (int u = threadIdx.x; u < units; u += 256) d[u] = s[u];
+    const T* __restrict__ s = reinterpret_cast<const T*>(src + (scatter ? (size_t)r : cache_row) * row_bytes);
+    T* __restrict__ d = reinterpret_cast<T*>(dst + (scatter ? cache_row : (size_t)r) * row_bytes);
+    // up to four units per thread loaded before any is stored, so their
+    // loads are in flight together
+    for (int u0 = threadIdx.x; u0 < units; u0 += 4 * 256) {
+      T v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (u0 + 256 * k < units) v[k] = s[u0 + 256 * k];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (u0 + 256 * k < units) d[u0 + 256 * k] = v[k];
+    }
   }
 }
 

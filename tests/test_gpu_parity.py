@@ -1039,6 +1039,14 @@ def test_salient_ffn_short_k_and_loose_bound(dlm):
     run_salient_ffn(dlm, B=1, S=1024, D=320, F=640, n_per_b=[300], seed=43, loose_bound=1024)
 
 
+def test_salient_ffn_many_rows_unsplit_tiles(dlm):
+    """2048 rows (two batch rows of 1024) with 256 gate/up output tiles: the
+    resident 256 x 256 tiling with the SwiGLU epilogue inside the GEMM kernel
+    (no split-K), as the benchmark's 2048-row case runs it; the down
+    projection has 8 tiles and splits K."""
+    run_salient_ffn(dlm, B=2, S=1024, D=256, F=4096, n_per_b=[1024, 1024], seed=45)
+
+
 def test_salient_ffn_one_layer_full_size(dlm):
     """One layer of 1024 positions, D = 4096, F = 12288, 102 salient rows."""
     run_salient_ffn(dlm, B=1, S=1024, D=4096, F=12288, n_per_b=[102], seed=44)
