@@ -376,7 +376,8 @@ def logit_margin(rows, w_lm):
     return srt[:, -1] - srt[:, -2], a.astype(np.int64)
 
 
-def lsp_adaptive_commit(margin, gen_lo, gen_hi, committed, frac_lo=0.25, frac_hi=0.5):
+def lsp_adaptive_commit(margin, gen_lo, gen_hi, committed, frac_lo=0.25, frac_hi=0.5,
+                        margin_floor=-math.inf):
     """[LSP] Methodologie, adaptive sizing: the threshold tau is searched so
     that the stable block at the start of the active suffix covers a fraction
     of the active length within [frac_lo, frac_hi]; at least one token is
@@ -387,8 +388,14 @@ def lsp_adaptive_commit(margin, gen_lo, gen_hi, committed, frac_lo=0.25, frac_hi
     the first lo active positions are all stable (their minimum margin), and
     the block is the run of leading positions with margin >= tau, cut at hi.
     margin [B,S] (float32 values compared exactly); committed [B] = committed
-    generated positions so far.  Returns (new committed [B], tau [B]; tau is
-    nan where nothing is active)."""
+    generated positions so far.
+
+    Optional absolute floor (the page's fallback, "if no token is stable
+    enough, commit at least one", needs a notion of enough): the threshold
+    used is max(tau, margin_floor); when even the first active position's
+    margin is below it, exactly one position is committed.  With the default
+    floor (-inf) the rule above is unchanged.  Returns (new committed [B],
+    threshold used [B]; nan where nothing is active)."""
     m = np.asarray(margin)
     B = m.shape[0]
     out = np.array(committed, dtype=np.int64, copy=True)
@@ -401,11 +408,11 @@ def lsp_adaptive_commit(margin, gen_lo, gen_hi, committed, frac_lo=0.25, frac_hi
         act = m[b, gen_lo + out[b]:gen_hi]
         lo = max(1, math.ceil(frac_lo * A))
         hi = max(lo, math.floor(frac_hi * A))
-        t = act[:lo].min()
+        t = max(act[:lo].min(), margin_floor)
         L = 0
         while L < A and act[L] >= t:
             L += 1
-        out[b] += min(L, hi)
+        out[b] += max(1, min(L, hi))
         tau[b] = t
     return out, tau
 

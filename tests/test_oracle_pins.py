@@ -586,6 +586,52 @@ def test_lsp_adaptive_commit_closed_forms():
     assert seen[:4] == [32, 48, 56, 60]
 
 
+def test_lsp_margin_floor():
+    """The optional floor: below every margin it changes nothing; above the
+    first active margin only the fallback commits (exactly one position); in
+    between it cuts the block at the first margin under it (fewer than lo
+    positions can then be committed), against a brute force over every
+    candidate threshold that counts only margins at or above the floor as
+    stable."""
+    def bf_floor(margins, committed, G, fl, fh, floor):
+        A = G - committed
+        if A <= 0:
+            return committed, None
+        act = margins[committed:]
+        lo, hi = max(1, math.ceil(fl * A)), max(max(1, math.ceil(fl * A)), math.floor(fh * A))
+        for t in sorted(set(act), reverse=True):
+            run = 0
+            while run < A and act[run] >= t:
+                run += 1
+            if run >= lo:
+                break
+        if t >= floor:
+            return committed + min(run, hi), t
+        run = 0
+        while run < A and act[run] >= floor:
+            run += 1
+        return committed + max(1, min(run, hi)), floor
+
+    rng = np.random.default_rng(19)
+    B, S, g0 = 6, 40, 8
+    G = S - g0
+    for trial in range(30):
+        m = np.round(np.abs(rng.standard_normal((B, S))) * 3, 1).astype(np.float32)
+        com = rng.integers(0, G + 1, B)
+        fl, fh = [(0.25, 0.5), (0.1, 0.3), (0.5, 0.5)][trial % 3]
+        floor = float([0.0, 1.5, 2.5, 9.0][trial % 4])
+        out, tau = O.lsp_adaptive_commit(m, g0, S, com, fl, fh, margin_floor=floor)
+        for b in range(B):
+            want, t = bf_floor([float(x) for x in m[b, g0:]], int(com[b]), G, fl, fh, floor)
+            assert out[b] == want and ((t is None and np.isnan(tau[b])) or tau[b] == t)
+    m = np.array([[9.0, 8, 7, 6, 5, 4, 3, 2]], np.float32)
+    assert O.lsp_adaptive_commit(m, 0, 8, [0], margin_floor=1.0)[0][0] == 2        # below every margin
+    assert O.lsp_adaptive_commit(m, 0, 8, [0], margin_floor=100.0)[0][0] == 1      # only the fallback
+    m2 = np.array([[9.0, 1, 9, 9, 9, 9, 9, 9]], np.float32)
+    assert O.lsp_adaptive_commit(m2, 0, 8, [0], margin_floor=5.0)[0][0] == 1       # cut by the floor
+    assert O.lsp_adaptive_commit(m2, 0, 8, [0])[0][0] == 4                          # no floor: tau = 1
+
+
 def test_colsum_sum_invariant_and_library_softmax():
     B, S, nq, Hq, Hkv, hd = 2, 11, 6, 4, 2, 3
     q, kc, vc, idx, offsets = _attn_inputs(B, S, nq, Hq, Hkv, hd, 13)
