@@ -402,15 +402,20 @@ int dlm_scatter_rows(const void* rows, const int32_t* idx, const int32_t* offset
  * gen_lo + committed[b]:
  *   lo = max(1, ceil(frac_lo * A)), hi = max(lo, floor(frac_hi * A))
  *        (computed in double from the float32 fractions)
- *   tau = min of the first lo active margins (the largest threshold under
- *         which they are all stable)
- *   committed[b] += min(run of leading active margins >= tau, hi)
- * tau [B] f32 (may be NULL) receives tau, or NaN where nothing is active.
- * 0 < frac_lo <= frac_hi <= 1, else DLM_ERR_INVALID_ARG.
+ *   tau = max(min of the first lo active margins (the largest threshold
+ *         under which they are all stable), margin_floor)
+ *   committed[b] += max(1, min(run of leading active margins >= tau, hi))
+ * margin_floor is an absolute notion of "stable enough" for the page's
+ * fallback (commit at least one when no token is stable enough): with it
+ * above the first active margin exactly one position is committed.
+ * -INFINITY: no floor (then the run always reaches lo).  tau [B] f32 (may be
+ * NULL) receives the threshold used, or NaN where nothing is active.
+ * 0 < frac_lo <= frac_hi <= 1 and margin_floor not NaN, else
+ * DLM_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------ */
 int dlm_lsp_adaptive_commit(const float* margin, int B, int S, int gen_lo, int gen_hi,
-                            float frac_lo, float frac_hi, int32_t* committed, float* tau,
-                            void* stream);
+                            float frac_lo, float frac_hi, float margin_floor, int32_t* committed,
+                            float* tau, void* stream);
 
 /* ------------------------------------------------------------------------
  * dlm_probe_mfma_bf16  (measurement aid, not a step of the method)

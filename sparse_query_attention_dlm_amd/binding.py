@@ -80,7 +80,7 @@ lib.dlm_salient_ffn_workspace_size.argtypes = [_I] * 4
 lib.dlm_salient_ffn.restype = _I
 lib.dlm_salient_ffn.argtypes = [_I, _P, _I, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _Z, _P]
 lib.dlm_lsp_adaptive_commit.restype = _I
-lib.dlm_lsp_adaptive_commit.argtypes = [_P, _I, _I, _I, _I, _F, _F, _P, _P, _P]
+lib.dlm_lsp_adaptive_commit.argtypes = [_P, _I, _I, _I, _I, _F, _F, _F, _P, _P, _P]
 lib.dlm_kl_lock_workspace_size.restype = _Z
 lib.dlm_kl_lock_workspace_size.argtypes = [_I] * 4
 lib.dlm_kl_lock.restype = _I
@@ -284,11 +284,12 @@ def dlm_salient_ffn(x, idx, offsets, max_rows, w_gu, w_down, out_cache, workspac
 
 
 def dlm_lsp_adaptive_commit(margin, gen_lo, gen_hi, committed, frac_lo=0.25, frac_hi=0.5, tau=None,
-                            stream=None):
+                            margin_floor=float("-inf"), stream=None):
     B, S = margin.shape
     rc = lib.dlm_lsp_adaptive_commit(
         _ptr(margin, "margin", torch.float32), B, S, int(gen_lo), int(gen_hi), float(frac_lo), float(frac_hi),
-        _ptr(committed, "committed", torch.int32), _ptr(tau, "tau", torch.float32, False), _stream(stream))
+        float(margin_floor), _ptr(committed, "committed", torch.int32), _ptr(tau, "tau", torch.float32, False),
+        _stream(stream))
     _check(rc)
 
 

@@ -700,8 +700,8 @@ int dlm_nonsalient_dv_update(int dtype, const void* q_cache, const float* lse_ca
 
 // ---------------------------------------------------------------------------
 int dlm_lsp_adaptive_commit(const float* margin, int B, int S, int gen_lo, int gen_hi,
-                            float frac_lo, float frac_hi, int32_t* committed, float* tau,
-                            void* stream) {
+                            float frac_lo, float frac_hi, float margin_floor, int32_t* committed,
+                            float* tau, void* stream) {
   REQUIRE_PTR(margin);
   REQUIRE_PTR(committed);
   REQUIRE(B > 0 && S > 0, "B and S must be positive");
@@ -709,8 +709,10 @@ int dlm_lsp_adaptive_commit(const float* margin, int B, int S, int gen_lo, int g
           gen_lo, gen_hi);
   REQUIRE(frac_lo > 0.f && frac_lo <= frac_hi && frac_hi <= 1.f,
           "fractions must satisfy 0 < frac_lo <= frac_hi <= 1 (got %g, %g)", frac_lo, frac_hi);
+  REQUIRE(margin_floor == margin_floor, "margin_floor must not be NaN (-INFINITY: no floor)");
   return hip_status(dlm::launch_lsp_adaptive(margin, B, S, gen_lo, gen_hi, frac_lo, frac_hi,
-                                             committed, tau, static_cast<hipStream_t>(stream)),
+                                             margin_floor, committed, tau,
+                                             static_cast<hipStream_t>(stream)),
                     "adaptive commit");
 }
 

@@ -149,8 +149,8 @@ hipError_t validate_rows(const int32_t* idx, const int32_t* offsets, int B, int 
 
 // prefix.hip
 hipError_t launch_lsp_adaptive(const float* margin, int B, int S, int gen_lo, int gen_hi,
-                               float frac_lo, float frac_hi, int32_t* committed, float* tau,
-                               hipStream_t st);
+                               float frac_lo, float frac_hi, float margin_floor, int32_t* committed,
+                               float* tau, hipStream_t st);
 hipError_t launch_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
                                 int gen_lo, int gen_hi, int32_t* ring, int W, int step, float thr,
                                 int min_commit, int32_t* committed, hipStream_t st);

@@ -54,11 +54,14 @@ __global__ __launch_bounds__(256) void stable_prefix_kernel(const int32_t* __res
 // active positions, lo = max(1, ceil(frac_lo A)) and hi = max(lo, floor(frac_hi
 // A)): tau is the largest threshold under which the first lo active positions
 // are stable (their minimum margin), and the block is the run of leading
-// positions with margin >= tau, cut at hi.  One workgroup per sequence: a
-// block min for tau, then an LDS atomicMin for the first position below it.
+// positions with margin >= tau, cut at hi.  An optional absolute floor (the
+// fallback's "stable enough"): the threshold used is max(tau, floor), and when
+// the first active margin is already below it one position is committed.  One
+// workgroup per sequence: a block min for tau, then an LDS atomicMin for the
+// first position below the threshold.
 __global__ __launch_bounds__(256) void lsp_adaptive_kernel(const float* __restrict__ margin, int S,
                                                            int gen_lo, int gen_hi, float frac_lo,
-                                                           float frac_hi,
+                                                           float frac_hi, float floor_m,
                                                            int32_t* __restrict__ committed,
                                                            float* __restrict__ tau) {
   __shared__ float s_min[4];
@@ -81,21 +84,21 @@ __global__ __launch_bounds__(256) void lsp_adaptive_kernel(const float* __restri
   if (lane == 0) s_min[wave] = m;
   if (tid == 0) s_first = A;
   __syncthreads();
-  const float t = fminf(fminf(s_min[0], s_min[1]), fminf(s_min[2], s_min[3]));
+  const float t = fmaxf(fminf(fminf(s_min[0], s_min[1]), fminf(s_min[2], s_min[3])), floor_m);
   for (int i = tid; i < A; i += 256)
     if (act[i] < t) atomicMin(&s_first, i);
   __syncthreads();
   if (tid == 0) {
-    committed[b] = c + min(s_first, hi);
+    committed[b] = c + max(1, min(s_first, hi));
     if (tau) tau[b] = t;
   }
 }
 
 hipError_t launch_lsp_adaptive(const float* margin, int B, int S, int gen_lo, int gen_hi,
-                               float frac_lo, float frac_hi, int32_t* committed, float* tau,
-                               hipStream_t st) {
+                               float frac_lo, float frac_hi, float margin_floor, int32_t* committed,
+                               float* tau, hipStream_t st) {
   hipLaunchKernelGGL(lsp_adaptive_kernel, dim3(B), dim3(256), 0, st, margin, S, gen_lo, gen_hi,
-                     frac_lo, frac_hi, committed, tau);
+                     frac_lo, frac_hi, margin_floor, committed, tau);
   return hipGetLastError();
 }
 

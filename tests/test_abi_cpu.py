@@ -282,8 +282,9 @@ def test_margin_mode_and_adaptive_commit_rejections(lib):
     # the margin mode needs the same LM-head partials as the confidence mode
     assert lib.dlm_select_workspace_size(MARGIN, 2, 64, 32768, 16) == lib.dlm_select_workspace_size(CONFIDENCE, 2, 64, 32768, 16)
 
-    def lsp(m=FAKE, B=2, S=32, lo=8, hi=32, fl=0.25, fh=0.5, com=FAKE, tau=0):
-        return lib.dlm_lsp_adaptive_commit(p(m), B, S, lo, hi, f(fl), f(fh), p(com), p(tau), p(0))
+    def lsp(m=FAKE, B=2, S=32, lo=8, hi=32, fl=0.25, fh=0.5, com=FAKE, tau=0, floor=float("-inf")):
+        return lib.dlm_lsp_adaptive_commit(p(m), B, S, lo, hi, f(fl), f(fh), f(floor), p(com), p(tau), p(0))
+    assert lsp(floor=float("nan")) == INVALID
     assert lsp(m=0) == INVALID
     assert lsp(com=0) == INVALID
     assert lsp(lo=8, hi=8) == INVALID

@@ -1114,20 +1114,23 @@ def test_margin_scores_lsp_workload_full_size(dlm):
 
 def test_lsp_adaptive_commit_bit_exact(dlm):
     """On given float32 margins (ties on purpose, every frontier including the
-    done and one-left cases, three fraction ranges): committed and tau
-    identical to the oracle."""
+    done and one-left cases, three fraction ranges, no floor and three margin
+    floors, the last above every margin so only the fallback commits):
+    committed and tau identical to the oracle."""
     rng = np.random.default_rng(52)
     B, S, gen_lo = 16, 700, 100
     G = S - gen_lo
-    for fl, fh in [(0.25, 0.5), (0.1, 0.3), (0.5, 0.5)]:
+    for fl, fh, floor in [(0.25, 0.5, -math.inf), (0.1, 0.3, -math.inf), (0.5, 0.5, -math.inf),
+                          (0.25, 0.5, 0.5), (0.25, 0.5, 1.5), (0.1, 0.3, 100.0)]:
         m = np.round(rng.standard_normal((B, S)) * 2, 1).astype(np.float32)
         com = rng.integers(0, G + 1, B).astype(np.int32)
         com[0], com[1], com[2] = G, G - 1, 0
         ct = i32(com)
         tau = torch.zeros(B, dtype=torch.float32, device="cuda")
-        dlm.dlm_lsp_adaptive_commit(torch.from_numpy(m).cuda(), gen_lo, S, ct, fl, fh, tau=tau)
+        dlm.dlm_lsp_adaptive_commit(torch.from_numpy(m).cuda(), gen_lo, S, ct, fl, fh, tau=tau, margin_floor=floor)
         torch.cuda.synchronize()
-        want, wt = O.lsp_adaptive_commit(m, gen_lo, S, com, float(np.float32(fl)), float(np.float32(fh)))
+        want, wt = O.lsp_adaptive_commit(m, gen_lo, S, com, float(np.float32(fl)), float(np.float32(fh)),
+                                         margin_floor=floor)
         assert np.array_equal(ct.cpu().numpy(), want)
         got_t = tau.cpu().numpy().astype(np.float64)
         assert np.array_equal(np.isnan(got_t), np.isnan(wt))
