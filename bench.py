@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--hbm-ceiling", action="store_true",
                     help="measure a plain streaming read and a 1 GiB copy (the reference for the "
                          "FETCH_SIZE / WRITE_SIZE byte counters) and exit")
+    ap.add_argument("--kernel-only", choices=KERNEL_ONLY,
+                    help="run ten eager calls of one dominant kernel's library call and exit "
+                         "(a short program for rocprofv3 counter passes)")
     return ap.parse_args()
 
 
@@ -213,6 +216,9 @@ def main():
     torch.cuda.set_device(0)
     if a.hbm_ceiling:
         print(json.dumps(hbm_ceiling()), flush=True)
+        return
+    if a.kernel_only:
+        print(json.dumps(kernel_only(dlm, W, a.kernel_only)), flush=True)
         return
     if a.only_extras:
         ceil = measured_ceilings(dlm)
@@ -537,6 +543,83 @@ def extra_colsum(dlm, W, a=None):
                             "frac_of_measured_mfma": of_measured(f_col / (t_col / 1e3), "mfma_bf16")},
             "tokens_per_s": n / ((t_attn + t_col) / 1e3),
             "colsum_topk_window_1024_keys": {"ms": t_colw, "TFLOP/s": f_col / 4 / t_colw / 1e9}}
+
+
+KERNEL_ONLY = ("attn_colsum_top64", "attn_lock_t0", "qkv_lock_t0", "lmhead_lsp")
+
+
+def kernel_only(dlm, W, which, calls=10):
+    """Ten eager calls of one library call, for counter passes: the partial
+    attention of the column-sum workload (B=4, S=4096, the 3072 masked rows of
+    each sequence, 32 x 128 heads) or of the lock loop's first step (B=8,
+    S=2048, every row, 32 query over 8 KV heads); the lock loop's first-step
+    Q/K/V GEMM (16,384 rows, K=4096, N=6144); the confidence LM head of the
+    LSP workload (3,680 rows, V=32768).  Inputs are seeded N(0,1)."""
+    import torch
+    if which.startswith("attn"):
+        sh = W.COLSUM_TOP64 if which == "attn_colsum_top64" else W.GQA_LOCK_LOOP
+        B, S, Hq, Hkv, hd = sh.B, sh.S, sh.Hq, sh.Hkv, sh.hd
+        lo = sh.prompt if which == "attn_colsum_top64" else 0
+        n = B * (S - lo)
+        q = _gen((n, Hq, hd), 411)
+        k = _gen((B, S, Hkv, hd), 412)
+        v = _gen((B, S, Hkv, hd), 413)
+        idx, offsets = _packed_rows([torch.arange(lo, S, device="cuda") for _ in range(B)])
+        o = torch.empty_like(q)
+        lse = torch.empty(n, Hq, dtype=torch.float32, device="cuda")
+        ws = torch.zeros(dlm.dlm_partial_attn_workspace_size(dlm.DLM_BF16, n, B, S, Hq, Hkv, hd),
+                         dtype=torch.uint8, device="cuda")
+        scale = 1.0 / math.sqrt(hd)
+        call = lambda: dlm.dlm_partial_attn(q, idx, offsets, n, k, v, scale, o, lse, workspace=ws)
+        flops = 4.0 * n * S * hd * Hq
+    elif which == "qkv_lock_t0":
+        sh = W.GQA_LOCK_LOOP
+        B, S, D, Hq, Hkv, hd = sh.B, sh.S, sh.D, sh.Hq, sh.Hkv, sh.hd
+        N, n = (Hq + 2 * Hkv) * hd, B * S
+        x = _gen((B, S, D), 421)
+        w = _gen((N, D), 422, scale=sh.w_std)
+        idx, offsets = _packed_rows([torch.arange(0, S, device="cuda") for _ in range(B)])
+        q = torch.empty(n, Hq, hd, dtype=torch.bfloat16, device="cuda")
+        kc = torch.zeros(B, S, Hkv, hd, dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        ws = torch.zeros(max(16, dlm.dlm_gather_qkv_workspace_size(dlm.DLM_BF16, n, D, Hq, Hkv, hd)),
+                         dtype=torch.uint8, device="cuda")
+        call = lambda: dlm.dlm_gather_qkv_scatter_kv(x, idx, offsets, n, w, Hq, Hkv, hd, q, kc, vc, workspace=ws)
+        flops = 2.0 * n * D * N
+    else:
+        sh = W.LSP_COMMIT
+        B, S, D, V = sh.B, sh.S, sh.D, sh.V
+        na = int(math.floor(sh.active_frac * (S - sh.prompt)))
+        h = _gen((B, S, D), 431)
+        w = _gen((V, D), 432, scale=sh.w_std)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(433)
+        rows = [torch.sort(torch.randperm(S - sh.prompt, generator=g, device="cuda")[:na])[0] + sh.prompt
+                for _ in range(B)]
+        eidx, eoff = _packed_rows(rows)
+        n = int(eidx.numel())
+        scores = torch.zeros(B, S, dtype=torch.float32, device="cuda")
+        argmax = torch.full((B, S), -1, dtype=torch.int32, device="cuda")
+        idx = torch.empty(B * S, dtype=torch.int32, device="cuda")
+        counts = torch.empty(B, dtype=torch.int32, device="cuda")
+        offsets = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+        ws = torch.zeros(dlm.dlm_select_workspace_size(dlm.DLM_SCORE_CONFIDENCE, B, S, V, n), dtype=torch.uint8,
+                         device="cuda")
+        call = lambda: dlm.dlm_saliency_select(dlm.DLM_SCORE_CONFIDENCE, h, w, lo=sh.prompt, hi=S,
+                                               threshold=sh.conf, idx=idx, counts=counts, offsets=offsets,
+                                               scores=scores, argmax=argmax, eval_idx=eidx, eval_offsets=eoff,
+                                               max_eval=n, workspace=ws)
+        flops = 2.0 * n * D * V
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    call()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    return {"kernel_only": which, "rows": n, "ms_per_call": ms, "TFLOP/s": flops / ms / 1e9}
 
 
 def extra_lsp(dlm, W, a=None):
