@@ -790,12 +790,25 @@ static int pf_for(int nk, int pfmax) {
   return 1;
 }
 
+// Split-K partial tiles (fp32) of the tilings that may split.  The device
+// plans the split from the real row count, which may be anything up to the
+// bound, so the workspace holds the most partial tiles any count <= the bound
+// can take: ks <= 8 splits of at most every output tile of the bound, and
+// never more than kSplitCap (a split of every tile stays below it; a split
+// last round holds fewer tiles than the resident grid).
 size_t gemm_workspace_bytes(int epi, int max_rows, int N, int K) {
   if (max_rows <= 0) return 0;
-  max_rows = gemm_token_rows(epi, max_rows);
-  if (epi_lm(epi)) return (size_t)kSplitCap * kLmTP * 256 * sizeof(float);
-  if (max_rows > 1024 && N % 256 == 0) return (size_t)kSplitCap * 256 * 256 * sizeof(float);
-  return 0;
+  const int rows = gemm_token_rows(epi, max_rows);
+  int TP;
+  if (epi_lm(epi))
+    TP = kLmTP;
+  else if (rows > 1024 && N % 256 == 0 && (K / 64) % 4 == 0)
+    TP = 256;  // the 256 x 256 tiling (other shapes never split)
+  else
+    return 0;
+  const long long units = (long long)(N / TP) * ((rows + 255) / 256);
+  const long long tiles = units * 8 < kSplitCap ? units * 8 : kSplitCap;
+  return (size_t)tiles * TP * 256 * sizeof(float);
 }
 
 template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST>

@@ -96,6 +96,12 @@ def test_select_workspace_size_covers_partials(lib):
     assert small >= 2 * 100 * 4
     big = lib.dlm_select_workspace_size(CONFIDENCE, 2, 100, 32768, 50)
     assert big >= small + 50 * (32768 // 256) * 16
+    # the LM head's split-K partials are sized by the bound: 50 rows x 32768
+    # = 128 output tiles may split 8 ways (1024 tiles); 20 rows of a 2048-word
+    # vocabulary = 8 tiles, at most 64 partial tiles
+    assert big >= 1024 * 256 * 256 * 4
+    tiny = lib.dlm_select_workspace_size(CONFIDENCE, 2, 100, 2048, 20)
+    assert 64 * 256 * 256 * 4 <= tiny < 65 * 256 * 256 * 4
 
 
 def gqkv(lib, dtype=BF16, x=FAKE, B=1, S=8, D=64, idx=FAKE, off=FAKE, max_rows=8, w=FAKE, Hq=2, Hkv=1,
@@ -117,13 +123,19 @@ def test_gather_qkv_rejections(lib):
     # 256 features, bounds up to 1024 rows: no tiling splits K, no scratch
     assert lib.dlm_gather_qkv_workspace_size(BF16, 1024, 64, 2, 1, 64) == 0
     assert lib.dlm_gather_qkv_workspace_size(BF16, 1024, 4096, 32, 32, 128) == 0
-    # a looser bound may split the large tiling on the device
-    need = lib.dlm_gather_qkv_workspace_size(BF16, 2048, 64, 2, 1, 64)
-    assert need > 0
-    assert lib.dlm_gather_qkv_scatter_kv(BF16, p(FAKE), 1, 2048, 64, p(FAKE), p(FAKE), 2048, p(FAKE), 2,
+    # K = 64 is too short for the 4-deep ring of the large tiling: the
+    # 128 x 128 tiling runs, unsplit, at any bound
+    assert lib.dlm_gather_qkv_workspace_size(BF16, 2048, 64, 2, 1, 64) == 0
+    # a looser bound may split the large tiling on the device: room for up to
+    # 8 fp32 256 x 256 partial tiles per output tile of the bound (2048 rows x
+    # 256 features = 8 tiles), never more than 1024 tiles
+    need = lib.dlm_gather_qkv_workspace_size(BF16, 2048, 256, 2, 1, 64)
+    assert need == 8 * 8 * 256 * 256 * 4
+    assert lib.dlm_gather_qkv_workspace_size(BF16, 16384, 4096, 32, 8, 128) == 1024 * 256 * 256 * 4
+    assert lib.dlm_gather_qkv_scatter_kv(BF16, p(FAKE), 1, 2048, 256, p(FAKE), p(FAKE), 2048, p(FAKE), 2,
                                          1, 64, p(FAKE), p(FAKE), p(FAKE), p(FAKE),
                                          ctypes.c_size_t(need - 1), p(0)) == WORKSPACE
-    assert lib.dlm_gather_qkv_scatter_kv(BF16, p(FAKE), 1, 2048, 64, p(FAKE), p(FAKE), 2048, p(FAKE), 2,
+    assert lib.dlm_gather_qkv_scatter_kv(BF16, p(FAKE), 1, 2048, 256, p(FAKE), p(FAKE), 2048, p(FAKE), 2,
                                          1, 64, p(FAKE), p(FAKE), p(FAKE), p(0), ctypes.c_size_t(0),
                                          p(0)) == WORKSPACE
 
