@@ -480,22 +480,33 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
 #pragma unroll
         for (int b = 0; b < FT; ++b) acc[a][b] = mfma32x32x16(fa[set][a], fb[set][b], acc[a][b]);
     };
+    // staging of chunks [j0, j1) of the next k-step: write them into the other
+    // LDS buffer (free since the last barrier), then reuse their registers for
+    // the loads of the k-step after it
+    auto stage = [&](int buf, int kt, int j0, int j1) {
+      u16* dst = ldsw + (buf ^ 1) * ROWS * PITCH;
+#pragma unroll
+      for (int j = j0; j < j1; ++j) {
+        *reinterpret_cast<u32x4*>(dst + RPJ * j * PITCH) = stg[0][j];
+        stg[0][j] = gload(j, min(kt + 2, nk - 1));
+      }
+    };
+    constexpr int CQ = CPT / 4;  // chunks staged per substep
     rd(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
       const int buf = kt & 1;
 #pragma unroll
       for (int kh = 0; kh < 3; ++kh) {
         rd(buf, kh + 1, (kh + 1) & 1);
+        stage(buf, kt, kh * CQ, (kh + 1) * CQ);
         mma(kh & 1, 0, FP);
       }
-      {
-        u16* dst = ldsw + (buf ^ 1) * ROWS * PITCH;
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(dst + RPJ * j * PITCH) = stg[0][j];
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) stg[0][j] = gload(j, min(kt + 2, nk - 1));
-        mma(1, 0, FP / 2);
-      }
+      stage(buf, kt, 3 * CQ, CPT);
+      mma(1, 0, FP / 2);
+      // The 64 KB of staging loads per k-step pass the CU's vector memory
+      // pipeline at 64 bytes a clock (1,024 cycles), so they are spread over
+      // the four substeps, a quarter beside each one's MFMAs, instead of
+      // being issued together in the last one.
 #pragma unroll
       for (int kh = 0; kh < 3; ++kh) {
 #pragma unroll
@@ -503,14 +514,21 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, FP * FT - (FP + FT), 0);
+#pragma unroll
+        for (int i = 0; i < CQ; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FP * FT - (FP + FT) - CQ, 0);
       }
 #pragma unroll
-      for (int i = 0; i < FP * FT / 2; ++i) {
+      for (int i = 0; i < CQ; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // DS write
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, FP * FT / 2 - CQ, 0);
       __syncthreads();
       rd(buf ^ 1, 0, 0);
       mma(1, FP / 2, FP);
