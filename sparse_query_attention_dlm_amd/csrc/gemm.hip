@@ -546,6 +546,49 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
       const int buf = (PF % 2 == 0) ? (u & 1) : (kt & 1);
       const u16* sW = lds + buf * ROWS * PITCH;
       const u16* sX = sW + TP * PITCH;
+      if constexpr (TP == 64) {
+        // Weight-streaming tiles do only 2-8 MFMAs per wave and k-step, too few
+        // to cover an LDS round trip per 16-wide substep: all of the k-step's
+        // fragments are read first, then the staging writes and loads issue
+        // beside the MFMAs.
+        constexpr int KH = BK / 16 / WK;
+        bf16x8 af[KH][FP], bfr[KH][FT];
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh) {
+          const int kk = wk * KH + kh;
+#pragma unroll
+          for (int a = 0; a < FP; ++a)
+            af[kh][a] = as_bf16x8(*reinterpret_cast<const u32x4*>(sW + (wp * WTP + a * 32 + lr) * PITCH +
+                                                                  kk * 16 + lg * 8));
+#pragma unroll
+          for (int b = 0; b < FT; ++b)
+            bfr[kh][b] = as_bf16x8(*reinterpret_cast<const u32x4*>(sX + (wt * WTT + b * 32 + lr) * PITCH +
+                                                                   kk * 16 + lg * 8));
+        }
+        const int slot = (u + 1) % PF;  // compile-time after unrolling
+        u16* dst = ldsw + (buf ^ 1) * ROWS * PITCH;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) *reinterpret_cast<u32x4*>(dst + RPJ * j * PITCH) = stg[slot][j];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) stg[slot][j] = gload(j, min(kt + 1 + PF, nk - 1));
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+          for (int a = 0; a < FP; ++a)
+#pragma unroll
+            for (int b = 0; b < FT; ++b) acc[a][b] = mfma32x32x16(af[kh][a], bfr[kh][b], acc[a][b]);
+        constexpr int NMF = KH * FP * FT;
+        __builtin_amdgcn_sched_group_barrier(0x100, KH * (FP + FT), 0);  // DS read
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+          if (i < NMF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        }
+        if (NMF > CPT) __builtin_amdgcn_sched_group_barrier(0x008, NMF - CPT, 0);
+        __syncthreads();
+        continue;
+      }
 #pragma unroll
       for (int kh = 0; kh < BK / 16 / WK; ++kh) {
         const int kk = wk * (BK / 16 / WK) + kh;
