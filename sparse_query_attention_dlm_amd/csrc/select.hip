@@ -29,49 +29,70 @@ __device__ __forceinline__ int block_sum(int v, int* s_wave) {
   return s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
 }
 
+// One chunk of NT*E consecutive positions [c0, c0 + NT*E) of a row's window:
+// thread t holds positions c0 + E*t .. +E-1 in `v` (thr past the window), and
+// writes its selected positions in ascending order after the block-wide
+// exclusive count, from out0 = the chunk's first output slot.  Returns the
+// chunk's selected count.
+template <int E>
+__device__ __forceinline__ int compact_chunk(const float (&v)[E], float thr, int lo, int c0, int out0,
+                                             int32_t* idx, int* s_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned mask = 0;
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool f = v[e] < thr;
+    mask |= unsigned(f) << e;
+    cnt += f;
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int wpre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int x = s_wave[w];
+    wpre += (w < wave) ? x : 0;
+    tot += x;
+  }
+  int out = out0 + wpre + incl - cnt;
+  const int p0 = c0 + tid * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((mask >> e) & 1u) idx[out++] = lo + p0 + e;
+  __syncthreads();  // s_wave is rewritten by the next chunk
+  return tot;
+}
+
+// Loads one chunk of a row's window for compact_chunk (thr past the window).
+template <int E>
+__device__ __forceinline__ void load_chunk(const float* row, int W, float thr, int c0, float (&v)[E]) {
+  const int p0 = c0 + (int)threadIdx.x * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = p0 + e < W ? row[p0 + e] : thr;
+}
+
 // Block-wide (256 threads) compaction of [lo,hi) of batch rows [b0, b1),
 // whose first index goes to idx[base].
 __device__ void compact_rows(const float* scores, int B, int S, int lo, int hi, float thr, int b0,
                              int b1, int base, int32_t* idx, int32_t* counts, int32_t* offsets) {
   constexpr int NT = kCompactNT, E = 8;
   __shared__ int s_wave[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int W = hi - lo;
   for (int b = b0; b < b1; ++b) {
     const float* row = scores + (size_t)b * S + lo;
     int rowcount = 0;
     for (int c0 = 0; c0 < W; c0 += NT * E) {
-      const int p0 = c0 + tid * E;
-      unsigned mask = 0;
-      int cnt = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int p = p0 + e;
-        const bool f = (p < W) && (row[p] < thr);
-        mask |= unsigned(f) << e;
-        cnt += f;
-      }
-      int incl = cnt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-      }
-      if (lane == 63) s_wave[wave] = incl;
-      __syncthreads();
-      int wpre = 0, tot = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int v = s_wave[w];
-        wpre += (w < wave) ? v : 0;
-        tot += v;
-      }
-      int out = base + rowcount + wpre + incl - cnt;
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if ((mask >> e) & 1u) idx[out++] = lo + p0 + e;
-      rowcount += tot;
-      __syncthreads();
+      float v[E];
+      load_chunk<E>(row, W, thr, c0, v);
+      rowcount += compact_chunk<E>(v, thr, lo, c0, base + rowcount, idx, s_wave);
     }
     if (tid == 0) {
       counts[b] = rowcount;
@@ -154,27 +175,46 @@ __global__ __launch_bounds__(256) void given_select_kernel(const float* __restri
     compact_rows(scores, B, S, lo, hi, thr, 0, B, 0, idx, counts, offsets);
     return;
   }
-  // one workgroup per batch row: the rows before it are counted again here
+  // One workgroup per batch row: the rows before it are counted again here
   // (a few KB of scores each), which gives this row's first output slot
-  // without any ordering between workgroups
-  __shared__ int s_sum[4];
-  const int b = blockIdx.x, W = hi - lo;
+  // without any ordering between workgroups.  The row's own first chunk and
+  // eight earlier rows at a time are loaded before anything is counted, so a
+  // workgroup waits out one or two memory round trips, not one per row.
+  constexpr int NT = kCompactNT, E = 8, RB = 8;
+  __shared__ int s_sum[4], s_cw[4];  // block_sum's and the chunks' (no reuse between them)
+  const int b = blockIdx.x, W = hi - lo, tid = threadIdx.x;
+  const float* own = scores + (size_t)b * S + lo;
+  float v0[E];
+  load_chunk<E>(own, W, thr, 0, v0);
   int before = 0;
-  for (int bb = 0; bb < b; ++bb) {
-    const float* row = scores + (size_t)bb * S + lo;
-    for (int p0 = threadIdx.x; p0 < W; p0 += 8 * kCompactNT) {
-      float v[8];  // eight loads in flight before any compare
+  for (int p0 = tid; p0 < W; p0 += E * NT) {
+    for (int bb0 = 0; bb0 < b; bb0 += RB) {
+      float v[RB][E];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int p = p0 + u * kCompactNT;
-        v[u] = p < W ? row[p] : thr;
-      }
+      for (int r = 0; r < RB; ++r)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) before += v[u] < thr;
+        for (int u = 0; u < E; ++u) {
+          const int p = p0 + u * NT;
+          v[r][u] = (bb0 + r < b && p < W) ? scores[(size_t)(bb0 + r) * S + lo + p] : thr;
+        }
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int u = 0; u < E; ++u) before += v[r][u] < thr;
     }
   }
   const int base = block_sum(before, s_sum);
-  compact_rows(scores, B, S, lo, hi, thr, b, b + 1, base, idx, counts, offsets);
+  int rowcount = compact_chunk<E>(v0, thr, lo, 0, base, idx, s_cw);
+  for (int c0 = NT * E; c0 < W; c0 += NT * E) {
+    float v[E];
+    load_chunk<E>(own, W, thr, c0, v);
+    rowcount += compact_chunk<E>(v, thr, lo, c0, base + rowcount, idx, s_cw);
+  }
+  if (tid == 0) {
+    counts[b] = rowcount;
+    offsets[b] = base;
+    if (b == B - 1) offsets[B] = base + rowcount;
+  }
 }
 
 // Merge of per-vocabulary-tile partials (max logit, sum exp(z - max), argmax,
