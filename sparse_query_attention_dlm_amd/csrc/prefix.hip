@@ -9,8 +9,8 @@
 // the confidence threshold.
 //
 // One workgroup per sequence: every thread pushes the latest argmax of its
-// positions into the W-deep ring, tests stability on the ring it just
-// updated, and the first unstable position at or after the frontier is found
+// positions into the W-deep ring, tests stability against the ring's older
+// entries, and the first unstable position at or after the frontier is found
 // with an LDS atomicMin.  Integer work only; the one float comparison uses the
 // float32 max-prob given.
 #include "common.hpp"
@@ -18,12 +18,18 @@
 
 namespace dlm {
 
+// WT > 0: the ring depth W == WT, known at compile time, so each thread's
+// loads (argmax, max-prob and the W - 1 older ring entries of up to PP
+// positions) all issue before any of them is used: one memory round trip per
+// PP * 256 positions instead of several per position.  WT = 0: any W.
+template <int WT>
 __global__ __launch_bounds__(256) void stable_prefix_kernel(const int32_t* __restrict__ argmax,
                                                             const float* __restrict__ maxprob,
                                                             int S, int gen_lo, int gen_hi,
                                                             int32_t* __restrict__ ring, int W,
                                                             int step, float thr, int min_commit,
                                                             int32_t* __restrict__ committed) {
+  constexpr int PP = 4;  // positions per thread per batch of loads
   __shared__ int s_first;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int S_gen = gen_hi - gen_lo;
@@ -31,14 +37,42 @@ __global__ __launch_bounds__(256) void stable_prefix_kernel(const int32_t* __res
   if (tid == 0) s_first = S_gen;
   __syncthreads();
   const int slot = step % W;
-  for (int i = tid; i < S_gen; i += 256) {
-    const size_t pos = (size_t)b * S + gen_lo + i;
-    const int a = argmax[pos];
-    int32_t* rr = ring + ((size_t)b * S_gen + i) * W;
-    rr[slot] = a;
-    bool stable = (a != -1) && (maxprob[pos] >= thr);
-    for (int w = 0; w < W; ++w) stable = stable && (rr[w] == a);
-    if (i >= L && !stable) atomicMin(&s_first, i);
+  if constexpr (WT > 0) {
+    for (int i0 = tid; i0 < S_gen; i0 += PP * 256) {
+      int a[PP], old[PP][WT];
+      float mp[PP];
+#pragma unroll
+      for (int k = 0; k < PP; ++k) {
+        const int i = i0 + k * 256;
+        const bool in = i < S_gen;
+        const size_t pos = (size_t)b * S + gen_lo + (in ? i : 0);
+        a[k] = in ? argmax[pos] : -1;
+        mp[k] = in ? maxprob[pos] : 0.f;
+        const int32_t* rr = ring + ((size_t)b * S_gen + (in ? i : 0)) * WT;
+#pragma unroll
+        for (int w = 0; w < WT; ++w) old[k][w] = in && w != slot ? rr[w] : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < PP; ++k) {
+        const int i = i0 + k * 256;
+        if (i >= S_gen) break;
+        ring[((size_t)b * S_gen + i) * WT + slot] = a[k];
+        bool stable = (a[k] != -1) && (mp[k] >= thr);
+#pragma unroll
+        for (int w = 0; w < WT; ++w) stable = stable && (w == slot || old[k][w] == a[k]);
+        if (i >= L && !stable) atomicMin(&s_first, i);
+      }
+    }
+  } else {
+    for (int i = tid; i < S_gen; i += 256) {
+      const size_t pos = (size_t)b * S + gen_lo + i;
+      const int a = argmax[pos];
+      int32_t* rr = ring + ((size_t)b * S_gen + i) * W;
+      rr[slot] = a;
+      bool stable = (a != -1) && (maxprob[pos] >= thr);
+      for (int w = 0; w < W; ++w) stable = stable && (rr[w] == a);
+      if (i >= L && !stable) atomicMin(&s_first, i);
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -105,8 +139,27 @@ hipError_t launch_lsp_adaptive(const float* margin, int B, int S, int gen_lo, in
 hipError_t launch_stable_prefix(const int32_t* argmax, const float* maxprob, int B, int S,
                                 int gen_lo, int gen_hi, int32_t* ring, int W, int step, float thr,
                                 int min_commit, int32_t* committed, hipStream_t st) {
-  hipLaunchKernelGGL(stable_prefix_kernel, dim3(B), dim3(256), 0, st, argmax, maxprob, S, gen_lo,
-                     gen_hi, ring, W, step, thr, min_commit, committed);
+  switch (W) {
+    case 1:
+      hipLaunchKernelGGL(stable_prefix_kernel<1>, dim3(B), dim3(256), 0, st, argmax, maxprob, S, gen_lo,
+                         gen_hi, ring, W, step, thr, min_commit, committed);
+      break;
+    case 2:
+      hipLaunchKernelGGL(stable_prefix_kernel<2>, dim3(B), dim3(256), 0, st, argmax, maxprob, S, gen_lo,
+                         gen_hi, ring, W, step, thr, min_commit, committed);
+      break;
+    case 3:
+      hipLaunchKernelGGL(stable_prefix_kernel<3>, dim3(B), dim3(256), 0, st, argmax, maxprob, S, gen_lo,
+                         gen_hi, ring, W, step, thr, min_commit, committed);
+      break;
+    case 4:
+      hipLaunchKernelGGL(stable_prefix_kernel<4>, dim3(B), dim3(256), 0, st, argmax, maxprob, S, gen_lo,
+                         gen_hi, ring, W, step, thr, min_commit, committed);
+      break;
+    default:
+      hipLaunchKernelGGL(stable_prefix_kernel<0>, dim3(B), dim3(256), 0, st, argmax, maxprob, S, gen_lo,
+                         gen_hi, ring, W, step, thr, min_commit, committed);
+  }
   return hipGetLastError();
 }
 

@@ -812,17 +812,20 @@ def test_confidence_full_size_first_step(dlm):
         assert np.array_equal(ix[offs[b]:offs[b + 1]], want), f"b {b}: selected set"
 
 
-def test_stable_prefix_bit_exact_on_given_inputs(dlm):
+@pytest.mark.parametrize("Wd,S,gen_lo", [(3, 700, 60), (1, 700, 60), (2, 700, 60), (4, 1500, 100), (6, 700, 60)])
+def test_stable_prefix_bit_exact_on_given_inputs(dlm, Wd, S, gen_lo):
     """Prefix step alone, fed identical float32 max-probs: the frontiers and the
-    ring must match the oracle bit for bit (decisions in the same precision)."""
+    ring must match the oracle bit for bit (decisions in the same precision).
+    Ring depths 1-4 take the kernel's unrolled paths (1,400 generated positions:
+    two batches of loads per thread), depth 6 its general loop."""
     rng = np.random.default_rng(21)
-    B, S, gen_lo, Wd = 5, 700, 60, 3
+    B = 5
     S_gen = S - gen_lo
     ring_o = np.full((B, S_gen, Wd), -1, np.int64)
     com_o = np.zeros(B, np.int64)
     ring = torch.full((B, S_gen, Wd), -1, dtype=torch.int32, device="cuda")
     com = torch.zeros(B, dtype=torch.int32, device="cuda")
-    say(f"[prefix] B={B} S={S} gen_lo={gen_lo}")
+    say(f"[prefix] B={B} S={S} gen_lo={gen_lo} W={Wd}")
     for t in range(12):
         am = rng.integers(0, 2, size=(B, S)).astype(np.int64)
         am[:, : gen_lo + 40 * t] = 1                                    # a growing stable head
