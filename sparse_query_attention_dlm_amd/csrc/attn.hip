@@ -9,8 +9,9 @@
 //   * A workgroup owns 128 or 256 query vectors (row, head) that share one KV
 //     head of one sequence (GQA packs the G query heads of a KV head
 //     together); each wave owns 32 of them.  256-vector workgroups (eight
-//     waves) serve selections with many query tiles: every K/V tile is read
-//     from L2 once per 256 vectors instead of once per 128.
+//     waves) serve MHA-like selections (fewer than 4 query heads per KV head)
+//     with many query tiles: every K/V tile is read from L2 once per 256
+//     vectors instead of once per 128.
 //   * Per 64-key tile, K and V come in through buffer loads (one tile ahead,
 //     in registers) and are staged in LDS; every wave computes the transposed
 //     score tiles S^T = K . Q^T (32 keys x 32 queries each) with 32x32x16
@@ -401,9 +402,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
 }
 
 // WQ = 1: 128 query vectors, two workgroups per CU (short selections, whose
-// splits spread the K/V stream over the CUs); WQ = 2: 256 query vectors in
-// eight waves, one workgroup per CU (many query tiles, where every tile of
-// K/V is re-read by each query tile of its head from L2).
+// splits spread the K/V stream over the CUs, and GQA with 4 or more query
+// heads per KV head); WQ = 2: 256 query vectors in eight waves, one workgroup
+// per CU (MHA-like selections with many query tiles, where every tile of K/V
+// is re-read by each query tile of its head from L2).
 template <int HD, int WQ>
 __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) u16 smem[AttnLds<HD>::WIDE];
@@ -663,11 +665,17 @@ hipError_t launch_attn(int dtype, const AttnArgs& a0, void* workspace, hipStream
   a.part_lse = may_split ? a.part_o + (size_t)kPartRows * a.hd : nullptr;
   // A bound of fewer than kSplitTarget 128-vector tiles means the device
   // always splits the keys (short selections): 128-vector workgroups.
-  // Otherwise 256-vector workgroups, which halve the K/V re-reads.
+  // Otherwise, with fewer than 4 query heads per KV head, 256-vector
+  // workgroups, which halve the K/V re-reads.  With 4 or more the K/V bytes
+  // per query are already a quarter of MHA's, and 128-vector workgroups (two
+  // per CU, from different tiles, so the two waves of a SIMD are not held in
+  // step by one workgroup's barriers; twice the tiles, so a step's last round
+  // is less empty) run the GQA lock loop's steps as fast or faster (t = 32:
+  // 338 -> 322 us, t = 56: 133 -> 112 us).
   auto max_units = [&](int QT) {
     return (ceil_div((long long)a.max_rows * G, QT) + a.B - 1) * (long long)a.Hkv;
   };
-  const bool wide = !(may_split && max_units(128) < kSplitTarget);
+  const bool wide = G < 4 && !(may_split && max_units(128) < kSplitTarget);
   const int QT = wide ? 256 : 128;
   // enough workgroups for every tile and for the split factor the device may
   // choose (units < kSplitTarget splits into fewer than 2 * kSplitTarget)

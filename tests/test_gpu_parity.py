@@ -294,7 +294,7 @@ def test_gqa_lock_loop_step_full_size(dlm, t, bound):
     loop passes (the exact count) and, for the last step, the loose bound B*S.
     The launches differ by step: t = 0 (16384 rows) and t = 32 (8480) run the
     256 x 256 GEMM tiling unsplit, its Q/K/V epilogue inside the GEMM kernel,
-    and 256-vector attention workgroups; t = 62 (1072 rows) splits K over spare
+    and 128-vector attention workgroups (GQA 4:1); t = 62 (1072 rows) splits K over spare
     workgroups (epilogue in the reduce pass); t = 63 (824 rows) runs the
     128 x 128 body of the dual launch and a split-KV merge (the loose bound
     the 256 x 256 tiling).  The caches hold seeded earlier rows.  Every Q row,
@@ -437,11 +437,12 @@ def run_attention_plan(dlm, B, S, Hq, Hkv, hd, rows_per_b, sample=None, seed=21,
 
 
 @pytest.mark.parametrize("hd", [64, 128])
-def test_attention_many_tiles_gqa_ragged(dlm, hd):
-    """>= 512 tiles of 128 query vectors: no key split, 256-vector workgroups
-    (GQA 4:1, ragged last query tile and last 64-key tile); sampled rows
-    against the oracle."""
-    run_attention_plan(dlm, B=2, S=1500, Hq=32, Hkv=8, hd=hd, rows_per_b=[1500, 1436], sample=48)
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (32, 16)])
+def test_attention_many_tiles_gqa_ragged(dlm, hd, Hq, Hkv):
+    """>= 512 tiles of 128 query vectors: no key split; GQA 4:1 runs 128-vector
+    workgroups (two per CU), GQA 2:1 the 256-vector ones; ragged last query
+    tile and last 64-key tile; sampled rows against the oracle."""
+    run_attention_plan(dlm, B=2, S=1500, Hq=Hq, Hkv=Hkv, hd=hd, rows_per_b=[1500, 1436], sample=48)
 
 
 @pytest.mark.parametrize("hd", [64, 128])
