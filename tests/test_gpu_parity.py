@@ -651,11 +651,12 @@ def test_colsum_topk_gqa_ragged(dlm):
     run_colsum(dlm, B=3, S=520, prompt=77, Hq=8, Hkv=2, k=24)
 
 
-@pytest.mark.parametrize("B,S", [(5, 1000), (70, 8192)])
+@pytest.mark.parametrize("B,S", [(5, 1000), (12, 3000), (70, 8192)])
 def test_given_select_batch_paths(dlm, B, S):
-    """Compaction of supplied scores over the window [3, S-5): B = 5 takes the
-    one-workgroup-per-row kernel, B = 70 (B*B*window over the limit for
-    recounting) the single-workgroup loop.  Index sets, counts and offsets
+    """Compaction of supplied scores over the window [3, S-5): B = 5 and
+    B = 12 take the one-workgroup-per-row kernel (B = 12: earlier rows counted
+    in two batches of eight, a 2,992-position window in two chunks), B = 70
+    (B*B*window over the limit for recounting) the single-workgroup loop.  Index sets, counts and offsets
     are bit-exact against the oracle (the scores are exact float32 values and
     0.5 is exact, so both sides take the same decisions)."""
     lo, hi = 3, S - 5
