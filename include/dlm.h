@@ -141,9 +141,11 @@ int dlm_saliency_select(int mode, int dtype, const void* a, const void* b,
  * Cache rows that are not selected are not touched (byte-identical).
  * bf16: D % 64 == 0, hd in {64,128}, x under 2 GiB, w_qkv under 4 GiB.  The
  * workspace (size from dlm_gather_qkv_workspace_size) holds split-K partial
- * tiles; only bounds above 1024 rows with (Hq+2*Hkv)*hd % 256 == 0 need one
- * (size 0 otherwise, and then workspace may be NULL).  f32: D % 4 == 0, no
- * workspace.
+ * tiles; only bounds above 1024 rows with (Hq+2*Hkv)*hd % 256 == 0 and D/64 a
+ * multiple of 4 need one (size 0 otherwise, and then workspace may be NULL).
+ * Its size covers the most partial tiles any real row count up to the bound
+ * can make the device split into: 8 per 256 x 256 output tile of the bound,
+ * at most 1024 tiles of 256 KB.  f32: D % 4 == 0, no workspace.
  * ------------------------------------------------------------------------ */
 size_t dlm_gather_qkv_workspace_size(int dtype, int max_rows, int D, int Hq, int Hkv, int hd);
 int dlm_gather_qkv_scatter_kv(int dtype, const void* x, int B, int S, int D,
