@@ -360,7 +360,10 @@ int dlm_nonsalient_dv_update(int dtype, const void* q_cache, const float* lse_ca
  *   out_cache [B,S,D] bf16  selected rows replaced; others not touched
  * D and F multiples of 64.  h (rounded to bf16) lives in the workspace of
  * dlm_salient_ffn_workspace_size(dtype, max_rows, D, F) bytes, followed by
- * split-K tiles for long selections.  dtype DLM_F32 -> DLM_ERR_UNSUPPORTED.
+ * fp32 split-K partial tiles: long selections may split either product;
+ * short ones (max_rows <= 128) split the down projection's K when it has
+ * fewer than 128 output tiles of 64 features (D < 8192), so that more CUs
+ * stream w_down.  dtype DLM_F32 -> DLM_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 size_t dlm_salient_ffn_workspace_size(int dtype, int max_rows, int D, int F);
 int dlm_salient_ffn(int dtype, const void* x, int B, int S, int D,

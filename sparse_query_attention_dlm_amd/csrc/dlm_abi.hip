@@ -541,7 +541,9 @@ size_t dlm_salient_ffn_workspace_size(int dtype, int max_rows, int D, int F) {
   if (dtype != DLM_BF16 || max_rows <= 0 || D <= 0 || F <= 0) return 0;
   const size_t h = round_up((size_t)max_rows * F * 2, 256);
   const size_t g1 = dlm::gemm_workspace_bytes(dlm::EPI_SWIGLU, max_rows, 2 * F, D);
-  const size_t g2 = dlm::gemm_workspace_bytes(dlm::EPI_ROWS, max_rows, D, F);
+  size_t g2 = dlm::gemm_workspace_bytes(dlm::EPI_ROWS, max_rows, D, F);
+  const size_t g3 = dlm::gemm_skinny_split_bytes(max_rows, D, F);  // the down projection's K split
+  if (g3 > g2) g2 = g3;
   return h + (g1 > g2 ? g1 : g2);
 }
 
@@ -611,6 +613,7 @@ int dlm_salient_ffn(int dtype, const void* x, int B, int S, int D, const int32_t
   d.out = out_cache;
   d.ld_out = D;
   d.part = part;
+  d.skinny_split = 1;  // a short selection splits K over the CUs (D / 64 tiles alone leave most idle)
   return hip_status(dlm::launch_gemm(dtype, dlm::EPI_ROWS, dlm::A_COMPACT, d, st), "FFN down");
 }
 

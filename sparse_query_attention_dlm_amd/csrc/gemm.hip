@@ -872,6 +872,24 @@ size_t gemm_workspace_bytes(int epi, int max_rows, int N, int K) {
   return (size_t)tiles * TP * 256 * sizeof(float);
 }
 
+// The weight-streaming tiling of a narrow output: N = 4096 features (the
+// FFN's down projection) make 64 tiles, so 64 CUs stream the weights while
+// the rest idle.  A caller that passes the partial tiles' memory
+// (GemmArgs::skinny_split) has K split until about kSkinnySplitItems work
+// items (one per CU) stream a K-slice each; the reduce pass then adds the
+// fp32 partials in split order.
+constexpr int kSkinnySplitUnits = 128;  // split only outputs of fewer tiles
+constexpr int kSkinnySplitItems = 256;  // double the splits while below this many items
+size_t gemm_skinny_split_bytes(int max_rows, int N, int K) {
+  if (max_rows <= 0 || max_rows > kSkinnyRows || N % 64 != 0 || K % 64 != 0 || (K / 64) % 4 != 0)
+    return 0;
+  const int units = N / 64;  // one row tile (at most 128 rows)
+  if (units >= kSkinnySplitUnits) return 0;
+  const GemmSplit s = gemm_split(units, K / 64, 4, kSkinnySplitUnits, kSkinnySplitItems, 0);
+  if (s.ks <= 1) return 0;
+  return (size_t)s.items() * 64 * 128 * sizeof(float);
+}
+
 template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST>
 static void launch_reduce(const GemmArgs& g, hipStream_t st) {
   hipLaunchKernelGGL((gemm_splitk_reduce_kernel<TP, TT, WP, WT, BK, PF, EPI, AMODE, GATE, SB, ST>),
@@ -895,7 +913,10 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
   int items = (g.N / TP) * m_tiles_max;
   if (SB > 0) {
     const int cap = ST < kSplitCap ? 2 * ST : kSplitCap;
-    if (items < cap) items = cap;
+    if (WK == 2 && m_tiles_max <= 1)
+      items = gemm_split(items, g.K / BK, PF, SB, ST, 0).items();  // the device plans these tiles or none
+    else if (items < cap)
+      items = cap;
   }
   const int grid = WK == 1 ? persistent_grid(items, TP, TT) : items;
   GemmArgs ga = g;
@@ -910,6 +931,12 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
 // flight) ran 36.7 us against 34.7 us for 64-wide steps with a 4-deep ring.
 template <int EPI, int AMODE, int GATE>
 static void launch_skinny(const GemmArgs& g, hipStream_t st) {
+  if constexpr (EPI == EPI_ROWS) {
+    if (g.skinny_split && gemm_skinny_split_bytes(g.max_rows, g.N, g.K) > 0) {
+      launch_bf16<64, 128, 64, 4, EPI, AMODE, GATE, kSkinnySplitUnits, kSkinnySplitItems, 2>(g, st);
+      return;
+    }
+  }
   if (pf_for(g.K / 64, 4) == 4)
     launch_bf16<64, 128, 64, 4, EPI, AMODE, GATE, 0, 0, 2>(g, st);
   else if (pf_for(g.K / 64, 4) == 2)

@@ -77,11 +77,16 @@ struct GemmArgs {
   int ntile;
   // split-K scratch (workspace): partial tiles
   float* part;
+  // nonzero: the weight-streaming tiling (at most 128 rows) of a narrow
+  // output (fewer than 128 tiles of 64 features) may split K over several
+  // workgroups; part then holds gemm_skinny_split_bytes() of partial tiles
+  int skinny_split;
   // set by the launcher: workgroups of the persistent grid (the split plan
   // fills its last round)
   int tile_grid;
 };
 size_t gemm_workspace_bytes(int epi, int max_rows, int N, int K);
+size_t gemm_skinny_split_bytes(int max_rows, int N, int K);
 hipError_t launch_gemm(int dtype, int epi, int amode, const GemmArgs& g, hipStream_t st);
 int gemm_lmhead_ntile(int V);
 

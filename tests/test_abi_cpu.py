@@ -284,6 +284,19 @@ def test_salient_ffn_rejections(lib):
     # h [max_rows, F] bf16 first, 256-byte aligned
     assert lib.dlm_salient_ffn_workspace_size(BF16, 8, 128, 256) == 8 * 256 * 2
     assert lib.dlm_salient_ffn_workspace_size(F32, 8, 128, 256) == 0
+    # a short selection (<= 128 rows) splits the down projection's K when it has
+    # fewer than 128 output tiles of 64 features: D = 4096 -> 64 tiles, F = 12288
+    # -> 192 k-steps of 64 in rings of 4; splits double (2, 4) while the items
+    # (tiles x splits) stay below 256, each split a 64 x 128 fp32 tile
+    ws = lib.dlm_salient_ffn_workspace_size
+    assert ws(BF16, 102, 4096, 12288) == 102 * 12288 * 2 + 64 * 4 * 64 * 128 * 4
+    # D = 1024: 16 tiles; F = 1024 has 16 k-steps, so a split of 4 would leave
+    # one ring per split (two are needed): 2 splits
+    assert ws(BF16, 100, 1024, 1024) == 100 * 1024 * 2 + 16 * 2 * 64 * 128 * 4
+    # no split: more than 128 rows, 128 tiles or more, or K too short to split
+    assert ws(BF16, 129, 4096, 12288) == 129 * 12288 * 2
+    assert ws(BF16, 64, 8192, 4096) == 64 * 4096 * 2
+    assert ws(BF16, 8, 128, 256) == 8 * 256 * 2
 
 
 def test_margin_mode_and_adaptive_commit_rejections(lib):

@@ -1034,6 +1034,28 @@ def test_salient_ffn_short_selection(dlm):
     run_salient_ffn(dlm, B=2, S=512, D=1024, F=1024, n_per_b=[100, 0])
 
 
+def test_salient_ffn_short_selection_loose_bound(dlm):
+    """40 rows under a bound of 128 (the device plans the down projection's
+    K split from the real count): 32 output tiles split 4 ways."""
+    run_salient_ffn(dlm, B=2, S=512, D=2048, F=2048, n_per_b=[30, 10], seed=46, loose_bound=128)
+
+
+def test_salient_ffn_no_rows(dlm):
+    """An empty selection under a bound of 64: nothing is written."""
+    B, S, D, F = 2, 256, 1024, 2048
+    rng = np.random.default_rng(47)
+    x = dev(W.round_bf16(rng.standard_normal((B, S, D))), "bf16")
+    w_gu = dev(W.round_bf16(rng.standard_normal((2 * F, D)) / 32), "bf16")
+    w_down = dev(W.round_bf16(rng.standard_normal((D, F)) / 45), "bf16")
+    cache = W.round_bf16(rng.standard_normal((B, S, D)))
+    out = dev(cache, "bf16")
+    ws = workspace(dlm.dlm_salient_ffn_workspace_size(dlm.DLM_BF16, 64, D, F))
+    dlm.dlm_salient_ffn(x, i32(np.zeros(64, np.int32)), i32(np.zeros(B + 1, np.int32)), 64, w_gu, w_down, out,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), cache)
+
+
 def test_salient_ffn_long_selection_split_k(dlm):
     """1300 rows: the resident 256x256 tiling with split-K partials (workspace)."""
     run_salient_ffn(dlm, B=2, S=1024, D=512, F=1536, n_per_b=[700, 600], seed=42)
