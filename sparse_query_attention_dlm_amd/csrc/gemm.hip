@@ -271,6 +271,34 @@ __host__ __device__ inline GemmSplit gemm_split(int units, int nk, int pf, int S
   return s;
 }
 
+// Order of the output tiles: groups of kGroupM row tiles, walked feature tile
+// by feature tile within a group (consecutive positions share a feature
+// tile's weights, and every 8 of them one set of token rows).  A bijection
+// of [0, m_tiles * n_tiles).
+constexpr int kGroupM = 8;
+__device__ __forceinline__ void tile_of(int q, int m_tiles, int n_tiles, int& mt, int& nt) {
+  const int grp = q / (kGroupM * n_tiles);
+  const int first = grp * kGroupM;
+  const int gsize = min(kGroupM, m_tiles - first);
+  const int r = q - grp * kGroupM * n_tiles;
+  mt = first + r % gsize;
+  nt = r / gsize;
+}
+
+// The hardware deals the workgroups of a launch round-robin to the 8 XCDs
+// (workgroup b on XCD b % 8), each with its own L2.  Items of a loop handled
+// round-robin by G workgroups (item w on workgroup w % G) are renumbered so
+// that the workgroups of one XCD take consecutive positions of each round:
+// with the grouped tile order, an XCD's tiles then form a compact block of
+// feature and row tiles whose slices its L2 fetches once, instead of every
+// weight slice being fetched by up to 8 L2s.  A bijection of [0, n).
+__device__ __forceinline__ int xcd_local(int w, int n, int G) {
+  const int r0 = w - w % G, b = w - r0;
+  const int L = min(G, n - r0);  // items of this round
+  const int x = b & 7, a = L >> 3, c = L & 7;
+  return r0 + x * a + min(x, c) + (b >> 3);
+}
+
 // u16 elements of the double-buffered LDS tile (rows padded by 8 elements)
 constexpr int gemm_lds_u16(int TP, int TT, int BK) { return 2 * (TP + TT) * (BK + 8); }
 
@@ -305,7 +333,8 @@ __device__ __forceinline__ void gemm_rows(const GemmArgs& g, int n_rows, int m0,
 template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK,
           int TPV>
 __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u16* lds, uint32_t* s_xoff,
-                                               int* s_drow, const GemmSplit sp, int unit, int ksi);
+                                               int* s_drow, const GemmSplit sp, int unit, int ksi,
+                                               int n_tiles);
 
 // TPV (<= TP): weight rows a tile really owns.  A tile of TP MFMA rows with
 // TPV = 48 < TP = 64 lets the 12288-feature Q/K/V projection spread over 256
@@ -337,20 +366,29 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
   const int nk_all = g.K / BK;
   const GemmSplit sp = gemm_split(m_tiles * n_tiles, nk_all, PF, SB, ST, g.tile_grid);
   const int total = sp.items();
-  // Work items (tile, k-split) go to workgroups round-robin: item w runs on
-  // workgroup w % gridDim.x, so a grid of one workgroup per CU keeps every
-  // workgroup on the same k-step of its current tile and the tiles running
-  // together on an XCD share their weight and row slices in its L2.  The
-  // split tiles' items come last (the last round).
-  for (int work = (int)blockIdx.x; work < total; work += (WK == 1 ? (int)gridDim.x : total)) {
-    int unit = work, ksi = 0;
-    if (work >= sp.whole) {
-      const int j = work - sp.whole, ns = sp.units - sp.whole;
+  const int G = (int)gridDim.x;
+  // Work items (tile position, k-split) go to workgroups round-robin: item w
+  // runs on workgroup w % G, so a grid of one workgroup per CU keeps every
+  // workgroup on the same k-step of its current tile.  Within each round the
+  // items are renumbered XCD by XCD (xcd_local) and the positions walk the
+  // grouped tile order (tile_of), so that the tiles running together on an
+  // XCD share their weight and row slices in its L2.  The split tiles'
+  // items come last (the last round; the renumbering needs the split
+  // region to start a round, which it does unless the grid runs one item
+  // per workgroup with unsplit tiles before it).
+  for (int work = (int)blockIdx.x; work < total; work += (WK == 1 ? G : total)) {
+    int unit, ksi = 0;
+    if (work < sp.whole) {
+      unit = xcd_local(work, sp.whole, G);
+    } else {
+      int j = work - sp.whole;
+      const int ns = sp.units - sp.whole;
+      if (sp.whole % G == 0) j = xcd_local(j, total - sp.whole, G);
       unit = sp.whole + j % ns;
       ksi = j / ns;
     }
     gemm_tile_work<TP, TT, WP, WT, BK, PF, EPI, AMODE, SB, ST, WK, TPV>(g, n_rows, lds, s_xoff, s_drow,
-                                                                        sp, unit, ksi);
+                                                                        sp, unit, ksi, n_tiles);
     if constexpr (WK == 1) __syncthreads();  // the next item rewrites the row table and tiles
   }
 }
@@ -358,7 +396,8 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs& g, int n_rows, u1
 template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int SB, int ST, int WK,
           int TPV>
 __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u16* lds, uint32_t* s_xoff,
-                                               int* s_drow, const GemmSplit sp, int unit, int ksi) {
+                                               int* s_drow, const GemmSplit sp, int unit, int ksi,
+                                               int n_tiles) {
   constexpr int NT = 256 * WK;   // threads
   constexpr int PITCH = BK + 8;  // u16 elements per LDS row (16 bytes of padding)
   constexpr int ROWS = TP + TT;
@@ -369,7 +408,8 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
   constexpr int WTP = TP / WP, WTT = TT / WT, FP = WTP / 32, FT = WTT / 32;
   const int m_tiles = (gemm_token_rows(EPI, n_rows) + TT - 1) / TT;
   const int nk_all = g.K / BK;
-  const int nt = unit / m_tiles, mt = unit % m_tiles;
+  int mt, nt;  // unit: the tile's position in the grouped order
+  tile_of(unit, m_tiles, n_tiles, mt, nt);
   const int m0 = mt * TT, n0 = nt * TPV;
   const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, wk = tid >> 8;
   const int ks = sp.splits_of(unit);
@@ -715,7 +755,8 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs g) {
   const int RS = epi_lm(EPI) ? 1 : min(NQ, (kReduceTarget + n_split - 1) / n_split);
   if ((int)blockIdx.x >= n_split * RS) return;
   const int unit = sp.whole + (int)blockIdx.x / RS, slice = (int)blockIdx.x % RS;
-  const int nt = unit / m_tiles, mt = unit % m_tiles;
+  int mt, nt;
+  tile_of(unit, m_tiles, n_tiles, mt, nt);
   const int m0 = mt * TT, n0 = nt * TP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
   const int wp = wave / WT, wt = wave % WT;
