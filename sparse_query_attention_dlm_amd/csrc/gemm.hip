@@ -216,8 +216,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
 // the reduce pass, recomputed from the same inputs).
 //   Fewer than SB output tiles: K is split over spare workgroups of the grid:
 //     ks is a power of two (<= 8) that divides the k-steps into whole
-//     prefetch rings (at least two rings per split), doubled while units * ks
-//     stays below ST and within kSplitCap (the workspace).
+//     prefetch rings (at least two rings per split), doubled while all
+//     units * ks items still fit in one round of the G-workgroup grid (in
+//     ST items when the grid is not known yet) and within kSplitCap (the
+//     workspace).  A split that needs more rounds does the same number of
+//     item-rounds of work and adds the partials' round trip: measured on
+//     the lock loop's Q/K/V GEMM with 240 tiles of 256 x 256 on 256
+//     workgroups, 4 splits (960 items) took 227 us.
 //   SB tiles or more: whole rounds of the G-workgroup resident grid run
 //     unsplit; only the rem = units % G tiles of the last, partial round are
 //     split, ks >= 4 ways with rem * ks <= G, so that the last round nearly
@@ -250,9 +255,10 @@ __host__ __device__ inline GemmSplit gemm_split(int units, int nk, int pf, int S
   auto can_split = [&](int k2) { return k2 <= 8 && nk % k2 == 0 && (nk / k2) % pf == 0 && nk / k2 >= 2 * pf; };
   if (units < SB) {
     s.whole = 0;
+    const int fit = G > 0 ? G : ST;
     while (true) {
       const int k2 = s.ks * 2;
-      if (units * k2 > kSplitCap || units * s.ks >= ST || !can_split(k2)) break;
+      if (units * k2 > fit || units * k2 > kSplitCap || !can_split(k2)) break;
       s.ks = k2;
     }
     return s;
@@ -918,11 +924,11 @@ size_t gemm_workspace_bytes(int epi, int max_rows, int N, int K) {
 // The weight-streaming tiling of a narrow output: N = 4096 features (the
 // FFN's down projection) make 64 tiles, so 64 CUs stream the weights while
 // the rest idle.  A caller that passes the partial tiles' memory
-// (GemmArgs::skinny_split) has K split until about kSkinnySplitItems work
-// items (one per CU) stream a K-slice each; the reduce pass then adds the
-// fp32 partials in split order.
+// (GemmArgs::skinny_split) has K split while the work items stay within
+// kSkinnySplitItems (one per CU), each streaming a K-slice; the reduce pass
+// then adds the fp32 partials in split order.
 constexpr int kSkinnySplitUnits = 128;  // split only outputs of fewer tiles
-constexpr int kSkinnySplitItems = 256;  // double the splits while below this many items
+constexpr int kSkinnySplitItems = 256;  // at most this many items (tiles x splits)
 size_t gemm_skinny_split_bytes(int max_rows, int N, int K) {
   if (max_rows <= 0 || max_rows > kSkinnyRows || N % 64 != 0 || K % 64 != 0 || (K / 64) % 4 != 0)
     return 0;
