@@ -287,19 +287,23 @@ def test_gqa_lock_loop_reduced(dlm):
             assert v_ <= TOL["bf16"], f"step {t} {k_}: {v_}"
 
 
-@pytest.mark.parametrize("t,bound", [(0, "exact"), (32, "exact"), (62, "exact"), (63, "exact"), (63, "loose")])
+@pytest.mark.parametrize("t,bound", [(0, "exact"), (32, "exact"), (40, "exact"), (62, "exact"), (63, "exact"),
+                                     (63, "loose")])
 def test_gqa_lock_loop_step_full_size(dlm, t, bound):
     """One step of the 64-step GQA lock loop at its full size (B = 8, S = 2048,
     D = 4096, 32 query / 8 KV heads of 128), with the row bound the benchmark's
     loop passes (the exact count) and, for the last step, the loose bound B*S.
-    The launches differ by step: t = 0 (16384 rows) and t = 32 (8480) run the
-    256 x 256 GEMM tiling unsplit, its Q/K/V epilogue inside the GEMM kernel,
-    and 128-vector attention workgroups (GQA 4:1); t = 62 (1072 rows) splits K over spare
-    workgroups (epilogue in the reduce pass); t = 63 (824 rows) runs the
-    128 x 128 body of the dual launch and a split-KV merge (the loose bound
-    the 256 x 256 tiling).  The caches hold seeded earlier rows.  Every Q row,
-    every cache row (selected against the oracle, others byte-identical) and
-    O/LSE of 48 sampled rows against the oracle."""
+    The launches differ by step: t = 0 (16384 rows, 1536 tiles of 256 x 256:
+    six whole rounds of the 256-workgroup grid) runs the GEMM unsplit, its
+    Q/K/V epilogue inside the GEMM kernel, and 128-vector attention
+    workgroups (GQA 4:1); t = 32 (8480 rows, 816 tiles) splits the 48 tiles
+    of its last round 4 ways (their epilogue in the reduce pass) and t = 40
+    (6504 rows, 624 tiles) leaves the 112 of its last round unsplit; t = 62
+    (1072 rows, 120 tiles) splits K 2 ways over spare workgroups; t = 63 (824 rows) runs
+    the 128 x 128 body of the dual launch and a split-KV merge (the loose
+    bound the 256 x 256 tiling).  The caches hold seeded earlier rows.  Every
+    Q row, every cache row (selected against the oracle, others
+    byte-identical) and O/LSE of 48 sampled rows against the oracle."""
     inp = W.lock_loop_inputs(W.GQA_LOCK_LOOP)
     s = inp.shape
     B, S = s.B, s.S
