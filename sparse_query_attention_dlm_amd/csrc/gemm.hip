@@ -60,6 +60,33 @@ __device__ __forceinline__ void epi_store4(const GemmArgs& g, int m, int drow, i
   *reinterpret_cast<u32x2*>(dst) = pk;
 }
 
+// One MFMA block's 16 accumulators, read into VGPRs where the LM-head
+// epilogues use them.  Left to itself the compiler copies all 256 accumulator
+// registers of the 256 x 256 tile out of the AGPRs together when the k-loop
+// ends, which pushes the loop's other live values to scratch (200-400 bytes
+// per lane).  The compiler does not count MFMA hazards for inline asm, so the
+// reads start with the 12 wait states it inserts itself between a 32x32x16
+// MFMA and a VALU read of its result; the AGPR inputs keep the producing
+// MFMA ahead of them.
+__device__ __forceinline__ void read_acc(const f32x16& c, float (&v)[16]) {
+  __asm__ volatile(
+      "s_nop 11\n\t"
+      "v_accvgpr_read_b32 %0, %8\n\tv_accvgpr_read_b32 %1, %9\n\t"
+      "v_accvgpr_read_b32 %2, %10\n\tv_accvgpr_read_b32 %3, %11\n\t"
+      "v_accvgpr_read_b32 %4, %12\n\tv_accvgpr_read_b32 %5, %13\n\t"
+      "v_accvgpr_read_b32 %6, %14\n\tv_accvgpr_read_b32 %7, %15"
+      : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(v[4]), "=v"(v[5]), "=v"(v[6]), "=v"(v[7])
+      : "a"(c[0]), "a"(c[1]), "a"(c[2]), "a"(c[3]), "a"(c[4]), "a"(c[5]), "a"(c[6]), "a"(c[7]));
+  __asm__ volatile(
+      "s_nop 11\n\t"
+      "v_accvgpr_read_b32 %0, %8\n\tv_accvgpr_read_b32 %1, %9\n\t"
+      "v_accvgpr_read_b32 %2, %10\n\tv_accvgpr_read_b32 %3, %11\n\t"
+      "v_accvgpr_read_b32 %4, %12\n\tv_accvgpr_read_b32 %5, %13\n\t"
+      "v_accvgpr_read_b32 %6, %14\n\tv_accvgpr_read_b32 %7, %15"
+      : "=v"(v[8]), "=v"(v[9]), "=v"(v[10]), "=v"(v[11]), "=v"(v[12]), "=v"(v[13]), "=v"(v[14]), "=v"(v[15])
+      : "a"(c[8]), "a"(c[9]), "a"(c[10]), "a"(c[11]), "a"(c[12]), "a"(c[13]), "a"(c[14]), "a"(c[15]));
+}
+
 // Epilogues on the accumulated tile.  Register i of acc[a][b] in lane l holds
 // feature n0 + wp*WTP + 32a + 8(i/4) + 4(l/32) + i%4 of token m0 + wt*WTT + 32b + l%32.
 template <int TP, int TT, int WP, int WT, int EPI, int TPV = TP>
@@ -77,14 +104,24 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
       const int drow = s_drow[ml];
       if (drow < 0) continue;
 #pragma unroll
-      for (int a = 0; a < FP; ++a)
+      for (int a = 0; a < FP; ++a) {
+        // the SwiGLU epilogue's exponentials and divisions spill the 256 x 256
+        // tile's live values when the accumulators are all copied out at once
+        float av[16];
+        if constexpr (EPI == EPI_SWIGLU && FP * FT == 16) {
+          read_acc(acc[a][b], av);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) av[i] = acc[a][b][i];
+        }
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int nl = wp * WTP + a * 32 + 8 * q4 + 4 * lg;  // feature within the tile
           if (TPV < TP && nl >= TPV) continue;                 // zero-filled padding rows
-          epi_store4<EPI>(g, m0 + ml, drow, n0 + nl, acc[a][b][4 * q4], acc[a][b][4 * q4 + 1],
-                          acc[a][b][4 * q4 + 2], acc[a][b][4 * q4 + 3]);
+          epi_store4<EPI>(g, m0 + ml, drow, n0 + nl, av[4 * q4], av[4 * q4 + 1], av[4 * q4 + 2],
+                          av[4 * q4 + 3]);
         }
+      }
     }
   } else if constexpr (EPI == EPI_LMKL) {
     // Token columns c and c + 16 of a 32-column block hold one position's
@@ -102,13 +139,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
       int am = 0x7fffffff;
 #pragma unroll
       for (int a = 0; a < FP; ++a) {
-        float cm = acc[a][b][0];
+        float av[16];
+        read_acc(acc[a][b], av);
+        float cm = av[0];
         int ca = n0 + wp * WTP + a * 32 + 4 * lg;
 #pragma unroll
         for (int i = 1; i < 16; ++i) {
           const int n = n0 + wp * WTP + a * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
-          if (acc[a][b][i] > cm) {  // rows grow with i, so ties keep the lower index
-            cm = acc[a][b][i];
+          if (av[i] > cm) {  // rows grow with i, so ties keep the lower index
+            cm = av[i];
             ca = n;
           }
         }
@@ -116,7 +155,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
         float cs = 0.f, cw = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float v = acc[a][b][i];
+          const float v = av[i];
           const float e = __builtin_amdgcn_exp2f(fmaf(v, kLog2e, -cm2));
           cs += e;
           cw = fmaf(e, v - __shfl_xor(v, 16, 64), cw);
@@ -157,19 +196,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
       const int ml = wt * WTT + b * 32 + lr;
       // running (max, sum exp(z - max), argmax) merged 16 logits at a time,
       // and for the margin the second-largest logit (the max itself when
-      // attained twice); the confidence epilogue leaves it out, as it costs
-      // registers in a kernel that already spills a little
+      // attained twice); the confidence epilogue leaves it out
       constexpr bool TOP2 = EPI == EPI_LMMARGIN;
       float m = -INFINITY, s = 0.f, t2 = -INFINITY;
       int am = 0x7fffffff;
 #pragma unroll
       for (int a = 0; a < FP; ++a) {
-        float cm = acc[a][b][0], c2 = -INFINITY;
+        float av[16];
+        read_acc(acc[a][b], av);
+        float cm = av[0], c2 = -INFINITY;
         int ca = n0 + wp * WTP + a * 32 + 4 * lg;
 #pragma unroll
         for (int i = 1; i < 16; ++i) {
           const int n = n0 + wp * WTP + a * 32 + 8 * (i >> 2) + 4 * lg + (i & 3);
-          const float v = acc[a][b][i];
+          const float v = av[i];
           if (v > cm) {  // rows grow with i, so ties keep the lower index
             if constexpr (TOP2) c2 = cm;
             cm = v;
@@ -181,7 +221,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g,
         const float cm2 = cm * kLog2e;
         float cs = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) cs += __builtin_amdgcn_exp2f(fmaf(acc[a][b][i], kLog2e, -cm2));
+        for (int i = 0; i < 16; ++i) cs += __builtin_amdgcn_exp2f(fmaf(av[i], kLog2e, -cm2));
         if constexpr (TOP2) t2 = merge_second(m, t2, cm, c2);
         merge_part(m, s, am, cm, cs, ca);
       }
