@@ -395,7 +395,8 @@ def extra_one_layer_step(dlm, W, a):
     D, N = sh.D, (s.Hq + 2 * s.Hkv) * s.hd
     qkv_bytes = N * D * 2 + n_sel * D * 2 + n_sel * N * 2
     sel_bytes = 2 * B * S * D * 2
-    attn_bytes = 2 * B * S * s.Hkv * s.hd * 2 + 2 * n_sel * s.Hq * s.hd * 2 * 2
+    # the K/V cache read once; the selected rows' Q read, their O and output-cache rows written
+    attn_bytes = 2 * B * S * s.Hkv * s.hd * 2 + 3 * n_sel * s.Hq * s.hd * 2
     attn_flops = 4.0 * n_sel * S * s.hd * s.Hq
     achieved = qkv_bytes / (stage_ms[1] / 1e3)
     digest = source_digest("gemm.hip", "common.hpp")
@@ -545,7 +546,7 @@ def extra_colsum(dlm, W, a=None):
             "colsum_topk_window_1024_keys": {"ms": t_colw, "TFLOP/s": f_col / 4 / t_colw / 1e9}}
 
 
-KERNEL_ONLY = ("attn_colsum_top64", "attn_lock_t0", "qkv_lock_t0", "lmhead_lsp")
+KERNEL_ONLY = ("attn_colsum_top64", "attn_lock_t0", "qkv_lock_t0", "lmhead_lsp", "step_s1024")
 
 
 def kernel_only(dlm, W, which, calls=10):
@@ -554,9 +555,32 @@ def kernel_only(dlm, W, which, calls=10):
     each sequence, 32 x 128 heads) or of the lock loop's first step (B=8,
     S=2048, every row, 32 query over 8 KV heads); the lock loop's first-step
     Q/K/V GEMM (16,384 rows, K=4096, N=6144); the confidence LM head of the
-    LSP workload (3,680 rows, V=32768).  Inputs are seeded N(0,1)."""
+    LSP workload (3,680 rows, V=32768); or the one-layer step (B=1, S=1024,
+    hidden 4096, 32 x 128 heads: cosine select, Q/K/V + K/V scatter, partial
+    attention + output scatter, loose row bound 1024) over four rotating
+    input sets.  Inputs are seeded N(0,1)."""
     import torch
-    if which.startswith("attn"):
+    if which == "step_s1024":
+        sh = W.BF16_S1024
+        max_rows = sh.B * sh.S
+        scale = 1.0 / math.sqrt(sh.hd)
+        sets = [StepSet(dlm, W, sh, r, max_rows) for r in range(4)]
+        rot = iter(range(1 << 30))
+
+        def call():
+            st = sets[next(rot) % len(sets)]
+            dlm.dlm_saliency_select(dlm.DLM_SCORE_COSINE, st.cur, st.prev, lo=0, hi=sh.S, threshold=sh.tau,
+                                    idx=st.idx, counts=st.counts, offsets=st.offsets, workspace=st.ws_sel)
+            dlm.dlm_gather_qkv_scatter_kv(st.cur, st.idx, st.offsets, max_rows, st.w, sh.Hq, sh.Hkv, sh.hd,
+                                          st.q, st.kc, st.vc, workspace=st.ws_qkv)
+            dlm.dlm_partial_attn(st.q, st.idx, st.offsets, max_rows, st.kc, st.vc, scale, st.o, st.lse,
+                                 out_cache=st.out, workspace=st.ws_attn)
+        call()
+        torch.cuda.synchronize()
+        n = int(sets[0].offsets[-1].item())
+        N = (sh.Hq + 2 * sh.Hkv) * sh.hd
+        flops = 2.0 * n * sh.D * N + 4.0 * n * sh.S * sh.hd * sh.Hq
+    elif which.startswith("attn"):
         sh = W.COLSUM_TOP64 if which == "attn_colsum_top64" else W.GQA_LOCK_LOOP
         B, S, Hq, Hkv, hd = sh.B, sh.S, sh.Hq, sh.Hkv, sh.hd
         lo = sh.prompt if which == "attn_colsum_top64" else 0
