@@ -14,15 +14,15 @@
 // bf16 kernel (gfx950 matrix cores), a skinny attention without a running max
 // (the cached LSE bounds every weight by about 1):
 //   * A workgroup of four (eight) waves owns 128 (256) query vectors:
-//     consecutive positions of one sequence times the G query heads of one KV
-//     head (vector v = position * G + head-in-group); each wave owns 32.
+//     consecutive stable positions of one sequence (the salient ones are
+//     skipped: the salient path recomputes them) times the G query heads of
+//     one KV head (vector v = stable rank * G + head-in-group); each wave
+//     owns 32 and finds its positions from the salient list itself.
 //   * Per 64-row tile of the salient set, K_old rows and the value change
 //     dV = v_new - v_old (rounded to bf16) are staged in LDS; S^T = K . Q^T and
 //     dO^T = dV^T . P^T run on 32x32x16 MFMAs in the layouts of the attention
 //     kernel (P^T is the B operand, dV^T comes from transposed LDS reads).
-//   * The salient positions that fall in the workgroup's own range are flagged
-//     in LDS while their rows are staged; the epilogue adds dO to the cached
-//     output of every other position.
+//   * The epilogue adds dO to the cached output of every vector's position.
 // fp32 kernel (small fp32 layers): one wave per (position, head), float32 FMA.
 #include "common.hpp"
 #include "launch.hpp"
@@ -36,6 +36,20 @@ __device__ __forceinline__ i16x4 dv_read_tr16(const u16* p) {
 }
 
 constexpr int kDvKT = 64;   // salient rows per tile
+
+// Work units are (sequence, KV head, tile of stable vectors), tiles fastest;
+// the units of one (sequence, KV head) all stream the same salient K_old,
+// V_old and new V rows.  The hardware deals a launch's workgroups round-robin
+// to the 8 XCDs, each with its own L2, so workgroup b takes unit
+// dv_xcd_unit(b, n) instead of unit b: each XCD then runs a contiguous range of
+// units and fetches a (sequence, KV head)'s rows into its L2 once.  A bijection
+// of [0, n).  Measured at B = 8, S = 2048, 32 / 8 heads, 1024 salient rows:
+// 478 -> 272 us (with the round-robin order the stable-only tiles spread every
+// XCD's resident units over twice the row sets its L2 holds).
+__device__ __forceinline__ int dv_xcd_unit(int b, int n) {
+  const int x = b & 7, a = n >> 3, c = n & 7;
+  return x * a + min(x, c) + (b >> 3);
+}
 
 // Row pitches (u16) for conflict-free LDS reads, as in the attention kernel:
 // K rows are 16-byte A-fragments read by 16 lanes on 16 consecutive rows
@@ -59,42 +73,27 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
   constexpr int RPJ = NT / CPR;        // tile rows between a thread's chunks
   constexpr int JT = kDvKT * CPR / NT; // chunks per tensor per thread
   __shared__ __attribute__((aligned(16))) u16 smem[DvLds<HD>::WORDS];
-  __shared__ int sflag[QT];
   u16* sK = smem;
   u16* sV = smem + kDvKT * PITCH;
 
   const int G = a.Hq / a.Hkv;
   const int tiles = (a.S * G + QT - 1) / QT;
-  const int t = blockIdx.x % tiles;
-  const int g = (blockIdx.x / tiles) % a.Hkv;
-  const int b = blockIdx.x / (tiles * a.Hkv);
+  const int unit = dv_xcd_unit((int)blockIdx.x, (int)gridDim.x);
+  const int t = unit % tiles;
+  const int g = (unit / tiles) % a.Hkv;
+  const int b = unit / (tiles * a.Hkv);
   const int r0 = min(a.offsets[b], a.max_rows), r1 = min(a.offsets[b + 1], a.max_rows);
   const int nb = r1 - r0;
   if (nb <= 0) return;  // no salient rows: every output stays
+  const int nstable = a.S - nb;  // positions outside the salient set
+  if ((long long)t * QT >= (long long)nstable * G) return;  // this tile holds no stable position
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
-  // positions [p_lo, p_lo + QT / G) belong to this workgroup
-  const int p_lo = t * QT / G;
-  const int vq = t * QT + wave * 32 + lr;
-  const bool qvalid = vq < a.S * G;
-  const int vqc = qvalid ? vq : a.S * G - 1;
-  const int pos = vqc / G, h = g * G + vqc % G;
-  if (tid < QT) sflag[tid] = 0;
-
-  const size_t qrow = ((size_t)b * a.S + pos) * a.Hq + h;
-  bf16x8 qf[NS];
-  {
-    const u16* qp = static_cast<const u16*>(a.q) + qrow * HD + lg * 8;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s));
-  }
-  const float c = a.scale * kLog2e;
-  const float l2 = a.lse[qrow] * kLog2e;
-
-  f32x16 acc[NDB];
-#pragma unroll
-  for (int d = 0; d < NDB; ++d) acc[d] = f32x16{};
-
+  // Vector v is (stable rank v / G, head v % G of the group).  Stable rank r
+  // sits at position r + J(r), J(r) = #{j : f(j) <= r} with f(j) = idx[j] - j,
+  // the number of stable positions before salient row j (non-decreasing along
+  // the ascending positions).  J <= nb and r < nstable keep every position
+  // inside the sequence whatever the index list holds.
   const u16* kold = static_cast<const u16*>(a.k_old);
   const u16* vold = static_cast<const u16*>(a.v_old);
   const u16* vcache = static_cast<const u16*>(a.v);
@@ -104,7 +103,7 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
   // sits at its position idx[r]: the positions are loaded one tile ahead of
   // the rows, so no tile waits for two memory round trips in a row.
   u32x4 kr[JT], vn[JT], vo[JT];
-  int rpos[JT], pnext[JT];
+  int pnext[JT];
   // branch-free: a row past the salient set reads the set's first row and is
   // then zeroed
   auto row_of = [&](int k0, int j) {
@@ -124,7 +123,6 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
       const u32x4 o = *reinterpret_cast<const u32x4*>(vold + (r * a.Hkv + g) * HD + ch * 8);
       const u32x4 n = *reinterpret_cast<const u32x4*>(vcache + (((size_t)b * a.S + ps[j]) * a.Hkv + g) * HD + ch * 8);
       const u32x4 z = u32x4{0, 0, 0, 0};
-      rpos[j] = ok ? ps[j] : -1;
       kr[j] = ok ? k : z;
       vo[j] = ok ? o : z;
       vn[j] = ok ? n : z;
@@ -136,6 +134,56 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
     load_tile(0, p0);
   }
   if (kDvKT < nb) load_pos(kDvKT, pnext);
+  const int vq = t * QT + wave * 32 + lr;
+  const bool qvalid = vq < nstable * G;
+  const int vqc = qvalid ? vq : nstable * G - 1;
+  const int rank = vqc / G, h = g * G + vqc % G;
+  const int rw0 = min(t * QT + wave * 32, nstable * G - 1) / G;       // the wave's ranks
+  const int rw1 = min(t * QT + wave * 32 + 31, nstable * G - 1) / G;
+  const int32_t* sidx = a.idx + r0;
+  // Skip the salient rows before the wave's first rank by a 64-way search
+  // (each lane probes one point of the interval, a ballot counts the probes
+  // with f <= rw0: a prefix of the lanes) until one 64-entry window is left:
+  // every row below lo then has f <= rw0.
+  int lo = 0, hi = nb;
+  while (hi - lo > 64) {
+    const int step = (hi - lo + 63) >> 6;
+    const int j = lo + lane * step;
+    const int cnt_le = __popcll(__ballot(j < hi && sidx[min(j, nb - 1)] - j <= rw0));
+    if (cnt_le == 0) break;  // f(lo) > rw0 already
+    hi = min(hi, lo + cnt_le * step);
+    lo += (cnt_le - 1) * step + 1;
+  }
+  // J(rank) - lo for each lane's rank from 64-entry windows of the salient list
+  // from lo on, one ballot per rank of the wave (at most 32 of them)
+  int extra = 0;
+  for (int base = lo; base < nb; base += 64) {
+    const int k = base + lane;
+    const int fk = k < nb ? sidx[k] - k : 0x7fffffff;
+    bool full = false;
+    for (int rr = rw0; rr <= rw1; ++rr) {
+      const unsigned long long m = __ballot(fk <= rr);
+      if (rank == rr) extra += __popcll(m);
+      if (rr == rw1) full = m == ~0ull;
+    }
+    if (!full) break;  // the window reaches past the wave's last rank
+  }
+  const int pos = rank + lo + extra;
+
+  const size_t qrow = ((size_t)b * a.S + pos) * a.Hq + h;
+  bf16x8 qf[NS];
+  {
+    const u16* qp = static_cast<const u16*>(a.q) + qrow * HD + lg * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s));
+  }
+  const float c = a.scale * kLog2e;
+  const float l2 = a.lse[qrow] * kLog2e;
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) acc[d] = f32x16{};
+
   for (int k0 = 0; k0 < nb; k0 += kDvKT) {
     __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
@@ -149,8 +197,6 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
       for (int e = 0; e < 4; ++e) dv[e] = pack_bf16x2(fn[2 * e] - fo[2 * e], fn[2 * e + 1] - fo[2 * e + 1]);
       *reinterpret_cast<u32x4*>(sK + rl * PITCH + ch * 8) = kr[j];
       *reinterpret_cast<u32x4*>(sV + rl * VPITCH + ch * 8) = dv;
-      // one chunk column flags the salient positions inside this workgroup's range
-      if (ch == 0 && rpos[j] >= p_lo && rpos[j] - p_lo < QT / G) sflag[rpos[j] - p_lo] = 1;
     }
     __syncthreads();
     // the next tile streams in during this tile's math, and the positions of
@@ -211,8 +257,7 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
         }
       }
   }
-  __syncthreads();  // the flags of every tile are in
-  if (!qvalid || sflag[pos - p_lo]) return;
+  if (!qvalid) return;
   // o += dO: register i of block d holds dimension 32 d + 8 (i / 4) + 4 lg + i % 4
   u16* op = static_cast<u16*>(a.o) + qrow * HD;
   u32x2 oin[NDB][4];  // all of the lane's cached output words in flight at once
