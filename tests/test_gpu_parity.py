@@ -885,7 +885,7 @@ def test_mfma_probe_matches_closed_form(dlm):
 # ---------------------------------------------------------------------------
 # non-salient value-change update, and the row copies that keep its caches
 # ---------------------------------------------------------------------------
-def run_dv_update(dlm, B, S, Hq, Hkv, hd, n_per_b, dtype="bf16", seed=31, loose_bound=None):
+def run_dv_update(dlm, B, S, Hq, Hkv, hd, n_per_b, dtype="bf16", seed=31, loose_bound=None, sal=None):
     """Previous step: each position's query and LSE over the old K (its last
     computation) and a cached output.  This step: the salient rows get new V.
     On the device the old K/V rows are gathered from the caches before the new
@@ -906,7 +906,11 @@ def run_dv_update(dlm, B, S, Hq, Hkv, hd, n_per_b, dtype="bf16", seed=31, loose_
             lse[b, :, h] = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
     lse = lse.astype(np.float32).astype(np.float64)
     o = rnd(0.5 * rng.standard_normal((B, S, Hq, hd)))
-    sal = [np.sort(rng.choice(S, n, replace=False)).astype(np.int32) for n in n_per_b]
+    if sal is None:
+        sal = [np.sort(rng.choice(S, n, replace=False)).astype(np.int32) for n in n_per_b]
+    else:
+        sal = [np.asarray(x, np.int32) for x in sal]
+        n_per_b = [len(x) for x in sal]
     idx = np.concatenate(sal).astype(np.int32)
     offsets = np.concatenate([[0], np.cumsum(n_per_b)]).astype(np.int32)
     v_new_c = v_old_c.copy()
@@ -958,6 +962,23 @@ def test_dv_update_wide_workgroups(dlm, hd):
     """Enough position tiles (B = 2, S = 2048, GQA 32/8) for the 256-vector
     workgroups; salient sets of 300 and 777 rows (ragged last tiles)."""
     run_dv_update(dlm, B=2, S=2048, Hq=32, Hkv=8, hd=hd, n_per_b=[300, 777], seed=37)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4)])
+def test_dv_update_clustered_and_dense_salient_sets(dlm, Hq, Hkv):
+    """Salient sets that a wave's stable positions must be found around: a run
+    of 300 consecutive salient positions among scattered ones (a wave whose
+    ranks straddle the run reads several 64-row windows of the salient list),
+    95 % salient, all but three salient, and every position salient (nothing
+    to update in that sequence)."""
+    S = 700
+    rng = np.random.default_rng(39)
+    scattered = rng.choice(np.setdiff1d(np.arange(S), np.arange(100, 400)), 20, replace=False)
+    sal = [np.sort(np.concatenate([np.arange(100, 400), scattered])),
+           np.sort(rng.choice(S, 665, replace=False)),
+           np.setdiff1d(np.arange(S), [0, 350, 699]),
+           np.arange(S)]
+    run_dv_update(dlm, B=4, S=S, Hq=Hq, Hkv=Hkv, hd=128, n_per_b=None, seed=40, sal=sal)
 
 
 def test_dv_update_loose_row_bound(dlm):
