@@ -89,15 +89,12 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
   if ((long long)t * QT >= (long long)nstable * G) return;  // this tile holds no stable position
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
-  // Vector v is (stable rank v / G, head v % G of the group).  Stable rank r
-  // sits at position r + J(r), J(r) = #{j : f(j) <= r} with f(j) = idx[j] - j,
-  // the number of stable positions before salient row j (non-decreasing along
-  // the ascending positions).  J <= nb and r < nstable keep every position
-  // inside the sequence whatever the index list holds.
   const u16* kold = static_cast<const u16*>(a.k_old);
   const u16* vold = static_cast<const u16*>(a.v_old);
   const u16* vcache = static_cast<const u16*>(a.v);
   const int ch = tid % CPR;
+  // The first salient tiles' loads go out before the positions of this
+  // workgroup's vectors are searched (they do not depend on them).
   // staging registers of one tile: chunk ch of tile rows tid / CPR + RPJ j
   // (rows past the salient set give zeros and position -1).  A row's new V
   // sits at its position idx[r]: the positions are loaded one tile ahead of
@@ -134,6 +131,12 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
     load_tile(0, p0);
   }
   if (kDvKT < nb) load_pos(kDvKT, pnext);
+
+  // Vector v is (stable rank v / G, head v % G of the group).  Stable rank r
+  // sits at position r + J(r), J(r) = #{j : f(j) <= r} with f(j) = idx[j] - j,
+  // the number of stable positions before salient row j (non-decreasing along
+  // the ascending positions).  J <= nb and r < nstable keep every position
+  // inside the sequence whatever the index list holds.
   const int vq = t * QT + wave * 32 + lr;
   const bool qvalid = vq < nstable * G;
   const int vqc = qvalid ? vq : nstable * G - 1;
