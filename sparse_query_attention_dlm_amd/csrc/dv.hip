@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
   // The first salient tiles' loads go out before the positions of this
   // workgroup's vectors are searched (they do not depend on them).
   // staging registers of one tile: chunk ch of tile rows tid / CPR + RPJ j
-  // (rows past the salient set give zeros and position -1).  A row's new V
+  // (rows past the salient set give zeros).  A row's new V
   // sits at its position idx[r]: the positions are loaded one tile ahead of
   // the rows, so no tile waits for two memory round trips in a row.
   u32x4 kr[JT], vn[JT], vo[JT];
