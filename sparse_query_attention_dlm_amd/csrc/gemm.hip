@@ -751,14 +751,14 @@ __device__ __forceinline__ void gemm_tile_work(const GemmArgs& g, int n_rows, u1
 // GATE: 0 = always run; 1 = run only when the device row count is <= kSkinnyRows;
 // 2 = run only when it is larger.
 template <int TP, int TT, int WP, int WT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST,
-          int WK = 1>
+          int WK = 1, int TPV = TP>
 __global__ __launch_bounds__(256 * WK) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) u16 lds[gemm_lds_u16(TP, TT, BK)];
   __shared__ uint32_t s_xoff[TT];
   __shared__ int s_drow[TT];
   const int n_rows = min(g.offsets[g.B], g.max_rows);
   if ((GATE == 1 && n_rows > kSkinnyRows) || (GATE == 2 && n_rows <= kSkinnyRows)) return;
-  gemm_tile_body<TP, TT, WP, WT, BK, PF, EPI, AMODE, SB, ST, WK>(g, n_rows, lds, s_xoff, s_drow);
+  gemm_tile_body<TP, TT, WP, WT, BK, PF, EPI, AMODE, SB, ST, WK, TPV>(g, n_rows, lds, s_xoff, s_drow);
 }
 
 // One launch for a host that only knows a loose row bound: the device row
@@ -993,13 +993,15 @@ static int persistent_grid(int items, int TP, int TT) {
   return items < resident ? items : resident;
 }
 
-template <int TP, int TT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST, int WK = 1>
+template <int TP, int TT, int BK, int PF, int EPI, int AMODE, int GATE, int SB, int ST, int WK = 1,
+          int TPV = TP>
 static void launch_bf16(const GemmArgs& g, hipStream_t st) {
+  static_assert(SB == 0 || TPV == TP, "split tiles own all their weight rows");
   // every output tile (and every split the device may choose when the real
   // selection turns out short) is a work item; the two-k-half tiling runs one
   // item per workgroup, the others loop over a resident grid
   const int m_tiles_max = (gemm_token_rows(EPI, g.max_rows) + TT - 1) / TT;
-  int items = (g.N / TP) * m_tiles_max;
+  int items = (g.N / TPV) * m_tiles_max;
   if (SB > 0) {
     const int cap = ST < kSplitCap ? 2 * ST : kSplitCap;
     if (WK == 2 && m_tiles_max <= 1)
@@ -1010,8 +1012,8 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
   const int grid = WK == 1 ? persistent_grid(items, TP, TT) : items;
   GemmArgs ga = g;
   ga.tile_grid = grid;  // the split plan fills the last round of this grid
-  hipLaunchKernelGGL((gemm_bf16_kernel<TP, TT, 2, 2, BK, PF, EPI, AMODE, GATE, SB, ST, WK>), dim3(grid),
-                     dim3(256 * WK), 0, st, ga);
+  hipLaunchKernelGGL((gemm_bf16_kernel<TP, TT, 2, 2, BK, PF, EPI, AMODE, GATE, SB, ST, WK, TPV>),
+                     dim3(grid), dim3(256 * WK), 0, st, ga);
   if (SB > 0) launch_reduce<TP, TT, 2, 2, BK, PF, EPI, AMODE, GATE, SB, ST>(ga, st);
 }
 
@@ -1026,7 +1028,12 @@ static void launch_skinny(const GemmArgs& g, hipStream_t st) {
       return;
     }
   }
-  if (pf_for(g.K / 64, 4) == 4)
+  // 48 weight rows per tile when they divide N, as in the dual launch: the
+  // 24576 gate/up features of the salient FFN make 512 tiles, two per CU,
+  // instead of 384 tiles that leave half the CUs with one
+  if (pf_for(g.K / 64, 4) == 4 && g.N % 48 == 0)
+    launch_bf16<64, 128, 64, 4, EPI, AMODE, GATE, 0, 0, 2, 48>(g, st);
+  else if (pf_for(g.K / 64, 4) == 4)
     launch_bf16<64, 128, 64, 4, EPI, AMODE, GATE, 0, 0, 2>(g, st);
   else if (pf_for(g.K / 64, 4) == 2)
     launch_bf16<64, 128, 64, 2, EPI, AMODE, GATE, 0, 0>(g, st);
