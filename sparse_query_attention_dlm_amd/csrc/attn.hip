@@ -45,17 +45,22 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const u16* p) {
 // Work plan shared by the attention and merge kernels, computed on the device
 // from the selection counts (the host only knows an upper bound):
 //   units  = sum_b ceil(n_b * G / QT) query tiles of QT vectors, times Hkv
-//   nsplit = 1 when units >= kSplitTarget, else ceil(kSplitTarget / units)
-//            capped at 16 and at S/256, so short selections still spread
-//            their K/V reads over the whole GPU (one CU streams only a few
-//            tens of GB/s, so a few workgroups cannot read a long cache fast);
-//            the merge pass combines the split partials by their LSE.  Each
-//            split keeps at least 256 keys: shorter ones cost more in partial
-//            outputs (written and merged) than they gain in spread.
+//   nsplit = CUs / units (rounded down) when at least two splits fit one
+//            workgroup per CU, else 1; capped at 16 and at S/256.  So short
+//            selections still spread their K/V reads over the whole GPU (one
+//            CU streams only a few tens of GB/s, so a few workgroups cannot
+//            read a long cache fast); the merge pass combines the split
+//            partials by their LSE.  Splitting further, to two workgroups per
+//            CU, gains nothing in these short launches (a CU's second
+//            workgroup adds no throughput here) and costs partial outputs,
+//            written and merged: measured at B = 8, S = 2048, 32/8 heads,
+//            256 units took 51.7 us unsplit and 62.3 us in two splits, 192
+//            units 49.9 against 62.2 us in three.  Each split keeps at least
+//            256 keys: shorter ones cost more in partials than they gain.
 // A last cap keeps nsplit * n_rows * Hq <= kPartRows, the bound the
 // workspace is sized for.
-constexpr int kSplitTarget = 512;
-constexpr int kPartRows = 2 * kSplitTarget * 128;
+constexpr int kShortUnits = 512;  // a row bound of fewer 128-vector tiles: a short selection
+constexpr int kPartRows = 2 * kShortUnits * 128;
 constexpr int kAttnKT = 64;      // keys per K/V tile
 constexpr int kMinSplitKeys = 256;  // keys per split at least
 constexpr float kLaneSumCap = 0x1p64f;  // a lane's tile sum above this: rescale
@@ -79,8 +84,8 @@ __device__ __forceinline__ AttnPlan attn_plan(const AttnArgs& a, int QT) {
   p.units = tiles * a.Hkv;
   p.n_rows = min(a.offsets[a.B], a.max_rows);
   int ns = 1;
-  if (p.units > 0 && p.units < kSplitTarget) {
-    ns = (kSplitTarget + p.units - 1) / p.units;
+  if (p.units > 0 && 2 * p.units <= a.split_fill) {
+    ns = a.split_fill / p.units;
     ns = min(ns, 16);
     ns = min(ns, max(1, a.S / kMinSplitKeys));
     if (p.n_rows > 0) ns = min(ns, max(1, kPartRows / (p.n_rows * a.Hq)));
@@ -663,8 +668,8 @@ hipError_t launch_attn(int dtype, const AttnArgs& a0, void* workspace, hipStream
   const bool may_split = a.S >= 2 * kMinSplitKeys;
   a.part_o = may_split ? static_cast<float*>(workspace) : nullptr;
   a.part_lse = may_split ? a.part_o + (size_t)kPartRows * a.hd : nullptr;
-  // A bound of fewer than kSplitTarget 128-vector tiles means the device
-  // always splits the keys (short selections): 128-vector workgroups.
+  // A bound of fewer than kShortUnits 128-vector tiles (a short selection,
+  // which the device may split along the keys): 128-vector workgroups.
   // Otherwise, with fewer than 4 query heads per KV head, 256-vector
   // workgroups, which halve the K/V re-reads.  With 4 or more the K/V bytes
   // per query are already a quarter of MHA's, and 128-vector workgroups (two
@@ -675,11 +680,12 @@ hipError_t launch_attn(int dtype, const AttnArgs& a0, void* workspace, hipStream
   auto max_units = [&](int QT) {
     return (ceil_div((long long)a.max_rows * G, QT) + a.B - 1) * (long long)a.Hkv;
   };
-  const bool wide = G < 4 && !(may_split && max_units(128) < kSplitTarget);
+  const bool wide = G < 4 && !(may_split && max_units(128) < kShortUnits);
   const int QT = wide ? 256 : 128;
   // enough workgroups for every tile and for the split factor the device may
-  // choose (units < kSplitTarget splits into fewer than 2 * kSplitTarget)
-  const int grid = (int)max_units(QT) + 2 * kSplitTarget;
+  // choose (split units fill at most one workgroup per CU)
+  a.split_fill = device_cus();
+  const int grid = (int)max_units(QT) + a.split_fill;
   const int threads = wide ? 512 : 256;
   if (a.hd == 64) {
     if (wide)

@@ -105,6 +105,7 @@ struct AttnArgs {
   void* ctx_out;            // out_cache [B][S][Hq*hd] or null (no W_o)
   float* part_o;            // split-KV partials (workspace)
   float* part_lse;
+  int split_fill;           // set by the launcher: CUs of the device (the split plan fills them)
 };
 size_t attn_workspace_bytes(int dtype, int max_rows, int B, int S, int Hq, int Hkv, int hd);
 hipError_t launch_attn(int dtype, const AttnArgs& a, void* workspace, hipStream_t st);

@@ -300,8 +300,9 @@ def test_gqa_lock_loop_step_full_size(dlm, t, bound):
     of its last round 4 ways (their epilogue in the reduce pass) and t = 40
     (6504 rows, 624 tiles) leaves the 112 of its last round unsplit; t = 62
     (1072 rows, 120 tiles) splits K 2 ways over spare workgroups; t = 63 (824 rows) runs
-    the 128 x 128 body of the dual launch and a split-KV merge (the loose
-    bound the 256 x 256 tiling).  The caches hold seeded earlier rows.  Every
+    the 128 x 128 body of the dual launch (the loose bound the 256 x 256
+    tiling), and its 256 attention units, one per CU, leave the keys unsplit.
+    The caches hold seeded earlier rows.  Every
     Q row, every cache row (selected against the oracle, others
     byte-identical) and O/LSE of 48 sampled rows against the oracle."""
     inp = W.lock_loop_inputs(W.GQA_LOCK_LOOP)
@@ -455,6 +456,14 @@ def test_attention_few_tiles_split_keys(dlm, hd):
     (more than 8, the merge's second register layout) and the LSE merge pass;
     every row against the oracle."""
     run_attention_plan(dlm, B=2, S=4200, Hq=4, Hkv=2, hd=hd, rows_per_b=[37, 5])
+
+
+def test_attention_two_key_splits(dlm):
+    """128 query tiles (B = 8, 33-64 rows each, GQA 4:1) on 256 CUs: the keys
+    split exactly 2 ways (the merge's two-slot layout); sampled rows against
+    the oracle."""
+    run_attention_plan(dlm, B=8, S=2048, Hq=32, Hkv=8, hd=128, rows_per_b=[64, 40, 33, 50, 64, 61, 37, 48],
+                       sample=64)
 
 
 @pytest.mark.parametrize("rows_per_b", [[40, 17], [2048, 1900]])
