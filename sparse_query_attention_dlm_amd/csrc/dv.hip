@@ -187,7 +187,10 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
 #pragma unroll
   for (int d = 0; d < NDB; ++d) acc[d] = f32x16{};
 
-  for (int k0 = 0; k0 < nb; k0 += kDvKT) {
+  // One tile of the salient set.  `masked` (a std::integral_constant)
+  // compiles the zero weights of rows past the salient set in, for the
+  // partial last tile only: full tiles skip the ~64 compares and selects.
+  auto tile = [&](int k0, auto masked) {
     __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
     for (int j = 0; j < JT; ++j) {
@@ -238,8 +241,11 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int i = 2 * j + u;
-          const int key = 32 * kb + 8 * (i >> 2) + 4 * lg + (i & 3);
-          e[u] = key < nvalid ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -l2)) : 0.f;
+          e[u] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -l2));
+          if constexpr (decltype(masked)::value) {
+            const int key = 32 * kb + 8 * (i >> 2) + 4 * lg + (i & 3);
+            if (key >= nvalid) e[u] = 0.f;
+          }
         }
         pw[kb][j >> 2][j & 3] = pack_bf16x2(e[0], e[1]);
       }
@@ -259,7 +265,10 @@ __global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void dv_update_bf16_kern
           acc[d] = mfma32x32x16(av, as_bf16x8(pw[kb][cc]), acc[d]);
         }
       }
-  }
+  };
+  int k0 = 0;
+  for (; k0 + kDvKT <= nb; k0 += kDvKT) tile(k0, std::false_type{});
+  if (k0 < nb) tile(k0, std::true_type{});
   if (!qvalid) return;
   // o += dO: register i of block d holds dimension 32 d + 8 (i / 4) + 4 lg + i % 4
   u16* op = static_cast<u16*>(a.o) + qrow * HD;
