@@ -341,8 +341,11 @@ __global__ __launch_bounds__(256) void dv_update_f32_kernel(DvArgs a) {
 }
 
 // Row gather (rows[r] = cache[b, idx[r]]) or scatter (cache[b, idx[r]] =
-// rows[r]) of row_bytes per row, one workgroup per selected row (grid-stride);
-// T is the copy unit (16 or 4 bytes).
+// rows[r]) of row_bytes per row, one workgroup per selected row (grid-stride
+// past 16384 rows, so every row's position lookup starts at once); T is the
+// copy unit (16 or 4 bytes).  Loads and stores are non-temporal: each byte is
+// touched once, and the streamed rows do not evict what the next kernel reads
+// from the caches.
 template <typename T>
 __global__ __launch_bounds__(256) void row_copy_kernel(const char* src, char* dst, const int32_t* idx,
                                                        const int32_t* offsets, int max_rows, int B,
@@ -360,10 +363,10 @@ __global__ __launch_bounds__(256) void row_copy_kernel(const char* src, char* ds
       T v[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if (u0 + 256 * k < units) v[k] = s[u0 + 256 * k];
+        if (u0 + 256 * k < units) v[k] = __builtin_nontemporal_load(s + u0 + 256 * k);
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if (u0 + 256 * k < units) d[u0 + 256 * k] = v[k];
+        if (u0 + 256 * k < units) __builtin_nontemporal_store(v[k], d + u0 + 256 * k);
     }
   }
 }
@@ -404,7 +407,7 @@ hipError_t launch_dv_update(int dtype, const DvArgs& a, hipStream_t st) {
 hipError_t launch_row_copy(const void* src, void* dst, const int32_t* idx, const int32_t* offsets,
                            int max_rows, int B, int S, int row_bytes, int scatter, hipStream_t st) {
   if (max_rows <= 0) return hipSuccess;
-  const int grid = max_rows < 4096 ? max_rows : 4096;
+  const int grid = max_rows < 16384 ? max_rows : 16384;
   const char* s = static_cast<const char*>(src);
   char* d = static_cast<char*>(dst);
   if (row_bytes % 16 == 0)
