@@ -1030,6 +1030,33 @@ def test_row_copies_four_byte_rows(dlm):
     assert np.array_equal(cd.cpu().numpy(), O.scatter_rows(new, idx, offsets, cache))
 
 
+def test_row_copies_more_rows_than_workgroups(dlm):
+    """22,793 selected rows of 16-byte units (more rows than the copy's
+    16,384 workgroups, so most workgroups copy a second row; a ragged split
+    over 13 batch rows, one of them empty) with a loose bound: gather and
+    scatter bit-exact against the oracle, unselected rows untouched."""
+    rng = np.random.default_rng(37)
+    B, S, H = 13, 2500, 24  # 96-byte rows: six 16-byte units
+    keep = [rng.random(S) < f for f in np.linspace(0.5, 1.0, B)]
+    keep[4][:] = False
+    idx = np.concatenate([np.nonzero(k)[0] for k in keep]).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum([k.sum() for k in keep])]).astype(np.int32)
+    n = int(offsets[-1])
+    say(f"[row copies] B={B} S={S} rows={n} bound={n + 100}")
+    assert n > 16384 + 4096
+    cache = rng.standard_normal((B, S, H)).astype(np.float32)
+    cd = torch.from_numpy(cache).cuda()
+    rows = torch.full((n + 100, H), -3.0, dtype=torch.float32, device="cuda")
+    dlm.dlm_gather_rows(cd, i32(idx), i32(offsets), n + 100, rows)
+    new = rng.standard_normal((n, H)).astype(np.float32)
+    dlm.dlm_scatter_rows(torch.from_numpy(new).cuda(), i32(idx), i32(offsets), n, cd)
+    torch.cuda.synchronize()
+    got = rows.cpu().numpy()
+    assert np.array_equal(got[:n], O.gather_rows(cache, idx, offsets))
+    assert np.all(got[n:] == -3.0), "rows past the selection were written"
+    assert np.array_equal(cd.cpu().numpy(), O.scatter_rows(new, idx, offsets, cache))
+
+
 # ---------------------------------------------------------------------------
 # FFN of the salient rows (SwiGLU; gate and up interleaved by row)
 # ---------------------------------------------------------------------------
