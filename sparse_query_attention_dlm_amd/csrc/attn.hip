@@ -12,10 +12,11 @@
 //     waves) serve MHA-like selections (fewer than 4 query heads per KV head)
 //     with many query tiles: every K/V tile is read from L2 once per 256
 //     vectors instead of once per 128.
-//   * Per 64-key tile, K and V come in through buffer loads (one tile ahead,
-//     in registers) and are staged in LDS; every wave computes the transposed
-//     score tiles S^T = K . Q^T (32 keys x 32 queries each) with 32x32x16
-//     MFMAs; Q^T stays in registers for the whole key loop.  The key mask is
+//   * Per 64-key tile (32-key tiles for long GQA selections at head dim 128,
+//     which then run three workgroups per CU), K and V come in through buffer
+//     loads (one tile ahead, in registers) and are staged in LDS; every wave
+//     computes the transposed score tiles S^T = K . Q^T (32 keys x 32 queries
+//     each) with 32x32x16 MFMAs; Q^T stays in registers for the whole key loop.  The key mask is
 //     compiled only into the copy of the tile math that runs the split's
 //     partial last tile.
 //   * In that layout a lane holds 16 keys of one query, so the running max and
@@ -61,7 +62,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const u16* p) {
 // workspace is sized for.
 constexpr int kShortUnits = 512;  // a row bound of fewer 128-vector tiles: a short selection
 constexpr int kPartRows = 2 * kShortUnits * 128;
-constexpr int kAttnKT = 64;      // keys per K/V tile
+constexpr int kAttnKT = 64;      // keys per K/V tile (and the split granule)
 constexpr int kMinSplitKeys = 256;  // keys per split at least
 constexpr float kLaneSumCap = 0x1p64f;  // a lane's tile sum above this: rescale
 constexpr int kMergeGrid = 1024; // workgroups of the merge pass (grid-stride)
@@ -98,7 +99,7 @@ __device__ __forceinline__ AttnPlan attn_plan(const AttnArgs& a, int QT) {
 }
 
 // LDS of the attention kernel (u16 elements)
-template <int HD>
+template <int HD, int KT = kAttnKT>
 // Row pitches (u16) chosen for conflict-free LDS access:
 //   K rows are read as 16-byte A-fragments by 16 lanes on 16 consecutive rows:
 //     a pitch of HD + 8 moves each row by 4 banks (HD = 128) or 36 banks (64).
@@ -108,7 +109,7 @@ template <int HD>
 struct AttnLds {
   static constexpr int KPITCH = HD + 8;
   static constexpr int VPITCH = HD + 32;
-  static constexpr int WIDE = kAttnKT * (KPITCH + VPITCH);
+  static constexpr int WIDE = KT * (KPITCH + VPITCH);
 };
 
 // Locate the (batch row, kv head, query tile) of a unit: tiles of QT query
@@ -213,11 +214,12 @@ __device__ __forceinline__ void attn_pv_block(const u16* sV, int kb0, const u32x
 // QT = 128*WQ query vectors per workgroup of 4*WQ waves (wave w owns vectors
 // 32w..32w+31) share every 64-key tile of the split: each tile is read from
 // L2 once per QT vectors, so WQ = 2 halves the K/V bytes a CU pulls per flop.
-template <int HD, int WQ>
+template <int HD, int WQ, int KT>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& plan, u16* smem) {
   constexpr int QT = 128 * WQ;   // query vectors per workgroup
   constexpr int NT = 256 * WQ;   // threads per workgroup
-  constexpr int KT = kAttnKT;    // keys per tile (two 32-key MFMA blocks)
+  constexpr int NKB = KT / 32;   // 32-key MFMA blocks per tile (1 or 2)
+  static_assert(KT == 32 || KT == 64, "tiles of one or two 32-key blocks");
   constexpr int PITCH = AttnLds<HD>::KPITCH, VPITCH = AttnLds<HD>::VPITCH;  // u16 per LDS row
   constexpr int NS = HD / 16;    // k-chunks of Q.K^T
   constexpr int NDB = HD / 32;   // 32-row blocks of O^T
@@ -281,13 +283,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
   // One K/V tile's scores, online softmax and P.V.  `masked` (a
   // std::integral_constant) compiles the key mask in for the last, partial tile.
   auto tile_math = [&](int nvalid, auto masked) {
-    // the two 32-key blocks' MFMA chains alternate, so each MFMA issues two
-    // slots after the one it depends on (a lone chain waits out its latency)
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    // with two 32-key blocks their MFMA chains alternate, so each MFMA issues
+    // two slots after the one it depends on (a lone chain waits out its
+    // latency; with one block per tile the third wave of the SIMD covers it)
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8 kf = as_bf16x8(
             *reinterpret_cast<const u32x4*>(sK + (32 * kb + lr) * PITCH + 16 * s + 8 * lg));
         sacc[kb] = mfma32x32x16(kf, qf[s], sacc[kb]);
@@ -298,14 +303,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
     // right before its MFMA and waits out the whole LDS latency 16 times)
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * NS - 4; ++i) {
+    for (int i = 0; i < NKB * NS - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     if constexpr (decltype(masked)::value) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 32 * kb + 8 * (i >> 2) + 4 * lg + (i & 3);
@@ -325,12 +330,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
     // P.V operand), and the lane sum adds those pairs with v_dot2_f32_bf16
     // against (1, 1): 16 instructions for 32 values instead of 32 adds, and
     // the sum holds exactly the weights that P.V applies.
-    u32x4 pw[2][2];
+    u32x4 pw[NKB][2];
     auto tile_exp = [&]() {
       const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
       float lq[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums (short dependency chains)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][2 * j], c, -m_run));
@@ -346,12 +351,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
       // tile max: four independent partial maxima (short dependency chains),
       // then the lane pair that holds the other half of the query's keys
       float mq[4];
+      constexpr int PER = 8 * NKB / 2;  // registers per partial maximum
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mq[j] = fmaxf(sacc[j >> 1][8 * (j & 1)], sacc[j >> 1][8 * (j & 1) + 1]);
+      for (int j = 0; j < 4; ++j) {
+        const f32x16& sa = sacc[(j * PER) / 16];
+        const int i0 = (j * PER) % 16;
+        mq[j] = fmaxf(sa[i0], sa[i0 + 1]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 2; i < 8; ++i) mq[j] = fmaxf(mq[j], sacc[j >> 1][8 * (j & 1) + i]);
+        for (int i = 2; i < PER; ++i) mq[j] = fmaxf(mq[j], sa[i0 + i]);
+      }
       const float mt = pair_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
       // the first tile of a split always holds a valid key, so m_run leaves
       // -inf there (alpha = 0 on the empty sums)
@@ -367,7 +375,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
     }
     l_run += lt;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) attn_pv_block<HD>(sV, 32 * kb, pw[kb], acc, lane);
+    for (int kb = 0; kb < NKB; ++kb) attn_pv_block<HD>(sV, 32 * kb, pw[kb], acc, lane);
   };
 
   if (kbeg < kend) load_tile(kbeg);
@@ -410,12 +418,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& pla
 // splits spread the K/V stream over the CUs, and GQA with 4 or more query
 // heads per KV head); WQ = 2: 256 query vectors in eight waves, one workgroup
 // per CU (MHA-like selections with many query tiles, where every tile of K/V
-// is re-read by each query tile of its head from L2).
-template <int HD, int WQ>
-__global__ __launch_bounds__(256 * WQ, WQ == 1 ? 2 : 1) void attn_fwd_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 smem[AttnLds<HD>::WIDE];
+// is re-read by each query tile of its head from L2).  KT = 32: one 32-key
+// block per tile, which needs 168 VGPRs instead of 221, so three workgroups
+// share a CU (three waves per SIMD, from different workgroups); for the long
+// GQA selections at head dim 128.
+template <int HD, int WQ, int KT>
+__global__ __launch_bounds__(256 * WQ, WQ == 2 ? 1 : (KT == 32 ? 3 : 2)) void attn_fwd_bf16_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 smem[AttnLds<HD, KT>::WIDE];
   const AttnPlan plan = attn_plan(a, 128 * WQ);
-  attn_body<HD, WQ>(a, plan, smem);
+  attn_body<HD, WQ, KT>(a, plan, smem);
 }
 
 // Combine split-KV partials: O = sum_s exp(lse_s - L) O_s with L = logsumexp_s lse_s.
@@ -680,23 +691,31 @@ hipError_t launch_attn(int dtype, const AttnArgs& a0, void* workspace, hipStream
   auto max_units = [&](int QT) {
     return (ceil_div((long long)a.max_rows * G, QT) + a.B - 1) * (long long)a.Hkv;
   };
-  const bool wide = G < 4 && !(may_split && max_units(128) < kShortUnits);
+  const bool short_sel = may_split && max_units(128) < kShortUnits;
+  const bool wide = G < 4 && !short_sel;
   const int QT = wide ? 256 : 128;
   // enough workgroups for every tile and for the split factor the device may
   // choose (split units fill at most one workgroup per CU)
   a.split_fill = device_cus();
   const int grid = (int)max_units(QT) + a.split_fill;
   const int threads = wide ? 512 : 256;
+  // Long GQA selections at head dim 128 take 32-key tiles and three
+  // workgroups per CU (same-process A/B on the lock loop, two rounds:
+  // attention stage 20.58 / 20.72 -> 20.46 / 20.44 ms per loop); short
+  // selections keep 64-key tiles (the lock loop's last step, 824 rows, took
+  // 51 -> 57 us with 32-key tiles).
   if (a.hd == 64) {
     if (wide)
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 2>), dim3(grid), dim3(threads), 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 2, 64>), dim3(grid), dim3(threads), 0, st, a);
     else
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 1>), dim3(grid), dim3(threads), 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 1, 64>), dim3(grid), dim3(threads), 0, st, a);
   } else {
     if (wide)
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 2>), dim3(grid), dim3(threads), 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 2, 64>), dim3(grid), dim3(threads), 0, st, a);
+    else if (short_sel)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 1, 64>), dim3(grid), dim3(threads), 0, st, a);
     else
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 1>), dim3(grid), dim3(threads), 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 1, 32>), dim3(grid), dim3(threads), 0, st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !may_split) return e;
