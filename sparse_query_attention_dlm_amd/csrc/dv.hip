@@ -383,10 +383,14 @@ hipError_t launch_dv_update(int dtype, const DvArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(dv_update_f32_kernel<128>, dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  // 256-vector workgroups once they still give two workgroups per CU
+  // 256-vector workgroups once they still give two workgroups per CU, unless
+  // 4 or more query heads share a KV head: then the salient rows' bytes per
+  // query are a quarter of MHA's and 128-vector workgroups (several per CU,
+  // from different position tiles) run faster (B = 8, S = 2048, 32 / 8 heads,
+  // 1024 salient rows per sequence: 252 -> 242 us, same-process A/B)
   const int G = a.Hq / a.Hkv;
   const long long wide_grid = ((long long)a.S * G + 255) / 256 * a.Hkv * a.B;
-  const bool wide = wide_grid >= 2LL * device_cus();
+  const bool wide = wide_grid >= 2LL * device_cus() && G < 4;
   const int QT = wide ? 256 : 128;
   const int grid = (int)(((long long)a.S * G + QT - 1) / QT * a.Hkv * a.B);
   const dim3 block(wide ? 512 : 256);

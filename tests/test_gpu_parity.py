@@ -967,10 +967,12 @@ def test_dv_update_gqa(dlm, Hq, Hkv):
 
 
 @pytest.mark.parametrize("hd", [64, 128])
-def test_dv_update_wide_workgroups(dlm, hd):
-    """Enough position tiles (B = 2, S = 2048, GQA 32/8) for the 256-vector
-    workgroups; salient sets of 300 and 777 rows (ragged last tiles)."""
-    run_dv_update(dlm, B=2, S=2048, Hq=32, Hkv=8, hd=hd, n_per_b=[300, 777], seed=37)
+@pytest.mark.parametrize("Hq,Hkv", [(32, 16), (32, 8)])
+def test_dv_update_many_position_tiles(dlm, hd, Hq, Hkv):
+    """Enough position tiles (B = 2, S = 2048) for two 256-vector workgroups
+    per CU: GQA 2:1 runs them, GQA 4:1 the 128-vector workgroups; salient sets
+    of 300 and 777 rows (ragged last tiles)."""
+    run_dv_update(dlm, B=2, S=2048, Hq=Hq, Hkv=Hkv, hd=hd, n_per_b=[300, 777], seed=37)
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4)])
