@@ -16,9 +16,9 @@
 //     which then run three workgroups per CU), K and V come in through buffer
 //     loads (one tile ahead, in registers) and are staged in LDS; every wave
 //     computes the transposed score tiles S^T = K . Q^T (32 keys x 32 queries
-//     each) with 32x32x16 MFMAs; Q^T stays in registers for the whole key loop.  The key mask is
-//     compiled only into the copy of the tile math that runs the split's
-//     partial last tile.
+//     each) with 32x32x16 MFMAs; Q^T stays in registers for the whole key
+//     loop.  The key mask is compiled only into the copy of the tile math that
+//     runs the split's partial last tile.
 //   * In that layout a lane holds 16 keys of one query, so the running max and
 //     sum are in-lane reductions plus one v_permlane32_swap with the lane that
 //     holds the other 16 keys of the same query.
@@ -212,7 +212,7 @@ __device__ __forceinline__ void attn_pv_block(const u16* sV, int kb0, const u32x
 }
 
 // QT = 128*WQ query vectors per workgroup of 4*WQ waves (wave w owns vectors
-// 32w..32w+31) share every 64-key tile of the split: each tile is read from
+// 32w..32w+31) share every KT-key tile of the split: each tile is read from
 // L2 once per QT vectors, so WQ = 2 halves the K/V bytes a CU pulls per flop.
 template <int HD, int WQ, int KT>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const AttnPlan& plan, u16* smem) {
