@@ -467,13 +467,16 @@ def test_attention_two_key_splits(dlm):
 
 
 @pytest.mark.parametrize("rows_per_b", [[40, 17], [2048, 1900]])
-def test_attention_rescale_on_late_large_scores(dlm, rows_per_b):
+@pytest.mark.parametrize("Hq,Hkv", [(8, 4), (32, 8)])
+def test_attention_rescale_on_late_large_scores(dlm, rows_per_b, Hq, Hkv):
     """Keys far above every earlier score appear after the first tiles (and in
     a later split): the running reference must move mid-sequence (a lane's
     tile sum of probabilities against the old reference would pass 2^64).
-    Short selections take the split-KV path, long ones the unsplit wide
-    tiles; outputs and LSE against the oracle."""
-    run_attention_plan(dlm, B=2, S=2048, Hq=8, Hkv=4, hd=128, rows_per_b=rows_per_b, sample=64,
+    The 57-row selections split their keys; GQA 2:1 at 3,948 rows stays on
+    the 64-key tiles unsplit (a short row bound: 252 tiles), GQA 4:1 at 3,948
+    rows takes the 32-key tiles (1,000 tiles); outputs and LSE against the
+    oracle."""
+    run_attention_plan(dlm, B=2, S=2048, Hq=Hq, Hkv=Hkv, hd=128, rows_per_b=rows_per_b, sample=64,
                        late_keys=[700, 701, 1500, 2040])
 
 
